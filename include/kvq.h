@@ -1,0 +1,179 @@
+/*
+ * kvq.h -- C ABI of libkvq, the MI355X (gfx950) KV-cache quantization library.
+ *
+ * Three schemes, each a quantize -> bit-pack -> unpack -> dequantize path over
+ * fp16 key/value tensors already resident in device memory:
+ *   - symmetric per-(token, head) q8 / q6 / q4 on paged storage
+ *     [MTPLX pull request #267, "feat(kv-cache): add q6 paged KV quantization",
+ *      PR description];
+ *   - KIVI asymmetric min/max group round trip
+ *     ["veloxquant_mlx.cache.kivi_cache" module source, KIVIKVCache];
+ *   - KVQuant-style non-uniform quantization with dense-and-sparse outliers and
+ *     attention-sink tokens ["veloxquant_mlx.cache.kvquant_cache module"].
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE memory owned by the caller unless marked [host]. The
+ *     library allocates nothing on these paths and keeps no device state.
+ *   - fp16 data is passed as uint16_t bit patterns (IEEE binary16).
+ *   - `stream` is a hipStream_t passed as void*; NULL is the null stream. Work
+ *     is enqueued on it; no entry point synchronises.
+ *   - All validation happens on the host before any HIP call: a bad argument
+ *     returns a kvq_status != KVQ_OK and enqueues nothing. Device-side data
+ *     that the host cannot see (slot mappings, block tables, sequence lengths)
+ *     is range-checked inside the kernels: out-of-range entries are skipped as
+ *     documented per call, never dereferenced.
+ *   - kvq_last_error() returns a thread-local description of the last failure.
+ *   - There is no fallback path: if the GPU code cannot run, the call fails
+ *     with KVQ_ERR_HIP.
+ *   - Base pointers of fp16 and code buffers must be 16-byte aligned
+ *     (KVQ_ERR_ALIGN otherwise); fp32/int32 buffers 4-byte aligned.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvq_status {
+  KVQ_OK = 0,
+  KVQ_ERR_NULL = 1,     /* a required pointer is NULL */
+  KVQ_ERR_BITS = 2,     /* bit width not in the scheme's table */
+  KVQ_ERR_SHAPE = 3,    /* sizes inconsistent or out of range */
+  KVQ_ERR_ALIGN = 4,    /* pointer not aligned as required */
+  KVQ_ERR_CAPACITY = 5, /* an output or workspace is too small */
+  KVQ_ERR_HIP = 6,      /* the HIP runtime reported an error (text in kvq_last_error) */
+  KVQ_ERR_MODE = 7,     /* unknown or rejected mode string */
+  KVQ_ERR_ARG = 8       /* other invalid scalar argument */
+} kvq_status;
+
+/* [host] Thread-local text of the most recent failure on this thread ("" if none). */
+const char *kvq_last_error(void);
+
+/* [host] Library version string. */
+const char *kvq_version(void);
+
+/* ------------------------------------------------------------------ symmetric
+ * [MTPLX PR #267, PR description] One symmetric quantizer per (token, KV head)
+ * row of head_dim values with one fp16 scale. qmax is an explicit table
+ * {8: 127, 6: 31, 4: 7}; any other width is rejected, never mapped to a
+ * neighbour. q6 codes are biased by +32 into 6-bit fields packed four per
+ * three bytes, little-endian, per the page's byte equations; q4 codes are
+ * biased by +8, two per byte, even element in the low nibble; q8 codes are
+ * int8 two's complement, one per byte.
+ *
+ * Per row x[0..D): a = max|x_i|; scale = fp16(a / qmax) (binary32 division,
+ * round-to-nearest-even); s = float(scale); q_i = 0 when s == 0, else
+ * clamp(rint(x_i * (1/s)), -qmax, qmax) with 1/s and the product in binary32
+ * and rint ties-to-even. Dequantization: x_i' = fp16(q_i * s).
+ */
+
+/* [host] Parse a mode name. Accepts "q8", "q6", "q4", "8", "6", "4", and the
+ * q6 aliases "6bit", "int6", "uint6"; case-sensitive. Rejects everything
+ * else, including "q6_k" and "q6_0" (a different format), with KVQ_ERR_MODE.
+ * *bits receives 8, 6 or 4.
+ * [MTPLX PR #267, PR description: q6 aliases kept narrow, q6_k/q6_0 rejected] */
+int kvq_parse_mode(const char *mode, int32_t *bits);
+
+/* [host] qmax for a width: 127, 31, 7; -1 for any other width. */
+int32_t kvq_sym_qmax(int32_t bits);
+
+/* [host] Bytes of packed codes per row: D*bits/8. -1 if bits is not 8/6/4,
+ * D <= 0, q6 with D % 4 != 0, or q4 with odd D. [MTPLX PR #267: packed_dim] */
+int64_t kvq_packed_dim(int32_t head_dim, int32_t bits);
+
+/* [host] Bytes of a K+V cache of `tokens` tokens: 2 * tokens * layers *
+ * kv_heads * (packed_dim + 2) (codes + one fp16 scale per row); bits == 16
+ * gives the unquantised fp16 size. -1 on invalid widths/shapes.
+ * [MTPLX PR #267, PR description: storage arithmetic] */
+int64_t kvq_sym_cache_bytes(int64_t tokens, int32_t layers, int32_t kv_heads, int32_t head_dim,
+                            int32_t bits);
+
+/* Geometry of a paged symmetric pool. One pool holds `layers` layers; each
+ * layer has num_pages pages of page_size token slots. Codes of layer l are
+ * uint8 [num_pages][page_size][kv_heads][packed_dim] starting at
+ * codes + l * num_pages*page_size*kv_heads*packed_dim; scales (fp16) are
+ * [num_pages][page_size][kv_heads] per layer. K and V use two pools of the
+ * same geometry. */
+typedef struct kvq_paged_layout {
+  int32_t layers;
+  int32_t num_pages;
+  int32_t page_size;
+  int32_t kv_heads;
+  int32_t head_dim;
+  int32_t bits; /* 8, 6 or 4 */
+} kvq_paged_layout;
+
+/* Quantize and pack tokens into the paged pools (write path).
+ *   k, v         fp16 [n_layers][n_tokens][kv_heads][head_dim], contiguous;
+ *                layer i of the input goes to pool layer layer0 + i.
+ *   slot_mapping int32 [n_tokens]: global slot page*page_size + slot of each
+ *                token (same for every layer). A negative entry, or one >=
+ *                num_pages*page_size, leaves that token unwritten.
+ *   k_codes/k_scales, v_codes/v_scales: the pools (updated in place).
+ * Either side may be skipped by passing NULL for its input AND both of its
+ * pool pointers. n_tokens == 0 or n_layers == 0 is a no-op.
+ * Errors: KVQ_ERR_NULL, KVQ_ERR_BITS, KVQ_ERR_SHAPE (layer range outside the
+ * pool, bad geometry), KVQ_ERR_ALIGN, KVQ_ERR_HIP. */
+int kvq_quant_sym(const kvq_paged_layout *layout, const uint16_t *k, const uint16_t *v,
+                  int32_t layer0, int32_t n_layers, int32_t n_tokens,
+                  const int32_t *slot_mapping, uint8_t *k_codes, uint16_t *k_scales,
+                  uint8_t *v_codes, uint16_t *v_scales, void *stream);
+
+/* Unpack and dequantize sequences out of the paged pools (read path).
+ *   block_table  int32 [n_seqs][max_blocks]: page id of each block of each sequence.
+ *   seq_lens     int32 [n_seqs]: tokens held by each sequence.
+ *   k_out, v_out fp16 [n_layers][n_seqs][max_len][kv_heads][head_dim].
+ * Position p of sequence s reads page block_table[s][p / page_size], slot
+ * p % page_size. Rows at p >= seq_lens[s], p >= max_blocks*page_size, or whose
+ * page id is outside [0, num_pages), are written as +0.
+ * Either side may be skipped by passing NULL for its pool pointers AND output.
+ * Errors: as kvq_quant_sym. */
+int kvq_dequant_sym(const kvq_paged_layout *layout, const uint8_t *k_codes,
+                    const uint16_t *k_scales, const uint8_t *v_codes, const uint16_t *v_scales,
+                    int32_t layer0, int32_t n_layers, const int32_t *block_table,
+                    int32_t max_blocks, const int32_t *seq_lens, int32_t n_seqs, int32_t max_len,
+                    uint16_t *k_out, uint16_t *v_out, void *stream);
+
+/* ------------------------------------------------------------------ KIVI
+ * ["veloxquant_mlx.cache.kivi_cache", KIVIKVCache._quant_dequant_along]
+ * Asymmetric min/max round trip in binary32: for each group,
+ * levels = 2^bits - 1, scale = max((max - min)/levels, eps),
+ * code = clamp(rint((x - min)/scale), 0, levels) (IEEE division, ties to
+ * even), x' = fp16(code*scale + min) (product then sum, not fused).
+ * Keys are grouped per channel along tokens (groups of group_size tokens
+ * starting at lo); values per token along channels (groups of group_size
+ * channels starting at channel 0). A last group shorter than group_size is
+ * its own group (equivalent to the page's edge-replicating pad). */
+
+/* [host] Quantization frontier: max(0, offset - residual_length) rounded down
+ * to a multiple of group_size ["kivi_cache", _quantization_boundary].
+ * -1 if group_size <= 0 or residual_length < 0 or offset < 0. */
+int64_t kvq_kivi_boundary(int64_t offset, int32_t residual_length, int32_t group_size);
+
+/* In-place KIVI round trip of tokens [lo, hi) of keys and values.
+ *   keys, values fp16 [B][H][S_cap][D] (batch and layers folded into B);
+ *                tokens outside [lo, hi) are not touched. Either may be NULL
+ *                to skip that side (its optional outputs must then be NULL).
+ *   bits         2, 4 or 8.  group_size >= 1.  eps > 0 (the page uses 1e-8).
+ *   Optional outputs (NULL to skip; each side independently):
+ *     *_codes    uint8 [B][H][hi-lo][D*bits/8], codes packed LSB-first along D
+ *                (requires D*bits % 8 == 0);
+ *     k_scale/k_min fp32 [B][H][ceil((hi-lo)/group_size)][D];
+ *     v_scale/v_min fp32 [B][H][hi-lo][ceil(D/group_size)].
+ *   Codes, scale and min reproduce the written fp16 values exactly.
+ * hi == lo is a no-op. Errors: KVQ_ERR_NULL, KVQ_ERR_BITS, KVQ_ERR_SHAPE,
+ * KVQ_ERR_ARG (eps), KVQ_ERR_ALIGN, KVQ_ERR_HIP. */
+int kvq_kivi_quant_dequant(uint16_t *keys, uint16_t *values, int32_t B, int32_t H, int32_t S_cap,
+                           int32_t D, int32_t lo, int32_t hi, int32_t bits, int32_t group_size,
+                           float eps, uint8_t *k_codes, float *k_scale, float *k_min,
+                           uint8_t *v_codes, float *v_scale, float *v_min, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

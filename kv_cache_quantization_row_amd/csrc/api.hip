@@ -1,0 +1,277 @@
+// C-ABI entry points of libkvq: host-side validation, then kernel launch on
+// the caller's stream. Declarations and argument documentation: include/kvq.h.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/kvq.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return KVQ_OK;
+}
+
+int hip_status(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int32_t qmax_of(int32_t bits) {
+  switch (bits) {  // explicit table; unknown widths are not mapped to a neighbour
+    case 8: return 127;
+    case 6: return 31;
+    case 4: return 7;
+    default: return -1;
+  }
+}
+
+int64_t packed(int32_t D, int32_t bits) {
+  if (D <= 0 || qmax_of(bits) < 0) return -1;
+  if (bits == 6 && D % 4) return -1;
+  if (bits == 4 && D % 2) return -1;
+  return (int64_t)D * bits / 8;
+}
+
+int h_shift_of(int32_t H) {
+  if (H <= 0 || (H & (H - 1))) return -1;
+  int s = 0;
+  while ((1 << s) < H) ++s;
+  return s;
+}
+
+int check_layout(const kvq_paged_layout *L) {
+  if (!L) return fail(KVQ_ERR_NULL, "layout is NULL");
+  if (qmax_of(L->bits) < 0) return fail(KVQ_ERR_BITS, "bits=%d is not one of 8, 6, 4", L->bits);
+  if (packed(L->head_dim, L->bits) < 0)
+    return fail(KVQ_ERR_SHAPE, "head_dim=%d is not valid for q%d (q6 needs D%%4==0, q4 even D)",
+                L->head_dim, L->bits);
+  if (L->layers <= 0 || L->num_pages <= 0 || L->page_size <= 0 || L->kv_heads <= 0)
+    return fail(KVQ_ERR_SHAPE, "layout sizes must be positive (layers=%d pages=%d page_size=%d heads=%d)",
+                L->layers, L->num_pages, L->page_size, L->kv_heads);
+  const int64_t slots = (int64_t)L->num_pages * L->page_size;
+  if (slots * L->kv_heads >= ((int64_t)1 << 40))
+    return fail(KVQ_ERR_SHAPE, "pool too large");
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kvq_last_error(void) { return g_err.c_str(); }
+
+const char *kvq_version(void) { return "kvq 0.1 gfx950"; }
+
+int kvq_parse_mode(const char *mode, int32_t *bits) {
+  if (!mode || !bits) return fail(KVQ_ERR_NULL, "mode or bits is NULL");
+  static const struct {
+    const char *name;
+    int32_t bits;
+  } table[] = {{"q8", 8}, {"8", 8}, {"q6", 6}, {"6", 6}, {"6bit", 6}, {"int6", 6},
+               {"uint6", 6}, {"q4", 4}, {"4", 4}};
+  for (const auto &e : table)
+    if (std::strcmp(mode, e.name) == 0) {
+      *bits = e.bits;
+      return ok();
+    }
+  return fail(KVQ_ERR_MODE, "unknown KV quantization mode '%s'", mode);
+}
+
+int32_t kvq_sym_qmax(int32_t bits) { return qmax_of(bits); }
+
+int64_t kvq_packed_dim(int32_t head_dim, int32_t bits) { return packed(head_dim, bits); }
+
+int64_t kvq_sym_cache_bytes(int64_t tokens, int32_t layers, int32_t kv_heads, int32_t head_dim,
+                            int32_t bits) {
+  if (tokens < 0 || layers <= 0 || kv_heads <= 0 || head_dim <= 0) return -1;
+  int64_t row;
+  if (bits == 16) {
+    row = 2 * (int64_t)head_dim;
+  } else {
+    const int64_t pd = packed(head_dim, bits);
+    if (pd < 0) return -1;
+    row = pd + 2;
+  }
+  return 2 * tokens * layers * kv_heads * row;
+}
+
+int kvq_quant_sym(const kvq_paged_layout *layout, const uint16_t *k, const uint16_t *v,
+                  int32_t layer0, int32_t n_layers, int32_t n_tokens,
+                  const int32_t *slot_mapping, uint8_t *k_codes, uint16_t *k_scales,
+                  uint8_t *v_codes, uint16_t *v_scales, void *stream) {
+  int rc = check_layout(layout);
+  if (rc) return rc;
+  const kvq_paged_layout &L = *layout;
+  if (n_tokens < 0 || n_layers < 0) return fail(KVQ_ERR_SHAPE, "negative n_tokens/n_layers");
+  if (layer0 < 0 || (int64_t)layer0 + n_layers > L.layers)
+    return fail(KVQ_ERR_SHAPE, "layers [%d, %d) outside the pool's %d layers", layer0,
+                layer0 + n_layers, L.layers);
+  const bool do_k = k || k_codes || k_scales, do_v = v || v_codes || v_scales;
+  if (do_k && (!k || !k_codes || !k_scales))
+    return fail(KVQ_ERR_NULL, "K side needs k, k_codes and k_scales together");
+  if (do_v && (!v || !v_codes || !v_scales))
+    return fail(KVQ_ERR_NULL, "V side needs v, v_codes and v_scales together");
+  if (!do_k && !do_v) return fail(KVQ_ERR_NULL, "neither K nor V given");
+  if (n_tokens == 0 || n_layers == 0) return ok();
+  if (!slot_mapping) return fail(KVQ_ERR_NULL, "slot_mapping is NULL");
+  const int64_t rows = (int64_t)n_tokens * L.kv_heads;
+  if (rows >= ((int64_t)1 << 31)) return fail(KVQ_ERR_SHAPE, "n_tokens*kv_heads must be < 2^31");
+  if (n_layers > 65535) return fail(KVQ_ERR_SHAPE, "at most 65535 layers per call");
+  for (const void *p : {(const void *)k, (const void *)v, (const void *)k_codes, (const void *)v_codes})
+    if (p && !aligned(p, 16)) return fail(KVQ_ERR_ALIGN, "fp16 input and code pools need 16-byte alignment");
+  for (const void *p : {(const void *)k_scales, (const void *)v_scales})
+    if (p && !aligned(p, 2)) return fail(KVQ_ERR_ALIGN, "scales need 2-byte alignment");
+  if (!aligned(slot_mapping, 4)) return fail(KVQ_ERR_ALIGN, "slot_mapping needs 4-byte alignment");
+
+  const int64_t pd = packed(L.head_dim, L.bits);
+  const int64_t slots = (int64_t)L.num_pages * L.page_size;
+  kvq::SymQuantArgs a{};
+  a.k = do_k ? k : nullptr;
+  a.v = do_v ? v : nullptr;
+  a.k_codes = k_codes;
+  a.v_codes = v_codes;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  a.slot_mapping = slot_mapping;
+  a.n_slots = slots;
+  a.code_layer_stride = slots * L.kv_heads * pd;
+  a.scale_layer_stride = slots * L.kv_heads;
+  a.rows_per_layer = (uint32_t)rows;
+  a.layer0 = layer0;
+  a.H = L.kv_heads;
+  a.D = L.head_dim;
+  a.h_shift = h_shift_of(L.kv_heads);
+  return hip_status(kvq::launch_sym_quant(a, L.bits, n_layers, (hipStream_t)stream), "kvq_quant_sym launch");
+}
+
+int kvq_dequant_sym(const kvq_paged_layout *layout, const uint8_t *k_codes,
+                    const uint16_t *k_scales, const uint8_t *v_codes, const uint16_t *v_scales,
+                    int32_t layer0, int32_t n_layers, const int32_t *block_table,
+                    int32_t max_blocks, const int32_t *seq_lens, int32_t n_seqs, int32_t max_len,
+                    uint16_t *k_out, uint16_t *v_out, void *stream) {
+  int rc = check_layout(layout);
+  if (rc) return rc;
+  const kvq_paged_layout &L = *layout;
+  if (n_seqs < 0 || n_layers < 0 || max_len < 0 || max_blocks < 0)
+    return fail(KVQ_ERR_SHAPE, "negative size");
+  if (layer0 < 0 || (int64_t)layer0 + n_layers > L.layers)
+    return fail(KVQ_ERR_SHAPE, "layers [%d, %d) outside the pool's %d layers", layer0,
+                layer0 + n_layers, L.layers);
+  const bool do_k = k_out || k_codes || k_scales, do_v = v_out || v_codes || v_scales;
+  if (do_k && (!k_out || !k_codes || !k_scales))
+    return fail(KVQ_ERR_NULL, "K side needs k_codes, k_scales and k_out together");
+  if (do_v && (!v_out || !v_codes || !v_scales))
+    return fail(KVQ_ERR_NULL, "V side needs v_codes, v_scales and v_out together");
+  if (!do_k && !do_v) return fail(KVQ_ERR_NULL, "neither K nor V given");
+  if (n_seqs == 0 || n_layers == 0 || max_len == 0) return ok();
+  if (!block_table || !seq_lens) return fail(KVQ_ERR_NULL, "block_table or seq_lens is NULL");
+  if (max_blocks == 0) return fail(KVQ_ERR_SHAPE, "max_blocks must be positive");
+  if ((int64_t)max_len * L.kv_heads >= ((int64_t)1 << 31))
+    return fail(KVQ_ERR_SHAPE, "max_len*kv_heads must be < 2^31");
+  if (n_seqs > 65535 || 2 * (int64_t)n_layers > 65535)
+    return fail(KVQ_ERR_SHAPE, "at most 65535 sequences and 32767 layers per call");
+  for (const void *p : {(const void *)k_out, (const void *)v_out, (const void *)k_codes, (const void *)v_codes})
+    if (p && !aligned(p, 16)) return fail(KVQ_ERR_ALIGN, "fp16 output and code pools need 16-byte alignment");
+  for (const void *p : {(const void *)k_scales, (const void *)v_scales})
+    if (p && !aligned(p, 2)) return fail(KVQ_ERR_ALIGN, "scales need 2-byte alignment");
+  if (!aligned(block_table, 4) || !aligned(seq_lens, 4))
+    return fail(KVQ_ERR_ALIGN, "block_table/seq_lens need 4-byte alignment");
+
+  const int64_t pd = packed(L.head_dim, L.bits);
+  const int64_t slots = (int64_t)L.num_pages * L.page_size;
+  kvq::SymDequantArgs a{};
+  a.k_codes = do_k ? k_codes : nullptr;
+  a.v_codes = do_v ? v_codes : nullptr;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  a.k_out = do_k ? k_out : nullptr;
+  a.v_out = do_v ? v_out : nullptr;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.code_layer_stride = slots * L.kv_heads * pd;
+  a.scale_layer_stride = slots * L.kv_heads;
+  a.layer0 = layer0;
+  a.H = L.kv_heads;
+  a.D = L.head_dim;
+  a.h_shift = h_shift_of(L.kv_heads);
+  a.num_pages = L.num_pages;
+  a.page_size = L.page_size;
+  a.max_blocks = max_blocks;
+  a.n_seqs = n_seqs;
+  a.max_len = max_len;
+  return hip_status(kvq::launch_sym_dequant(a, L.bits, n_layers, (hipStream_t)stream),
+                    "kvq_dequant_sym launch");
+}
+
+int64_t kvq_kivi_boundary(int64_t offset, int32_t residual_length, int32_t group_size) {
+  if (group_size <= 0 || residual_length < 0 || offset < 0) return -1;
+  int64_t aged = offset - residual_length;
+  if (aged < 0) aged = 0;
+  return (aged / group_size) * group_size;
+}
+
+int kvq_kivi_quant_dequant(uint16_t *keys, uint16_t *values, int32_t B, int32_t H, int32_t S_cap,
+                           int32_t D, int32_t lo, int32_t hi, int32_t bits, int32_t group_size,
+                           float eps, uint8_t *k_codes, float *k_scale, float *k_min,
+                           uint8_t *v_codes, float *v_scale, float *v_min, void *stream) {
+  if (!keys && !values) return fail(KVQ_ERR_NULL, "neither keys nor values given");
+  if (!keys && (k_codes || k_scale || k_min))
+    return fail(KVQ_ERR_NULL, "key outputs given without keys");
+  if (!values && (v_codes || v_scale || v_min))
+    return fail(KVQ_ERR_NULL, "value outputs given without values");
+  if (bits != 2 && bits != 4 && bits != 8) return fail(KVQ_ERR_BITS, "bits=%d is not one of 2, 4, 8", bits);
+  if (B < 0 || H < 0 || S_cap < 0 || D <= 0) return fail(KVQ_ERR_SHAPE, "bad B/H/S_cap/D");
+  if (lo < 0 || hi < lo || hi > S_cap) return fail(KVQ_ERR_SHAPE, "need 0 <= lo <= hi <= S_cap");
+  if (group_size <= 0) return fail(KVQ_ERR_SHAPE, "group_size must be positive");
+  if (!(eps > 0.0f) || !(eps < 3.0e38f)) return fail(KVQ_ERR_ARG, "eps must be positive and finite");
+  if ((k_codes || v_codes) && (D % 8 || group_size % 8))
+    return fail(KVQ_ERR_SHAPE, "packed code output needs D %% 8 == 0 and group_size %% 8 == 0");
+  for (const void *p : {(const void *)keys, (const void *)values, (const void *)k_codes, (const void *)v_codes})
+    if (p && !aligned(p, 16)) return fail(KVQ_ERR_ALIGN, "fp16 tensors and code buffers need 16-byte alignment");
+  for (const void *p : {(const void *)k_scale, (const void *)k_min, (const void *)v_scale, (const void *)v_min})
+    if (p && !aligned(p, 4)) return fail(KVQ_ERR_ALIGN, "scale/min buffers need 4-byte alignment");
+  const int64_t BH = (int64_t)B * H;
+  if (hi == lo || BH == 0) return ok();
+  const int64_t n = hi - lo;
+  if (BH * n * D >= ((int64_t)1 << 46)) return fail(KVQ_ERR_SHAPE, "tensor too large");
+  if ((BH * n + 255) / 256 * 64 >= ((int64_t)1 << 31)) return fail(KVQ_ERR_SHAPE, "too many rows");
+  kvq::KiviArgs a{};
+  a.keys = keys;
+  a.values = values;
+  a.k_codes = k_codes;
+  a.v_codes = v_codes;
+  a.k_scale = k_scale;
+  a.k_min = k_min;
+  a.v_scale = v_scale;
+  a.v_min = v_min;
+  a.BH = BH;
+  a.S_cap = S_cap;
+  a.D = D;
+  a.lo = lo;
+  a.hi = hi;
+  a.bits = bits;
+  a.gs = group_size;
+  a.eps = eps;
+  return hip_status(kvq::launch_kivi(a, (hipStream_t)stream), "kvq_kivi_quant_dequant launch");
+}
+
+}  // extern "C"

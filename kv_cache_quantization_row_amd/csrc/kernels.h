@@ -1,0 +1,46 @@
+// Internal launch interface between the C-ABI layer (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+struct SymQuantArgs {
+  const uint16_t *k, *v;           // fp16 [n_layers][n_tokens][H][D]
+  uint8_t *k_codes, *v_codes;      // pools
+  uint16_t *k_scales, *v_scales;
+  const int32_t *slot_mapping;     // [n_tokens]
+  int64_t n_slots;                 // num_pages * page_size
+  int64_t code_layer_stride;       // bytes per pool layer
+  int64_t scale_layer_stride;      // scales per pool layer
+  uint32_t rows_per_layer;         // n_tokens * H
+  int32_t layer0, H, D, h_shift;   // h_shift = log2(H) when H is a power of two, else -1
+};
+
+struct SymDequantArgs {
+  const uint8_t *k_codes, *v_codes;
+  const uint16_t *k_scales, *v_scales;
+  uint16_t *k_out, *v_out;         // fp16 [n_layers][n_seqs][max_len][H][D]
+  const int32_t *block_table;      // [n_seqs][max_blocks]
+  const int32_t *seq_lens;         // [n_seqs]
+  int64_t code_layer_stride, scale_layer_stride;
+  int32_t layer0, H, D, h_shift;
+  int32_t num_pages, page_size, max_blocks, n_seqs, max_len;
+};
+
+hipError_t launch_sym_quant(const SymQuantArgs &a, int bits, int n_layers, hipStream_t st);
+hipError_t launch_sym_dequant(const SymDequantArgs &a, int bits, int n_layers, hipStream_t st);
+
+struct KiviArgs {
+  uint16_t *keys, *values;         // fp16 [B][H][S_cap][D], in place on [lo, hi)
+  uint8_t *k_codes, *v_codes;      // optional
+  float *k_scale, *k_min, *v_scale, *v_min;
+  int64_t BH;
+  int32_t S_cap, D, lo, hi, bits, gs;
+  float eps;
+};
+
+hipError_t launch_kivi(const KiviArgs &a, hipStream_t st);
+
+}  // namespace kvq

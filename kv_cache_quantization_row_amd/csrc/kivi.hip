@@ -1,0 +1,441 @@
+// KIVI asymmetric min/max group round trip, in place on fp16 [BH][S_cap][D].
+//
+// ["veloxquant_mlx.cache.kivi_cache" module source, KIVIKVCache and its
+//  _quant_dequant_along] keys are grouped per channel along tokens, values
+// per token along channels; per group in binary32: levels = 2^b - 1,
+// scale = max((max - min)/levels, eps), code = clip(round_half_even((x -
+// min)/scale), 0, levels), recon = code*scale + min (product, then sum),
+// stored back as fp16. Only tokens [lo, hi) are touched; key groups start at
+// lo. A short last group is its own group.
+//
+// Layout on the GPU (fast paths; D/8 a power of two dividing 64):
+//  keys   one wave per (bh, group of gs tokens): the gs x D tile is read with
+//         16-byte loads, lane l holding channels 8*(l % CL).. of tokens
+//         l / CL + TPI*j (CL = D/8 lanes per token row, TPI = 64/CL rows per
+//         load). Per-channel min/max reduce first over the lane's own tokens,
+//         then across the lanes that share l % CL (DPP rotate for 8, lane
+//         shuffles for 16/32).
+//  values lane l holds channels 8*(l % CL).. of token row l / CL; a group of
+//         gs channels is gs/8 consecutive lanes, reduced with DPP.
+// Other shapes use one-thread-per-(vector, group) generic kernels.
+#include "common.h"
+#include "kernels.h"
+
+namespace kvq {
+
+// One element: returns the fp16 reconstruction, writes the integer code.
+__device__ __forceinline__ uint16_t kivi_elem(float x, float mn, float scale, float levels,
+                                              uint32_t &code) {
+  const float t = (x - mn) / scale;  // IEEE division, as the page computes it
+  const float c = __builtin_amdgcn_fmed3f(__builtin_rintf(t), 0.0f, levels);
+  code = (uint32_t)c;
+  const float prod = c * scale;
+  return f2h(prod + mn);
+}
+
+__device__ __forceinline__ float kivi_scale(float mn, float mx, float levels, float eps) {
+  const float s = (mx - mn) / levels;
+  return fmaxf(s, eps);
+}
+
+// Pack 8 codes of `bits` bits LSB-first into the low 8*bits bits.
+template <int BITS>
+__device__ __forceinline__ uint64_t pack8(const uint32_t *c) {
+  uint64_t v = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v |= (uint64_t)c[i] << (BITS * i);
+  return v;
+}
+
+template <int BITS>
+__device__ __forceinline__ void store_codes8(uint8_t *dst, const uint32_t *c) {
+  const uint64_t v = pack8<BITS>(c);
+  if constexpr (BITS == 2) *reinterpret_cast<uint16_t *>(dst) = (uint16_t)v;
+  else if constexpr (BITS == 4) *reinterpret_cast<uint32_t *>(dst) = (uint32_t)v;
+  else *reinterpret_cast<uint64_t *>(dst) = v;
+}
+
+// ------------------------------------------------------------------ keys
+template <int BITS, int CL, int NI>
+__global__ __launch_bounds__(256) void kivi_keys_fast(KiviArgs a) {
+  constexpr int TPI = 64 / CL;  // token rows per load instruction
+  constexpr float LEV = (float)((1 << BITS) - 1);
+  const int D = CL * 8;
+  const int n = a.hi - a.lo;
+  const int ng = (n + a.gs - 1) / a.gs;
+  const int lane = threadIdx.x & 63;
+  const int64_t tile = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (tile >= a.BH * ng) return;  // wave-uniform
+  const int64_t bh = tile / ng;
+  const int g = (int)(tile - bh * ng);
+  const int t0 = a.lo + g * a.gs;
+  const int cnt = min(a.gs, a.hi - t0);
+  const int ch = lane % CL, tr = lane / CL;
+  uint16_t *base = a.keys + ((size_t)bh * a.S_cap + t0) * D + ch * 8;
+
+  uint4 v[NI];
+  bool ok[NI];
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int t = tr + TPI * j;
+    ok[j] = t < cnt;
+    v[j] = ok[j] ? *reinterpret_cast<const uint4 *>(base + (size_t)t * D) : make_uint4(0, 0, 0, 0);
+  }
+  float mn[8], mx[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    mn[i] = __builtin_inff();
+    mx[i] = -__builtin_inff();
+  }
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    if (!ok[j]) continue;
+    const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = lo_h2f(w[i]), hi = hi_h2f(w[i]);
+      mn[2 * i] = fminf(mn[2 * i], lo);
+      mx[2 * i] = fmaxf(mx[2 * i], lo);
+      mn[2 * i + 1] = fminf(mn[2 * i + 1], hi);
+      mx[2 * i + 1] = fmaxf(mx[2 * i + 1], hi);
+    }
+  }
+  // reduce across the lanes holding the same channels (lane bits >= log2(CL))
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if constexpr (CL <= 8) {
+      mn[i] = fminf(mn[i], dppf<DPP_ROR8>(mn[i]));
+      mx[i] = fmaxf(mx[i], dppf<DPP_ROR8>(mx[i]));
+    }
+    if constexpr (CL <= 16) {
+      mn[i] = fminf(mn[i], __shfl_xor(mn[i], 16));
+      mx[i] = fmaxf(mx[i], __shfl_xor(mx[i], 16));
+    }
+    if constexpr (CL <= 32) {
+      mn[i] = fminf(mn[i], __shfl_xor(mn[i], 32));
+      mx[i] = fmaxf(mx[i], __shfl_xor(mx[i], 32));
+    }
+  }
+  if constexpr (CL <= 4) {  // rows of 4 channel-lanes: also reduce across lane bits 2..3
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (CL <= 4) {
+        mn[i] = fminf(mn[i], dppf<0x124>(mn[i]));  // row_ror:4
+        mx[i] = fmaxf(mx[i], dppf<0x124>(mx[i]));
+      }
+      if constexpr (CL <= 2) {
+        mn[i] = fminf(mn[i], dppf<0x122>(mn[i]));  // row_ror:2
+        mx[i] = fmaxf(mx[i], dppf<0x122>(mx[i]));
+      }
+      if constexpr (CL <= 1) {
+        mn[i] = fminf(mn[i], dppf<0x121>(mn[i]));  // row_ror:1
+        mx[i] = fmaxf(mx[i], dppf<0x121>(mx[i]));
+      }
+    }
+  }
+  float sc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sc[i] = kivi_scale(mn[i], mx[i], LEV, a.eps);
+
+  const int64_t nrow0 = bh * n + (t0 - a.lo);  // row of token t0 in the [BH][n] code layout
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    if (!ok[j]) continue;
+    const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+    uint32_t o[4], c[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint16_t r0 = kivi_elem(lo_h2f(w[i]), mn[2 * i], sc[2 * i], LEV, c[2 * i]);
+      const uint16_t r1 = kivi_elem(hi_h2f(w[i]), mn[2 * i + 1], sc[2 * i + 1], LEV, c[2 * i + 1]);
+      o[i] = (uint32_t)r0 | ((uint32_t)r1 << 16);
+    }
+    const int t = tr + TPI * j;
+    *reinterpret_cast<uint4 *>(base + (size_t)t * D) = make_uint4(o[0], o[1], o[2], o[3]);
+    if (a.k_codes)
+      store_codes8<BITS>(a.k_codes + (size_t)(nrow0 + t) * (D * BITS / 8) + ch * BITS, c);
+  }
+  if (tr == 0) {
+    const size_t p = ((size_t)bh * ng + g) * D + ch * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (a.k_scale) a.k_scale[p + i] = sc[i];
+      if (a.k_min) a.k_min[p + i] = mn[i] + 0.0f;
+    }
+  }
+}
+
+// generic keys: one thread per (bh, group, chunk of C channels); C = 8 when
+// D % 8 == 0 (then the chunk's codes are whole bytes), else 1 (no codes).
+template <int C>
+__global__ __launch_bounds__(256) void kivi_keys_generic(KiviArgs a) {
+  const int D = a.D;
+  const int nch = D / C;
+  const int n = a.hi - a.lo;
+  const int ng = (n + a.gs - 1) / a.gs;
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= a.BH * ng * nch) return;
+  const int ck = (int)(id % nch);
+  const int64_t tg = id / nch;
+  const int g = (int)(tg % ng);
+  const int64_t bh = tg / ng;
+  const int t0 = a.lo + g * a.gs, t1 = min(t0 + a.gs, a.hi);
+  const float lev = (float)((1 << a.bits) - 1);
+  uint16_t *col = a.keys + (size_t)bh * a.S_cap * D + ck * C;
+  float mn[C], mx[C], sc[C];
+  for (int i = 0; i < C; ++i) {
+    mn[i] = __builtin_inff();
+    mx[i] = -__builtin_inff();
+  }
+  for (int t = t0; t < t1; ++t)
+    for (int i = 0; i < C; ++i) {
+      const float x = h2f(col[(size_t)t * D + i]);
+      mn[i] = fminf(mn[i], x);
+      mx[i] = fmaxf(mx[i], x);
+    }
+  for (int i = 0; i < C; ++i) sc[i] = kivi_scale(mn[i], mx[i], lev, a.eps);
+  const int cpr = D * a.bits / 8;
+  for (int t = t0; t < t1; ++t) {
+    uint64_t packed = 0;
+    for (int i = 0; i < C; ++i) {
+      uint32_t c;
+      col[(size_t)t * D + i] = kivi_elem(h2f(col[(size_t)t * D + i]), mn[i], sc[i], lev, c);
+      packed |= (uint64_t)c << (a.bits * i);
+    }
+    if (C == 8 && a.k_codes) {
+      uint8_t *dst = a.k_codes + ((size_t)bh * n + (t - a.lo)) * cpr + ck * a.bits;
+      for (int b = 0; b < a.bits; ++b) dst[b] = (uint8_t)(packed >> (8 * b));
+    }
+  }
+  for (int i = 0; i < C; ++i) {
+    const size_t p = ((size_t)bh * ng + g) * D + ck * C + i;
+    if (a.k_scale) a.k_scale[p] = sc[i];
+    if (a.k_min) a.k_min[p] = mn[i] + 0.0f;  // a zero minimum is exported as +0
+  }
+}
+
+// ------------------------------------------------------------------ values
+template <int BITS, int CL, int LPG, int U>
+__global__ __launch_bounds__(256) void kivi_values_fast(KiviArgs a) {
+  constexpr int RPW = 64 / CL;  // token rows per wave
+  constexpr float LEV = (float)((1 << BITS) - 1);
+  const int D = CL * 8;
+  const int n = a.hi - a.lo;
+  const int64_t rows = a.BH * n;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int ch = lane % CL, tr = lane / CL;
+  const int ng = D / (LPG * 8);
+
+  uint4 v[U];
+  int64_t rowid[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    rowid[u] = (wave * U + u) * RPW + tr;
+    if (rowid[u] < rows) {
+      const int64_t bh = rowid[u] / n;
+      const int t = a.lo + (int)(rowid[u] - bh * n);
+      v[u] = *reinterpret_cast<const uint4 *>(a.values + ((size_t)bh * a.S_cap + t) * D + ch * 8);
+    } else {
+      v[u] = make_uint4(0, 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = lo_h2f(w[i]);
+      x[2 * i + 1] = hi_h2f(w[i]);
+    }
+    float mn = x[0], mx = x[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) {
+      mn = fminf(mn, x[i]);
+      mx = fmaxf(mx, x[i]);
+    }
+    group_minmax_f32<LPG>(mn, mx);
+    const float sc = kivi_scale(mn, mx, LEV, a.eps);
+    uint32_t o[4], c[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint16_t r0 = kivi_elem(x[2 * i], mn, sc, LEV, c[2 * i]);
+      const uint16_t r1 = kivi_elem(x[2 * i + 1], mn, sc, LEV, c[2 * i + 1]);
+      o[i] = (uint32_t)r0 | ((uint32_t)r1 << 16);
+    }
+    if (rowid[u] < rows) {
+      const int64_t bh = rowid[u] / n;
+      const int t = a.lo + (int)(rowid[u] - bh * n);
+      *reinterpret_cast<uint4 *>(a.values + ((size_t)bh * a.S_cap + t) * D + ch * 8) =
+          make_uint4(o[0], o[1], o[2], o[3]);
+      if (a.v_codes) store_codes8<BITS>(a.v_codes + (size_t)rowid[u] * (D * BITS / 8) + ch * BITS, c);
+      if (ch % LPG == 0) {
+        const size_t p = (size_t)rowid[u] * ng + ch / LPG;
+        if (a.v_scale) a.v_scale[p] = sc;
+        if (a.v_min) a.v_min[p] = mn + 0.0f;
+      }
+    }
+  }
+}
+
+// generic values: one thread per (bh, token, group)
+__global__ __launch_bounds__(256) void kivi_values_generic(KiviArgs a) {
+  const int D = a.D;
+  const int n = a.hi - a.lo;
+  const int ng = (D + a.gs - 1) / a.gs;
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= a.BH * n * ng) return;
+  const int g = (int)(id % ng);
+  const int64_t row = id / ng;  // bh * n + (t - lo)
+  const int64_t bh = row / n;
+  const int t = a.lo + (int)(row - bh * n);
+  const int d0 = g * a.gs, d1 = min(d0 + a.gs, D);
+  const float lev = (float)((1 << a.bits) - 1);
+  uint16_t *r = a.values + ((size_t)bh * a.S_cap + t) * D;
+  float mn = __builtin_inff(), mx = -__builtin_inff();
+  for (int d = d0; d < d1; ++d) {
+    const float x = h2f(r[d]);
+    mn = fminf(mn, x);
+    mx = fmaxf(mx, x);
+  }
+  const float sc = kivi_scale(mn, mx, lev, a.eps);
+  // codes (only requested when D % 8 == 0 and gs % 8 == 0): the group covers
+  // whole 8-channel chunks, each chunk is `bits` whole bytes
+  uint8_t *cr = a.v_codes ? a.v_codes + (size_t)row * (D * a.bits / 8) : nullptr;
+  uint64_t packed = 0;
+  for (int d = d0; d < d1; ++d) {
+    uint32_t c;
+    r[d] = kivi_elem(h2f(r[d]), mn, sc, lev, c);
+    packed |= (uint64_t)c << (a.bits * (d % 8));
+    if (cr && (d % 8 == 7 || d == d1 - 1)) {
+      uint8_t *dst = cr + (d / 8) * a.bits;
+      for (int b = 0; b < a.bits; ++b) dst[b] = (uint8_t)(packed >> (8 * b));
+      packed = 0;
+    }
+  }
+  const size_t p = (size_t)row * ng + g;
+  if (a.v_scale) a.v_scale[p] = sc;
+  if (a.v_min) a.v_min[p] = mn + 0.0f;
+}
+
+// ------------------------------------------------------------------ launch
+namespace {
+template <int BITS, int CL>
+hipError_t keys_cl(const KiviArgs &a, int ng, hipStream_t st) {
+  constexpr int TPI = 64 / CL;
+  const int64_t tiles = a.BH * ng;
+  const dim3 grid((unsigned)((tiles + 3) / 4));
+  switch (a.gs / TPI) {  // loads per lane; fast path only when gs % TPI == 0
+    case 1: hipLaunchKernelGGL((kivi_keys_fast<BITS, CL, 1>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((kivi_keys_fast<BITS, CL, 2>), grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((kivi_keys_fast<BITS, CL, 4>), grid, dim3(256), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((kivi_keys_fast<BITS, CL, 8>), grid, dim3(256), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((kivi_keys_fast<BITS, CL, 16>), grid, dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+bool keys_fast_ok(const KiviArgs &a) {
+  const int CL = a.D / 8;
+  if (a.D % 8 || (CL & (CL - 1)) || CL > 32 || CL < 1) return false;
+  const int TPI = 64 / CL;
+  if (a.gs % TPI) return false;
+  const int ni = a.gs / TPI;
+  return ni == 1 || ni == 2 || ni == 4 || ni == 8 || ni == 16;
+}
+
+template <int BITS>
+hipError_t launch_keys(const KiviArgs &a, hipStream_t st) {
+  const int n = a.hi - a.lo;
+  const int ng = (n + a.gs - 1) / a.gs;
+  if (keys_fast_ok(a)) {
+    switch (a.D / 8) {
+      case 1: return keys_cl<BITS, 1>(a, ng, st);
+      case 2: return keys_cl<BITS, 2>(a, ng, st);
+      case 4: return keys_cl<BITS, 4>(a, ng, st);
+      case 8: return keys_cl<BITS, 8>(a, ng, st);
+      case 16: return keys_cl<BITS, 16>(a, ng, st);
+      case 32: return keys_cl<BITS, 32>(a, ng, st);
+    }
+  }
+  if (a.D % 8 == 0) {
+    const int64_t total = a.BH * ng * (a.D / 8);
+    hipLaunchKernelGGL((kivi_keys_generic<8>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, a);
+  } else {
+    const int64_t total = a.BH * ng * a.D;
+    hipLaunchKernelGGL((kivi_keys_generic<1>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+template <int BITS, int CL, int LPG>
+hipError_t values_cfg(const KiviArgs &a, hipStream_t st) {
+  constexpr int U = 2, RPW = 64 / CL;
+  const int64_t rows = a.BH * (int64_t)(a.hi - a.lo);
+  const int64_t waves = (rows + RPW * U - 1) / (RPW * U);
+  hipLaunchKernelGGL((kivi_values_fast<BITS, CL, LPG, U>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
+                     st, a);
+  return hipGetLastError();
+}
+
+template <int BITS, int CL>
+hipError_t values_cl(const KiviArgs &a, hipStream_t st) {
+  switch (a.gs / 8) {
+    case 1: return values_cfg<BITS, CL, 1>(a, st);
+    case 2: if constexpr (CL >= 2) return values_cfg<BITS, CL, 2>(a, st); break;
+    case 4: if constexpr (CL >= 4) return values_cfg<BITS, CL, 4>(a, st); break;
+    case 8: if constexpr (CL >= 8) return values_cfg<BITS, CL, 8>(a, st); break;
+    case 16: if constexpr (CL >= 16) return values_cfg<BITS, CL, 16>(a, st); break;
+    case 32: if constexpr (CL >= 32) return values_cfg<BITS, CL, 32>(a, st); break;
+    case 64: if constexpr (CL >= 64) return values_cfg<BITS, CL, 64>(a, st); break;
+  }
+  return hipErrorInvalidValue;
+}
+
+bool values_fast_ok(const KiviArgs &a) {
+  const int CL = a.D / 8;
+  if (a.D % 8 || (CL & (CL - 1)) || CL > 64 || CL < 1) return false;
+  if (a.gs % 8) return false;
+  const int lpg = a.gs / 8;
+  return (lpg & (lpg - 1)) == 0 && lpg <= CL && a.D % a.gs == 0;
+}
+
+template <int BITS>
+hipError_t launch_values(const KiviArgs &a, hipStream_t st) {
+  if (values_fast_ok(a)) {
+    switch (a.D / 8) {
+      case 1: return values_cl<BITS, 1>(a, st);
+      case 2: return values_cl<BITS, 2>(a, st);
+      case 4: return values_cl<BITS, 4>(a, st);
+      case 8: return values_cl<BITS, 8>(a, st);
+      case 16: return values_cl<BITS, 16>(a, st);
+      case 32: return values_cl<BITS, 32>(a, st);
+      case 64: return values_cl<BITS, 64>(a, st);
+    }
+  }
+  const int n = a.hi - a.lo;
+  const int ng = (a.D + a.gs - 1) / a.gs;
+  const int64_t total = a.BH * n * (int64_t)ng;
+  hipLaunchKernelGGL(kivi_values_generic, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t launch_bits(const KiviArgs &a, hipStream_t st) {
+  hipError_t e = hipSuccess;
+  if (a.keys) e = launch_keys<BITS>(a, st);
+  if (e == hipSuccess && a.values) e = launch_values<BITS>(a, st);
+  return e;
+}
+}  // namespace
+
+hipError_t launch_kivi(const KiviArgs &a, hipStream_t st) {
+  switch (a.bits) {
+    case 2: return launch_bits<2>(a, st);
+    case 4: return launch_bits<4>(a, st);
+    default: return launch_bits<8>(a, st);
+  }
+}
+
+}  // namespace kvq

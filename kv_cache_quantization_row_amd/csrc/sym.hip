@@ -1,0 +1,425 @@
+// Symmetric per-(token, head) q8 / q6 / q4 quantization on paged storage.
+//
+// [MTPLX pull request #267, "feat(kv-cache): add q6 paged KV quantization",
+//  PR description] one fp16 scale per (token, KV head) row, qmax table
+//  {8:127, 6:31, 4:7}, q6 codes biased +32 into 6-bit fields, four fields per
+//  three little-endian bytes; q4 two codes per byte, q8 one ("Summary").
+//
+// Fast path (head_dim a power of two in [16, 1024]): a row is handled by
+// LPR = D/16 consecutive lanes, 16 elements (32 bytes of fp16) per lane, so
+// a wave holds 64/LPR rows; at D = 256 one 16-lane DPP row is one KV row and
+// one wave is one token of four heads. The row's |x| maximum is taken on fp16
+// bit patterns with packed 16-bit max, then across the row's lanes with DPP.
+// Each lane packs its 16 codes into 16*bits/8 bytes (16 / 12 / 8) and stores
+// them with one dword-vector store. The generic path (other head dims) runs
+// one wave per row.
+//
+// Rounding: codes need rint(x * r) with ties-to-even, clipped to +-qmax. The
+// clipped product c is added to 1.5*2^23 + bias: in [2^23, 2^24) the float
+// spacing is 1, so that single IEEE addition rounds c to the nearest integer
+// with ties to even (the addend is even) and leaves rint(c) + bias in the low
+// mantissa bits.
+#include "common.h"
+#include "kernels.h"
+
+namespace kvq {
+
+template <int BITS>
+struct SymFmt;
+template <>
+struct SymFmt<8> {
+  static constexpr int QMAX = 127, BIAS = 0;
+};
+template <>
+struct SymFmt<6> {
+  static constexpr int QMAX = 31, BIAS = 32;
+};
+template <>
+struct SymFmt<4> {
+  static constexpr int QMAX = 7, BIAS = 8;
+};
+
+template <int BITS>
+__device__ __forceinline__ uint32_t encode(float x, float r) {
+  constexpr float Q = (float)SymFmt<BITS>::QMAX;
+  float t = x * r;
+  float c = __builtin_amdgcn_fmed3f(t, -Q, Q);
+  float m = c + (12582912.0f + (float)SymFmt<BITS>::BIAS);
+  return __builtin_bit_cast(uint32_t, m) - 0x4b400000u;
+}
+
+// Row scale: fp16(absmax / qmax) and the binary32 reciprocal of its value.
+template <int BITS>
+__device__ __forceinline__ void row_scale(uint32_t amax_bits, uint16_t &s16, float &r) {
+  float a = h2f((uint16_t)amax_bits);
+  s16 = f2h(a / (float)SymFmt<BITS>::QMAX);
+  float s = h2f(s16);
+  r = (s != 0.0f) ? 1.0f / s : 0.0f;
+}
+
+// Pack 16 biased codes (low bits of c[i]) into BITS/2 dwords, LSB-first.
+template <int BITS>
+__device__ __forceinline__ void pack16(const uint32_t *c, uint32_t *o) {
+  if constexpr (BITS == 8) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      o[j] = (c[4 * j] & 0xffu) | ((c[4 * j + 1] & 0xffu) << 8) | ((c[4 * j + 2] & 0xffu) << 16) |
+             (c[4 * j + 3] << 24);
+  } else if constexpr (BITS == 6) {
+    uint32_t g[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      g[j] = c[4 * j] | (c[4 * j + 1] << 6) | (c[4 * j + 2] << 12) | (c[4 * j + 3] << 18);
+    o[0] = g[0] | (g[1] << 24);
+    o[1] = (g[1] >> 8) | (g[2] << 16);
+    o[2] = (g[2] >> 16) | (g[3] << 8);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v |= c[8 * j + i] << (4 * i);
+      o[j] = v;
+    }
+  }
+}
+
+// Unpack 16 biased codes from BITS/2 dwords.
+template <int BITS>
+__device__ __forceinline__ void unpack16(const uint32_t *w, uint32_t *u) {
+  if constexpr (BITS == 8) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) u[i] = (w[i / 4] >> (8 * (i % 4))) & 0xffu;
+  } else if constexpr (BITS == 6) {
+    uint32_t g[4];
+    g[0] = w[0] & 0xffffffu;
+    g[1] = (w[0] >> 24) | ((w[1] & 0xffffu) << 8);
+    g[2] = (w[1] >> 16) | ((w[2] & 0xffu) << 16);
+    g[3] = w[2] >> 8;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) u[i] = (g[i / 4] >> (6 * (i % 4))) & 63u;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) u[i] = (w[i / 8] >> (4 * (i % 8))) & 15u;
+  }
+}
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+// fp16 pair fp16(q0*s), fp16(q1*s) from two biased codes. q = u - bias is
+// formed exactly in fp16 (1024 + u with spacing 1, minus 1024 + bias); the
+// fp16 product is the single correctly rounded q*s (the binary32 product
+// q*s is exact, so this equals rounding that product to fp16).
+template <int BITS>
+__device__ __forceinline__ uint32_t decode_pair(uint32_t u0, uint32_t u1, h2 ss) {
+  uint32_t b;
+  if constexpr (BITS == 8) {
+    // int8 two's complement: u ^ 0x80 is q + 128 in [1, 255]
+    b = ((u0 ^ 0x80u) | ((u1 ^ 0x80u) << 16)) | 0x64006400u;
+    const h2 off = {(_Float16)(-1152.0f), (_Float16)(-1152.0f)};
+    h2 q = __builtin_bit_cast(h2, b) + off;
+    return __builtin_bit_cast(uint32_t, q * ss);
+  } else {
+    constexpr float O = -(1024.0f + (float)SymFmt<BITS>::BIAS);
+    b = (u0 | (u1 << 16)) | 0x64006400u;
+    const h2 off = {(_Float16)O, (_Float16)O};
+    h2 q = __builtin_bit_cast(h2, b) + off;
+    return __builtin_bit_cast(uint32_t, q * ss);
+  }
+}
+
+// ----------------------------------------------------------------- write path
+template <int BITS, int LPR, int U>
+__global__ __launch_bounds__(256) void sym_quant_fast(SymQuantArgs a) {
+  constexpr int D = LPR * 16, RPW = 64 / LPR, PD = D * BITS / 8, OW = BITS / 2;
+  const int side = blockIdx.z;
+  const uint16_t *x = side ? a.v : a.k;
+  uint8_t *codes = side ? a.v_codes : a.k_codes;
+  uint16_t *scales = side ? a.v_scales : a.k_scales;
+  if (x == nullptr) return;
+  const uint32_t layer = blockIdx.y;
+  const uint32_t rows = a.rows_per_layer;
+  const int lane = threadIdx.x & 63;
+  const uint32_t wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int sub = lane / LPR, li = lane % LPR;
+  const uint16_t *xl = x + (size_t)layer * rows * D;
+  uint8_t *cl = codes + (size_t)(a.layer0 + layer) * a.code_layer_stride;
+  uint16_t *sl = scales + (size_t)(a.layer0 + layer) * a.scale_layer_stride;
+
+  uint32_t w[U][8];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t row = (wave * U + u) * RPW + sub;
+    if (row < rows) {
+      const uint4 *p = reinterpret_cast<const uint4 *>(xl + (size_t)row * D + li * 16);
+      uint4 v0 = p[0], v1 = p[1];
+      w[u][0] = v0.x; w[u][1] = v0.y; w[u][2] = v0.z; w[u][3] = v0.w;
+      w[u][4] = v1.x; w[u][5] = v1.y; w[u][6] = v1.z; w[u][7] = v1.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[u][i] = 0;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t row = (wave * U + u) * RPW + sub;
+    const uint32_t amax = group_max_u32<LPR>(absmax_bits(w[u], 8));
+    uint16_t s16;
+    float r;
+    row_scale<BITS>(amax, s16, r);
+    uint32_t c[16], o[OW];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      c[2 * i] = encode<BITS>(lo_h2f(w[u][i]), r);
+      c[2 * i + 1] = encode<BITS>(hi_h2f(w[u][i]), r);
+    }
+    pack16<BITS>(c, o);
+    if (row < rows) {
+      const uint32_t t = a.h_shift >= 0 ? (row >> a.h_shift) : row / a.H;
+      const uint32_t h = row - t * a.H;
+      const int64_t slot = a.slot_mapping[t];
+      if (slot >= 0 && slot < a.n_slots) {
+        const size_t orow = (size_t)slot * a.H + h;
+        uint32_t *dst = reinterpret_cast<uint32_t *>(cl + orow * PD + li * (OW * 4));
+#pragma unroll
+        for (int j = 0; j < OW; ++j) dst[j] = o[j];
+        if (li == 0) sl[orow] = s16;
+      }
+    }
+  }
+}
+
+// Generic write path: one wave per row, any head_dim valid for the width.
+template <int BITS>
+__global__ __launch_bounds__(256) void sym_quant_generic(SymQuantArgs a) {
+  const int side = blockIdx.z;
+  const uint16_t *x = side ? a.v : a.k;
+  uint8_t *codes = side ? a.v_codes : a.k_codes;
+  uint16_t *scales = side ? a.v_scales : a.k_scales;
+  if (x == nullptr) return;
+  const int D = a.D;
+  const int PD = D * BITS / 8;
+  const uint32_t layer = blockIdx.y;
+  const uint32_t rows = a.rows_per_layer;
+  const int lane = threadIdx.x & 63;
+  const uint32_t row = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (row >= rows) return;  // wave-uniform
+  const uint16_t *xr = x + ((size_t)layer * rows + row) * D;
+  uint32_t m = 0;
+  for (int i = lane; i < D; i += 64) m = max(m, (uint32_t)(xr[i] & 0x7fffu));
+  m = group_max_u32<64>(m);
+  uint16_t s16;
+  float r;
+  row_scale<BITS>(m, s16, r);
+  const uint32_t t = row / a.H, h = row - t * a.H;
+  const int64_t slot = a.slot_mapping[t];
+  if (slot < 0 || slot >= a.n_slots) return;
+  const size_t orow = (size_t)slot * a.H + h;
+  uint8_t *dst = codes + (size_t)(a.layer0 + layer) * a.code_layer_stride + orow * PD;
+  constexpr int G = BITS == 6 ? 4 : (BITS == 4 ? 2 : 1);  // elements per packing group
+  for (int g = lane; g < D / G; g += 64) {
+    uint32_t c[4];
+#pragma unroll
+    for (int i = 0; i < G; ++i) c[i] = encode<BITS>(h2f(xr[g * G + i]), r);
+    if constexpr (BITS == 6) {
+      uint32_t v = (c[0] & 63u) | ((c[1] & 63u) << 6) | ((c[2] & 63u) << 12) | ((c[3] & 63u) << 18);
+      dst[3 * g] = (uint8_t)v;
+      dst[3 * g + 1] = (uint8_t)(v >> 8);
+      dst[3 * g + 2] = (uint8_t)(v >> 16);
+    } else if constexpr (BITS == 4) {
+      dst[g] = (uint8_t)((c[0] & 15u) | ((c[1] & 15u) << 4));
+    } else {
+      dst[g] = (uint8_t)c[0];
+    }
+  }
+  if (lane == 0) scales[(size_t)(a.layer0 + layer) * a.scale_layer_stride + orow] = s16;
+}
+
+// ----------------------------------------------------------------- read path
+__device__ __forceinline__ bool locate(const SymDequantArgs &a, uint32_t seq, uint32_t p,
+                                       int32_t len, size_t &slot) {
+  if ((int32_t)p >= len) return false;
+  const uint32_t blk = p / (uint32_t)a.page_size;
+  if ((int32_t)blk >= a.max_blocks) return false;
+  const int32_t page = a.block_table[(size_t)seq * a.max_blocks + blk];
+  if (page < 0 || page >= a.num_pages) return false;
+  slot = (size_t)page * a.page_size + (p - blk * (uint32_t)a.page_size);
+  return true;
+}
+
+template <int BITS, int LPR, int U>
+__global__ __launch_bounds__(256) void sym_dequant_fast(SymDequantArgs a) {
+  constexpr int D = LPR * 16, RPW = 64 / LPR, PD = D * BITS / 8, OW = BITS / 2;
+  const int side = blockIdx.z & 1;
+  const uint32_t layer = blockIdx.z >> 1;
+  const uint8_t *codes = side ? a.v_codes : a.k_codes;
+  const uint16_t *scales = side ? a.v_scales : a.k_scales;
+  uint16_t *out = side ? a.v_out : a.k_out;
+  if (out == nullptr) return;
+  const uint32_t seq = blockIdx.y;
+  const uint32_t rows = (uint32_t)a.max_len * a.H;  // rows per (layer, sequence)
+  const int lane = threadIdx.x & 63;
+  const uint32_t wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int sub = lane / LPR, li = lane % LPR;
+  const int32_t len = a.seq_lens[seq];
+  const uint8_t *cl = codes + (size_t)(a.layer0 + layer) * a.code_layer_stride;
+  const uint16_t *sl = scales + (size_t)(a.layer0 + layer) * a.scale_layer_stride;
+  uint16_t *ol = out + ((size_t)layer * a.n_seqs + seq) * rows * D;
+
+  uint32_t w[U][OW];
+  uint16_t s16[U];
+  bool valid[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t row = (wave * U + u) * RPW + sub;
+    size_t slot = 0;
+    const uint32_t p = a.h_shift >= 0 ? (row >> a.h_shift) : row / a.H;
+    const uint32_t h = row - p * a.H;
+    valid[u] = row < rows && locate(a, seq, p, len, slot);
+    if (valid[u]) {
+      const size_t irow = slot * a.H + h;
+      const uint32_t *src = reinterpret_cast<const uint32_t *>(cl + irow * PD + li * (OW * 4));
+#pragma unroll
+      for (int j = 0; j < OW; ++j) w[u][j] = src[j];
+      s16[u] = sl[irow];
+    } else {
+#pragma unroll
+      for (int j = 0; j < OW; ++j) w[u][j] = 0;
+      s16[u] = 0;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t row = (wave * U + u) * RPW + sub;
+    uint32_t cu[16], o[8];
+    unpack16<BITS>(w[u], cu);
+    if (!valid[u]) {  // +0 output: q = 0 with scale 0
+#pragma unroll
+      for (int i = 0; i < 16; ++i) cu[i] = SymFmt<BITS>::BIAS;
+    }
+    const _Float16 s = __builtin_bit_cast(_Float16, s16[u]);
+    const h2 ss = {s, s};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = decode_pair<BITS>(cu[2 * i], cu[2 * i + 1], ss);
+    if (row < rows) {
+      uint4 *dst = reinterpret_cast<uint4 *>(ol + (size_t)row * D + li * 16);
+      dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+      dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+  }
+}
+
+template <int BITS>
+__global__ __launch_bounds__(256) void sym_dequant_generic(SymDequantArgs a) {
+  const int side = blockIdx.z & 1;
+  const uint32_t layer = blockIdx.z >> 1;
+  const uint8_t *codes = side ? a.v_codes : a.k_codes;
+  const uint16_t *scales = side ? a.v_scales : a.k_scales;
+  uint16_t *out = side ? a.v_out : a.k_out;
+  if (out == nullptr) return;
+  const int D = a.D;
+  const int PD = D * BITS / 8;
+  const uint32_t seq = blockIdx.y;
+  const uint32_t rows = (uint32_t)a.max_len * a.H;
+  const int lane = threadIdx.x & 63;
+  const uint32_t row = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const uint32_t p = row / a.H, h = row - p * a.H;
+  uint16_t *o = out + (((size_t)layer * a.n_seqs + seq) * rows + row) * D;
+  size_t slot;
+  if (!locate(a, seq, p, a.seq_lens[seq], slot)) {
+    for (int i = lane; i < D; i += 64) o[i] = 0;
+    return;
+  }
+  const size_t irow = slot * a.H + h;
+  const uint8_t *src = codes + (size_t)(a.layer0 + layer) * a.code_layer_stride + irow * PD;
+  const float s = h2f(scales[(size_t)(a.layer0 + layer) * a.scale_layer_stride + irow]);
+  for (int i = lane; i < D; i += 64) {
+    int q;
+    if constexpr (BITS == 8) {
+      q = (int)(int8_t)src[i];
+    } else if constexpr (BITS == 6) {
+      const int g = i / 4, k = i % 4;
+      const uint32_t v = src[3 * g] | (src[3 * g + 1] << 8) | (src[3 * g + 2] << 16);
+      q = (int)((v >> (6 * k)) & 63u) - 32;
+    } else {
+      q = (int)((src[i / 2] >> (4 * (i % 2))) & 15u) - 8;
+    }
+    o[i] = f2h((float)q * s);
+  }
+}
+
+// ----------------------------------------------------------------- launchers
+namespace {
+template <int BITS, int LPR>
+hipError_t launch_quant_lpr(const SymQuantArgs &a, int n_layers, hipStream_t st) {
+  constexpr int U = 2, RPW = 64 / LPR, WPB = 4;
+  const uint32_t per_block = RPW * U * WPB;
+  dim3 grid((a.rows_per_layer + per_block - 1) / per_block, n_layers, 2);
+  hipLaunchKernelGGL((sym_quant_fast<BITS, LPR, U>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+template <int BITS, int LPR>
+hipError_t launch_dequant_lpr(const SymDequantArgs &a, int n_layers, hipStream_t st) {
+  constexpr int U = 2, RPW = 64 / LPR, WPB = 4;
+  const uint32_t per_block = RPW * U * WPB;
+  const uint32_t rows = (uint32_t)a.max_len * a.H;
+  dim3 grid((rows + per_block - 1) / per_block, a.n_seqs, 2 * n_layers);
+  hipLaunchKernelGGL((sym_dequant_fast<BITS, LPR, U>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t launch_quant_bits(const SymQuantArgs &a, int n_layers, hipStream_t st) {
+  switch (a.D) {
+    case 16: return launch_quant_lpr<BITS, 1>(a, n_layers, st);
+    case 32: return launch_quant_lpr<BITS, 2>(a, n_layers, st);
+    case 64: return launch_quant_lpr<BITS, 4>(a, n_layers, st);
+    case 128: return launch_quant_lpr<BITS, 8>(a, n_layers, st);
+    case 256: return launch_quant_lpr<BITS, 16>(a, n_layers, st);
+    case 512: return launch_quant_lpr<BITS, 32>(a, n_layers, st);
+    case 1024: return launch_quant_lpr<BITS, 64>(a, n_layers, st);
+    default: {
+      dim3 grid((a.rows_per_layer + 3) / 4, n_layers, 2);
+      hipLaunchKernelGGL((sym_quant_generic<BITS>), grid, dim3(256), 0, st, a);
+      return hipGetLastError();
+    }
+  }
+}
+template <int BITS>
+hipError_t launch_dequant_bits(const SymDequantArgs &a, int n_layers, hipStream_t st) {
+  switch (a.D) {
+    case 16: return launch_dequant_lpr<BITS, 1>(a, n_layers, st);
+    case 32: return launch_dequant_lpr<BITS, 2>(a, n_layers, st);
+    case 64: return launch_dequant_lpr<BITS, 4>(a, n_layers, st);
+    case 128: return launch_dequant_lpr<BITS, 8>(a, n_layers, st);
+    case 256: return launch_dequant_lpr<BITS, 16>(a, n_layers, st);
+    case 512: return launch_dequant_lpr<BITS, 32>(a, n_layers, st);
+    case 1024: return launch_dequant_lpr<BITS, 64>(a, n_layers, st);
+    default: {
+      const uint32_t rows = (uint32_t)a.max_len * a.H;
+      dim3 grid((rows + 3) / 4, a.n_seqs, 2 * n_layers);
+      hipLaunchKernelGGL((sym_dequant_generic<BITS>), grid, dim3(256), 0, st, a);
+      return hipGetLastError();
+    }
+  }
+}
+}  // namespace
+
+hipError_t launch_sym_quant(const SymQuantArgs &a, int bits, int n_layers, hipStream_t st) {
+  switch (bits) {
+    case 8: return launch_quant_bits<8>(a, n_layers, st);
+    case 6: return launch_quant_bits<6>(a, n_layers, st);
+    default: return launch_quant_bits<4>(a, n_layers, st);
+  }
+}
+
+hipError_t launch_sym_dequant(const SymDequantArgs &a, int bits, int n_layers, hipStream_t st) {
+  switch (bits) {
+    case 8: return launch_dequant_bits<8>(a, n_layers, st);
+    case 6: return launch_dequant_bits<6>(a, n_layers, st);
+    default: return launch_dequant_bits<4>(a, n_layers, st);
+  }
+}
+
+}  // namespace kvq

@@ -231,7 +231,7 @@ void kivi_group(float *vals, int n, int levels, float eps, int *codes, float *sc
     vals[i] = prod + mn;
   }
   *scale_out = scale;
-  *min_out = mn;
+  *min_out = mn + 0.0f;  // reading: a zero group minimum is exported as +0
 }
 
 void put_code(uint8_t *row, int d, int bits, int code) {

@@ -1,0 +1,136 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol
+include/kvq.h declares, its host helpers agree with the oracle and the pages'
+printed values, and invalid arguments are rejected on the host (before any
+HIP call) with the documented status codes."""
+import ctypes as C
+import os
+import subprocess
+
+import pytest
+
+from kv_cache_quantization_row_amd import kvq
+
+FAKE = 1 << 20  # an aligned non-null address; never dereferenced (calls fail validation first)
+
+
+def test_exports_every_declared_symbol():
+    names = kvq.declared_symbols()
+    assert {"kvq_quant_sym", "kvq_dequant_sym", "kvq_kivi_quant_dequant"} <= set(names)
+    L = kvq.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    dyn = subprocess.run(["nm", "-D", "--defined-only", kvq.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in dyn.splitlines() if " T " in l}
+    assert set(names) <= exported
+
+
+def test_host_helpers_match_oracle(orc):
+    for bits in range(0, 17):
+        assert kvq.kvq_sym_qmax(bits) == orc.sym_qmax(bits)
+        for D in range(-1, 600):
+            assert kvq.kvq_packed_dim(D, bits) == (orc.packed_dim(D, bits) if D > 0 else -1)
+    for bits in (4, 6, 8, 16):
+        for t, l, h, d in [(1, 1, 1, 256), (262144, 16, 4, 256), (33024, 16, 4, 128), (7, 3, 5, 64)]:
+            assert kvq.kvq_sym_cache_bytes(t, l, h, d, bits) == orc.sym_cache_bytes(t, l, h, d, bits)
+    for off in range(0, 700, 7):
+        for R, gs in [(128, 32), (0, 1), (5, 3), (64, 64)]:
+            assert kvq.kvq_kivi_boundary(off, R, gs) == orc.kivi_boundary(off, R, gs)
+    assert kvq.kvq_kivi_boundary(10, 128, 0) == -1
+
+
+def test_parse_mode():
+    for m, b in [("q8", 8), ("q6", 6), ("q4", 4), ("6", 6), ("6bit", 6), ("int6", 6), ("uint6", 6),
+                 ("8", 8), ("4", 4)]:
+        assert kvq.kvq_parse_mode(m) == b
+    for m in ["q6_k", "q6_0", "Q6", "q5", "6bits", "", "int8", "q16"]:
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.kvq_parse_mode(m)
+        assert e.value.code == kvq.KVQ_ERR_MODE
+
+
+def _quant(lay, k=FAKE, v=FAKE, layer0=0, n_layers=1, n_tokens=4, sm=FAKE, kc=FAKE, ks=FAKE,
+           vc=FAKE, vs=FAKE):
+    L = kvq.lib()
+    return L.kvq_quant_sym(C.byref(lay), k, v, layer0, n_layers, n_tokens, sm, kc, ks, vc, vs, None)
+
+
+def _dequant(lay, kc=FAKE, ks=FAKE, vc=FAKE, vs=FAKE, layer0=0, n_layers=1, bt=FAKE, mb=4, sl=FAKE,
+             n_seqs=2, max_len=16, ko=FAKE, vo=FAKE):
+    L = kvq.lib()
+    return L.kvq_dequant_sym(C.byref(lay), kc, ks, vc, vs, layer0, n_layers, bt, mb, sl, n_seqs,
+                             max_len, ko, vo, None)
+
+
+def test_sym_validation_errors():
+    good = kvq.layout(2, 8, 16, 4, 256, 6)
+    assert _quant(kvq.layout(2, 8, 16, 4, 256, 5)) == kvq.KVQ_ERR_BITS
+    assert _quant(kvq.layout(2, 8, 16, 4, 256, 16)) == kvq.KVQ_ERR_BITS
+    assert _quant(kvq.layout(2, 8, 16, 4, 254, 6)) == kvq.KVQ_ERR_SHAPE   # q6 needs D % 4
+    assert _quant(kvq.layout(2, 8, 16, 4, 255, 4)) == kvq.KVQ_ERR_SHAPE   # q4 needs even D
+    assert _quant(kvq.layout(0, 8, 16, 4, 256, 6)) == kvq.KVQ_ERR_SHAPE
+    assert _quant(good, layer0=1, n_layers=2) == kvq.KVQ_ERR_SHAPE        # beyond the pool
+    assert _quant(good, layer0=-1) == kvq.KVQ_ERR_SHAPE
+    assert _quant(good, n_tokens=-1) == kvq.KVQ_ERR_SHAPE
+    assert _quant(good, vc=None) == kvq.KVQ_ERR_NULL                      # V side incomplete
+    assert _quant(good, k=None, kc=None, ks=None, v=None, vc=None, vs=None) == kvq.KVQ_ERR_NULL
+    assert _quant(good, sm=None) == kvq.KVQ_ERR_NULL
+    assert _quant(good, k=FAKE + 2) == kvq.KVQ_ERR_ALIGN
+    assert _quant(good, vc=FAKE + 8) == kvq.KVQ_ERR_ALIGN
+    assert _quant(good, sm=FAKE + 2) == kvq.KVQ_ERR_ALIGN
+    assert kvq.lib().kvq_quant_sym(None, FAKE, FAKE, 0, 1, 1, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   None) == kvq.KVQ_ERR_NULL
+    # empty work is a successful no-op that enqueues nothing
+    assert _quant(good, n_tokens=0) == kvq.KVQ_OK
+    assert _quant(good, n_layers=0) == kvq.KVQ_OK
+    assert _quant(good, sm=None, n_tokens=0) == kvq.KVQ_OK
+    assert "layers" in kvq.lib().kvq_last_error().decode() or kvq.lib().kvq_last_error() == b""
+
+
+def test_sym_dequant_validation_errors():
+    good = kvq.layout(2, 8, 16, 4, 256, 8)
+    assert _dequant(kvq.layout(2, 8, 16, 4, 256, 3)) == kvq.KVQ_ERR_BITS
+    assert _dequant(good, layer0=2) == kvq.KVQ_ERR_SHAPE
+    assert _dequant(good, ko=None) == kvq.KVQ_ERR_NULL
+    assert _dequant(good, bt=None) == kvq.KVQ_ERR_NULL
+    assert _dequant(good, mb=0) == kvq.KVQ_ERR_SHAPE
+    assert _dequant(good, n_seqs=-3) == kvq.KVQ_ERR_SHAPE
+    assert _dequant(good, ko=FAKE + 4) == kvq.KVQ_ERR_ALIGN
+    assert _dequant(good, sl=FAKE + 1) == kvq.KVQ_ERR_ALIGN
+    assert _dequant(good, n_seqs=0) == kvq.KVQ_OK
+    assert _dequant(good, max_len=0) == kvq.KVQ_OK
+
+
+def _kivi(k=FAKE, v=FAKE, B=2, H=2, S=64, D=64, lo=0, hi=32, bits=2, gs=32, eps=1e-8, kc=None,
+          ks=None, km=None, vc=None, vs=None, vm=None):
+    return kvq.lib().kvq_kivi_quant_dequant(k, v, B, H, S, D, lo, hi, bits, gs, eps, kc, ks, km, vc,
+                                            vs, vm, None)
+
+
+def test_kivi_validation_errors():
+    assert _kivi(bits=3) == kvq.KVQ_ERR_BITS
+    assert _kivi(bits=1) == kvq.KVQ_ERR_BITS
+    assert _kivi(lo=10, hi=5) == kvq.KVQ_ERR_SHAPE
+    assert _kivi(hi=65) == kvq.KVQ_ERR_SHAPE
+    assert _kivi(lo=-1) == kvq.KVQ_ERR_SHAPE
+    assert _kivi(gs=0) == kvq.KVQ_ERR_SHAPE
+    assert _kivi(D=0) == kvq.KVQ_ERR_SHAPE
+    assert _kivi(eps=0.0) == kvq.KVQ_ERR_ARG
+    assert _kivi(eps=float("nan")) == kvq.KVQ_ERR_ARG
+    assert _kivi(D=60, kc=FAKE) == kvq.KVQ_ERR_SHAPE   # packed codes need D % 8 == 0
+    assert _kivi(gs=20, vc=FAKE) == kvq.KVQ_ERR_SHAPE  # ... and group_size % 8 == 0
+    assert _kivi(k=None, v=None) == kvq.KVQ_ERR_NULL
+    assert _kivi(k=None, kc=FAKE) == kvq.KVQ_ERR_NULL
+    assert _kivi(k=FAKE + 2) == kvq.KVQ_ERR_ALIGN
+    assert _kivi(vs=FAKE + 2) == kvq.KVQ_ERR_ALIGN
+    assert _kivi(lo=7, hi=7) == kvq.KVQ_OK
+    assert _kivi(B=0) == kvq.KVQ_OK
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    lay = kvq.layout(1, 4, 16, 4, 256, 6)
+    x = torch.zeros((1, 4, 4, 256), dtype=torch.float16)
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_quant_sym(lay, x, None, torch.zeros(4, dtype=torch.int32),
+                          torch.zeros(1, dtype=torch.uint8), torch.zeros(1, dtype=torch.int16), None, None)
