@@ -1,0 +1,349 @@
+"""Benchmark of the KV-cache quantize -> pack -> unpack -> dequantize path on one MI355X.
+
+Default workload (the one the headline metric is quoted on): paged symmetric
+q8/q6/q4 cache, 16 layers x 4 KV heads x head_dim 256, page size 16; 16
+sequences x 32,768-token prefill quantized into pages (one launch covers all
+16 layers), 256 single-token decode appends per sequence (one launch per step,
+all layers), then a full-cache dequant sweep of 16 x 33,024 tokens. fp16 input
+N(0,1) with 1% of channels x10 per (layer, head) and 5% of token positions
+drawn from Laplace(0,1). One step = that whole sequence for each width in
+--bits. Inputs are generated on the GPU and resident in HBM before timing.
+
+Output: one JSON line (metric, value in GB/s of fp16-equivalent KV processed,
+roofline of the dominant kernel, CPU-oracle baseline on a bounded sample).
+Other workloads (--workload kivi | long_context | single_layer | nuq) print a
+line of the same form for their own configuration.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, 8 TB/s
+METRIC = "KV quant+pack / unpack+dequant GB/s (fp16-equiv) and % of HBM peak, 1 GPU"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+class Timers:
+    """Per-kernel-class HIP event pairs recorded on the launch stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def span(self, name):
+        torch = self.torch
+        timers = self
+
+        class _S:
+            def __enter__(self_):
+                self_.a = torch.cuda.Event(enable_timing=True)
+                self_.b = torch.cuda.Event(enable_timing=True)
+                self_.a.record()
+
+            def __exit__(self_, *exc):
+                self_.b.record()
+                timers.pairs.setdefault(name, []).append((self_.a, self_.b))
+
+        return _S()
+
+    def mean_ms(self):
+        return {k: sum(a.elapsed_time(b) for a, b in v) / len(v) for k, v in self.pairs.items()}
+
+    def count(self):
+        return {k: len(v) for k, v in self.pairs.items()}
+
+
+# --------------------------------------------------------------------------- paged symmetric
+class PagedSym:
+    """16 layers x 4 heads x 256, page 16, 16 seqs x 32,768 prefill + 256 appends + sweep."""
+
+    def __init__(self, torch, args):
+        self.torch = torch
+        self.L, self.H, self.D, self.P = 16, 4, 256, 16
+        self.S, self.T, self.N_DEC = 16, args.prefill_tokens, args.decode_steps
+        self.bits_list = [int(b) for b in args.bits.split(",")]
+        self.total = self.T + self.N_DEC
+        self.name = "paged_sym"
+        self.page_order = args.page_order
+
+    def setup(self):
+        torch = self.torch
+        from kv_cache_quantization_row_amd import inputs, kvq
+
+        self.kvq = kvq
+        d = torch.device("cuda:0")
+        L, H, D, P, S, T = self.L, self.H, self.D, self.P, self.S, self.T
+        self.bt, self.num_pages = inputs.paged_block_table(S, self.total, P, seed=2002)
+        if self.page_order == "identity":  # pages of each sequence consecutive in the pool
+            import torch as _t
+            self.bt = _t.arange(self.bt.numel(), dtype=_t.int32).view(self.bt.shape).contiguous()
+        self.max_blocks = self.bt.shape[1]
+        self.slot_prefill = inputs.slot_mapping_for(self.bt, P, 0, T).to(d)
+        self.slot_dec = [inputs.slot_mapping_for(self.bt, P, T + i, 1).to(d) for i in range(self.N_DEC)]
+        log("generating %d layers x %d tokens x %d x %d fp16 K and V" % (L, S * T, H, D))
+        self.k = torch.empty((L, S * T, H, D), dtype=torch.float16, device=d)
+        self.v = torch.empty_like(self.k)
+        for l in range(L):
+            self.k[l] = inputs.sym_layer(S * T, H, D, seed=2100 + l, device=d, laplace_token_frac=0.05,
+                                         channel_seed=3100 + l)
+            self.v[l] = inputs.sym_layer(S * T, H, D, seed=2200 + l, device=d, laplace_token_frac=0.05,
+                                         channel_seed=3200 + l)
+        self.kd = inputs.sym_layer(self.N_DEC * L * S, H, D, seed=2300, device=d,
+                                   laplace_token_frac=0.05).view(self.N_DEC, L, S, H, D)
+        self.vd = inputs.sym_layer(self.N_DEC * L * S, H, D, seed=2400, device=d,
+                                   laplace_token_frac=0.05).view(self.N_DEC, L, S, H, D)
+        slots = self.num_pages * P
+        self.kc = torch.empty((L * slots * H * D,), dtype=torch.uint8, device=d)  # sized for q8
+        self.vc = torch.empty_like(self.kc)
+        self.ks = torch.empty((L, slots, H), dtype=torch.int16, device=d)
+        self.vs = torch.empty_like(self.ks)
+        self.ko = torch.empty((L, S, self.total, H, D), dtype=torch.float16, device=d)
+        self.vo = torch.empty_like(self.ko)
+        self.bt_d = self.bt.to(d)
+        self.lens = torch.full((S,), self.total, dtype=torch.int32, device=d)
+        self.lay = {b: kvq.layout(L, self.num_pages, P, H, D, b) for b in self.bits_list}
+        torch.cuda.synchronize()
+
+    def step(self, tm):
+        kvq = self.kvq
+        for b in self.bits_list:
+            lay = self.lay[b]
+            with tm.span("quant_prefill_q%d" % b):
+                kvq.kvq_quant_sym(lay, self.k, self.v, self.slot_prefill, self.kc, self.ks, self.vc, self.vs)
+            with tm.span("decode_append_q%d_x%d" % (b, self.N_DEC)):
+                for i in range(self.N_DEC):
+                    kvq.kvq_quant_sym(lay, self.kd[i], self.vd[i], self.slot_dec[i], self.kc, self.ks,
+                                      self.vc, self.vs)
+            with tm.span("dequant_sweep_q%d" % b):
+                kvq.kvq_dequant_sym(lay, self.kc, self.ks, self.vc, self.vs, self.bt_d, self.lens,
+                                    self.ko, self.vo)
+
+    # elements processed per step (fp16 values quantized + values dequantized, K and V)
+    def elems(self):
+        per_bits = 2 * self.L * self.H * self.D * (self.S * self.T + self.N_DEC * self.S + self.S * self.total)
+        return per_bits * len(self.bits_list)
+
+    def kernel_bytes(self, name):
+        """Algorithmic HBM bytes of one launch of a kernel class."""
+        L, H, D, S = self.L, self.H, self.D, self.S
+        b = int(name.split("_q")[1].split("_")[0])
+        per_elem = 2 + b / 8 + 2 / D  # fp16 in/out + packed code + fp16 scale per row
+        if name.startswith("quant_prefill"):
+            return 2 * L * S * self.T * H * D * per_elem
+        if name.startswith("dequant_sweep"):
+            return 2 * L * S * self.total * H * D * per_elem
+        return 2 * L * S * H * D * per_elem * self.N_DEC
+
+    def config(self):
+        return {"workload": "paged symmetric q8/q6/q4 KV cache: 16 layers x 4 KV heads x D=256, page 16, "
+                            "16 seqs x %d-token prefill + %d decode appends + full dequant sweep"
+                            % (self.T, self.N_DEC),
+                "bits": self.bits_list, "layers": self.L, "kv_heads": self.H, "head_dim": self.D,
+                "page_size": self.P, "seqs": self.S, "prefill_tokens": self.T,
+                "decode_steps": self.N_DEC, "tokens_per_seq_after_decode": self.total}
+
+    def cpu_baseline(self, budget_tokens):
+        """Oracle (single thread) on layer 0, the first budget_tokens/16 tokens of each sequence."""
+        import numpy as np
+        import oracle
+        from kv_cache_quantization_row_amd import inputs
+
+        n = budget_tokens
+        k = inputs.sym_layer(n, self.H, self.D, seed=2100, laplace_token_frac=0.05, channel_seed=3100)
+        v = inputs.sym_layer(n, self.H, self.D, seed=2200, laplace_token_frac=0.05, channel_seed=3200)
+        kk = k.view(__import__("torch").int16).numpy().view(np.uint16)
+        vv = v.view(__import__("torch").int16).numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        elems = 0
+        for b in self.bits_list:
+            for x in (kk, vv):
+                c, s = oracle.sym_quant_rows(x, b)
+                oracle.sym_dequant_rows(c, s, self.D, b)
+                elems += 2 * x.size
+        dt = time.perf_counter() - t0
+        return {"value": round(2 * elems / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": "layer 0, %d tokens x 4 heads x 256 of K and V, quantize + dequantize at q%s "
+                          "(%.1f s single-threaded)" % (n, "/q".join(map(str, self.bits_list)), dt)}
+
+
+# --------------------------------------------------------------------------- KIVI
+class Kivi:
+    """B=8 x 16 layers folded (128), 8 heads, 8192 tokens, D=64, gs 32, residual 128, b in --kivi-bits."""
+
+    def __init__(self, torch, args):
+        self.torch = torch
+        self.B, self.H, self.S, self.D, self.gs = 128, 8, 8192, 64, 32
+        self.bits_list = [int(b) for b in args.kivi_bits.split(",")]
+        self.name = "kivi"
+
+    def setup(self):
+        torch = self.torch
+        import oracle  # noqa: F401  (boundary helper lives in the library too)
+        from kv_cache_quantization_row_amd import inputs, kvq
+
+        self.kvq = kvq
+        d = torch.device("cuda:0")
+        self.hi = kvq.kvq_kivi_boundary(self.S, 128, self.gs)
+        self.k0, self.v0 = inputs.kivi_kv(self.B, self.H, self.S, self.D, seed=1003, device=d)
+        self.k = self.k0.clone()
+        self.v = self.v0.clone()
+        torch.cuda.synchronize()
+
+    def step(self, tm):
+        for b in self.bits_list:
+            # the round trip is in place: re-running it on its own output is the
+            # same work (same groups, same bytes); the data stays resident
+            with tm.span("kivi_keys_values_b%d" % b):
+                self.kvq.kvq_kivi_quant_dequant(self.k, self.v, 0, self.hi, b, self.gs)
+
+    def elems(self):
+        return 2 * self.B * self.H * self.hi * self.D * len(self.bits_list)
+
+    def kernel_bytes(self, name):
+        return 2 * self.B * self.H * self.hi * self.D * 4.0
+
+    def config(self):
+        return {"workload": "KIVI round trip: batch 8 x 16 layers (B=128) x 8 KV heads x 8192 tokens x D=64, "
+                            "group 32, residual 128 (tokens [0, %d)), keys per channel, values per token" % self.hi,
+                "bits": self.bits_list}
+
+    def cpu_baseline(self, budget_tokens):
+        import numpy as np
+        import oracle
+        from kv_cache_quantization_row_amd import inputs
+
+        nbh = max(1, budget_tokens // self.S)
+        k, v = inputs.kivi_kv(nbh, 1, self.S, self.D, seed=1003)
+        t0 = time.perf_counter()
+        elems = 0
+        for b in self.bits_list:
+            oracle.kivi_round_trip(k.numpy().view(np.uint16), 0, self.hi, 1, b, self.gs)
+            oracle.kivi_round_trip(v.numpy().view(np.uint16), 0, self.hi, 0, b, self.gs)
+            elems += 2 * nbh * self.hi * self.D
+        dt = time.perf_counter() - t0
+        return {"value": round(2 * elems / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": "%d (batch, head) slices of 8192 x 64 keys and values (%.1f s)" % (nbh, dt)}
+
+
+class Copy:
+    """Plain device-to-device copy of 4 GiB (torch copy kernel): the practical
+    HBM ceiling on this machine and the reference for scaling traffic counters."""
+
+    def __init__(self, torch, args):
+        self.torch = torch
+        self.n = 1 << 31  # fp16 elements = 4 GiB
+        self.name = "copy"
+
+    def setup(self):
+        torch = self.torch
+        d = torch.device("cuda:0")
+        self.src = torch.ones(self.n, dtype=torch.float16, device=d)
+        self.dst = torch.empty_like(self.src)
+        torch.cuda.synchronize()
+
+    def step(self, tm):
+        with tm.span("copy_4GiB"):
+            self.dst.copy_(self.src)
+
+    def elems(self):
+        return self.n
+
+    def kernel_bytes(self, name):
+        return 2 * 2 * self.n
+
+    def config(self):
+        return {"workload": "plain device copy, 4 GiB read + 4 GiB written"}
+
+    def cpu_baseline(self, budget_tokens):
+        return None
+
+
+WORKLOADS = {"paged_sym": PagedSym, "kivi": Kivi, "copy": Copy}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="paged_sym", choices=sorted(WORKLOADS))
+    ap.add_argument("--bits", default="8,6,4")
+    ap.add_argument("--kivi-bits", default="2,4")
+    ap.add_argument("--prefill-tokens", type=int, default=32768)
+    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--cpu-tokens", type=int, default=65536)
+    ap.add_argument("--page-order", default="random", choices=["random", "identity"],
+                    help="pool page assignment of the paged workload (random = fragmented pool)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from kv_cache_quantization_row_amd import kvq
+
+    kvq.lib()  # fails loudly if the HIP library is missing
+    torch.cuda.init()
+    wl = WORKLOADS[args.workload](torch, args)
+    wl.setup()
+    log("warmup %d" % args.warmup)
+    warm = Timers(torch)
+    for _ in range(args.warmup):
+        wl.step(warm)
+    torch.cuda.synchronize()
+    tm = Timers(torch)
+    log("timing %d steps" % args.steps)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for _ in range(args.steps):
+        wl.step(tm)
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    value = 2.0 * wl.elems() / (ms_per_step / 1e3) / 1e9
+
+    means = tm.mean_ms()
+    kernels = {}
+    for name, ms in means.items():
+        nbytes = wl.kernel_bytes(name)
+        gbs = nbytes / (ms / 1e3) / 1e9
+        kernels[name] = {"avg_ms": round(ms, 4), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    totals = {n: means[n] * c for n, c in tm.count().items()}
+    dom = max((n for n in totals if "decode" not in n), key=lambda n: totals[n])
+    roof = {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["GB/s"], "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": kernels[dom]["frac_hbm"], "traffic": None}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline")
+        cpu = wl.cpu_baseline(args.cpu_tokens)
+    line = {"metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": wl.config(), "roofline": roof, "cpu_baseline": cpu, "kernels": kernels,
+            "wall_s": round(wall, 3)}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

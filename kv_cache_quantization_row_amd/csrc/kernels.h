@@ -27,6 +27,7 @@ struct SymDequantArgs {
   int64_t code_layer_stride, scale_layer_stride;
   int32_t layer0, H, D, h_shift;
   int32_t num_pages, page_size, max_blocks, n_seqs, max_len;
+  int32_t ppb;                     // positions per workgroup (set by the launcher)
 };
 
 hipError_t launch_sym_quant(const SymQuantArgs &a, int bits, int n_layers, hipStream_t st);
