@@ -307,7 +307,7 @@ void nuq_fit(const uint16_t *u_bits, int m, int L, int iters, float *lev) {
     double f = (double)(num % den) / (double)den;
     double v = u[i];
     if (f != 0.0) v = u[i] + f * (u[i + 1] - u[i]);
-    lev[j] = (float)v;
+    lev[j] = (float)v + 0.0f;  // reading: a zero level is +0 (the sort does not order -0/+0)
   }
   std::vector<long long> sum(L), cnt(L);
   for (int it = 0; it < iters; ++it) {
