@@ -290,7 +290,8 @@ float mean_rn32(long long sum_units, long long count) {
 // rounded once to binary32], then `iters` rounds of (assign every sample to
 // its nearest level, ties to the lower index; replace every non-empty level
 // by the binary32-rounded exact mean of its samples; an empty level keeps its
-// value). u: the inlier samples (fp16 bit patterns, any order).
+// value; then the table is sorted ascending). u: the inlier samples (fp16 bit
+// patterns, any order).
 void nuq_fit(const uint16_t *u_bits, int m, int L, int iters, float *lev) {
   if (m == 0) {
     for (int j = 0; j < L; ++j) lev[j] = 0.0f;
@@ -320,6 +321,11 @@ void nuq_fit(const uint16_t *u_bits, int m, int L, int iters, float *lev) {
     }
     for (int j = 0; j < L; ++j)
       if (cnt[j] > 0) lev[j] = mean_rn32(sum[j], cnt[j]);
+    // reading: the level table stays an ordered table ("signpost" table on
+    // the kvquant_cache page). A cell left empty keeps its level, so when the
+    // quantile initialisation produced duplicates the lower copy can move past
+    // its frozen twin; re-sorting after each update keeps the order.
+    std::stable_sort(lev, lev + L);
   }
 }
 

@@ -90,6 +90,28 @@ def test_lloyd_properties_on_tiny_inputs(orc):
                 assert lev[j] == np.float32(uf[a == j].sum() / np.sum(a == j))
 
 
+def test_tie_heavy_data_keeps_an_ordered_table(orc):
+    """Quantile initialisation on heavily tied data yields duplicate levels;
+    the empty duplicate must not end up out of order (ordered signpost table),
+    and the result must still be a Lloyd fixed point of the same codebook."""
+    rng = np.random.default_rng(21)
+    seen_dup_init = 0
+    for trial in range(400):
+        u = f16(rng.choice([-2, -1, 0, 1, 2, 3], size=32, p=[.04, .1, .5, .26, .08, .02]))
+        init = orc.nuq_fit(u, 4, 0)
+        seen_dup_init += int(np.any(np.diff(init) == 0))
+        for it in range(1, 9):
+            lev = orc.nuq_fit(u, 4, it)
+            assert np.all(np.diff(lev) >= 0), (trial, it, lev)
+        uf = u.astype(np.float64)
+        lev = orc.nuq_fit(u, 4, 60)
+        a = _assign(uf, lev)
+        for j in range(4):
+            if np.any(a == j):
+                assert lev[j] == np.float32(uf[a == j].sum() / np.sum(a == j))
+    assert seen_dup_init > 50  # the case this pin is about does occur
+
+
 def test_one_bit_gaussian_closed_form(orc):
     # symmetrised sample: the 2-level Lloyd fixed point is +-mean|x|, which for
     # N(0,1) tends to sqrt(2/pi) (sampling sd ~ 0.005 at this size)
