@@ -172,6 +172,71 @@ int kvq_kivi_quant_dequant(uint16_t *keys, uint16_t *values, int32_t B, int32_t 
                            float eps, uint8_t *k_codes, float *k_scale, float *k_min,
                            uint8_t *v_codes, float *v_scale, float *v_min, void *stream);
 
+/* ------------------------------------------------------------------ NUQ
+ * ["veloxquant_mlx.cache.kvquant_cache module", module docstring] KVQuant-style
+ * non-uniform quantization. Keys get one table of L = 2^bits levels per
+ * channel (samples: the channel's values over tokens), values one table per
+ * token (samples: the token's D channels). Per vector of n samples:
+ *   k = floor(frac * n) (in double); tau = the (k+1)-th largest |x|; samples
+ *   with |x| > tau are outliers (at most k), kept exact in a side channel;
+ *   the inliers are fit by `lloyd_iters` Lloyd-Max iterations (unweighted
+ *   1-D k-means) from linear-interpolated quantiles at probabilities
+ *   (j + 1/2)/L; a sample's code is its nearest level (ties to the lower
+ *   index); an empty cell keeps its level; a level is the binary32 rounding
+ *   of its cell's exact mean (exact while a cell's |sum| < 2^29); after each
+ *   update the table is sorted ascending (an ordered "signpost" table).
+ * Attention sinks: when start_pos == 0 the first n_sink tokens of the call
+ * are sinks: exact, code 0, excluded from every fit and threshold, and their
+ * value-level rows are 0 (module docstring, "Attention Sink-Aware").
+ * Level lifecycle ("Level lifecycle"): fit_keys = 1 fits key levels and
+ * |key| thresholds on this call's non-sink tokens and writes them to
+ * key_levels / key_thresh (prefill); fit_keys = 0 reads them as given (frozen)
+ * and a key is an outlier iff |x| > key_thresh of its channel. Value levels
+ * are fit on every call.
+ * Outputs: codes packed LSB-first along D, [BH][S][D*bits/8] (outliers and
+ * sinks: code 0); outlier lists of (int32 flat index into this call's
+ * [BH][S][D], fp16 value) in ascending index order, keys and values
+ * separately, counts in out_counts[0] (keys) and [1] (values); optional
+ * reconstructions fp16 [BH][S][D] (inliers: fp16 of their level; outliers and
+ * sinks: x). */
+
+/* [host] Upper bound on the outlier-list length of one call (which = 0 keys,
+ * 1 values): keys fit_keys ? BH*D*floor(frac*n_fit) : BH*n_fit*D, values
+ * BH*n_fit*floor(frac*D), with n_fit = S minus the call's sink tokens.
+ * -1 on invalid arguments. */
+int64_t kvq_nuq_outlier_bound(int32_t BH, int32_t S, int32_t D, int32_t start_pos, int32_t n_sink,
+                              float frac, int32_t fit_keys, int32_t which);
+
+/* [host] Bytes of device workspace kvq_nuq_fit_quant needs for these sizes
+ * (scratch: per-channel thresholds, per-block counters, outlier staging).
+ * -1 on invalid arguments. */
+int64_t kvq_nuq_workspace_bytes(int32_t BH, int32_t S, int32_t D, int32_t bits, int32_t start_pos,
+                                int32_t n_sink, float frac, int32_t fit_keys);
+
+/* One NUQ call over fp16 keys and values [BH][S][D] (BH = batch*kv_heads).
+ *   bits 1..4 (L = 2^bits); D in {32, 64, 128, 256}; 0 <= frac < 1;
+ *   lloyd_iters >= 0; a key fit (fit_keys = 1) covers at most 8192 non-sink
+ *   tokens per call.
+ *   key_levels fp32 [BH][D][L] and key_thresh fp16 [BH][D]: written when
+ *   fit_keys = 1, read otherwise (each channel's table ascending, as a fit
+ *   leaves it). value_levels fp32 [BH][S][L] (written).
+ *   k_codes/v_codes uint8 [BH][S][D*bits/8]. k_opos/k_oval, v_opos/v_oval:
+ *   out_cap entries each; out_cap must be >= kvq_nuq_outlier_bound for both
+ *   lists (else KVQ_ERR_CAPACITY). out_counts int64 [2] (device).
+ *   k_recon / v_recon: optional (NULL to skip).
+ *   workspace: device memory of at least kvq_nuq_workspace_bytes, owned by
+ *   the caller, 16-byte aligned; its contents on entry do not matter.
+ * Calls that share a workspace must not overlap.
+ * Errors: KVQ_ERR_NULL, KVQ_ERR_BITS, KVQ_ERR_SHAPE, KVQ_ERR_ARG (frac,
+ * iters), KVQ_ERR_CAPACITY, KVQ_ERR_ALIGN, KVQ_ERR_HIP. */
+int kvq_nuq_fit_quant(const uint16_t *keys, const uint16_t *values, int32_t BH, int32_t S, int32_t D,
+                      int32_t start_pos, int32_t bits, float frac, int32_t lloyd_iters, int32_t n_sink,
+                      int32_t fit_keys, float *key_levels, uint16_t *key_thresh, float *value_levels,
+                      uint8_t *k_codes, uint8_t *v_codes, int32_t *k_opos, uint16_t *k_oval,
+                      int32_t *v_opos, uint16_t *v_oval, int64_t out_cap, int64_t *out_counts,
+                      uint16_t *k_recon, uint16_t *v_recon, void *workspace, int64_t workspace_bytes,
+                      void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,5 +1,6 @@
 // C-ABI entry points of libkvq: host-side validation, then kernel launch on
 // the caller's stream. Declarations and argument documentation: include/kvq.h.
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -272,6 +273,132 @@ int kvq_kivi_quant_dequant(uint16_t *keys, uint16_t *values, int32_t B, int32_t 
   a.gs = group_size;
   a.eps = eps;
   return hip_status(kvq::launch_kivi(a, (hipStream_t)stream), "kvq_kivi_quant_dequant launch");
+}
+
+// ------------------------------------------------------------------ NUQ
+namespace {
+struct NuqPlan {
+  int n_sink_eff, n_fit, key_cpc, val_cpc;
+  int64_t kb, vb;  // outlier bounds
+  int64_t k_blk_x, v_nblk;
+  int64_t off_ctr, off_kcut, off_kblk, off_vblk, off_kpos, off_kval, off_vpos, off_vval, total;
+};
+
+int64_t floor_frac(float frac, int64_t n) { return (int64_t)std::floor((double)frac * (double)n); }
+
+int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+int nuq_plan(int32_t BH, int32_t S, int32_t D, int32_t bits, int32_t start_pos, int32_t n_sink,
+             float frac, int32_t fit_keys, NuqPlan &p) {
+  if (bits < 1 || bits > 4) return fail(KVQ_ERR_BITS, "NUQ bits=%d is not in 1..4", bits);
+  if (BH <= 0 || S <= 0) return fail(KVQ_ERR_SHAPE, "BH and S must be positive");
+  if (D != 32 && D != 64 && D != 128 && D != 256) return fail(KVQ_ERR_SHAPE, "NUQ head_dim must be 32, 64, 128 or 256 (got %d)", D);
+  if (!(frac >= 0.0f && frac < 1.0f)) return fail(KVQ_ERR_ARG, "outlier fraction must be in [0, 1)");
+  if (start_pos < 0 || n_sink < 0) return fail(KVQ_ERR_ARG, "start_pos and n_sink must be >= 0");
+  if ((int64_t)BH * S * D >= ((int64_t)1 << 31)) return fail(KVQ_ERR_SHAPE, "BH*S*D must be < 2^31 (int32 outlier positions)");
+  if (BH > 65535) return fail(KVQ_ERR_SHAPE, "BH must be <= 65535");
+  p.n_sink_eff = start_pos == 0 ? (n_sink < S ? n_sink : S) : 0;
+  p.n_fit = S - p.n_sink_eff;
+  if (fit_keys && p.n_fit > 8192) return fail(KVQ_ERR_SHAPE, "a key fit covers at most 8192 non-sink tokens per call (got %d)", p.n_fit);
+  int chunks = (p.n_fit + 127) / 128, cpc = 1;
+  while (cpc < chunks) cpc <<= 1;
+  p.key_cpc = cpc;
+  p.val_cpc = D <= 128 ? 1 : 2;
+  p.kb = fit_keys ? (int64_t)BH * D * floor_frac(frac, p.n_fit) : (int64_t)BH * p.n_fit * D;
+  p.vb = (int64_t)BH * p.n_fit * floor_frac(frac, D);
+  const int rpw = 512 / D;
+  p.k_blk_x = (S + 4 * rpw - 1) / (4 * rpw);
+  p.v_nblk = ((int64_t)BH * S + (64 / p.val_cpc) - 1) / (64 / p.val_cpc);
+  int64_t o = 0;
+  p.off_ctr = o; o = align256(o + 16);
+  p.off_kcut = o; o = align256(o + (int64_t)BH * D * 16 * 2);
+  p.off_kblk = o; o = align256(o + p.k_blk_x * BH * 8);
+  p.off_vblk = o; o = align256(o + p.v_nblk * 8);
+  p.off_kpos = o; o = align256(o + p.kb * 4);
+  p.off_kval = o; o = align256(o + p.kb * 2);
+  p.off_vpos = o; o = align256(o + p.vb * 4);
+  p.off_vval = o; o = align256(o + p.vb * 2);
+  p.total = o;
+  return KVQ_OK;
+}
+}  // namespace
+
+int64_t kvq_nuq_outlier_bound(int32_t BH, int32_t S, int32_t D, int32_t start_pos, int32_t n_sink,
+                              float frac, int32_t fit_keys, int32_t which) {
+  NuqPlan p;
+  if (nuq_plan(BH, S, D, 1, start_pos, n_sink, frac, fit_keys, p) != KVQ_OK) return -1;
+  return which == 0 ? p.kb : (which == 1 ? p.vb : -1);
+}
+
+int64_t kvq_nuq_workspace_bytes(int32_t BH, int32_t S, int32_t D, int32_t bits, int32_t start_pos,
+                                int32_t n_sink, float frac, int32_t fit_keys) {
+  NuqPlan p;
+  if (nuq_plan(BH, S, D, bits, start_pos, n_sink, frac, fit_keys, p) != KVQ_OK) return -1;
+  return p.total;
+}
+
+int kvq_nuq_fit_quant(const uint16_t *keys, const uint16_t *values, int32_t BH, int32_t S, int32_t D,
+                      int32_t start_pos, int32_t bits, float frac, int32_t lloyd_iters, int32_t n_sink,
+                      int32_t fit_keys, float *key_levels, uint16_t *key_thresh, float *value_levels,
+                      uint8_t *k_codes, uint8_t *v_codes, int32_t *k_opos, uint16_t *k_oval,
+                      int32_t *v_opos, uint16_t *v_oval, int64_t out_cap, int64_t *out_counts,
+                      uint16_t *k_recon, uint16_t *v_recon, void *workspace, int64_t workspace_bytes,
+                      void *stream) {
+  NuqPlan p;
+  int rc = nuq_plan(BH, S, D, bits, start_pos, n_sink, frac, fit_keys, p);
+  if (rc) return rc;
+  if (lloyd_iters < 0 || lloyd_iters > 1000) return fail(KVQ_ERR_ARG, "lloyd_iters must be in [0, 1000]");
+  if (!keys || !values || !key_levels || !key_thresh || !value_levels || !k_codes || !v_codes ||
+      !k_opos || !k_oval || !v_opos || !v_oval || !out_counts || !workspace)
+    return fail(KVQ_ERR_NULL, "a required NUQ pointer is NULL");
+  if (out_cap < p.kb || out_cap < p.vb)
+    return fail(KVQ_ERR_CAPACITY, "out_cap=%lld below the outlier bound (keys %lld, values %lld)",
+                (long long)out_cap, (long long)p.kb, (long long)p.vb);
+  if (workspace_bytes < p.total)
+    return fail(KVQ_ERR_CAPACITY, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
+                (long long)p.total);
+  for (const void *q : {(const void *)keys, (const void *)values, (const void *)k_codes, (const void *)v_codes,
+                        (const void *)k_recon, (const void *)v_recon, (const void *)workspace})
+    if (q && !aligned(q, 16)) return fail(KVQ_ERR_ALIGN, "fp16 tensors, code buffers and the workspace need 16-byte alignment");
+  for (const void *q : {(const void *)key_levels, (const void *)value_levels, (const void *)k_opos, (const void *)v_opos})
+    if (!aligned(q, 4)) return fail(KVQ_ERR_ALIGN, "level tables and position lists need 4-byte alignment");
+  if (!aligned(key_thresh, 2) || !aligned(k_oval, 2) || !aligned(v_oval, 2) || !aligned(out_counts, 8))
+    return fail(KVQ_ERR_ALIGN, "misaligned threshold, value list or counts");
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  kvq::NuqArgs a{};
+  a.keys = keys;
+  a.values = values;
+  a.BH = BH;
+  a.S = S;
+  a.D = D;
+  a.bits = bits;
+  a.iters = lloyd_iters;
+  a.fit_keys = fit_keys ? 1 : 0;
+  a.n_sink_eff = p.n_sink_eff;
+  a.frac = frac;
+  a.key_levels = key_levels;
+  a.key_thresh = key_thresh;
+  a.value_levels = value_levels;
+  a.k_codes = k_codes;
+  a.v_codes = v_codes;
+  a.k_opos = k_opos;
+  a.v_opos = v_opos;
+  a.k_oval = k_oval;
+  a.v_oval = v_oval;
+  a.out_counts = out_counts;
+  a.k_recon = k_recon;
+  a.v_recon = v_recon;
+  a.ws_ctr = reinterpret_cast<uint32_t *>(ws + p.off_ctr);
+  a.ws_kcut = reinterpret_cast<uint16_t *>(ws + p.off_kcut);
+  a.ws_kblk = reinterpret_cast<uint32_t *>(ws + p.off_kblk);
+  a.ws_vblk = reinterpret_cast<uint32_t *>(ws + p.off_vblk);
+  a.ws_kpos = reinterpret_cast<int32_t *>(ws + p.off_kpos);
+  a.ws_kval = reinterpret_cast<uint16_t *>(ws + p.off_kval);
+  a.ws_vpos = reinterpret_cast<int32_t *>(ws + p.off_vpos);
+  a.ws_vval = reinterpret_cast<uint16_t *>(ws + p.off_vval);
+  a.k_blk_x = p.k_blk_x;
+  a.v_nblk = p.v_nblk;
+  return hip_status(kvq::launch_nuq(a, p.key_cpc, p.val_cpc, (hipStream_t)stream), "kvq_nuq_fit_quant launch");
 }
 
 }  // extern "C"

@@ -44,4 +44,27 @@ struct KiviArgs {
 
 hipError_t launch_kivi(const KiviArgs &a, hipStream_t st);
 
+struct NuqArgs {
+  const uint16_t *keys, *values;   // fp16 [BH][S][D]
+  int32_t BH, S, D, bits, iters, fit_keys, n_sink_eff;
+  float frac;
+  float *key_levels;               // [BH][D][L]
+  uint16_t *key_thresh;            // [BH][D]
+  float *value_levels;             // [BH][S][L]
+  uint8_t *k_codes, *v_codes;      // [BH][S][D*bits/8]
+  int32_t *k_opos, *v_opos;
+  uint16_t *k_oval, *v_oval;
+  int64_t *out_counts;             // [2]
+  uint16_t *k_recon, *v_recon;     // optional
+  // workspace
+  uint32_t *ws_ctr;                // 4 counters
+  uint16_t *ws_kcut;               // [BH][D][16] cut keys
+  uint32_t *ws_kblk, *ws_vblk;     // per block (staging base, count -> final offset)
+  int32_t *ws_kpos, *ws_vpos;      // staging
+  uint16_t *ws_kval, *ws_vval;
+  int64_t k_blk_x, v_nblk;
+};
+
+hipError_t launch_nuq(const NuqArgs &a, int key_cpc, int val_cpc, hipStream_t st);
+
 }  // namespace kvq

@@ -48,7 +48,7 @@ _SIGS = {
     "kvq_kivi_boundary": (_L, [_L, _I, _I]),
     "kvq_kivi_quant_dequant": (C.c_int, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F,
                                          _P, _P, _P, _P, _P, _P, _P]),
-    "kvq_nuq_workspace_bytes": (_L, [_I, _I, _I, _I, _I, _F, _I, _I]),
+    "kvq_nuq_workspace_bytes": (_L, [_I, _I, _I, _I, _I, _I, _F, _I]),
     "kvq_nuq_outlier_bound": (_L, [_I, _I, _I, _I, _I, _F, _I, _I]),
     "kvq_nuq_fit_quant": (C.c_int, [_P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I,
                                     _P, _P, _P, _P, _P, _P, _P, _P, _P, _L, _P, _P, _P, _P, _L, _P]),
@@ -169,3 +169,28 @@ def kvq_kivi_quant_dequant(keys, values, lo: int, hi: int, bits: int, group_size
     _err(lib().kvq_kivi_quant_dequant(_ptr(keys), _ptr(values), B, H, S_cap, D, lo, hi, bits,
                                       group_size, eps, _ptr(k_codes), _ptr(k_scale), _ptr(k_min),
                                       _ptr(v_codes), _ptr(v_scale), _ptr(v_min), _stream(stream)))
+
+
+# ------------------------------------------------------------------ NUQ
+def kvq_nuq_outlier_bound(BH, S, D, start_pos, n_sink, frac, fit_keys, which) -> int:
+    return lib().kvq_nuq_outlier_bound(BH, S, D, start_pos, n_sink, frac, int(fit_keys), which)
+
+
+def kvq_nuq_workspace_bytes(BH, S, D, bits, start_pos, n_sink, frac, fit_keys) -> int:
+    return lib().kvq_nuq_workspace_bytes(BH, S, D, bits, start_pos, n_sink, frac, int(fit_keys))
+
+
+def kvq_nuq_fit_quant(keys, values, start_pos, bits, frac, lloyd_iters, n_sink, fit_keys,
+                      key_levels, key_thresh, value_levels, k_codes, v_codes, k_opos, k_oval,
+                      v_opos, v_oval, out_counts, workspace, k_recon=None, v_recon=None, stream=None):
+    """keys/values fp16 [BH][S][D]; all outputs preallocated device tensors (see include/kvq.h)."""
+    _dev(keys, values, key_levels, key_thresh, value_levels, k_codes, v_codes, k_opos, k_oval,
+         v_opos, v_oval, out_counts, workspace, k_recon, v_recon)
+    BH, S, D = (int(x) for x in keys.shape)
+    out_cap = min(int(k_opos.numel()), int(k_oval.numel()), int(v_opos.numel()), int(v_oval.numel()))
+    _err(lib().kvq_nuq_fit_quant(_ptr(keys), _ptr(values), BH, S, D, start_pos, bits, frac,
+                                 lloyd_iters, n_sink, int(fit_keys), _ptr(key_levels),
+                                 _ptr(key_thresh), _ptr(value_levels), _ptr(k_codes), _ptr(v_codes),
+                                 _ptr(k_opos), _ptr(k_oval), _ptr(v_opos), _ptr(v_oval), out_cap,
+                                 _ptr(out_counts), _ptr(k_recon), _ptr(v_recon), _ptr(workspace),
+                                 int(workspace.numel() * workspace.element_size()), _stream(stream)))

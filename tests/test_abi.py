@@ -134,3 +134,49 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(kvq.KvqError):
         kvq.kvq_quant_sym(lay, x, None, torch.zeros(4, dtype=torch.int32),
                           torch.zeros(1, dtype=torch.uint8), torch.zeros(1, dtype=torch.int16), None, None)
+
+
+def _nuq(k=FAKE, v=FAKE, BH=2, S=64, D=128, sp=0, bits=3, frac=0.01, iters=8, ns=4, fk=1, cap=None,
+         ws=FAKE, wsb=None, recon=None):
+    L = kvq.lib()
+    if cap is None:
+        cap = max(kvq.kvq_nuq_outlier_bound(BH, S, D, sp, ns, frac, fk, 0),
+                  kvq.kvq_nuq_outlier_bound(BH, S, D, sp, ns, frac, fk, 1), 1)
+    if wsb is None:
+        wsb = max(kvq.kvq_nuq_workspace_bytes(BH, S, D, bits, sp, ns, frac, fk), 1)
+    return L.kvq_nuq_fit_quant(k, v, BH, S, D, sp, bits, frac, iters, ns, fk, FAKE, FAKE, FAKE, FAKE,
+                               FAKE, FAKE, FAKE, FAKE, FAKE, cap, FAKE, recon, recon, ws, wsb, None)
+
+
+def test_nuq_host_helpers():
+    import math
+    f = 0.01
+    for BH, S, D, sp, ns, fk in [(32, 4096, 128, 0, 4, 1), (32, 1, 128, 4096, 4, 0), (3, 70, 64, 0, 4, 1),
+                                 (2, 3, 32, 0, 4, 1), (1, 100, 256, 5, 4, 1)]:
+        nse = min(ns, S) if sp == 0 else 0
+        nf = S - nse
+        kb = BH * D * math.floor(float(__import__("numpy").float32(f)) * nf) if fk else BH * nf * D
+        vb = BH * nf * math.floor(float(__import__("numpy").float32(f)) * D)
+        assert kvq.kvq_nuq_outlier_bound(BH, S, D, sp, ns, f, fk, 0) == kb
+        assert kvq.kvq_nuq_outlier_bound(BH, S, D, sp, ns, f, fk, 1) == vb
+        assert kvq.kvq_nuq_workspace_bytes(BH, S, D, 3, sp, ns, f, fk) >= 6 * (kb + vb)
+    assert kvq.kvq_nuq_workspace_bytes(2, 64, 96, 3, 0, 4, 0.01, 1) == -1
+    assert kvq.kvq_nuq_outlier_bound(2, 64, 128, 0, 4, 1.0, 1, 0) == -1
+
+
+def test_nuq_validation_errors():
+    assert _nuq(bits=5) == kvq.KVQ_ERR_BITS
+    assert _nuq(bits=0) == kvq.KVQ_ERR_BITS
+    assert _nuq(D=96) == kvq.KVQ_ERR_SHAPE
+    assert _nuq(S=0) == kvq.KVQ_ERR_SHAPE
+    assert _nuq(S=8197, ns=4) == kvq.KVQ_ERR_SHAPE          # key fit over 8193 tokens
+    assert _nuq(frac=1.0) == kvq.KVQ_ERR_ARG
+    assert _nuq(frac=-0.1) == kvq.KVQ_ERR_ARG
+    assert _nuq(iters=-1) == kvq.KVQ_ERR_ARG
+    assert _nuq(k=None) == kvq.KVQ_ERR_NULL
+    assert _nuq(ws=None) == kvq.KVQ_ERR_NULL
+    assert _nuq(S=640, frac=0.05, cap=10) == kvq.KVQ_ERR_CAPACITY
+    assert _nuq(wsb=16) == kvq.KVQ_ERR_CAPACITY
+    assert _nuq(k=FAKE + 8) == kvq.KVQ_ERR_ALIGN
+    assert _nuq(ws=FAKE + 4) == kvq.KVQ_ERR_ALIGN
+    assert _nuq(recon=FAKE + 2) == kvq.KVQ_ERR_ALIGN
