@@ -236,6 +236,229 @@ class Kivi:
                 "sample": "%d (batch, head) slices of 8192 x 64 keys and values (%.1f s)" % (nbh, dt)}
 
 
+# --------------------------------------------------------------------------- NUQ
+class Nuq:
+    """Batch 4 x 8 KV heads (BH=32), 4096-token prefill, D=128, 3 bits, 1% outliers,
+    8 Lloyd iterations, 4 sinks; then 64 single-token decode calls against the
+    frozen key levels. Student-t(4) K/V. The 64 MiB working set is rotated over
+    16 resident copies (~1 GiB) so the 256 MB last-level cache does not serve it."""
+
+    def __init__(self, torch, args):
+        self.torch = torch
+        self.BH, self.S, self.D, self.bits = 32, 4096, 128, 3
+        self.frac, self.iters, self.ns, self.n_dec = 0.01, 8, 4, 64
+        self.copies = 16
+        self.name = "nuq"
+
+    def setup(self):
+        torch = self.torch
+        from kv_cache_quantization_row_amd import inputs, kvq
+
+        self.kvq = kvq
+        d = torch.device("cuda:0")
+        BH, S, D, L = self.BH, self.S, self.D, 1 << self.bits
+        self.k = [inputs.student_t((BH, S, D), 4, seed=1004 + 10 * i, device=d) for i in range(self.copies)]
+        self.v = [inputs.student_t((BH, S, D), 4, seed=1005 + 10 * i, device=d) for i in range(self.copies)]
+        self.kd = inputs.student_t((self.n_dec, BH, 1, D), 4, seed=5000, device=d)
+        self.vd = inputs.student_t((self.n_dec, BH, 1, D), 4, seed=6000, device=d)
+        z = lambda *sh, dt=torch.float32: torch.zeros(sh, dtype=dt, device=d)
+        self.kl, self.kt = z(BH, D, L), z(BH, D, dt=torch.int16)
+        self.vl, self.vl1 = z(BH, S, L), z(BH, 1, L)
+        cb = D * self.bits // 8
+        self.kc, self.vc = z(BH, S, cb, dt=torch.uint8), z(BH, S, cb, dt=torch.uint8)
+        self.kc1, self.vc1 = z(BH, 1, cb, dt=torch.uint8), z(BH, 1, cb, dt=torch.uint8)
+        cap = max(kvq.kvq_nuq_outlier_bound(BH, S, D, 0, self.ns, self.frac, 1, w) for w in (0, 1))
+        cap1 = max(kvq.kvq_nuq_outlier_bound(BH, 1, D, S, self.ns, self.frac, 0, w) for w in (0, 1))
+        self.lists = [z(cap, dt=torch.int32), z(cap, dt=torch.int16), z(cap, dt=torch.int32), z(cap, dt=torch.int16)]
+        self.lists1 = [z(cap1, dt=torch.int32), z(cap1, dt=torch.int16), z(cap1, dt=torch.int32), z(cap1, dt=torch.int16)]
+        self.cnt, self.cnt1 = z(2, dt=torch.int64), z(2, dt=torch.int64)
+        self.ws = z(kvq.kvq_nuq_workspace_bytes(BH, S, D, self.bits, 0, self.ns, self.frac, 1), dt=torch.uint8)
+        self.ws1 = z(kvq.kvq_nuq_workspace_bytes(BH, 1, D, self.bits, S, self.ns, self.frac, 0), dt=torch.uint8)
+        self.i = 0
+        torch.cuda.synchronize()
+
+    def step(self, tm):
+        kvq = self.kvq
+        c = self.i % self.copies
+        self.i += 1
+        with tm.span("nuq_prefill"):
+            kvq.kvq_nuq_fit_quant(self.k[c], self.v[c], 0, self.bits, self.frac, self.iters, self.ns, 1,
+                                  self.kl, self.kt, self.vl, self.kc, self.vc, *self.lists, self.cnt, self.ws)
+        with tm.span("nuq_decode_x%d" % self.n_dec):
+            for t in range(self.n_dec):
+                kvq.kvq_nuq_fit_quant(self.kd[t], self.vd[t], self.S + t, self.bits, self.frac, self.iters,
+                                      self.ns, 0, self.kl, self.kt, self.vl1, self.kc1, self.vc1,
+                                      *self.lists1, self.cnt1, self.ws1)
+
+    def elems(self):
+        return 2 * self.BH * self.D * (self.S + self.n_dec)
+
+    def kernel_bytes(self, name):
+        BH, S, D, L = self.BH, self.S, self.D, 1 << self.bits
+        n_out = int(self.cnt.sum().item())
+        if name == "nuq_prefill":
+            return (2 * 2 * BH * S * D + 2 * BH * S * D * self.bits / 8 + BH * D * (4 * L + 2)
+                    + BH * S * 4 * L + 6 * n_out)
+        n_out1 = int(self.cnt1.sum().item())
+        return self.n_dec * (2 * 2 * BH * D + 2 * BH * D * self.bits / 8 + BH * D * (4 * L + 2)
+                             + BH * 4 * L + 6 * n_out1)
+
+    def config(self):
+        return {"workload": "KVQuant-style NUQ 3-bit: batch 4 x 8 KV heads, D=128, 4096-token prefill "
+                            "(1%% outliers, 8 Lloyd iterations, 4 sinks) + %d decode calls" % self.n_dec,
+                "bits": self.bits, "outlier_fraction": self.frac, "lloyd_iters": self.iters,
+                "n_sink": self.ns, "rotation_copies": self.copies}
+
+    def cpu_baseline(self, budget_tokens):
+        import numpy as np
+        import oracle
+        from kv_cache_quantization_row_amd import inputs
+
+        nbh = 1
+        k = inputs.student_t((nbh, self.S, self.D), 4, seed=1004).numpy().view(np.uint16)
+        v = inputs.student_t((nbh, self.S, self.D), 4, seed=1005).numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        oracle.nuq_fit_quant(k, v, 0, self.bits, self.frac, self.iters, self.ns, 1)
+        dt = time.perf_counter() - t0
+        return {"value": round(2 * 2 * nbh * self.S * self.D / dt / 1e9, 5), "unit": "GB/s", "cores": 1,
+                "kind": "oracle", "sample": "prefill of 1 of 32 (batch, head) slices, 4096 x 128 K and V (%.1f s)" % dt}
+
+
+# --------------------------------------------------------------------------- long context
+class LongContext:
+    """One 262,144-token sequence, 16 layers x 4 KV heads x D=256, q6, page 16:
+    quantized in 64 chunks of 4096 tokens (one launch per chunk, all layers),
+    1,024 single-token appends, then a full dequant of 263,168 tokens."""
+
+    def __init__(self, torch, args):
+        self.torch = torch
+        self.L, self.H, self.D, self.P, self.bits = 16, 4, 256, 16, 6
+        self.T, self.CH, self.N_DEC = 262144, 4096, args.decode_steps_long
+        self.total = self.T + self.N_DEC
+        self.name = "long_context"
+
+    def setup(self):
+        torch = self.torch
+        from kv_cache_quantization_row_amd import inputs, kvq
+
+        self.kvq = kvq
+        d = torch.device("cuda:0")
+        L, H, D, P = self.L, self.H, self.D, self.P
+        self.bt, self.num_pages = inputs.paged_block_table(1, self.total, P, seed=5005)
+        nch = self.T // self.CH
+        self.slots = [inputs.slot_mapping_for(self.bt, P, c * self.CH, self.CH).to(d) for c in range(nch)]
+        self.slot_dec = inputs.slot_mapping_for(self.bt, P, self.T, self.N_DEC).to(d)
+        log("generating %d chunks of %d layers x %d tokens" % (nch, L, self.CH))
+        self.k = torch.empty((nch, L, self.CH, H, D), dtype=torch.float16, device=d)
+        self.v = torch.empty_like(self.k)
+        for l in range(L):
+            self.k[:, l] = inputs.sym_layer(self.T, H, D, seed=7100 + l, device=d, channel_seed=8100 + l).view(nch, self.CH, H, D)
+            self.v[:, l] = inputs.sym_layer(self.T, H, D, seed=7200 + l, device=d, channel_seed=8200 + l).view(nch, self.CH, H, D)
+        self.kd = inputs.sym_layer(self.N_DEC * L, H, D, seed=7300, device=d).view(self.N_DEC, L, 1, H, D)
+        self.vd = inputs.sym_layer(self.N_DEC * L, H, D, seed=7400, device=d).view(self.N_DEC, L, 1, H, D)
+        slots = self.num_pages * P
+        pd = kvq.kvq_packed_dim(D, self.bits)
+        self.kc = torch.empty((L, slots, H, pd), dtype=torch.uint8, device=d)
+        self.vc = torch.empty_like(self.kc)
+        self.ks = torch.empty((L, slots, H), dtype=torch.int16, device=d)
+        self.vs = torch.empty_like(self.ks)
+        self.ko = torch.empty((L, 1, self.total, H, D), dtype=torch.float16, device=d)
+        self.vo = torch.empty_like(self.ko)
+        self.bt_d = self.bt.to(d)
+        self.lens = torch.full((1,), self.total, dtype=torch.int32, device=d)
+        self.lay = kvq.layout(L, self.num_pages, P, H, D, self.bits)
+        torch.cuda.synchronize()
+
+    def step(self, tm):
+        kvq = self.kvq
+        with tm.span("quant_chunks_q6_x%d" % len(self.slots)):
+            for c, sm in enumerate(self.slots):
+                kvq.kvq_quant_sym(self.lay, self.k[c], self.v[c], sm, self.kc, self.ks, self.vc, self.vs)
+        with tm.span("decode_append_q6_x%d" % self.N_DEC):
+            for i in range(self.N_DEC):
+                kvq.kvq_quant_sym(self.lay, self.kd[i], self.vd[i], self.slot_dec[i:i + 1], self.kc, self.ks,
+                                  self.vc, self.vs)
+        with tm.span("dequant_full_q6"):
+            kvq.kvq_dequant_sym(self.lay, self.kc, self.ks, self.vc, self.vs, self.bt_d, self.lens, self.ko, self.vo)
+
+    def elems(self):
+        return 2 * self.L * self.H * self.D * (self.T + self.N_DEC + self.total)
+
+    def kernel_bytes(self, name):
+        per = 2 + self.bits / 8 + 2 / self.D
+        rows = 2 * self.L * self.H
+        if name.startswith("quant_chunks"):
+            return rows * self.T * self.D * per
+        if name.startswith("dequant_full"):
+            return rows * self.total * self.D * per
+        return rows * self.N_DEC * self.D * per
+
+    def config(self):
+        return {"workload": "long-context q6 paged cache: one 262,144-token sequence, 16 layers x 4 KV heads x "
+                            "D=256, 64 chunks of 4096 tokens + %d appends + full dequant of %d tokens"
+                            % (self.N_DEC, self.total), "bits": self.bits,
+                "packed_GiB": round(self.kvq.kvq_sym_cache_bytes(self.T, 16, 4, 256, 6) / 2 ** 30, 4)}
+
+    def cpu_baseline(self, budget_tokens):
+        return None
+
+
+# --------------------------------------------------------------------------- single layer
+class SingleLayer:
+    """One layer, K and V each [1024][4][256], q6, 64 pages of 16 (slots in token
+    order), then the read-back; 256 resident copies (~1 GiB) rotated per call."""
+
+    def __init__(self, torch, args):
+        self.torch = torch
+        self.T, self.H, self.D, self.P, self.bits, self.copies = 1024, 4, 256, 16, 6, 256
+        self.name = "single_layer"
+
+    def setup(self):
+        torch = self.torch
+        from kv_cache_quantization_row_amd import inputs, kvq
+
+        self.kvq = kvq
+        d = torch.device("cuda:0")
+        T, H, D, P, C = self.T, self.H, self.D, self.P, self.copies
+        self.k = torch.stack([inputs.sym_layer(T, H, D, seed=1001 + 2 * i, device=d) for i in range(C)])[:, None]
+        self.v = torch.stack([inputs.sym_layer(T, H, D, seed=1002 + 2 * i, device=d) for i in range(C)])[:, None]
+        pd = kvq.kvq_packed_dim(D, self.bits)
+        self.kc = torch.empty((C, T, H, pd), dtype=torch.uint8, device=d)
+        self.vc = torch.empty_like(self.kc)
+        self.ks = torch.empty((C, T, H), dtype=torch.int16, device=d)
+        self.vs = torch.empty_like(self.ks)
+        self.ko = torch.empty((C, 1, 1, T, H, D), dtype=torch.float16, device=d)
+        self.vo = torch.empty_like(self.ko)
+        self.slot = torch.arange(T, dtype=torch.int32, device=d)
+        self.bt = torch.arange(T // P, dtype=torch.int32, device=d)[None]
+        self.lens = torch.full((1,), T, dtype=torch.int32, device=d)
+        self.lay = kvq.layout(1, T // P, P, H, D, self.bits)
+        torch.cuda.synchronize()
+
+    def step(self, tm):
+        kvq = self.kvq
+        with tm.span("quant_q6_x%d" % self.copies):
+            for c in range(self.copies):
+                kvq.kvq_quant_sym(self.lay, self.k[c], self.v[c], self.slot, self.kc[c], self.ks[c], self.vc[c], self.vs[c])
+        with tm.span("dequant_q6_x%d" % self.copies):
+            for c in range(self.copies):
+                kvq.kvq_dequant_sym(self.lay, self.kc[c], self.ks[c], self.vc[c], self.vs[c], self.bt, self.lens,
+                                    self.ko[c], self.vo[c])
+
+    def elems(self):
+        return 2 * 2 * self.T * self.H * self.D * self.copies
+
+    def kernel_bytes(self, name):
+        return 2 * self.T * self.H * self.D * (2 + self.bits / 8 + 2 / self.D) * self.copies
+
+    def config(self):
+        return {"workload": "single-layer q6 round trip: K and V [1024][4][256], 64 pages of 16, rotated over "
+                            "%d resident copies" % self.copies, "bits": self.bits}
+
+    def cpu_baseline(self, budget_tokens):
+        return None
+
+
 class Copy:
     """Plain device-to-device copy of 4 GiB (torch copy kernel): the practical
     HBM ceiling on this machine and the reference for scaling traffic counters."""
@@ -269,7 +492,8 @@ class Copy:
         return None
 
 
-WORKLOADS = {"paged_sym": PagedSym, "kivi": Kivi, "copy": Copy}
+WORKLOADS = {"paged_sym": PagedSym, "kivi": Kivi, "nuq": Nuq, "long_context": LongContext,
+             "single_layer": SingleLayer, "copy": Copy}
 
 
 def main():
@@ -282,6 +506,7 @@ def main():
     ap.add_argument("--kivi-bits", default="2,4")
     ap.add_argument("--prefill-tokens", type=int, default=32768)
     ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--decode-steps-long", type=int, default=1024)
     ap.add_argument("--cpu-tokens", type=int, default=65536)
     ap.add_argument("--page-order", default="random", choices=["random", "identity"],
                     help="pool page assignment of the paged workload (random = fragmented pool)")
@@ -329,7 +554,8 @@ def main():
         gbs = nbytes / (ms / 1e3) / 1e9
         kernels[name] = {"avg_ms": round(ms, 4), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
     totals = {n: means[n] * c for n, c in tm.count().items()}
-    dom = max((n for n in totals if "decode" not in n), key=lambda n: totals[n])
+    cands = [n for n in totals if "decode" not in n] or list(totals)
+    dom = max(cands, key=lambda n: totals[n])
     roof = {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["GB/s"], "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": kernels[dom]["frac_hbm"], "traffic": None}
 
