@@ -30,6 +30,43 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, 8 TB/s
 METRIC = "KV quant+pack / unpack+dequant GB/s (fp16-equiv) and % of HBM peak, 1 GPU"
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_sym_kivi.md")
+CSRC = os.path.join(ROOT, "kv_cache_quantization_row_amd", "csrc")
+
+
+def measured_traffic(kernel_class):
+    """HBM bytes per launch of a kernel class from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE summary, or None when there is no entry or the
+    kernel source changed since the counters were taken."""
+    import hashlib
+    import re
+
+    if kernel_class.startswith("quant_prefill_q"):
+        b = kernel_class[-1]
+        names, src = ["sym_quant_fast<%s, 16, 2>" % b], "sym.hip"
+    elif kernel_class.startswith("dequant_sweep_q"):
+        b = kernel_class[-1]
+        names, src = ["sym_dequant_page<%s, 256>" % b], "sym.hip"
+    elif kernel_class.startswith("kivi_keys_values_b"):
+        b = kernel_class[-1]
+        names, src = ["kivi_keys_fast<%s, 8, 4>" % b, "kivi_values_fast<%s, 8, 4, 2>" % b], "kivi.hip"
+    else:
+        return None
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    sha = hashlib.sha1(open(os.path.join(CSRC, src), "rb").read()).hexdigest()
+    best = {}
+    for line in open(TRAFFIC_FILE):
+        m = re.match(r"traffic (.+?) grid=(\d+) bytes=(\d+) src_sha1=([0-9a-f]+)", line.strip())
+        if m and m.group(1) in names and m.group(4) == sha:
+            g = int(m.group(2))
+            if g > best.get(m.group(1), (0, 0))[0]:
+                best[m.group(1)] = (g, int(m.group(3)))
+    if len(best) != len(names):
+        return None
+    return sum(v[1] for v in best.values())
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -557,7 +594,8 @@ def main():
     cands = [n for n in totals if "decode" not in n] or list(totals)
     dom = max(cands, key=lambda n: totals[n])
     roof = {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["GB/s"], "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": kernels[dom]["frac_hbm"], "traffic": None}
+            "unit": "GB/s", "frac": kernels[dom]["frac_hbm"], "traffic": measured_traffic(dom),
+            "algorithmic_bytes": int(wl.kernel_bytes(dom))}
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -68,7 +68,7 @@ def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise KvqError(KVQ_ERR_HIP, "libkvq.so is not built (run __graft_entry__.build())")
+            raise KvqError(KVQ_ERR_HIP, "libkvq.so is not built (python -m kv_cache_quantization_row_amd.build)")
         L = C.CDLL(LIB_PATH)
         for name in declared_symbols():
             fn = getattr(L, name)
