@@ -47,6 +47,17 @@ __device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
   return v;
 }
 
+template <int N>
+__device__ __forceinline__ uint32_t group_min_u32(uint32_t v) {
+  if constexpr (N >= 2) v = min(v, dpp<DPP_XOR1>(v));
+  if constexpr (N >= 4) v = min(v, dpp<DPP_XOR2>(v));
+  if constexpr (N >= 8) v = min(v, dpp<DPP_HALF_MIRROR>(v));
+  if constexpr (N >= 16) v = min(v, dpp<DPP_MIRROR>(v));
+  if constexpr (N >= 32) v = min(v, (uint32_t)__shfl_xor((int)v, 16));
+  if constexpr (N >= 64) v = min(v, (uint32_t)__shfl_xor((int)v, 32));
+  return v;
+}
+
 // Min and max over groups of N consecutive lanes of a float.
 template <int N>
 __device__ __forceinline__ void group_minmax_f32(float &mn, float &mx) {

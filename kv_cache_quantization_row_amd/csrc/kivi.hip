@@ -55,6 +55,56 @@ __device__ __forceinline__ void store_codes8(uint8_t *dst, const uint32_t *c) {
   else *reinterpret_cast<uint64_t *>(dst) = v;
 }
 
+// ----- exact quotient via the group's reciprocal
+// t' = RN(a * RN(1/scale)) is within 2^-22 |a/scale| of the IEEE quotient
+// RN(a/scale) (two roundings of 2^-24 each, plus the quotient's own). If t'
+// is farther than (levels+2)*2^-21 from every half-integer, t' and the IEEE
+// quotient round (ties-to-even) to the same integer, and beyond levels+1.5
+// both clamp to levels. Otherwise the IEEE division is done; on this
+// workload about 1e-4 of the elements take that branch.
+// Eight elements at a time: the quotients a[i]*inv[i] and their tie flags
+// are computed branch-free; only if some lane of the wave has a flagged
+// element in this group of eight does the wave redo the group with IEEE
+// divisions (one wave-uniform branch per group).
+template <int BITS>
+__device__ __forceinline__ void kivi_codes8(const float *a, const float *scale, const float *inv, float *cf) {
+  constexpr float LEV = (float)((1 << BITS) - 1);
+  constexpr float MARGIN = (LEV + 2.0f) * 4.76837158203125e-07f;  // (levels+2) * 2^-21
+  float t[8];
+  bool near = false;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    t[i] = a[i] * inv[i];
+    near |= __builtin_fabsf(__builtin_amdgcn_fractf(t[i]) - 0.5f) <= MARGIN;
+  }
+  if (__any(near)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bool ni = __builtin_fabsf(__builtin_amdgcn_fractf(t[i]) - 0.5f) <= MARGIN;
+      t[i] = ni ? a[i] / scale[i] : t[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) cf[i] = __builtin_amdgcn_fmed3f(__builtin_rintf(t[i]), 0.0f, LEV);
+}
+
+// packed 16-bit order keys of fp16 pairs (min/max without NaN canonicalisation)
+__device__ __forceinline__ uint32_t kkey_pair(uint32_t w) {
+  typedef short s2 __attribute__((ext_vector_type(2)));
+  const s2 sg = __builtin_bit_cast(s2, w) >> (short)15;
+  return w ^ 0x80008000u ^ (__builtin_bit_cast(uint32_t, sg) & 0x7fff7fffu);
+}
+__device__ __forceinline__ float kunkey_f(uint32_t k) {
+  const uint32_t h = (k & 0x8000u) ? (k & 0x7fffu) : (~k & 0xffffu);
+  return h2f((uint16_t)h);
+}
+__device__ __forceinline__ uint32_t pkmin(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
+}
+__device__ __forceinline__ uint32_t pkmax(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
+}
+
 // ------------------------------------------------------------------ keys
 template <int BITS, int CL, int NI>
 __global__ __launch_bounds__(256) void kivi_keys_fast(KiviArgs a) {
@@ -81,61 +131,56 @@ __global__ __launch_bounds__(256) void kivi_keys_fast(KiviArgs a) {
     ok[j] = t < cnt;
     v[j] = ok[j] ? *reinterpret_cast<const uint4 *>(base + (size_t)t * D) : make_uint4(0, 0, 0, 0);
   }
-  float mn[8], mx[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    mn[i] = __builtin_inff();
-    mx[i] = -__builtin_inff();
-  }
+  // per channel pair: packed min/max of order keys over this lane's tokens
+  uint32_t kmn[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
+  uint32_t kmx[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
     if (!ok[j]) continue;
     const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float lo = lo_h2f(w[i]), hi = hi_h2f(w[i]);
-      mn[2 * i] = fminf(mn[2 * i], lo);
-      mx[2 * i] = fmaxf(mx[2 * i], lo);
-      mn[2 * i + 1] = fminf(mn[2 * i + 1], hi);
-      mx[2 * i + 1] = fmaxf(mx[2 * i + 1], hi);
+      const uint32_t kk = kkey_pair(w[i]);
+      kmn[i] = pkmin(kmn[i], kk);
+      kmx[i] = pkmax(kmx[i], kk);
     }
   }
   // reduce across the lanes holding the same channels (lane bits >= log2(CL))
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 4; ++i) {
     if constexpr (CL <= 8) {
-      mn[i] = fminf(mn[i], dppf<DPP_ROR8>(mn[i]));
-      mx[i] = fmaxf(mx[i], dppf<DPP_ROR8>(mx[i]));
+      kmn[i] = pkmin(kmn[i], dpp<DPP_ROR8>(kmn[i]));
+      kmx[i] = pkmax(kmx[i], dpp<DPP_ROR8>(kmx[i]));
     }
     if constexpr (CL <= 16) {
-      mn[i] = fminf(mn[i], __shfl_xor(mn[i], 16));
-      mx[i] = fmaxf(mx[i], __shfl_xor(mx[i], 16));
+      kmn[i] = pkmin(kmn[i], (uint32_t)__shfl_xor((int)kmn[i], 16));
+      kmx[i] = pkmax(kmx[i], (uint32_t)__shfl_xor((int)kmx[i], 16));
     }
     if constexpr (CL <= 32) {
-      mn[i] = fminf(mn[i], __shfl_xor(mn[i], 32));
-      mx[i] = fmaxf(mx[i], __shfl_xor(mx[i], 32));
+      kmn[i] = pkmin(kmn[i], (uint32_t)__shfl_xor((int)kmn[i], 32));
+      kmx[i] = pkmax(kmx[i], (uint32_t)__shfl_xor((int)kmx[i], 32));
+    }
+    if constexpr (CL <= 4) {
+      kmn[i] = pkmin(kmn[i], dpp<0x124>(kmn[i]));  // row_ror:4
+      kmx[i] = pkmax(kmx[i], dpp<0x124>(kmx[i]));
+    }
+    if constexpr (CL <= 2) {
+      kmn[i] = pkmin(kmn[i], dpp<0x122>(kmn[i]));  // row_ror:2
+      kmx[i] = pkmax(kmx[i], dpp<0x122>(kmx[i]));
+    }
+    if constexpr (CL <= 1) {
+      kmn[i] = pkmin(kmn[i], dpp<0x121>(kmn[i]));  // row_ror:1
+      kmx[i] = pkmax(kmx[i], dpp<0x121>(kmx[i]));
     }
   }
-  if constexpr (CL <= 4) {  // rows of 4 channel-lanes: also reduce across lane bits 2..3
+  float mn[8], sc[8], inv[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if constexpr (CL <= 4) {
-        mn[i] = fminf(mn[i], dppf<0x124>(mn[i]));  // row_ror:4
-        mx[i] = fmaxf(mx[i], dppf<0x124>(mx[i]));
-      }
-      if constexpr (CL <= 2) {
-        mn[i] = fminf(mn[i], dppf<0x122>(mn[i]));  // row_ror:2
-        mx[i] = fmaxf(mx[i], dppf<0x122>(mx[i]));
-      }
-      if constexpr (CL <= 1) {
-        mn[i] = fminf(mn[i], dppf<0x121>(mn[i]));  // row_ror:1
-        mx[i] = fmaxf(mx[i], dppf<0x121>(mx[i]));
-      }
-    }
+  for (int i = 0; i < 8; ++i) {
+    mn[i] = kunkey_f((kmn[i / 2] >> (16 * (i & 1))) & 0xffffu);
+    const float mx = kunkey_f((kmx[i / 2] >> (16 * (i & 1))) & 0xffffu);
+    sc[i] = kivi_scale(mn[i], mx, LEV, a.eps);
+    inv[i] = 1.0f / sc[i];
   }
-  float sc[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) sc[i] = kivi_scale(mn[i], mx[i], LEV, a.eps);
 
   const int64_t nrow0 = bh * n + (t0 - a.lo);  // row of token t0 in the [BH][n] code layout
 #pragma unroll
@@ -143,11 +188,15 @@ __global__ __launch_bounds__(256) void kivi_keys_fast(KiviArgs a) {
     if (!ok[j]) continue;
     const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
     uint32_t o[4], c[8];
+    float ad[8], cf[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint16_t r0 = kivi_elem(lo_h2f(w[i]), mn[2 * i], sc[2 * i], LEV, c[2 * i]);
-      const uint16_t r1 = kivi_elem(hi_h2f(w[i]), mn[2 * i + 1], sc[2 * i + 1], LEV, c[2 * i + 1]);
-      o[i] = (uint32_t)r0 | ((uint32_t)r1 << 16);
+    for (int i = 0; i < 8; ++i) ad[i] = ((i & 1) ? hi_h2f(w[i / 2]) : lo_h2f(w[i / 2])) - mn[i];
+    kivi_codes8<BITS>(ad, sc, inv, cf);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      c[i] = (uint32_t)cf[i];
+      const uint32_t r = f2h(cf[i] * sc[i] + mn[i]);
+      if (i & 1) o[i / 2] |= r << 16; else o[i / 2] = r;
     }
     const int t = tr + TPI * j;
     *reinterpret_cast<uint4 *>(base + (size_t)t * D) = make_uint4(o[0], o[1], o[2], o[3]);
@@ -248,22 +297,35 @@ __global__ __launch_bounds__(256) void kivi_values_fast(KiviArgs a) {
       x[2 * i] = lo_h2f(w[i]);
       x[2 * i + 1] = hi_h2f(w[i]);
     }
-    float mn = x[0], mx = x[0];
+    uint32_t kp = kkey_pair(w[0]);
+    uint32_t kq = kp;
 #pragma unroll
-    for (int i = 1; i < 8; ++i) {
-      mn = fminf(mn, x[i]);
-      mx = fmaxf(mx, x[i]);
+    for (int i = 1; i < 4; ++i) {
+      const uint32_t kk = kkey_pair(w[i]);
+      kp = pkmin(kp, kk);
+      kq = pkmax(kq, kk);
     }
-    group_minmax_f32<LPG>(mn, mx);
+    uint32_t kmn = min(kp & 0xffffu, kp >> 16), kmx = max(kq & 0xffffu, kq >> 16);
+    kmn = group_min_u32<LPG>(kmn);
+    kmx = group_max_u32<LPG>(kmx);
+    const float mn = kunkey_f(kmn), mx = kunkey_f(kmx);
     const float sc = kivi_scale(mn, mx, LEV, a.eps);
+    const float inv = 1.0f / sc;
     uint32_t o[4], c[8];
+    float ad[8], scv[8], invv[8], cf[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint16_t r0 = kivi_elem(x[2 * i], mn, sc, LEV, c[2 * i]);
-      const uint16_t r1 = kivi_elem(x[2 * i + 1], mn, sc, LEV, c[2 * i + 1]);
-      o[i] = (uint32_t)r0 | ((uint32_t)r1 << 16);
+    for (int i = 0; i < 8; ++i) {
+      ad[i] = x[i] - mn;
+      scv[i] = sc;
+      invv[i] = inv;
     }
-    if (rowid[u] < rows) {
+    kivi_codes8<BITS>(ad, scv, invv, cf);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      c[i] = (uint32_t)cf[i];
+      const uint32_t r = f2h(cf[i] * sc + mn);
+      if (i & 1) o[i / 2] |= r << 16; else o[i / 2] = r;
+    }    if (rowid[u] < rows) {
       const int64_t bh = rowid[u] / n;
       const int t = a.lo + (int)(rowid[u] - bh * n);
       *reinterpret_cast<uint4 *>(a.values + ((size_t)bh * a.S_cap + t) * D + ch * 8) =
