@@ -62,6 +62,31 @@ __device__ __forceinline__ void store_codes8(uint8_t *dst, const uint32_t *c) {
 // quotient round (ties-to-even) to the same integer, and beyond levels+1.5
 // both clamp to levels. Otherwise the IEEE division is done; on this
 // workload about 1e-4 of the elements take that branch.
+// RN(x / levels) for x >= 0 without a division: x*RN(1/levels) corrected by
+// one fused remainder step. Checked against IEEE division for every
+// non-negative finite binary32 x and levels 3, 15 and 255 (all plain IEEE
+// operations, so the check holds on any conforming device).
+template <int BITS>
+__device__ __forceinline__ float div_levels(float x) {
+  constexpr float LEV = (float)((1 << BITS) - 1);
+  constexpr float Y = 1.0f / LEV;
+  const float q0 = x * Y;
+  const float r = __builtin_fmaf(-q0, LEV, x);
+  return __builtin_fmaf(r, Y, q0);
+}
+// reciprocal of a scale (>= eps) to within 2^-23 relative: hardware estimate
+// plus one Newton step. Only used for the tie-guarded quotient below, whose
+// margin covers that error.
+__device__ __forceinline__ float recip(float s) {
+  const float y0 = __builtin_amdgcn_rcpf(s);
+  const float e = __builtin_fmaf(-s, y0, 1.0f);
+  return __builtin_fmaf(e, y0, y0);
+}
+template <int BITS>
+__device__ __forceinline__ float kivi_scale_c(float mn, float mx, float eps) {
+  return fmaxf(div_levels<BITS>(mx - mn), eps);
+}
+
 // Eight elements at a time: the quotients a[i]*inv[i] and their tie flags
 // are computed branch-free; only if some lane of the wave has a flagged
 // element in this group of eight does the wave redo the group with IEEE
@@ -109,15 +134,13 @@ __device__ __forceinline__ uint32_t pkmax(uint32_t a, uint32_t b) {
 template <int BITS, int CL, int NI>
 __global__ __launch_bounds__(256) void kivi_keys_fast(KiviArgs a) {
   constexpr int TPI = 64 / CL;  // token rows per load instruction
-  constexpr float LEV = (float)((1 << BITS) - 1);
   const int D = CL * 8;
   const int n = a.hi - a.lo;
   const int ng = (n + a.gs - 1) / a.gs;
   const int lane = threadIdx.x & 63;
-  const int64_t tile = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  if (tile >= a.BH * ng) return;  // wave-uniform
-  const int64_t bh = tile / ng;
-  const int g = (int)(tile - bh * ng);
+  const int g = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);  // group of this wave
+  if (g >= ng) return;  // wave-uniform
+  const int64_t bh = blockIdx.y;
   const int t0 = a.lo + g * a.gs;
   const int cnt = min(a.gs, a.hi - t0);
   const int ch = lane % CL, tr = lane / CL;
@@ -178,8 +201,8 @@ __global__ __launch_bounds__(256) void kivi_keys_fast(KiviArgs a) {
   for (int i = 0; i < 8; ++i) {
     mn[i] = kunkey_f((kmn[i / 2] >> (16 * (i & 1))) & 0xffffu);
     const float mx = kunkey_f((kmx[i / 2] >> (16 * (i & 1))) & 0xffffu);
-    sc[i] = kivi_scale(mn[i], mx, LEV, a.eps);
-    inv[i] = 1.0f / sc[i];
+    sc[i] = kivi_scale_c<BITS>(mn[i], mx, a.eps);
+    inv[i] = recip(sc[i]);
   }
 
   const int64_t nrow0 = bh * n + (t0 - a.lo);  // row of token t0 in the [BH][n] code layout
@@ -266,27 +289,21 @@ __global__ __launch_bounds__(256) void kivi_keys_generic(KiviArgs a) {
 template <int BITS, int CL, int LPG, int U>
 __global__ __launch_bounds__(256) void kivi_values_fast(KiviArgs a) {
   constexpr int RPW = 64 / CL;  // token rows per wave
-  constexpr float LEV = (float)((1 << BITS) - 1);
   const int D = CL * 8;
   const int n = a.hi - a.lo;
-  const int64_t rows = a.BH * n;
   const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int64_t bh = blockIdx.y;
   const int ch = lane % CL, tr = lane / CL;
   const int ng = D / (LPG * 8);
+  uint16_t *vb = a.values + ((size_t)bh * a.S_cap + a.lo) * D + ch * 8;
 
   uint4 v[U];
-  int64_t rowid[U];
+  int tok[U];  // token offset from lo
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    rowid[u] = (wave * U + u) * RPW + tr;
-    if (rowid[u] < rows) {
-      const int64_t bh = rowid[u] / n;
-      const int t = a.lo + (int)(rowid[u] - bh * n);
-      v[u] = *reinterpret_cast<const uint4 *>(a.values + ((size_t)bh * a.S_cap + t) * D + ch * 8);
-    } else {
-      v[u] = make_uint4(0, 0, 0, 0);
-    }
+    tok[u] = (wave * U + u) * RPW + tr;
+    v[u] = tok[u] < n ? *reinterpret_cast<const uint4 *>(vb + (size_t)tok[u] * D) : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -309,8 +326,8 @@ __global__ __launch_bounds__(256) void kivi_values_fast(KiviArgs a) {
     kmn = group_min_u32<LPG>(kmn);
     kmx = group_max_u32<LPG>(kmx);
     const float mn = kunkey_f(kmn), mx = kunkey_f(kmx);
-    const float sc = kivi_scale(mn, mx, LEV, a.eps);
-    const float inv = 1.0f / sc;
+    const float sc = kivi_scale_c<BITS>(mn, mx, a.eps);
+    const float inv = recip(sc);
     uint32_t o[4], c[8];
     float ad[8], scv[8], invv[8], cf[8];
 #pragma unroll
@@ -325,14 +342,12 @@ __global__ __launch_bounds__(256) void kivi_values_fast(KiviArgs a) {
       c[i] = (uint32_t)cf[i];
       const uint32_t r = f2h(cf[i] * sc + mn);
       if (i & 1) o[i / 2] |= r << 16; else o[i / 2] = r;
-    }    if (rowid[u] < rows) {
-      const int64_t bh = rowid[u] / n;
-      const int t = a.lo + (int)(rowid[u] - bh * n);
-      *reinterpret_cast<uint4 *>(a.values + ((size_t)bh * a.S_cap + t) * D + ch * 8) =
-          make_uint4(o[0], o[1], o[2], o[3]);
-      if (a.v_codes) store_codes8<BITS>(a.v_codes + (size_t)rowid[u] * (D * BITS / 8) + ch * BITS, c);
+    }    if (tok[u] < n) {
+      const size_t rowid = (size_t)bh * n + tok[u];  // row of the [BH][n] code layout
+      *reinterpret_cast<uint4 *>(vb + (size_t)tok[u] * D) = make_uint4(o[0], o[1], o[2], o[3]);
+      if (a.v_codes) store_codes8<BITS>(a.v_codes + rowid * (D * BITS / 8) + ch * BITS, c);
       if (ch % LPG == 0) {
-        const size_t p = (size_t)rowid[u] * ng + ch / LPG;
+        const size_t p = rowid * ng + ch / LPG;
         if (a.v_scale) a.v_scale[p] = sc;
         if (a.v_min) a.v_min[p] = mn + 0.0f;
       }
@@ -385,8 +400,7 @@ namespace {
 template <int BITS, int CL>
 hipError_t keys_cl(const KiviArgs &a, int ng, hipStream_t st) {
   constexpr int TPI = 64 / CL;
-  const int64_t tiles = a.BH * ng;
-  const dim3 grid((unsigned)((tiles + 3) / 4));
+  const dim3 grid((unsigned)((ng + 3) / 4), (unsigned)a.BH);
   switch (a.gs / TPI) {  // loads per lane; fast path only when gs % TPI == 0
     case 1: hipLaunchKernelGGL((kivi_keys_fast<BITS, CL, 1>), grid, dim3(256), 0, st, a); break;
     case 2: hipLaunchKernelGGL((kivi_keys_fast<BITS, CL, 2>), grid, dim3(256), 0, st, a); break;
@@ -399,6 +413,7 @@ hipError_t keys_cl(const KiviArgs &a, int ng, hipStream_t st) {
 }
 
 bool keys_fast_ok(const KiviArgs &a) {
+  if (a.BH > 65535) return false;
   const int CL = a.D / 8;
   if (a.D % 8 || (CL & (CL - 1)) || CL > 32 || CL < 1) return false;
   const int TPI = 64 / CL;
@@ -434,10 +449,9 @@ hipError_t launch_keys(const KiviArgs &a, hipStream_t st) {
 template <int BITS, int CL, int LPG>
 hipError_t values_cfg(const KiviArgs &a, hipStream_t st) {
   constexpr int U = 2, RPW = 64 / CL;
-  const int64_t rows = a.BH * (int64_t)(a.hi - a.lo);
-  const int64_t waves = (rows + RPW * U - 1) / (RPW * U);
-  hipLaunchKernelGGL((kivi_values_fast<BITS, CL, LPG, U>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
-                     st, a);
+  const int64_t waves = ((a.hi - a.lo) + RPW * U - 1) / (RPW * U);  // per (b, h)
+  hipLaunchKernelGGL((kivi_values_fast<BITS, CL, LPG, U>), dim3((unsigned)((waves + 3) / 4), (unsigned)a.BH),
+                     dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -456,6 +470,7 @@ hipError_t values_cl(const KiviArgs &a, hipStream_t st) {
 }
 
 bool values_fast_ok(const KiviArgs &a) {
+  if (a.BH > 65535) return false;
   const int CL = a.D / 8;
   if (a.D % 8 || (CL & (CL - 1)) || CL > 64 || CL < 1) return false;
   if (a.gs % 8) return false;
