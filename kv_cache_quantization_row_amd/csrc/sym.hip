@@ -5,14 +5,14 @@
 //  {8:127, 6:31, 4:7}, q6 codes biased +32 into 6-bit fields, four fields per
 //  three little-endian bytes; q4 two codes per byte, q8 one ("Summary").
 //
-// Fast path (head_dim a power of two in [16, 1024]): a row is handled by
-// LPR = D/16 consecutive lanes, 16 elements (32 bytes of fp16) per lane, so
-// a wave holds 64/LPR rows; at D = 256 one 16-lane DPP row is one KV row and
-// one wave is one token of four heads. The row's |x| maximum is taken on fp16
-// bit patterns with packed 16-bit max, then across the row's lanes with DPP.
-// Each lane packs its 16 codes into 16*bits/8 bytes (16 / 12 / 8) and stores
-// them with one dword-vector store. The generic path (other head dims) runs
-// one wave per row.
+// Fast paths (head_dim a power of two in [16, 1024]). Large writes use
+// sym_quant_v8: a row is handled by D/8 consecutive lanes, one 16-byte load of
+// 8 fp16 values per lane, so every wave load is one contiguous 1 KiB run.
+// Small writes (decode appends) and D = 1024 use sym_quant_fast, with
+// LPR = D/16 lanes of 16 elements per row and several rows per wave. The
+// row's |x| maximum is taken on fp16 bit patterns with packed 16-bit max,
+// then across the row's lanes with DPP. The generic path (other head dims)
+// runs one wave per row.
 //
 // Rounding: codes need rint(x * r) with ties-to-even, clipped to +-qmax. The
 // clipped product c is added to 1.5*2^23 + bias: in [2^23, 2^24) the float
@@ -80,6 +80,55 @@ __device__ __forceinline__ uint32_t encode(float x, float r) {
   float c = __builtin_amdgcn_fmed3f(t, -Q, Q);
   float m = c + (12582912.0f + (float)SymFmt<BITS>::BIAS);
   return __builtin_bit_cast(uint32_t, m) - 0x4b400000u;
+}
+
+// Raw encoding of one element: the bit pattern of RN(x*r) + 1.5*2^23 + bias,
+// i.e. 0x4b400000 + rint(x*r) + bias. x*r is formed as fma(x, r, +0), a
+// single rounding of the exact product (only a zero's sign can differ, and
+// it vanishes in the addition). CLAMP clips to +-qmax first; it is needed
+// only when the row's fp16 scale is subnormal: with a normal scale
+// s = RN16(RN32(a/qmax)) we have |x*r| <= qmax (1 + 2^-11 + 2^-22) < qmax + 1/2.
+template <int BITS, bool CLAMP>
+__device__ __forceinline__ uint32_t enc_raw(uint16_t h, float r) {
+  constexpr float Q = (float)SymFmt<BITS>::QMAX;
+  float t = __builtin_fmaf((float)__builtin_bit_cast(_Float16, h), r, 0.0f);
+  if constexpr (CLAMP) t = __builtin_amdgcn_fmed3f(t, -Q, Q);
+  return __builtin_bit_cast(uint32_t, t + (12582912.0f + (float)SymFmt<BITS>::BIAS));
+}
+
+// Pack 16 raw encodings (0x4b400000 + biased code) into BITS/2 dwords,
+// LSB-first. The packing is done modulo 2^32 on the raw patterns and the
+// constant contribution of 0x4b400000 is removed once per word: fields never
+// overlap (biased codes are < 2^BITS), so no carries cross them.
+template <int BITS>
+__device__ __forceinline__ void pack16_raw(const uint32_t *m, uint32_t *o) {
+  constexpr uint32_t K = 0x4b400000u;
+  if constexpr (BITS == 8) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = __builtin_amdgcn_perm(m[4 * j + 1], m[4 * j], 0x0c0c0400u);
+      const uint32_t hi = __builtin_amdgcn_perm(m[4 * j + 3], m[4 * j + 2], 0x04000c0cu);
+      o[j] = lo | hi;
+    }
+  } else if constexpr (BITS == 6) {
+    constexpr uint32_t C = K + (K << 6) + (K << 12) + (K << 18);
+    uint32_t g[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      g[j] = (m[4 * j] + (m[4 * j + 1] << 6) + (m[4 * j + 2] << 12) + (m[4 * j + 3] << 18)) - C;
+    o[0] = g[0] | (g[1] << 24);
+    o[1] = (g[1] >> 8) | (g[2] << 16);
+    o[2] = (g[2] >> 16) | (g[3] << 8);
+  } else {
+    constexpr uint32_t C = K + (K << 4) + (K << 8) + (K << 12) + (K << 16) + (K << 20) + (K << 24) + (K << 28);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint32_t v = m[8 * j];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) v += m[8 * j + i] << (4 * i);
+      o[j] = v - C;
+    }
+  }
 }
 
 // Row scale: fp16(absmax / qmax) and the binary32 reciprocal of its value.
@@ -205,12 +254,20 @@ __global__ __launch_bounds__(256) void sym_quant_fast(SymQuantArgs a) {
     float r;
     row_scale<BITS>(amax, s16, r);
     uint32_t c[16], o[OW];
+    if (__any(s16 != 0 && s16 < 0x0400u)) {  // some row of the wave has a subnormal scale
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      c[2 * i] = encode<BITS>(lo_h2f(w[u][i]), r);
-      c[2 * i + 1] = encode<BITS>(hi_h2f(w[u][i]), r);
+      for (int i = 0; i < 8; ++i) {
+        c[2 * i] = enc_raw<BITS, true>((uint16_t)(w[u][i] & 0xffffu), r);
+        c[2 * i + 1] = enc_raw<BITS, true>((uint16_t)(w[u][i] >> 16), r);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        c[2 * i] = enc_raw<BITS, false>((uint16_t)(w[u][i] & 0xffffu), r);
+        c[2 * i + 1] = enc_raw<BITS, false>((uint16_t)(w[u][i] >> 16), r);
+      }
     }
-    pack16<BITS>(c, o);
+    pack16_raw<BITS>(c, o);
     if (row < rows && slot[u] >= 0 && slot[u] < a.n_slots) {
       const uint32_t t = a.h_shift >= 0 ? (row >> a.h_shift) : row / a.H;
       const uint32_t h = row - t * a.H;
@@ -223,6 +280,84 @@ __global__ __launch_bounds__(256) void sym_quant_fast(SymQuantArgs a) {
       }
     }
   }
+}
+
+// Write path, 8 elements per lane: a row of D is owned by L8 = D/8 lanes, one
+// fully coalesced 16-byte load per lane; the wave holds 64/L8 rows and a
+// 256-thread workgroup 256/L8 rows. Each lane packs 8 codes into BITS bytes;
+// for q6 the odd lane hands its 6 bytes to the even lane (DPP), which stores
+// 12 bytes.
+template <int BITS, int L8>
+__global__ __launch_bounds__(256) void sym_quant_v8(SymQuantArgs a) {
+  constexpr int D = L8 * 8, RPW = 64 / L8, PD = D * BITS / 8;
+  const int side = blockIdx.z;
+  const uint16_t *x = side ? a.v : a.k;
+  uint8_t *codes = side ? a.v_codes : a.k_codes;
+  uint16_t *scales = side ? a.v_scales : a.k_scales;
+  if (x == nullptr) return;
+  const uint32_t layer = blockIdx.y;
+  const uint32_t rows = a.rows_per_layer;
+  const int lane = threadIdx.x & 63;
+  const uint32_t wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int sub = lane / L8, li = lane % L8;
+  const uint32_t row = wave * RPW + sub;
+  const uint16_t *xl = x + (size_t)layer * rows * D;
+  uint4 in = make_uint4(0, 0, 0, 0);
+  int64_t slot = -1;
+  if (row < rows) {
+    in = ld_stream(reinterpret_cast<const uint4 *>(xl + (size_t)row * D + li * 8));
+    slot = a.slot_mapping[a.h_shift >= 0 ? (row >> a.h_shift) : row / a.H];
+  }
+  const uint32_t w[4] = {in.x, in.y, in.z, in.w};
+  uint32_t amax = absmax_bits(w, 4);
+  amax = group_max_u32<L8>(amax);
+  uint16_t s16;
+  float r;
+  row_scale<BITS>(amax, s16, r);
+  uint32_t m[8];
+  if (__any(s16 != 0 && s16 < 0x0400u)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      m[2 * i] = enc_raw<BITS, true>((uint16_t)(w[i] & 0xffffu), r);
+      m[2 * i + 1] = enc_raw<BITS, true>((uint16_t)(w[i] >> 16), r);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      m[2 * i] = enc_raw<BITS, false>((uint16_t)(w[i] & 0xffffu), r);
+      m[2 * i + 1] = enc_raw<BITS, false>((uint16_t)(w[i] >> 16), r);
+    }
+  }
+  constexpr uint32_t K = 0x4b400000u;
+  uint8_t *cl = codes + (size_t)(a.layer0 + layer) * a.code_layer_stride;
+  const bool ok = row < rows && slot >= 0 && slot < a.n_slots;
+  const size_t orow = ok ? (size_t)slot * a.H + (row - (a.h_shift >= 0 ? (row >> a.h_shift) : row / a.H) * a.H) : 0;
+  if constexpr (BITS == 8) {
+    const uint32_t o0 = __builtin_amdgcn_perm(m[1], m[0], 0x0c0c0400u) | __builtin_amdgcn_perm(m[3], m[2], 0x04000c0cu);
+    const uint32_t o1 = __builtin_amdgcn_perm(m[5], m[4], 0x0c0c0400u) | __builtin_amdgcn_perm(m[7], m[6], 0x04000c0cu);
+    if (ok) *reinterpret_cast<uint2 *>(cl + orow * PD + li * 8) = make_uint2(o0, o1);
+  } else if constexpr (BITS == 4) {
+    constexpr uint32_t C = K + (K << 4) + (K << 8) + (K << 12) + (K << 16) + (K << 20) + (K << 24) + (K << 28);
+    uint32_t v = m[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) v += m[i] << (4 * i);
+    if (ok) *reinterpret_cast<uint32_t *>(cl + orow * PD + li * 4) = v - C;
+  } else {
+    constexpr uint32_t C = K + (K << 6) + (K << 12) + (K << 18);
+    const uint32_t g0 = (m[0] + (m[1] << 6) + (m[2] << 12) + (m[3] << 18)) - C;
+    const uint32_t g1 = (m[4] + (m[5] << 6) + (m[6] << 12) + (m[7] << 18)) - C;
+    // this lane's 6 bytes: g0 (24 bits) then g1 (24 bits)
+    const uint32_t lo = g0 | (g1 << 24), hi = g1 >> 8;  // 48 bits
+    // the odd neighbour's 48 bits, moved to the even lane (quad_perm [1,1,3,3])
+    const uint32_t nlo = dpp<0xf5>(lo), nhi = dpp<0xf5>(hi);
+    if (ok && (li & 1) == 0) {
+      uint32_t *dst = reinterpret_cast<uint32_t *>(cl + orow * PD + li * 6);
+      dst[0] = lo;
+      dst[1] = hi | (nlo << 16);
+      dst[2] = (nlo >> 16) | (nhi << 16);
+    }
+  }
+  if (ok && li == 0) scales[(size_t)(a.layer0 + layer) * a.scale_layer_stride + orow] = s16;
 }
 
 // Generic write path: one wave per row, any head_dim valid for the width.
@@ -467,8 +602,23 @@ hipError_t launch_quant_u(const SymQuantArgs &a, int n_layers, hipStream_t st) {
   hipLaunchKernelGGL((sym_quant_fast<BITS, LPR, U>), grid, dim3(64 * WPB), 0, st, a);
   return hipGetLastError();
 }
+#ifndef KVQ_SYM_QUANT_V8
+#define KVQ_SYM_QUANT_V8 1  // 8-elements-per-lane write path for large launches (+4..8% measured)
+#endif
+template <int BITS, int L8>
+hipError_t launch_quant_v8(const SymQuantArgs &a, int n_layers, hipStream_t st) {
+  constexpr int RPW = 64 / L8;
+  const uint32_t per_block = RPW * 4;
+  dim3 grid((a.rows_per_layer + per_block - 1) / per_block, n_layers, 2);
+  hipLaunchKernelGGL((sym_quant_v8<BITS, L8>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
 template <int BITS, int LPR>
 hipError_t launch_quant_lpr(const SymQuantArgs &a, int n_layers, hipStream_t st) {
+  if constexpr (LPR <= 32) {
+    if (KVQ_SYM_QUANT_V8 && (int64_t)a.rows_per_layer * n_layers > 16384)
+      return launch_quant_v8<BITS, 2 * LPR>(a, n_layers, st);
+  }
   // small (decode-sized) launches: one row group per wave spreads the few rows
   // over more waves; large launches: several row groups per wave
   if ((int64_t)a.rows_per_layer * n_layers <= 16384) return launch_quant_u<BITS, LPR, 1>(a, n_layers, st);
