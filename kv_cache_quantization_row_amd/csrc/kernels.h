@@ -58,11 +58,10 @@ struct NuqArgs {
   uint16_t *k_recon, *v_recon;     // optional
   // workspace
   uint32_t *ws_ctr;                // 4 counters
-  uint16_t *ws_kcut;               // [BH][D][16] cut keys
   uint32_t *ws_kblk, *ws_vblk;     // per block (staging base, count -> final offset)
   int32_t *ws_kpos, *ws_vpos;      // staging
   uint16_t *ws_kval, *ws_vval;
-  int64_t k_blk_x, v_nblk;
+  int64_t k_blk_x, v_nblk;         // key-quant workgroups along S (16384/D rows each); value workgroups
 };
 
 hipError_t launch_nuq(const NuqArgs &a, int key_cpc, int val_cpc, hipStream_t st);

@@ -155,23 +155,42 @@ struct Chunk {
   }
 };
 
-// sums over groups of G consecutive lanes
-template <int G>
-__device__ __forceinline__ int gsum(int v) {
-#pragma unroll
-  for (int m = 1; m < G; m <<= 1) v += __shfl_xor(v, m);
+// reductions over groups of G consecutive lanes (G a power of two <= 64):
+// DPP inside a 16-lane row (pairs, quads, half-row mirror, row mirror), then
+// a lane swizzle across rows; every lane of the group receives the result
+template <int G, typename Op>
+__device__ __forceinline__ uint32_t gred_u32(uint32_t v, Op op) {
+  if constexpr (G >= 2) v = op(v, dpp<DPP_XOR1>(v));
+  if constexpr (G >= 4) v = op(v, dpp<DPP_XOR2>(v));
+  if constexpr (G >= 8) v = op(v, dpp<DPP_HALF_MIRROR>(v));
+  if constexpr (G >= 16) v = op(v, dpp<DPP_MIRROR>(v));
+  if constexpr (G >= 32) v = op(v, (uint32_t)__shfl_xor((int)v, 16));
+  if constexpr (G >= 64) v = op(v, (uint32_t)__shfl_xor((int)v, 32));
   return v;
 }
 template <int G>
-__device__ __forceinline__ double gsum(double v) {
-#pragma unroll
-  for (int m = 1; m < G; m <<= 1) v += __shfl_xor(v, m);
-  return v;
+__device__ __forceinline__ int gsum(int v) {
+  return (int)gred_u32<G>((uint32_t)v, [](uint32_t x, uint32_t y) { return x + y; });
 }
 template <int G>
 __device__ __forceinline__ uint32_t gmin(uint32_t v) {
-#pragma unroll
-  for (int m = 1; m < G; m <<= 1) v = min(v, (uint32_t)__shfl_xor((int)v, m));
+  return gred_u32<G>(v, [](uint32_t x, uint32_t y) { return min(x, y); });
+}
+template <int CTRL>
+__device__ __forceinline__ double dppd(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint64_t lo = dpp<CTRL>((uint32_t)b), hi = dpp<CTRL>((uint32_t)(b >> 32));
+  return __builtin_bit_cast(double, lo | (hi << 32));
+}
+// (the partial sums are exact, so the reduction order does not matter)
+template <int G>
+__device__ __forceinline__ double gsum(double v) {
+  if constexpr (G >= 2) v += dppd<DPP_XOR1>(v);
+  if constexpr (G >= 4) v += dppd<DPP_XOR2>(v);
+  if constexpr (G >= 8) v += dppd<DPP_HALF_MIRROR>(v);
+  if constexpr (G >= 16) v += dppd<DPP_MIRROR>(v);
+  if constexpr (G >= 32) v += __shfl_xor(v, 16);
+  if constexpr (G >= 64) v += __shfl_xor(v, 32);
   return v;
 }
 
@@ -299,41 +318,63 @@ __device__ void fit_vector(const Chunk &c, int nq, float frac, int iters, float 
   const int lo = c.lower(klo);
   const int hi = c.upper(key16(tau));
   const int m = gsum<CPC>(hi - lo);
-  // ---- quantile initialisation (positions exact in integers)
-  auto select = [&](int r) -> uint32_t {  // key of the r-th smallest inlier (0-based)
-    if (CPC == 1) return c.at(lo + r);
-    int pos = 0;
-#pragma unroll 1
-    for (int s = 32768; s >= 1; s >>= 1) {
-      const int cand = pos + s - 1;  // key
-      bool adv;
-      if (cand > 0xfbff) {
-        adv = false;
-      } else {
-        const int cnt = min(max(c.upper((uint32_t)cand), lo), hi) - lo;
-        adv = gsum<CPC>(cnt) <= r;
-      }
-      if (adv) pos += s;
-    }
-    return (uint32_t)pos;
-  };
-  auto successor = [&](int r, uint32_t kr) -> uint32_t {  // key of the (r+1)-th smallest inlier
-    if (CPC == 1) return c.at(lo + r + 1);
-    const int le = min(max(c.upper(kr), lo), hi) - lo;
-    if (gsum<CPC>(le) > r + 1) return kr;
-    const int idx = min(max(c.upper(kr), lo), hi);
-    return gmin<CPC>(idx < hi ? c.at(idx) : 0xffffu);
-  };
+  // ---- quantile initialisation (positions exact in integers): level j
+  // interpolates between the r_j-th and (r_j+1)-th smallest inliers with
+  // r_j + f_j = (j + 1/2)(m - 1)/L
+  int rk[L];
+  int rem[L];
 #pragma unroll
   for (int j = 0; j < L; ++j) {
     const long long num = (long long)(2 * j + 1) * (long long)(m - 1);
-    const int r = (int)(num / (2 * L));
-    const long long rem = num % (2 * L);
-    const uint32_t kr = select(r);
-    double v = kval(kr);
-    if (rem != 0) {
-      const double u1 = kval(successor(r, kr));
-      v = v + ((double)rem / (double)(2 * L)) * (u1 - v);
+    rk[j] = (int)(num / (2 * L));
+    rem[j] = (int)(num % (2 * L));
+  }
+  uint32_t kr[L], ks[L];  // keys of the r_j-th and (r_j+1)-th smallest inliers
+  if (CPC == 1) {
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+      kr[j] = c.at(lo + rk[j]);
+      ks[j] = rem[j] ? c.at(lo + rk[j] + 1) : kr[j];
+    }
+  } else {
+    // all L ranks in one bitwise search over the 16-bit key line: after the
+    // step for bit s, pos[j] is the largest prefix with #{inliers with key <
+    // pos[j]} <= r_j
+    int pos[L];
+#pragma unroll
+    for (int j = 0; j < L; ++j) pos[j] = 0;
+#pragma unroll 1
+    for (int sbit = 32768; sbit >= 1; sbit >>= 1) {
+      int cnt[L];
+#pragma unroll
+      for (int j = 0; j < L; ++j) {
+        const int cand = pos[j] + sbit - 1;
+        cnt[j] = cand > 0xfbff ? 0 : min(max(c.upper((uint32_t)cand), lo), hi) - lo;
+      }
+#pragma unroll
+      for (int j = 0; j < L; ++j) {
+        const int cand = pos[j] + sbit - 1;
+        const int tot = gsum<CPC>(cnt[j]);
+        if (cand <= 0xfbff && tot <= rk[j]) pos[j] += sbit;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+      kr[j] = (uint32_t)pos[j];
+      // successor: the same key while more than r_j + 1 inliers are <= it,
+      // else the smallest inlier key above it
+      const int idx = min(max(c.upper(kr[j]), lo), hi);
+      const int le = gsum<CPC>(idx - lo);
+      const uint32_t nx = gmin<CPC>(idx < hi ? c.at(idx) : 0xffffu);
+      ks[j] = le > rk[j] + 1 ? kr[j] : nx;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < L; ++j) {
+    double v = kval(kr[j]);
+    if (rem[j] != 0) {
+      const double u1 = kval(ks[j]);
+      v = v + ((double)rem[j] / (double)(2 * L)) * (u1 - v);
     }
     lev[j] = (float)v + 0.0f;
   }
@@ -345,12 +386,23 @@ __device__ void fit_vector(const Chunk &c, int nq, float frac, int iters, float 
     cut_keys<L>(lev, T);
     if (it == 0) {
       // one pass over the inliers, cell by cell, recording the running sum at every cut
+      // (four independent partial sums; every partial sum is exact, so the
+      // order of the additions does not matter)
       double acc = 0.0;
       int prev = lo;
 #pragma unroll
       for (int q = 0; q < L; ++q) {
         const int nc = q < L - 1 ? min(max(c.upper(T[q]), lo), hi) : hi;
-        for (int i = prev; i < nc; ++i) acc += kval(c.at(i));
+        double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+        int i = prev;
+        for (; i + 4 <= nc; i += 4) {
+          a0 += kval(c.at(i));
+          a1 += kval(c.at(i + 1));
+          a2 += kval(c.at(i + 2));
+          a3 += kval(c.at(i + 3));
+        }
+        for (; i < nc; ++i) a0 += kval(c.at(i));
+        acc += (a0 + a1) + (a2 + a3);
         P[q] = acc;
         cut[q] = nc;
         prev = max(prev, nc);
@@ -420,40 +472,59 @@ __global__ void nuq_zero(uint32_t *ctr) {
 }
 
 // Key fit: lanes (channel g, chunk q) with CPC chunks per channel; a
-// workgroup of 256 lanes covers 256/CPC channels of one (b,h).
+// workgroup of 256 lanes covers 256/CPC channels of one (b,h). The tile of
+// CPC*128 tokens x 256/CPC channels is read with coalesced dword loads (two
+// channels of one token each), transposed into the lanes' chunks through
+// LDS, then every lane sorts its chunk in registers and stores it back.
 template <int CPC, int L>
 __global__ __launch_bounds__(256) void nuq_key_fit(NuqArgs a) {
   extern __shared__ uint32_t lds[];
+  constexpr int CHANS = 256 / CPC, NP = CHANS / 2;  // channels, channel pairs
   const int lane = threadIdx.x;
-  const int chans = 256 / CPC;
   const int bh = blockIdx.y;
   const int g = lane / CPC, q = lane % CPC;
-  const int d = blockIdx.x * chans + g;
+  const int d0 = blockIdx.x * CHANS;
+  const int d = d0 + g;
   const bool active = d < a.D;
-  const int t0 = a.n_sink_eff + q * CH;
-  uint32_t raw[64];
-#pragma unroll
-  for (int i = 0; i < 64; ++i) raw[i] = 0x7c007c00u;  // fp16 +inf padding sorts last
-  int nq = 0;
-  if (active) {
-    const uint16_t *col = a.keys + (size_t)bh * a.S * a.D + d;
-    nq = max(0, min(CH, a.S - t0));
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      if (i < nq) {
-        const uint32_t x = col[(size_t)(t0 + i) * a.D];
-        raw[i / 2] = (raw[i / 2] & (0xffffu << (16 * (1 - (i & 1))))) | (x << (16 * (i & 1)));
+  const int t0 = a.n_sink_eff;
+  const int nfit = a.S - t0;
+  // raw staging: word k (tokens 2k, 2k+1 of the chunk) of lane l at
+  // l*64 + (k ^ 4*swz(l)); groups of 4 words stay contiguous
+  auto swz = [](int l) { return ((l % CPC) + 5 * (l / CPC)) & 15; };
+  {
+    const uint16_t *base = a.keys + (size_t)bh * a.S * a.D;
+#pragma unroll 8
+    for (int u = lane; u < 64 * CPC * NP; u += 256) {
+      const int pp = u % NP, rp = u / NP;  // channel pair, token pair
+      const int c = 2 * pp, r = 2 * rp;
+      uint32_t x0 = 0x7c007c00u, x1 = 0x7c007c00u;  // +inf padding sorts last
+      if (d0 + c < a.D) {
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(base + (size_t)(t0 + r) * a.D + d0 + c);
+        if (r < nfit) x0 = src[0];
+        if (r + 1 < nfit) x1 = src[a.D / 2];
       }
+      const int l0 = c * CPC + r / 128, l1 = l0 + CPC;  // lanes of channels c, c+1
+      const int k = (r % 128) / 2;
+      lds[l0 * 64 + (k ^ (4 * swz(l0)))] = (x0 & 0xffffu) | (x1 << 16);
+      lds[l1 * 64 + (k ^ (4 * swz(l1)))] = (x0 >> 16) | (x1 & 0xffff0000u);
     }
   }
-  uint32_t v[64];
-  to_sort_layout(raw, v);
-  sort128(v);
-  const int sw = lane & 63;
-  uint32_t *w = lds + lane * 64;
-  store_chunk(w, sw, v);
   __syncthreads();
-  Chunk c{w, sw};
+  const int nq = active ? max(0, min(CH, nfit - q * CH)) : 0;
+  {
+    uint32_t raw[64];
+    const int sz = 4 * swz(lane);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint4 w4 = *reinterpret_cast<const uint4 *>(lds + lane * 64 + ((4 * j) ^ sz));
+      raw[4 * j] = w4.x; raw[4 * j + 1] = w4.y; raw[4 * j + 2] = w4.z; raw[4 * j + 3] = w4.w;
+    }
+    uint32_t v[64];
+    to_sort_layout(raw, v);
+    sort128(v);
+    store_chunk(lds + lane * 64, lane & 63, v);  // this lane's own words only
+  }
+  Chunk c{lds + lane * 64, lane & 63};
   float lev[L];
   FitOut fo;
   fit_vector<CPC, L>(c, nq, a.frac, a.iters, lev, fo);
@@ -465,101 +536,161 @@ __global__ __launch_bounds__(256) void nuq_key_fit(NuqArgs a) {
   }
 }
 
-// Frozen-level cut keys per key channel (every call; also after a fit).
-template <int L>
-__global__ __launch_bounds__(256) void nuq_key_cuts(NuqArgs a) {
-  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (id >= (int64_t)a.BH * a.D) return;
-  float lev[L];
-#pragma unroll
-  for (int j = 0; j < L; ++j) lev[j] = a.key_levels[id * L + j];
-  uint32_t T[L];
-  cut_keys<L>(lev, T);
-  uint16_t *dst = a.ws_kcut + id * 16;
-#pragma unroll
-  for (int j = 0; j < L - 1; ++j) dst[j] = (uint16_t)T[j];
-}
-
-// Key quantize: flat order. A wave handles 64 / (D/8) token rows per step,
-// lane = 8 consecutive channels; 4 lanes pack their codes into one
-// dword-aligned store. Outliers are compacted in flat order per block.
+// Key quantize against the (frozen or just fitted) per-channel tables. A
+// workgroup covers KQ_NIT * 4 * 64 / (D/8) consecutive token rows of one
+// (b,h): each of its 4 waves a contiguous run of KQ_NIT row steps, each step
+// 64 / (D/8) rows with D/8 lanes per row and 8 consecutive channels per lane
+// (one 16-byte load). The workgroup first turns the D level tables into cut
+// keys in LDS; each lane then keeps the cut keys and |x| thresholds of its 8
+// channels in registers, packed in channel pairs, and classifies two samples
+// per packed 16-bit operation. Outliers are recorded as per-step bit masks
+// and written in flat order once the workgroup has reserved its staging range.
+constexpr int KQ_NIT = 8;
 template <int BITS>
 __global__ __launch_bounds__(256) void nuq_key_quant(NuqArgs a) {
   constexpr int L = 1 << BITS;
+  __shared__ uint16_t cut_s[256 * 16];  // [channel][j]: cut key between levels j and j+1
+  __shared__ uint16_t tau_s[256];
+  __shared__ float lev_s[256 * L];      // level tables of this (b,h)
   __shared__ int wave_cnt[4];
   __shared__ uint32_t blk_base;
   const int D = a.D;
-  const int CL = D / 8;               // lanes per token row
-  const int RPW = 64 / CL;            // rows per wave
+  const int CL = D / 8;                 // lanes per token row
+  const int RPW = 64 / CL;              // rows per wave step
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int bh = blockIdx.y;
-  const int row = (blockIdx.x * 4 + wv) * RPW + lane / CL;  // token within bh
   const int ck = lane % CL;
-  const bool valid = row < a.S;
-  uint32_t codes = 0;
-  uint16_t x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  uint16_t rec[8];
-  bool out[8];
-  int nout = 0;
-  if (valid) {
-    const uint4 in = *reinterpret_cast<const uint4 *>(a.keys + ((size_t)bh * a.S + row) * D + ck * 8);
-    const uint32_t wds[4] = {in.x, in.y, in.z, in.w};
+  const bool want_rec = a.k_recon != nullptr;
+  // ---- cut keys of this (b,h): T[j] = key of thr16(l_j, l_{j+1}) for distinct
+  // neighbours; a duplicate level takes the cut above it (empty cell); the
+  // last cut is above every finite key
+  const float *kl = a.key_levels + (size_t)bh * D * L;
+  {
+    float lv[(256 * L) / 256];  // all level loads in flight at once
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = (uint16_t)(wds[i / 2] >> (16 * (i & 1)));
+    for (int i = 0; i < L; ++i)
+      if (threadIdx.x + 256 * i < D * L) lv[i] = kl[threadIdx.x + 256 * i];
+#pragma unroll
+    for (int i = 0; i < L; ++i)
+      if (threadIdx.x + 256 * i < D * L) lev_s[threadIdx.x + 256 * i] = lv[i];
+    if (threadIdx.x < D) tau_s[threadIdx.x] = a.key_thresh[(size_t)bh * D + threadIdx.x];
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < D * (L - 1); t += 256) {
+    const int c = t / (L - 1), j = t - c * (L - 1);
+    const float l0 = lev_s[c * L + j], l1 = lev_s[c * L + j + 1];
+    cut_s[c * 16 + j] = l0 < l1 ? (uint16_t)key16(thr16(l0, l1)) : (uint16_t)0;  // key 0 is a NaN: marks "none"
+  }
+  __syncthreads();
+  if (threadIdx.x < D) {
+    uint32_t nt = 0xffffu;
+    for (int j = L - 2; j >= 0; --j) {
+      const uint32_t r = cut_s[threadIdx.x * 16 + j];
+      if (r) nt = r;
+      cut_s[threadIdx.x * 16 + j] = (uint16_t)nt;
+    }
+  }
+  __syncthreads();
+  // ---- this lane's 8 channels: cut keys and thresholds as channel pairs
+  u16x2v cutp[4][L - 1], taup[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int c = ck * 8 + 2 * p;
+#pragma unroll
+    for (int j = 0; j < L - 1; ++j) cutp[p][j] = u16x2v{cut_s[c * 16 + j], cut_s[(c + 1) * 16 + j]};
+    taup[p] = u16x2v{tau_s[c], tau_s[c + 1]};
+  }
+  const int row_w = (blockIdx.x * 4 + wv) * (RPW * KQ_NIT) + lane / CL;  // first row of this lane
+  const uint16_t *kin = a.keys + (size_t)bh * a.S * D + ck * 8;
+  uint8_t *kout = a.k_codes + (size_t)bh * a.S * (D * BITS / 8);
+  uint32_t omask[KQ_NIT];  // bit e: channel ck*8+e of step it is an outlier
+  const u16x2v one = {1, 1};
+#pragma unroll
+  for (int it = 0; it < KQ_NIT; ++it) {
+    const int row = row_w + it * RPW;
+    const bool valid = row < a.S;
     const bool sink = row < a.n_sink_eff;
+    uint4 in = make_uint4(0, 0, 0, 0);
+    if (valid) in = *reinterpret_cast<const uint4 *>(kin + (size_t)row * D);
+    const uint32_t wd[4] = {in.x, in.y, in.z, in.w};
+    uint32_t codes = 0, om = 0;
+    uint32_t rec[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int d = ck * 8 + i;
-      const size_t ch = (size_t)bh * D + d;
-      const uint16_t tau = a.key_thresh[ch];
-      const bool o = !sink && h2f((uint16_t)(x[i] & 0x7fffu)) > h2f(tau);
-      out[i] = o;
-      nout += o;
-      uint32_t code = 0;
-      if (!sink && !o) {
-        const uint32_t kx = key16(x[i]);
-        const uint16_t *cuts = a.ws_kcut + ch * 16;
+    for (int p = 0; p < 4; ++p) {
+      const u16x2v kx = __builtin_bit_cast(u16x2v, key_pair(wd[p]));
+      const u16x2v ax = __builtin_bit_cast(u16x2v, wd[p] & 0x7fff7fffu);
+      // outlier: |x| > tau (non-negative fp16 patterns order as integers)
+      const u16x2v isout = __builtin_elementwise_min(__builtin_elementwise_sub_sat(ax, taup[p]), one);
+      u16x2v code = {0, 0};
 #pragma unroll
-        for (int j = 0; j < L - 1; ++j) code += kx > cuts[j];
+      for (int j = 0; j < L - 1; ++j)
+        code += __builtin_elementwise_min(__builtin_elementwise_sub_sat(kx, cutp[p][j]), one);
+      code *= (one - isout);  // outliers get code 0
+      uint32_t c0 = code.x, c1 = code.y, o0 = isout.x, o1 = isout.y;
+      if (sink) { c0 = c1 = 0; o0 = o1 = 0; }
+      codes |= (c0 | (c1 << BITS)) << (2 * p * BITS);
+      om |= (o0 | (o1 << 1)) << (2 * p);
+      if (want_rec) {
+        const int c = ck * 8 + 2 * p;
+        const uint32_t x0 = wd[p] & 0xffffu, x1 = wd[p] >> 16;
+        const uint32_t r0 = (sink || o0) ? x0 : (uint32_t)f2h(lev_s[c * L + c0]);
+        const uint32_t r1 = (sink || o1) ? x1 : (uint32_t)f2h(lev_s[(c + 1) * L + c1]);
+        rec[p] = r0 | (r1 << 16);
       }
-      codes |= code << (BITS * i);
-      rec[i] = (sink || o) ? x[i] : f2h(a.key_levels[ch * L + code]);
     }
-  } else {
+    omask[it] = valid ? om : 0u;
+    // pack: the 4 lanes of a quad hold 32 consecutive codes = 4*BITS bytes
+    const uint32_t n1 = dpp<0x39>(codes), n2 = dpp<0x4e>(codes), n3 = dpp<0x93>(codes);  // lanes +1, +2, +3
+    if (valid && (ck & 3) == 0) {
+      const uint64_t lo = (uint64_t)codes | ((uint64_t)n1 << (8 * BITS));
+      const uint64_t hi = (uint64_t)n2 | ((uint64_t)n3 << (8 * BITS));
+      uint32_t *dst = reinterpret_cast<uint32_t *>(kout + (size_t)row * (D * BITS / 8) + (ck / 4) * 4 * BITS);
+      uint32_t wo[4];
+      if constexpr (BITS == 1) { wo[0] = (uint32_t)(lo | (hi << 16)); }
+      if constexpr (BITS == 2) { wo[0] = (uint32_t)lo; wo[1] = (uint32_t)hi; }
+      if constexpr (BITS == 3) {  // lo and hi hold 48 bits each
+        wo[0] = (uint32_t)lo; wo[1] = (uint32_t)(lo >> 32) | (uint32_t)(hi << 16); wo[2] = (uint32_t)(hi >> 16);
+      }
+      if constexpr (BITS == 4) {
+        wo[0] = (uint32_t)lo; wo[1] = (uint32_t)(lo >> 32); wo[2] = (uint32_t)hi; wo[3] = (uint32_t)(hi >> 32);
+      }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) { out[i] = false; rec[i] = 0; }
+      for (int j = 0; j < BITS; ++j) dst[j] = wo[j];
+    }
+    if (valid && want_rec)
+      *reinterpret_cast<uint4 *>(a.k_recon + ((size_t)bh * a.S + row) * D + ck * 8) =
+          make_uint4(rec[0], rec[1], rec[2], rec[3]);
   }
-  // pack: 4 consecutive lanes hold 32 codes = 4*BITS bytes
-  const uint32_t c1 = __shfl_down(codes, 1), c2 = __shfl_down(codes, 2), c3 = __shfl_down(codes, 3);
-  if (valid && (ck & 3) == 0) {
-    const uint64_t lo = (uint64_t)codes | ((uint64_t)c1 << (8 * BITS));
-    const uint64_t hi = (uint64_t)c2 | ((uint64_t)c3 << (8 * BITS));
-    uint32_t *dst = reinterpret_cast<uint32_t *>(a.k_codes + ((size_t)bh * a.S + row) * (D * BITS / 8) +
-                                                 (ck / 4) * 4 * BITS);
-    // 16*BITS bits per half: write BITS dwords
-    uint32_t wd[4];
-    if constexpr (BITS == 1) { wd[0] = (uint32_t)(lo | (hi << 16)); }
-    if constexpr (BITS == 2) { wd[0] = (uint32_t)lo; wd[1] = (uint32_t)hi; }
-    if constexpr (BITS == 3) {  // lo and hi hold 48 bits each
-      wd[0] = (uint32_t)lo; wd[1] = (uint32_t)(lo >> 32) | (uint32_t)(hi << 16); wd[2] = (uint32_t)(hi >> 16);
-    }
-    if constexpr (BITS == 4) {
-      wd[0] = (uint32_t)lo; wd[1] = (uint32_t)(lo >> 32); wd[2] = (uint32_t)hi; wd[3] = (uint32_t)(hi >> 32);
-    }
+  // ---- ordered compaction: flat order is (wave, step, lane, channel). Step
+  // counts (<= 8 per lane, <= 512 per wave) are scanned three at a time in
+  // 10-bit fields of one word.
+  int pre[KQ_NIT], stot[KQ_NIT];
 #pragma unroll
-    for (int j = 0; j < BITS; ++j) dst[j] = wd[j];
+  for (int g = 0; g < KQ_NIT; g += 3) {
+    uint32_t packed = 0;
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+      if (g + t < KQ_NIT) packed |= (uint32_t)__builtin_popcount(omask[g + t]) << (10 * t);
+    int tot;
+    const uint32_t ex = (uint32_t)wave_excl((int)packed, tot);
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+      if (g + t < KQ_NIT) {
+        pre[g + t] = (int)((ex >> (10 * t)) & 1023u);
+        stot[g + t] = (int)(((uint32_t)tot >> (10 * t)) & 1023u);
+      }
   }
-  if (valid && a.k_recon) {
-    *reinterpret_cast<uint4 *>(a.k_recon + ((size_t)bh * a.S + row) * D + ck * 8) =
-        make_uint4(rec[0] | (rec[1] << 16), rec[2] | ((uint32_t)rec[3] << 16),
-                   rec[4] | ((uint32_t)rec[5] << 16), rec[6] | ((uint32_t)rec[7] << 16));
+  int wsum = 0;
+#pragma unroll
+  for (int it = 0; it < KQ_NIT; ++it) {
+    const int s_ = stot[it];
+    stot[it] = wsum;  // now: offset of step it inside the wave
+    wsum += s_;
   }
-  // ordered compaction of outliers (lane order = flat order inside the block)
-  int wtot;
-  const int wpre = wave_excl(nout, wtot);
-  if (lane == 0) wave_cnt[wv] = wtot;
+  if (lane == 0) wave_cnt[wv] = wsum;
   __syncthreads();
   int before = 0, btot = 0;
+#pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (i < wv) before += wave_cnt[i];
     btot += wave_cnt[i];
@@ -572,13 +703,23 @@ __global__ __launch_bounds__(256) void nuq_key_quant(NuqArgs a) {
     a.ws_kblk[blk * 2 + 1] = (uint32_t)btot;
   }
   __syncthreads();
-  int slot = blk_base + before + wpre;
+  const int wbase = (int)blk_base + before;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if (out[i]) {
-      a.ws_kpos[slot] = (int32_t)(((size_t)bh * a.S + row) * D + ck * 8 + i);
-      a.ws_kval[slot] = x[i];
-      ++slot;
+  for (int it = 0; it < KQ_NIT; ++it) {
+    uint32_t m = omask[it];
+    if (m) {
+      const int row = row_w + it * RPW;
+      const uint4 in = *reinterpret_cast<const uint4 *>(kin + (size_t)row * D);
+      const uint32_t wd[4] = {in.x, in.y, in.z, in.w};
+      int slot = wbase + stot[it] + pre[it];
+      const int32_t fpos = (int32_t)(((size_t)bh * a.S + row) * D + ck * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (m & (1u << e)) {
+          a.ws_kpos[slot] = fpos + e;
+          a.ws_kval[slot] = (uint16_t)(wd[e / 2] >> (16 * (e & 1)));
+          ++slot;
+        }
     }
   }
 }
@@ -600,10 +741,12 @@ __global__ __launch_bounds__(64) void nuq_value(NuqArgs a) {
   const int c0 = q * CH;                          // first channel of this lane
   const int nch = max(0, min(CH, D - c0));        // channels held by this lane
   const uint16_t *row = a.values + (size_t)(valid ? tok : 0) * D;
+  // the lane's channels as fp16 pairs (element i in word i/2); channels past
+  // nch are +inf padding, which sorts last
   uint32_t raw[64];
 #pragma unroll
   for (int i = 0; i < 64; ++i) raw[i] = 0x7c007c00u;
-  if (valid && !sink) {
+  if (valid) {
 #pragma unroll
     for (int i = 0; i < CH / 8; ++i)
       if (i * 8 < nch) {
@@ -612,14 +755,14 @@ __global__ __launch_bounds__(64) void nuq_value(NuqArgs a) {
       }
   }
   const int nq = (valid && !sink) ? nch : 0;
-  uint32_t v[64];
-  to_sort_layout(raw, v);
-  sort128(v);
-  const int sw = lane & 63;
-  uint32_t *w = lds + lane * 64;
-  store_chunk(w, sw, v);
+  {
+    uint32_t v[64];
+    to_sort_layout(raw, v);  // a sink's fit reads nothing, so its chunk content is irrelevant
+    sort128(v);
+    store_chunk(lds + lane * 64, lane & 63, v);
+  }
   __syncthreads();
-  Chunk c{w, sw};
+  Chunk c{lds + lane * 64, lane & 63};
   float lev[L];
   FitOut fo;
   fit_vector<CPC, L>(c, nq, a.frac, a.iters, lev, fo);
@@ -630,39 +773,52 @@ __global__ __launch_bounds__(64) void nuq_value(NuqArgs a) {
 #pragma unroll
     for (int j = 0; j < L; ++j) vl[j] = sink ? 0.0f : lev[j];
   }
-  // quantize this lane's channels: codes packed LSB-first along D
+  // quantize this lane's channels, 8 at a time: the row is read again
+  // (16-byte loads, L2 hits) rather than kept in registers across the sort
+  // and the fit; codes are packed LSB-first along D
+  const uint32_t tau_abs = sink ? 0x7fffu : fo.tau;  // no outliers in sink tokens
   int nout = 0;
   constexpr int OBW = CH * BITS / 32;  // dwords of packed codes for 128 channels
   uint32_t ob[OBW + 1];
 #pragma unroll
   for (int i = 0; i <= OBW; ++i) ob[i] = 0;
-  if (valid) {
+  const bool want_rec = valid && a.v_recon != nullptr;
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      if (i < nch) {
-        const uint16_t x = row[c0 + i];
-        uint32_t code = 0;
-        bool o = false;
-        if (!sink) {
-          o = h2f((uint16_t)(x & 0x7fffu)) > h2f(fo.tau);
-          if (!o) {
-            const uint32_t kx = key16(x);
+  for (int g = 0; g < CH / 8; ++g) {
+    if (g * 8 >= nch) break;
+    uint4 in = make_uint4(0, 0, 0, 0);
+    if (valid) in = *reinterpret_cast<const uint4 *>(row + c0 + g * 8);
+    const uint32_t wd[4] = {in.x, in.y, in.z, in.w};
+    uint32_t rw[4];
 #pragma unroll
-            for (int j = 0; j < L - 1; ++j) code += kx > T[j];
-          }
-        }
-        nout += o;
-        const int bit = i * BITS;
-        ob[bit / 32] |= code << (bit % 32);
-        if (bit % 32 + BITS > 32) ob[bit / 32 + 1] |= code >> (32 - bit % 32);
-        if (a.v_recon) {
-          float lv = lev[0];
+    for (int e = 0; e < 8; ++e) {
+      const int i = g * 8 + e;
+      const uint32_t x = (wd[e / 2] >> (16 * (e & 1))) & 0xffffu;
+      // |x| > tau on non-negative fp16 patterns is an integer comparison
+      const bool o = (x & 0x7fffu) > tau_abs;
+      uint32_t code = 0;
+      if (!sink) {
+        const uint32_t kx = key16(x);
 #pragma unroll
-          for (int j = 1; j < L; ++j) lv = code == (uint32_t)j ? lev[j] : lv;
-          a.v_recon[(size_t)tok * D + c0 + i] = (sink || o) ? x : f2h(lv);
-        }
+        for (int j = 0; j < L - 1; ++j) code += kx > T[j];
+        code = o ? 0u : code;
+      }
+      nout += o ? 1 : 0;
+      const int bit = i * BITS;
+      ob[bit / 32] |= code << (bit % 32);
+      if (bit % 32 + BITS > 32) ob[bit / 32 + 1] |= code >> (32 - bit % 32);
+      if (want_rec) {
+        float lv = lev[0];
+#pragma unroll
+        for (int j = 1; j < L; ++j) lv = code == (uint32_t)j ? lev[j] : lv;
+        const uint32_t r16 = (sink || o) ? x : (uint32_t)f2h(lv);
+        if (e & 1) rw[e / 2] |= r16 << 16; else rw[e / 2] = r16;
       }
     }
+    if (want_rec)
+      *reinterpret_cast<uint4 *>(a.v_recon + (size_t)tok * D + c0 + g * 8) = make_uint4(rw[0], rw[1], rw[2], rw[3]);
+  }
+  if (valid) {
     // the lane's code bytes start on a dword boundary (D >= 32, 128-channel chunks)
     uint32_t *crow = reinterpret_cast<uint32_t *>(a.v_codes + (size_t)tok * (D * BITS / 8) +
                                                   (size_t)c0 * BITS / 8);
@@ -682,14 +838,19 @@ __global__ __launch_bounds__(64) void nuq_value(NuqArgs a) {
     a.ws_vblk[blockIdx.x * 2 + 1] = (uint32_t)tot;
   }
   __syncthreads();
-  if (valid && !sink && nout) {
+  if (nout) {
     int slot = base_s + pre;
-    for (int i = 0; i < nch; ++i) {
-      const uint16_t x = row[c0 + i];
-      if (h2f((uint16_t)(x & 0x7fffu)) > h2f(fo.tau)) {
-        a.ws_vpos[slot] = (int32_t)((size_t)tok * D + c0 + i);
-        a.ws_vval[slot] = x;
-        ++slot;
+    for (int g = 0; g < CH / 8 && g * 8 < nch; ++g) {
+      const uint4 in = *reinterpret_cast<const uint4 *>(row + c0 + g * 8);
+      const uint32_t wd[4] = {in.x, in.y, in.z, in.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t x = (wd[e / 2] >> (16 * (e & 1))) & 0xffffu;
+        if ((x & 0x7fffu) > tau_abs) {
+          a.ws_vpos[slot] = (int32_t)((size_t)tok * D + c0 + g * 8 + e);
+          a.ws_vval[slot] = (uint16_t)x;
+          ++slot;
+        }
       }
     }
   }
@@ -767,9 +928,6 @@ hipError_t launch_bits(const NuqArgs &a, int key_cpc, int val_cpc, hipStream_t s
   hipLaunchKernelGGL(nuq_zero, dim3(1), dim3(64), 0, st, a.ws_ctr);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.fit_keys && (e = launch_key_fit<L>(a, key_cpc, st)) != hipSuccess) return e;
-  const int64_t nch = (int64_t)a.BH * a.D;
-  hipLaunchKernelGGL((nuq_key_cuts<L>), dim3((unsigned)((nch + 255) / 256)), dim3(256), 0, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((nuq_key_quant<BITS>), dim3((unsigned)a.k_blk_x, a.BH), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (val_cpc == 1)
