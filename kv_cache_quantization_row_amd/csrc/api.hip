@@ -281,7 +281,7 @@ struct NuqPlan {
   int n_sink_eff, n_fit, key_cpc, val_cpc;
   int64_t kb, vb;  // outlier bounds
   int64_t k_blk_x, v_nblk;
-  int64_t off_ctr, off_kblk, off_vblk, off_kpos, off_kval, off_vpos, off_vval, total;
+  int64_t off_ctr, off_kblk, off_vblk, off_ksup, off_vsup, off_kpos, off_kval, off_vpos, off_vval, total;
 };
 
 int64_t floor_frac(float frac, int64_t n) { return (int64_t)std::floor((double)frac * (double)n); }
@@ -303,16 +303,20 @@ int nuq_plan(int32_t BH, int32_t S, int32_t D, int32_t bits, int32_t start_pos, 
   int chunks = (p.n_fit + 127) / 128, cpc = 1;
   while (cpc < chunks) cpc <<= 1;
   p.key_cpc = cpc;
-  p.val_cpc = D <= 128 ? 1 : 2;
+  // values: one wave per token for up to 4096 tokens (latency), else one
+  // lane (D <= 128) or two lanes (D = 256) per token (throughput)
+  p.val_cpc = (int64_t)BH * S <= 4096 ? 0 : (D <= 128 ? 1 : 2);
   p.kb = fit_keys ? (int64_t)BH * D * floor_frac(frac, p.n_fit) : (int64_t)BH * p.n_fit * D;
   p.vb = (int64_t)BH * p.n_fit * floor_frac(frac, D);
   const int rpb = 16384 / D;  // key-quant rows per workgroup: 4 waves x 8 steps x 512/D rows
   p.k_blk_x = (S + rpb - 1) / rpb;
-  p.v_nblk = ((int64_t)BH * S + (64 / p.val_cpc) - 1) / (64 / p.val_cpc);
+  p.v_nblk = p.val_cpc == 0 ? (int64_t)BH * S : ((int64_t)BH * S + (64 / p.val_cpc) - 1) / (64 / p.val_cpc);
   int64_t o = 0;
   p.off_ctr = o; o = align256(o + 16);
   p.off_kblk = o; o = align256(o + p.k_blk_x * BH * 8);
   p.off_vblk = o; o = align256(o + p.v_nblk * 8);
+  p.off_ksup = o; o = align256(o + (p.k_blk_x * BH + 63) / 64 * 4);
+  p.off_vsup = o; o = align256(o + (p.v_nblk + 63) / 64 * 4);
   p.off_kpos = o; o = align256(o + p.kb * 4);
   p.off_kval = o; o = align256(o + p.kb * 2);
   p.off_vpos = o; o = align256(o + p.vb * 4);
@@ -390,6 +394,8 @@ int kvq_nuq_fit_quant(const uint16_t *keys, const uint16_t *values, int32_t BH, 
   a.ws_ctr = reinterpret_cast<uint32_t *>(ws + p.off_ctr);
   a.ws_kblk = reinterpret_cast<uint32_t *>(ws + p.off_kblk);
   a.ws_vblk = reinterpret_cast<uint32_t *>(ws + p.off_vblk);
+  a.ws_ksup = reinterpret_cast<uint32_t *>(ws + p.off_ksup);
+  a.ws_vsup = reinterpret_cast<uint32_t *>(ws + p.off_vsup);
   a.ws_kpos = reinterpret_cast<int32_t *>(ws + p.off_kpos);
   a.ws_kval = reinterpret_cast<uint16_t *>(ws + p.off_kval);
   a.ws_vpos = reinterpret_cast<int32_t *>(ws + p.off_vpos);

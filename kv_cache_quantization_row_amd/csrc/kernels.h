@@ -58,7 +58,8 @@ struct NuqArgs {
   uint16_t *k_recon, *v_recon;     // optional
   // workspace
   uint32_t *ws_ctr;                // 4 counters
-  uint32_t *ws_kblk, *ws_vblk;     // per block (staging base, count -> final offset)
+  uint32_t *ws_kblk, *ws_vblk;     // per workgroup (staging base, count)
+  uint32_t *ws_ksup, *ws_vsup;     // per 64 workgroups: sum of their counts
   int32_t *ws_kpos, *ws_vpos;      // staging
   uint16_t *ws_kval, *ws_vval;
   int64_t k_blk_x, v_nblk;         // key-quant workgroups along S (16384/D rows each); value workgroups

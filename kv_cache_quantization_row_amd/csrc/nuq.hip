@@ -34,9 +34,10 @@
 //     so each level is the exact mean rounded once to binary32.
 // Codes are then #{j : x > T_j}, which equals the first index of the nearest
 // level. The side channel (flat index, fp16 value) is emitted in ascending
-// flat order: each block reserves a staging range with one atomic, an
-// ordered scan of the block counts places the blocks, a copy kernel moves the
-// entries (no inter-block waiting).
+// flat order: each workgroup reserves a staging range with one atomic and
+// adds its count to a per-64-workgroup sum; one placement kernel then puts
+// every workgroup's entries at the sum of the counts before it (no
+// inter-workgroup waiting).
 #include "common.h"
 #include "kernels.h"
 
@@ -467,8 +468,12 @@ __device__ __forceinline__ int wave_excl(int v, int &total) {
 }  // namespace
 
 // ================================================================== kernels
-__global__ void nuq_zero(uint32_t *ctr) {
-  if (threadIdx.x < 4) ctr[threadIdx.x] = 0;
+// staging counters and the per-64-workgroup count sums start at zero
+__global__ __launch_bounds__(256) void nuq_zero(NuqArgs a) {
+  if (threadIdx.x < 4) a.ws_ctr[threadIdx.x] = 0;
+  const int64_t ks = (a.k_blk_x * a.BH + 63) >> 6, vs = (a.v_nblk + 63) >> 6;
+  for (int64_t i = threadIdx.x; i < ks; i += 256) a.ws_ksup[i] = 0;
+  for (int64_t i = threadIdx.x; i < vs; i += 256) a.ws_vsup[i] = 0;
 }
 
 // Key fit: lanes (channel g, chunk q) with CPC chunks per channel; a
@@ -698,6 +703,7 @@ __global__ __launch_bounds__(256) void nuq_key_quant(NuqArgs a) {
   const int64_t blk = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
   if (threadIdx.x == 0) {
     const uint32_t base = btot ? atomicAdd(&a.ws_ctr[0], (uint32_t)btot) : 0u;
+    if (btot) atomicAdd(&a.ws_ksup[blk >> 6], (uint32_t)btot);
     blk_base = base;
     a.ws_kblk[blk * 2] = base;
     a.ws_kblk[blk * 2 + 1] = (uint32_t)btot;
@@ -833,6 +839,7 @@ __global__ __launch_bounds__(64) void nuq_value(NuqArgs a) {
   __shared__ uint32_t base_s;
   if (lane == 0) {
     const uint32_t base = tot ? atomicAdd(&a.ws_ctr[1], (uint32_t)tot) : 0u;
+    if (tot) atomicAdd(&a.ws_vsup[blockIdx.x >> 6], (uint32_t)tot);
     base_s = base;
     a.ws_vblk[blockIdx.x * 2] = base;
     a.ws_vblk[blockIdx.x * 2 + 1] = (uint32_t)tot;
@@ -856,48 +863,307 @@ __global__ __launch_bounds__(64) void nuq_value(NuqArgs a) {
   }
 }
 
-// exclusive scan of block counts in block order (one workgroup), then the
-// totals; info[2b] = staging base, info[2b+1] = count -> final offset in [2b+1]
-__global__ __launch_bounds__(1024) void nuq_scan(uint32_t *info, int64_t nblk, int64_t *total) {
-  __shared__ uint32_t part[1024];
-  uint32_t carry = 0;
-  for (int64_t b0 = 0; b0 < nblk; b0 += 1024) {
-    const int64_t b = b0 + threadIdx.x;
-    const uint32_t cnt = b < nblk ? info[b * 2 + 1] : 0u;
-    part[threadIdx.x] = cnt;
-    __syncthreads();
-    for (int d = 1; d < 1024; d <<= 1) {
-      const uint32_t y = threadIdx.x >= (unsigned)d ? part[threadIdx.x - d] : 0u;
-      __syncthreads();
-      part[threadIdx.x] += y;
-      __syncthreads();
+// Value fit + quantize for few tokens (decode steps, short chunks): one wave
+// per token, channel l*E + e in lane l (E = max(1, D/64)). The token's keys
+// are sorted across the wave (bitonic network on packed 16-bit keys, sorted
+// element i in lane i % 64, slot i / 64, two slots per register), with exact
+// double prefix sums of the sorted values. Then every count is a ballot over
+// the wave, tau is a bitwise search with ballot counts, the quantile order
+// statistics are reads of the sorted keys, and a Lloyd cell sum is the
+// difference of two prefix sums at its cut positions; the per-level work of
+// an iteration (one cut threshold, one division) is spread over lanes and
+// broadcast. The arithmetic is the same as in nuq_value.
+template <int E>
+__device__ __forceinline__ int wave_count(const bool (&p)[E]) {
+  int c = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) c += __popcll(__ballot(p[e]));
+  return c;
+}
+template <int L>
+__device__ __forceinline__ float pick(const float (&v)[L], int i) {  // v[i] for a lane-varying i
+  float r = v[0];
+#pragma unroll
+  for (int j = 1; j < L; ++j) r = i == j ? v[j] : r;
+  return r;
+}
+template <int J>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {  // value of lane ^ J
+  if constexpr (J == 1) return dpp<DPP_XOR1>(v);
+  else if constexpr (J == 2) return dpp<DPP_XOR2>(v);
+  else if constexpr (J < 32) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (J << 10) | 0x1f);
+  else return (uint32_t)__shfl_xor((int)v, 32);
+}
+// one bitonic stage (block K, distance J) over NS = 2R slots of 64 lanes
+template <int R, int K, int J>
+__device__ __forceinline__ void bstage(uint32_t (&v)[R], int lane) {
+  if constexpr (J >= 128) {  // slots s and s ^ 2: registers 0 and 1; K = 256, ascending
+    const u16x2v a = __builtin_bit_cast(u16x2v, v[0]), b = __builtin_bit_cast(u16x2v, v[1]);
+    v[0] = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(a, b));
+    v[1] = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
+  } else if constexpr (J == 64) {  // slots 2r and 2r+1: the two halves of register r
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t lo = v[r] & 0xffffu, hi = v[r] >> 16;
+      const bool asc = ((128 * r) & K) == 0;
+      const uint32_t mn = min(lo, hi), mx = max(lo, hi);
+      v[r] = asc ? (mn | (mx << 16)) : (mx | (mn << 16));
     }
-    const uint32_t incl = part[threadIdx.x];
-    if (b < nblk) {
-      info[b * 2 + 1] = carry + incl - cnt;  // final offset
-      // keep the count recoverable: next offset - this offset
+  } else {  // partner lane ^ J, same slot
+    const bool lower = (lane & J) == 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t p = lane_xor<J>(v[r]);
+      const u16x2v a = __builtin_bit_cast(u16x2v, v[r]), b = __builtin_bit_cast(u16x2v, p);
+      const uint32_t mn = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(a, b));
+      const uint32_t mx = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
+      const bool asc0 = ((lane + 64 * (2 * r)) & K) == 0, asc1 = ((lane + 64 * (2 * r + 1)) & K) == 0;
+      const uint32_t sel = ((asc0 == lower) ? 0x0000ffffu : 0u) | ((asc1 == lower) ? 0xffff0000u : 0u);
+      v[r] = (mn & sel) | (mx & ~sel);
     }
-    const uint32_t last = part[1023];
-    __syncthreads();
-    carry += last;
   }
-  if (threadIdx.x == 0) *total = carry;
+}
+template <int R, int K, int J>
+__device__ __forceinline__ void bmerge(uint32_t (&v)[R], int lane) {
+  bstage<R, K, J>(v, lane);
+  if constexpr (J > 1) bmerge<R, K, J / 2>(v, lane);
+}
+template <int R, int K>
+__device__ __forceinline__ void bsort(uint32_t (&v)[R], int lane) {
+  if constexpr (K <= 128 * R) {
+    bmerge<R, K, K / 2>(v, lane);
+    bsort<R, 2 * K>(v, lane);
+  }
+}
+template <int E, int BITS>
+__global__ __launch_bounds__(64) void nuq_value_wave(NuqArgs a) {
+  constexpr int L = 1 << BITS;
+  constexpr int R = E == 4 ? 2 : 1;  // packed sort registers per lane
+  __shared__ uint8_t cb[256];        // one code per channel
+  __shared__ uint32_t base_s;
+  const int lane = threadIdx.x;
+  const int64_t tok = blockIdx.x;  // flat token bh*S + s
+  const bool sink = (int)(tok % a.S) < a.n_sink_eff;
+  const int D = a.D;
+  const uint16_t *row = a.values + (size_t)tok * D;
+  uint32_t x[E];
+  bool ok[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) ok[e] = lane * E + e < D;
+  if constexpr (E == 1) {
+    x[0] = ok[0] ? row[lane] : 0u;
+  } else if constexpr (E == 2) {
+    const uint32_t w = *reinterpret_cast<const uint32_t *>(row + 2 * lane);
+    x[0] = w & 0xffffu; x[1] = w >> 16;
+  } else {
+    const uint2 w = *reinterpret_cast<const uint2 *>(row + 4 * lane);
+    x[0] = w.x & 0xffffu; x[1] = w.x >> 16; x[2] = w.y & 0xffffu; x[3] = w.y >> 16;
+  }
+  uint32_t ky[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) ky[e] = key16(x[e]);
+  float lev[L];
+#pragma unroll
+  for (int j = 0; j < L; ++j) lev[j] = 0.0f;
+  uint32_t tau = 0x7fffu;  // no outliers in sink tokens
+  if (!sink) {
+    const long long k = (long long)floor((double)a.frac * (double)D);
+    // ---- tau: largest c with #{|x| >= c} >= k + 1
+    int pos = 0;
+    for (int sb = 16384; sb >= 1; sb >>= 1) {
+      const int cand = pos + sb - 1;
+      if (cand > 0x7bff) continue;
+      bool p[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) p[e] = ok[e] && (x[e] & 0x7fffu) >= (uint32_t)cand;
+      if (wave_count<E>(p) >= k + 1) pos += sb;
+    }
+    tau = (uint32_t)(pos - 1);
+    const uint32_t klo = tau == 0 ? key16(0x8000u) : key16(tau | 0x8000u);
+    bool inl[E], below[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      inl[e] = ok[e] && (x[e] & 0x7fffu) <= tau;
+      below[e] = ok[e] && ky[e] < klo;
+    }
+    const int m = wave_count<E>(inl);
+    const int lo = wave_count<E>(below), hi = lo + m;  // inliers: sorted positions [lo, hi)
+    // ---- sort the keys across the wave (absent channels are 0xffff and sort last)
+    uint32_t v[R];
+    if constexpr (E == 1) v[0] = (ok[0] ? ky[0] : 0xffffu) | 0xffff0000u;
+    else if constexpr (E == 2) v[0] = ky[0] | (ky[1] << 16);
+    else { v[0] = ky[0] | (ky[1] << 16); v[1] = ky[2] | (ky[3] << 16); }
+    bsort<R, 2>(v, lane);
+    auto key_at = [&](int i) -> uint32_t {  // sorted key i (uniform i)
+      const int s_ = i >> 6;
+      const uint32_t w = (uint32_t)__builtin_amdgcn_readlane((int)((s_ >> 1) ? v[R - 1] : v[0]), i & 63);
+      return (s_ & 1) ? (w >> 16) : (w & 0xffffu);
+    };
+    // ---- exact inclusive prefix sums of the sorted values, slot by slot
+    double ps[2 * R];
+    double carry = 0.0;
+#pragma unroll
+    for (int sl = 0; sl < 2 * R; ++sl) {
+      const uint32_t kk = (sl & 1) ? (v[sl >> 1] >> 16) : (v[sl >> 1] & 0xffffu);
+      double t = kk == 0xffffu ? 0.0 : kval(kk);
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const double y = __shfl_up(t, d);
+        t += lane >= d ? y : 0.0;
+      }
+      ps[sl] = t + carry;
+      carry = __shfl(ps[sl], 63);
+    }
+    auto pref = [&](int c) -> double {  // sum of the c smallest values (uniform c)
+      if (c == 0) return 0.0;
+      const int i = c - 1, sl = i >> 6;
+      double w = ps[0];
+#pragma unroll
+      for (int t = 1; t < 2 * R; ++t) w = sl == t ? ps[t] : w;
+      const uint64_t b = __builtin_bit_cast(uint64_t, w);
+      const uint32_t l32 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, i & 63);
+      const uint32_t h32 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), i & 63);
+      return __builtin_bit_cast(double, (uint64_t)l32 | ((uint64_t)h32 << 32));
+    };
+    // ---- quantile initialisation
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+      const long long num = (long long)(2 * j + 1) * (long long)(m - 1);
+      const int r = (int)(num / (2 * L));
+      const int rem = (int)(num % (2 * L));
+      double val = kval(key_at(lo + r));
+      if (rem != 0) val = val + ((double)rem / (double)(2 * L)) * (kval(key_at(lo + r + 1)) - val);
+      lev[j] = (float)val + 0.0f;
+    }
+    // ---- Lloyd iterations: cells are sorted ranges cut at the threshold keys
+    for (int it = 0; it < a.iters; ++it) {
+      uint32_t tj = 0;  // lane j < L-1: cut key between levels j and j+1 (0: equal levels)
+      if (lane < L - 1) {
+        const float l0 = pick<L>(lev, lane), l1 = pick<L>(lev, lane + 1);
+        if (l0 < l1) tj = key16(thr16(l0, l1));
+      }
+      uint32_t nt = 0xffffu;
+      int cut[L];
+      cut[L - 1] = hi;
+#pragma unroll
+      for (int j = L - 2; j >= 0; --j) {
+        const uint32_t r = (uint32_t)__builtin_amdgcn_readlane((int)tj, j);
+        if (r) nt = r;
+        bool p[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) p[e] = ok[e] && ky[e] <= nt;
+        cut[j] = min(max(wave_count<E>(p), lo), hi);
+      }
+      // lane q: cell q's count and exact sum
+      int my_cnt = 0;
+      double my_sum = 0.0;
+      int prev = lo;
+      double pprev = pref(lo);
+#pragma unroll
+      for (int q = 0; q < L; ++q) {
+        const double pc = pref(cut[q]);
+        if (lane == q) { my_cnt = cut[q] - prev; my_sum = pc - pprev; }
+        prev = cut[q];
+        pprev = pc;
+      }
+      const float cur = pick<L>(lev, lane);
+      const float nl = my_cnt > 0 ? (float)(my_sum / (double)my_cnt) : cur;
+#pragma unroll
+      for (int q = 0; q < L; ++q) lev[q] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, nl), q));
+      sort_levels<L>(lev);
+    }
+  }
+  // ---- codes, reconstruction, level row
+  uint32_t T[L];
+  cut_keys<L>(lev, T);
+  bool out[E];
+  uint32_t code[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    out[e] = ok[e] && (x[e] & 0x7fffu) > tau;
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < L - 1; ++j) c += ky[e] > T[j];
+    code[e] = (sink || out[e]) ? 0u : c;
+    if (ok[e]) cb[lane * E + e] = (uint8_t)code[e];
+  }
+  if (a.v_recon) {
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (ok[e])
+        a.v_recon[(size_t)tok * D + lane * E + e] =
+            (sink || out[e]) ? (uint16_t)x[e] : f2h(pick<L>(lev, (int)code[e]));
+  }
+  if (lane < L) a.value_levels[(size_t)tok * L + lane] = sink ? 0.0f : pick<L>(lev, lane);
+  __syncthreads();
+  // codes LSB-first along D: lane w builds dword w of the row
+  if (lane < D * BITS / 32) {
+    const int bit0 = 32 * lane;
+    uint32_t acc = 0;
+    for (int c = bit0 / BITS; c * BITS < bit0 + 32; ++c) {
+      const int sh = c * BITS - bit0;
+      acc |= sh >= 0 ? (uint32_t)cb[c] << sh : (uint32_t)cb[c] >> -sh;
+    }
+    reinterpret_cast<uint32_t *>(a.v_codes + (size_t)tok * (D * BITS / 8))[lane] = acc;
+  }
+  // ---- side channel: flat order is (lane, e)
+  const int nout = wave_count<E>(out);
+  if (lane == 0) {
+    const uint32_t base = nout ? atomicAdd(&a.ws_ctr[1], (uint32_t)nout) : 0u;
+    if (nout) atomicAdd(&a.ws_vsup[blockIdx.x >> 6], (uint32_t)nout);
+    base_s = base;
+    a.ws_vblk[blockIdx.x * 2] = base;
+    a.ws_vblk[blockIdx.x * 2 + 1] = (uint32_t)nout;
+  }
+  __syncthreads();
+  int nb = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint64_t b = __ballot(out[e]);
+    nb += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+  }
+  int slot = (int)base_s + nb;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (out[e]) {
+      a.ws_vpos[slot] = (int32_t)((size_t)tok * D + lane * E + e);
+      a.ws_vval[slot] = (uint16_t)x[e];
+      ++slot;
+    }
 }
 
-// move each block's staged entries to their final place; counts are the
-// differences of consecutive final offsets
-__global__ __launch_bounds__(256) void nuq_copy(const uint32_t *info, int64_t nblk, const int64_t *total,
-                                                const int32_t *spos, const uint16_t *sval, int32_t *opos,
-                                                uint16_t *oval) {
-  const int64_t b = blockIdx.x;
-  if (b >= nblk) return;
-  const uint32_t off = info[b * 2 + 1];
-  const uint32_t end = b + 1 < nblk ? info[b * 2 + 3] : (uint32_t)*total;
-  const uint32_t base = info[b * 2];
-  for (uint32_t i = threadIdx.x; i < end - off; i += blockDim.x) {
+// Place the staged side-channel entries in flat order, keys and values in one
+// launch: workgroups [0, kn) move the key-quant workgroups' entries, the rest
+// the value workgroups'. A producer workgroup b left (staging base, count) in
+// info[2b], info[2b+1] and added its count to sup[b/64]; the output offset of
+// b is the sum of the counts before it, read as whole groups of 64 from sup
+// plus single counts inside its own group. The last workgroup of each list
+// writes the list length.
+__global__ __launch_bounds__(256) void nuq_place(NuqArgs a, int64_t kn) {
+  __shared__ uint32_t red[4];
+  const bool isv = (int64_t)blockIdx.x >= kn;
+  const int64_t b = isv ? (int64_t)blockIdx.x - kn : (int64_t)blockIdx.x;
+  const int64_t nblk = isv ? a.v_nblk : kn;
+  const uint32_t *info = isv ? a.ws_vblk : a.ws_kblk;
+  const uint32_t *sup = isv ? a.ws_vsup : a.ws_ksup;
+  const int64_t g0 = b >> 6;
+  uint32_t part = 0;
+  for (int64_t i = threadIdx.x; i < g0; i += 256) part += sup[i];
+  for (int64_t i = (g0 << 6) + threadIdx.x; i < b; i += 256) part += info[2 * i + 1];
+  for (int m = 1; m < 64; m <<= 1) part += (uint32_t)__shfl_xor((int)part, m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = part;
+  __syncthreads();
+  const uint32_t off = red[0] + red[1] + red[2] + red[3];
+  const uint32_t base = info[2 * b], cnt = info[2 * b + 1];
+  const int32_t *spos = isv ? a.ws_vpos : a.ws_kpos;
+  const uint16_t *sval = isv ? a.ws_vval : a.ws_kval;
+  int32_t *opos = isv ? a.v_opos : a.k_opos;
+  uint16_t *oval = isv ? a.v_oval : a.k_oval;
+  for (uint32_t i = threadIdx.x; i < cnt; i += 256) {
     opos[off + i] = spos[base + i];
     oval[off + i] = sval[base + i];
   }
+  if (b == nblk - 1 && threadIdx.x == 0) a.out_counts[isv ? 1 : 0] = (int64_t)off + cnt;
 }
 
 // ================================================================== launch
@@ -925,24 +1191,26 @@ template <int BITS>
 hipError_t launch_bits(const NuqArgs &a, int key_cpc, int val_cpc, hipStream_t st) {
   constexpr int L = 1 << BITS;
   hipError_t e;
-  hipLaunchKernelGGL(nuq_zero, dim3(1), dim3(64), 0, st, a.ws_ctr);
+  hipLaunchKernelGGL(nuq_zero, dim3(1), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.fit_keys && (e = launch_key_fit<L>(a, key_cpc, st)) != hipSuccess) return e;
   hipLaunchKernelGGL((nuq_key_quant<BITS>), dim3((unsigned)a.k_blk_x, a.BH), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (val_cpc == 1)
+  if (val_cpc == 0) {  // one wave per token
+    if (a.D <= 64)
+      hipLaunchKernelGGL((nuq_value_wave<1, BITS>), dim3((unsigned)a.v_nblk), dim3(64), 0, st, a);
+    else if (a.D == 128)
+      hipLaunchKernelGGL((nuq_value_wave<2, BITS>), dim3((unsigned)a.v_nblk), dim3(64), 0, st, a);
+    else
+      hipLaunchKernelGGL((nuq_value_wave<4, BITS>), dim3((unsigned)a.v_nblk), dim3(64), 0, st, a);
+  } else if (val_cpc == 1) {
     hipLaunchKernelGGL((nuq_value<1, BITS>), dim3((unsigned)a.v_nblk), dim3(64), 0, st, a);
-  else
+  } else {
     hipLaunchKernelGGL((nuq_value<2, BITS>), dim3((unsigned)a.v_nblk), dim3(64), 0, st, a);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t k_nblk = a.k_blk_x * (int64_t)a.BH;
-  hipLaunchKernelGGL(nuq_scan, dim3(1), dim3(1024), 0, st, a.ws_kblk, k_nblk, a.out_counts);
-  hipLaunchKernelGGL(nuq_scan, dim3(1), dim3(1024), 0, st, a.ws_vblk, a.v_nblk, a.out_counts + 1);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(nuq_copy, dim3((unsigned)k_nblk), dim3(256), 0, st, a.ws_kblk, k_nblk, a.out_counts,
-                     a.ws_kpos, a.ws_kval, a.k_opos, a.k_oval);
-  hipLaunchKernelGGL(nuq_copy, dim3((unsigned)a.v_nblk), dim3(256), 0, st, a.ws_vblk, a.v_nblk,
-                     a.out_counts + 1, a.ws_vpos, a.ws_vval, a.v_opos, a.v_oval);
+  hipLaunchKernelGGL(nuq_place, dim3((unsigned)(k_nblk + a.v_nblk)), dim3(256), 0, st, a, k_nblk);
   return hipGetLastError();
 }
 }  // namespace

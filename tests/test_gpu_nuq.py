@@ -101,6 +101,19 @@ def test_prefill_then_decode(bits, D):
         compare(g, r, what="decode %d" % step)
 
 
+@pytest.mark.parametrize("bits", [3, 1, 2, 4])
+@pytest.mark.parametrize("D", [128, 32, 64, 256])
+def test_many_tokens_value_path(bits, D):
+    """More than 4096 (batch, head, token) value vectors: the value fit runs one
+    lane (or two at D=256) per token instead of one wave per token."""
+    say("nuq many tokens", bits, D)
+    BH, S = 33, 130
+    k, v = t4((BH, S, D), 30 + D + bits), t4((BH, S, D), 40 + D + bits)
+    g = gpu_nuq(k, v, 0, bits, 0.02, 8, 4, 1)
+    r = oracle.nuq_fit_quant(k, v, 0, bits, 0.02, 8, 4, 1)
+    compare(g, r, what="BH=%d S=%d" % (BH, S))
+
+
 @pytest.mark.parametrize("S", [1, 3, 4, 5, 129, 260, 1000, 2049])
 def test_ragged_lengths_and_sinks(S):
     say("nuq ragged", S)
@@ -112,10 +125,11 @@ def test_ragged_lengths_and_sinks(S):
         compare(g, r, what="S=%d start=%d sinks=%d" % (S, sp, ns))
 
 
+@pytest.mark.parametrize("BH", [2, 48])  # 48 x 90 tokens: the lane-per-token value path
 @pytest.mark.parametrize("case", ["ties", "zeros", "signed_zeros", "extremes", "subnormal", "const"])
-def test_degenerate_data(case):
-    say("nuq degenerate", case)
-    BH, S, D = 2, 90, 32
+def test_degenerate_data(case, BH):
+    say("nuq degenerate", case, BH)
+    S, D = 90, 32
     rng = np.random.default_rng(["ties", "zeros", "signed_zeros", "extremes", "subnormal", "const"].index(case))
     if case == "ties":
         x = rng.integers(-3, 4, size=(2, BH, S, D)).astype(np.float16)
