@@ -38,6 +38,8 @@
 // adds its count to a per-64-workgroup sum; one placement kernel then puts
 // every workgroup's entries at the sum of the counts before it (no
 // inter-workgroup waiting).
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -1187,15 +1189,35 @@ hipError_t launch_key_fit(const NuqArgs &a, int cpc, hipStream_t st) {
     default: return launch_key_fit_cpc<64, L>(a, st);
   }
 }
+// The value fit reads nothing the key kernels write, so for many tokens it
+// runs on a second stream of the device, forked from the caller's stream
+// after the counters are cleared and joined before the placement kernel: the
+// two fits then share the machine instead of running back to back. One stream
+// and two events per device, created on first use (default priority); the
+// fork/join section is serialised on the host so that concurrent callers
+// never interleave their event records.
+struct Fork {
+  hipStream_t aux = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_fork_mu;
+Fork g_fork[64];
+hipError_t fork_for_device(Fork *&f) {  // g_fork_mu held
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  f = &g_fork[dev];
+  if (f->aux == nullptr) {
+    if ((e = hipEventCreateWithFlags(&f->fork, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&f->join, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipStreamCreateWithFlags(&f->aux, hipStreamNonBlocking)) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 template <int BITS>
-hipError_t launch_bits(const NuqArgs &a, int key_cpc, int val_cpc, hipStream_t st) {
-  constexpr int L = 1 << BITS;
-  hipError_t e;
-  hipLaunchKernelGGL(nuq_zero, dim3(1), dim3(256), 0, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (a.fit_keys && (e = launch_key_fit<L>(a, key_cpc, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((nuq_key_quant<BITS>), dim3((unsigned)a.k_blk_x, a.BH), dim3(256), 0, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+hipError_t launch_values(const NuqArgs &a, int val_cpc, hipStream_t st) {
   if (val_cpc == 0) {  // one wave per token
     if (a.D <= 64)
       hipLaunchKernelGGL((nuq_value_wave<1, BITS>), dim3((unsigned)a.v_nblk), dim3(64), 0, st, a);
@@ -1208,7 +1230,33 @@ hipError_t launch_bits(const NuqArgs &a, int key_cpc, int val_cpc, hipStream_t s
   } else {
     hipLaunchKernelGGL((nuq_value<2, BITS>), dim3((unsigned)a.v_nblk), dim3(64), 0, st, a);
   }
+  return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t launch_bits(const NuqArgs &a, int key_cpc, int val_cpc, hipStream_t st) {
+  constexpr int L = 1 << BITS;
+  hipError_t e;
+  hipLaunchKernelGGL(nuq_zero, dim3(1), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (val_cpc == 0) {  // few tokens: short kernels, where a cross-stream join costs more than it hides
+    if (a.fit_keys && (e = launch_key_fit<L>(a, key_cpc, st)) != hipSuccess) return e;
+    hipLaunchKernelGGL((nuq_key_quant<BITS>), dim3((unsigned)a.k_blk_x, a.BH), dim3(256), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_values<BITS>(a, val_cpc, st)) != hipSuccess) return e;
+  } else {
+    std::lock_guard<std::mutex> lock(g_fork_mu);
+    Fork *f = nullptr;
+    if ((e = fork_for_device(f)) != hipSuccess) return e;
+    if ((e = hipEventRecord(f->fork, st)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(f->aux, f->fork, 0)) != hipSuccess) return e;
+    if ((e = launch_values<BITS>(a, val_cpc, f->aux)) != hipSuccess) return e;
+    if ((e = hipEventRecord(f->join, f->aux)) != hipSuccess) return e;
+    if (a.fit_keys && (e = launch_key_fit<L>(a, key_cpc, st)) != hipSuccess) return e;
+    hipLaunchKernelGGL((nuq_key_quant<BITS>), dim3((unsigned)a.k_blk_x, a.BH), dim3(256), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(st, f->join, 0)) != hipSuccess) return e;
+  }
   const int64_t k_nblk = a.k_blk_x * (int64_t)a.BH;
   hipLaunchKernelGGL(nuq_place, dim3((unsigned)(k_nblk + a.v_nblk)), dim3(256), 0, st, a, k_nblk);
   return hipGetLastError();
