@@ -198,32 +198,18 @@ __device__ __forceinline__ double gsum(double v) {
 }
 
 // ----------------------------------------------------------------- exact thresholds
-__device__ __forceinline__ uint16_t next16(uint16_t h) {
-  if ((h & 0x7fffu) == 0) return 0x0001u;
-  if (h & 0x8000u) {
-    const uint16_t r = (uint16_t)(h - 1);
-    return r == 0x8000u ? (uint16_t)0 : r;
-  }
-  return h == 0x7bffu ? h : (uint16_t)(h + 1);
-}
 __device__ __forceinline__ uint16_t prev16(uint16_t h) {
   if ((h & 0x7fffu) == 0) return 0x8001u;
   if (h & 0x8000u) return h == 0xfbffu ? h : (uint16_t)(h + 1);
   return (uint16_t)(h - 1);
 }
-// exact test 2u > a + b. TwoSum gives s + e == a + b exactly. If 2u and s
-// are within a factor of two (same sign), d = 2u - s is exact (Sterbenz) and
-// the sign of 2u - s - e is that of d - e; otherwise |d| >= |s|/2 > |e|, so
-// the sign is that of d. In both cases "d > e" decides exactly.
-__device__ __forceinline__ bool upper_of(double u, double a, double b) {
-  const double s = a + b;
-  const double bb = s - a;
-  const double e = (a - (s - bb)) + (b - bb);
-  const double d = 2.0 * u - s;
-  return d > e;
-}
-// largest finite fp16 t with 2t <= a + b, for levels a < b
-__device__ uint16_t thr16(float a, float b) {
+// largest finite fp16 t with 2t <= a + b, for levels a < b (the smallest
+// finite fp16 if there is none). With s + e == a + b exactly (TwoSum) and
+// m = s/2, no fp16 value lies strictly between m and the true midpoint
+// m + e/2 (their distance is below one double ulp of m), so the answer is
+// the largest fp16 <= m, stepped down once more when m is itself an fp16
+// value and e < 0. c = fp16(m) is one of the two fp16 neighbours of m.
+__device__ __forceinline__ uint16_t thr16(float a, float b) {
   const double da = a, db = b;
   const double s = da + db;
   const double bb = s - da;
@@ -231,17 +217,8 @@ __device__ uint16_t thr16(float a, float b) {
   const double m = s * 0.5;
   uint16_t c = f2h((float)m);
   if ((c & 0x7fffu) > 0x7bffu) c = (uint16_t)((c & 0x8000u) | 0x7bffu);
-  if (e == 0.0) {
-    // the midpoint is exact: c is within one fp16 step of it, on either side
-    if ((double)h2f(c) > m) c = prev16(c);
-  } else {
-    for (int i = 0; i < 4 && upper_of((double)h2f(c), da, db); ++i) c = prev16(c);
-    for (int i = 0; i < 4; ++i) {
-      const uint16_t n = next16(c);
-      if (n == c || upper_of((double)h2f(n), da, db)) break;
-      c = n;
-    }
-  }
+  const double hc = (double)h2f(c);
+  if (hc > m || (hc == m && e < 0.0)) c = prev16(c);
   return c == 0x8000u ? (uint16_t)0 : c;
 }
 // cut keys for sorted levels: cell j is (T[j-1], T[j]] on the key line;
@@ -411,14 +388,18 @@ __device__ void fit_vector(const Chunk &c, int nq, float frac, int iters, float 
         prev = max(prev, nc);
       }
     } else {
+      // cuts move little between iterations: walk each from its old position
+      // (the same result as a fresh search clamped to [lo, hi]), updating
+      // its prefix sum with the elements it passes
 #pragma unroll
       for (int q = 0; q < L - 1; ++q) {
-        const int nc = min(max(c.upper(T[q]), lo), hi);
-        double p = P[q];
-        for (int i = cut[q]; i < nc; ++i) p += kval(c.at(i));
-        for (int i = nc; i < cut[q]; ++i) p -= kval(c.at(i));
-        P[q] = p;
-        cut[q] = nc;
+        int pc = cut[q];
+        double ps = P[q];
+        const uint32_t t = T[q];
+        while (pc < hi && c.at(pc) <= t) { ps += kval(c.at(pc)); ++pc; }
+        while (pc > lo && c.at(pc - 1) > t) { --pc; ps -= kval(c.at(pc)); }
+        P[q] = ps;
+        cut[q] = pc;
       }
     }
     int prev_cut = lo;
@@ -568,6 +549,12 @@ __global__ __launch_bounds__(256) void nuq_key_quant(NuqArgs a) {
   const int bh = blockIdx.y;
   const int ck = lane % CL;
   const bool want_rec = a.k_recon != nullptr;
+  const int row_w = (blockIdx.x * 4 + wv) * (RPW * KQ_NIT) + lane / CL;  // first row of this lane
+  const uint16_t *kin = a.keys + (size_t)bh * a.S * D + ck * 8;
+  // the first row step's load is issued before the table set-up so that its
+  // latency overlaps it (a decode call has only this step)
+  uint4 first = make_uint4(0, 0, 0, 0);
+  if (row_w < a.S) first = *reinterpret_cast<const uint4 *>(kin + (size_t)row_w * D);
   // ---- cut keys of this (b,h): T[j] = key of thr16(l_j, l_{j+1}) for distinct
   // neighbours; a duplicate level takes the cut above it (empty cell); the
   // last cut is above every finite key
@@ -607,8 +594,6 @@ __global__ __launch_bounds__(256) void nuq_key_quant(NuqArgs a) {
     for (int j = 0; j < L - 1; ++j) cutp[p][j] = u16x2v{cut_s[c * 16 + j], cut_s[(c + 1) * 16 + j]};
     taup[p] = u16x2v{tau_s[c], tau_s[c + 1]};
   }
-  const int row_w = (blockIdx.x * 4 + wv) * (RPW * KQ_NIT) + lane / CL;  // first row of this lane
-  const uint16_t *kin = a.keys + (size_t)bh * a.S * D + ck * 8;
   uint8_t *kout = a.k_codes + (size_t)bh * a.S * (D * BITS / 8);
   uint32_t omask[KQ_NIT];  // bit e: channel ck*8+e of step it is an outlier
   const u16x2v one = {1, 1};
@@ -617,8 +602,11 @@ __global__ __launch_bounds__(256) void nuq_key_quant(NuqArgs a) {
     const int row = row_w + it * RPW;
     const bool valid = row < a.S;
     const bool sink = row < a.n_sink_eff;
-    uint4 in = make_uint4(0, 0, 0, 0);
-    if (valid) in = *reinterpret_cast<const uint4 *>(kin + (size_t)row * D);
+    uint4 in = first;
+    if (it > 0) {
+      in = make_uint4(0, 0, 0, 0);
+      if (valid) in = *reinterpret_cast<const uint4 *>(kin + (size_t)row * D);
+    }
     const uint32_t wd[4] = {in.x, in.y, in.z, in.w};
     uint32_t codes = 0, om = 0;
     uint32_t rec[4];
