@@ -319,31 +319,55 @@ __device__ void fit_vector(const Chunk &c, int nq, float frac, int iters, float 
   } else {
     // all L ranks in one bitwise search over the 16-bit key line: after the
     // step for bit s, pos[j] is the largest prefix with #{inliers with key <
-    // pos[j]} <= r_j
-    int pos[L];
+    // pos[j]} <= r_j. Each lane keeps, per rank, the window [wa, wb] of its
+    // chunk that holds the count of any remaining candidate (wa = count of
+    // inliers <= pos - 1, wb = count <= pos + s - 1), so each step searches
+    // only inside the window, which shrinks with the key range.
+    int pos[L], wa[L], wb[L];
 #pragma unroll
-    for (int j = 0; j < L; ++j) pos[j] = 0;
+    for (int j = 0; j < L; ++j) { pos[j] = 0; wa[j] = lo; wb[j] = hi; }
 #pragma unroll 1
     for (int sbit = 32768; sbit >= 1; sbit >>= 1) {
-      int cnt[L];
+      int sa[L], sb[L];
+      uint32_t cd[L];
 #pragma unroll
       for (int j = 0; j < L; ++j) {
-        const int cand = pos[j] + sbit - 1;
-        cnt[j] = cand > 0xfbff ? 0 : min(max(c.upper((uint32_t)cand), lo), hi) - lo;
+        cd[j] = (uint32_t)(pos[j] + sbit - 1);
+        sa[j] = wa[j];
+        sb[j] = cd[j] > 0xfbffu ? wa[j] : wb[j];  // beyond the finite keys: no advance, nothing to search
+      }
+      for (;;) {  // binary searches inside the windows (no cross-lane operations)
+        bool act = false;
+#pragma unroll
+        for (int j = 0; j < L; ++j) act |= sa[j] < sb[j];
+        if (!act) break;
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+          const int m = (sa[j] + sb[j]) >> 1;
+          const bool le = c.at(m) <= cd[j];
+          const bool on = sa[j] < sb[j];
+          sa[j] = on && le ? m + 1 : sa[j];
+          sb[j] = on && !le ? m : sb[j];
+        }
       }
 #pragma unroll
       for (int j = 0; j < L; ++j) {
-        const int cand = pos[j] + sbit - 1;
-        const int tot = gsum<CPC>(cnt[j]);
-        if (cand <= 0xfbff && tot <= rk[j]) pos[j] += sbit;
+        const int tot = gsum<CPC>(sa[j] - lo);
+        if (cd[j] <= 0xfbffu && tot <= rk[j]) {
+          pos[j] += sbit;
+          wa[j] = sa[j];
+        } else {
+          wb[j] = cd[j] > 0xfbffu ? wb[j] : sa[j];
+        }
       }
     }
 #pragma unroll
     for (int j = 0; j < L; ++j) {
       kr[j] = (uint32_t)pos[j];
       // successor: the same key while more than r_j + 1 inliers are <= it,
-      // else the smallest inlier key above it
-      const int idx = min(max(c.upper(kr[j]), lo), hi);
+      // else the smallest inlier key above it; wb[j] is now the count of
+      // this lane's inliers <= kr[j]
+      const int idx = wb[j];
       const int le = gsum<CPC>(idx - lo);
       const uint32_t nx = gmin<CPC>(idx < hi ? c.at(idx) : 0xffffu);
       ks[j] = le > rk[j] + 1 ? kr[j] : nx;
@@ -535,7 +559,7 @@ __global__ __launch_bounds__(256) void nuq_key_fit(NuqArgs a) {
 // and written in flat order once the workgroup has reserved its staging range.
 constexpr int KQ_NIT = 8;
 template <int BITS>
-__global__ __launch_bounds__(256) void nuq_key_quant(NuqArgs a) {
+__device__ __forceinline__ void key_quant_body(const NuqArgs &a, int bx, int bh, int64_t blk) {
   constexpr int L = 1 << BITS;
   __shared__ uint16_t cut_s[256 * 16];  // [channel][j]: cut key between levels j and j+1
   __shared__ uint16_t tau_s[256];
@@ -546,10 +570,9 @@ __global__ __launch_bounds__(256) void nuq_key_quant(NuqArgs a) {
   const int CL = D / 8;                 // lanes per token row
   const int RPW = 64 / CL;              // rows per wave step
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int bh = blockIdx.y;
   const int ck = lane % CL;
   const bool want_rec = a.k_recon != nullptr;
-  const int row_w = (blockIdx.x * 4 + wv) * (RPW * KQ_NIT) + lane / CL;  // first row of this lane
+  const int row_w = (bx * 4 + wv) * (RPW * KQ_NIT) + lane / CL;  // first row of this lane
   const uint16_t *kin = a.keys + (size_t)bh * a.S * D + ck * 8;
   // the first row step's load is issued before the table set-up so that its
   // latency overlaps it (a decode call has only this step)
@@ -690,7 +713,6 @@ __global__ __launch_bounds__(256) void nuq_key_quant(NuqArgs a) {
     if (i < wv) before += wave_cnt[i];
     btot += wave_cnt[i];
   }
-  const int64_t blk = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
   if (threadIdx.x == 0) {
     const uint32_t base = btot ? atomicAdd(&a.ws_ctr[0], (uint32_t)btot) : 0u;
     if (btot) atomicAdd(&a.ws_ksup[blk >> 6], (uint32_t)btot);
@@ -718,6 +740,11 @@ __global__ __launch_bounds__(256) void nuq_key_quant(NuqArgs a) {
         }
     }
   }
+}
+
+template <int BITS>
+__global__ __launch_bounds__(256) void nuq_key_quant(NuqArgs a) {
+  key_quant_body<BITS>(a, blockIdx.x, blockIdx.y, (int64_t)blockIdx.y * gridDim.x + blockIdx.x);
 }
 
 // Value fit + quantize: one token per lane group of CPC lanes (128 channels
@@ -925,29 +952,34 @@ __device__ __forceinline__ void bsort(uint32_t (&v)[R], int lane) {
     bsort<R, 2 * K>(v, lane);
   }
 }
+// one token per wave; every wave of the workgroup runs the body (inactive
+// waves too: the body's barriers are workgroup-wide), cb / base_s are the
+// wave's own LDS
 template <int E, int BITS>
-__global__ __launch_bounds__(64) void nuq_value_wave(NuqArgs a) {
+__device__ __forceinline__ void value_wave_body(const NuqArgs &a, int64_t tok, bool active, uint8_t *cb,
+                                                uint32_t *base_s) {
   constexpr int L = 1 << BITS;
   constexpr int R = E == 4 ? 2 : 1;  // packed sort registers per lane
-  __shared__ uint8_t cb[256];        // one code per channel
-  __shared__ uint32_t base_s;
-  const int lane = threadIdx.x;
-  const int64_t tok = blockIdx.x;  // flat token bh*S + s
-  const bool sink = (int)(tok % a.S) < a.n_sink_eff;
+  const int lane = threadIdx.x & 63;
+  const bool sink = !active || (int)(tok % a.S) < a.n_sink_eff;
   const int D = a.D;
   const uint16_t *row = a.values + (size_t)tok * D;
   uint32_t x[E];
   bool ok[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) ok[e] = lane * E + e < D;
-  if constexpr (E == 1) {
-    x[0] = ok[0] ? row[lane] : 0u;
-  } else if constexpr (E == 2) {
-    const uint32_t w = *reinterpret_cast<const uint32_t *>(row + 2 * lane);
-    x[0] = w & 0xffffu; x[1] = w >> 16;
-  } else {
-    const uint2 w = *reinterpret_cast<const uint2 *>(row + 4 * lane);
-    x[0] = w.x & 0xffffu; x[1] = w.x >> 16; x[2] = w.y & 0xffffu; x[3] = w.y >> 16;
+  for (int e = 0; e < E; ++e) ok[e] = active && lane * E + e < D;
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = 0;
+  if (active) {
+    if constexpr (E == 1) {
+      x[0] = ok[0] ? row[lane] : 0u;
+    } else if constexpr (E == 2) {
+      const uint32_t w = *reinterpret_cast<const uint32_t *>(row + 2 * lane);
+      x[0] = w & 0xffffu; x[1] = w >> 16;
+    } else {
+      const uint2 w = *reinterpret_cast<const uint2 *>(row + 4 * lane);
+      x[0] = w.x & 0xffffu; x[1] = w.x >> 16; x[2] = w.y & 0xffffu; x[3] = w.y >> 16;
+    }
   }
   uint32_t ky[E];
 #pragma unroll
@@ -1084,10 +1116,10 @@ __global__ __launch_bounds__(64) void nuq_value_wave(NuqArgs a) {
         a.v_recon[(size_t)tok * D + lane * E + e] =
             (sink || out[e]) ? (uint16_t)x[e] : f2h(pick<L>(lev, (int)code[e]));
   }
-  if (lane < L) a.value_levels[(size_t)tok * L + lane] = sink ? 0.0f : pick<L>(lev, lane);
+  if (active && lane < L) a.value_levels[(size_t)tok * L + lane] = sink ? 0.0f : pick<L>(lev, lane);
   __syncthreads();
   // codes LSB-first along D: lane w builds dword w of the row
-  if (lane < D * BITS / 32) {
+  if (active && lane < D * BITS / 32) {
     const int bit0 = 32 * lane;
     uint32_t acc = 0;
     for (int c = bit0 / BITS; c * BITS < bit0 + 32; ++c) {
@@ -1098,12 +1130,12 @@ __global__ __launch_bounds__(64) void nuq_value_wave(NuqArgs a) {
   }
   // ---- side channel: flat order is (lane, e)
   const int nout = wave_count<E>(out);
-  if (lane == 0) {
+  if (active && lane == 0) {
     const uint32_t base = nout ? atomicAdd(&a.ws_ctr[1], (uint32_t)nout) : 0u;
-    if (nout) atomicAdd(&a.ws_vsup[blockIdx.x >> 6], (uint32_t)nout);
-    base_s = base;
-    a.ws_vblk[blockIdx.x * 2] = base;
-    a.ws_vblk[blockIdx.x * 2 + 1] = (uint32_t)nout;
+    if (nout) atomicAdd(&a.ws_vsup[tok >> 6], (uint32_t)nout);
+    *base_s = base;
+    a.ws_vblk[tok * 2] = base;
+    a.ws_vblk[tok * 2 + 1] = (uint32_t)nout;
   }
   __syncthreads();
   int nb = 0;
@@ -1112,7 +1144,7 @@ __global__ __launch_bounds__(64) void nuq_value_wave(NuqArgs a) {
     const uint64_t b = __ballot(out[e]);
     nb += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
   }
-  int slot = (int)base_s + nb;
+  int slot = (int)*base_s + nb;
 #pragma unroll
   for (int e = 0; e < E; ++e)
     if (out[e]) {
@@ -1120,6 +1152,81 @@ __global__ __launch_bounds__(64) void nuq_value_wave(NuqArgs a) {
       a.ws_vval[slot] = (uint16_t)x[e];
       ++slot;
     }
+}
+
+template <int E, int BITS>
+__global__ __launch_bounds__(64) void nuq_value_wave(NuqArgs a) {
+  __shared__ uint8_t cb[256];  // one code per channel
+  __shared__ uint32_t base_s;
+  value_wave_body<E, BITS>(a, blockIdx.x, true, cb, &base_s);
+}
+
+// Both side-channel lists placed by one workgroup: exclusive scans of the
+// producer counts in producer order, then each thread copies its producer's
+// staged entries.
+__device__ void place_all(const NuqArgs &a, int64_t kn, int64_t vn) {
+  __shared__ uint32_t wsum[4];
+  for (int side = 0; side < 2; ++side) {
+    const int64_t nblk = side ? vn : kn;
+    const uint32_t *info = side ? a.ws_vblk : a.ws_kblk;
+    const int32_t *spos = side ? a.ws_vpos : a.ws_kpos;
+    const uint16_t *sval = side ? a.ws_vval : a.ws_kval;
+    int32_t *opos = side ? a.v_opos : a.k_opos;
+    uint16_t *oval = side ? a.v_oval : a.k_oval;
+    uint32_t running = 0;
+    for (int64_t b0 = 0; b0 < nblk; b0 += 256) {
+      const int64_t b = b0 + threadIdx.x;
+      const uint32_t cnt = b < nblk ? info[2 * b + 1] : 0u;
+      int wtot;
+      const int ex = wave_excl((int)cnt, wtot);
+      if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = (uint32_t)wtot;
+      __syncthreads();
+      uint32_t before = 0, all = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        if (w < (int)(threadIdx.x >> 6)) before += wsum[w];
+        all += wsum[w];
+      }
+      if (b < nblk) {
+        const uint32_t off = running + before + (uint32_t)ex, base = info[2 * b];
+        for (uint32_t i = 0; i < cnt; ++i) {
+          opos[off + i] = spos[base + i];
+          oval[off + i] = sval[base + i];
+        }
+      }
+      running += all;
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) a.out_counts[side] = (int64_t)running;
+  }
+}
+
+// Small calls: key quantization, the value fits (one token per wave, four
+// per workgroup) and the placement of both side-channel lists in one
+// launch. Workgroups [0, kn) quantize keys, the rest fit values; each
+// workgroup publishes its writes (device-scope fence) and counts itself
+// done, and the one that finishes last places the lists. Nothing waits.
+template <int E, int BITS>
+__global__ __launch_bounds__(256) void nuq_small(NuqArgs a, int64_t kn, int64_t ntok) {
+  __shared__ uint8_t cbs[4][256];
+  __shared__ uint32_t bases[4];
+  __shared__ int last;
+  const int64_t b = blockIdx.x;
+  if (b < kn) {
+    key_quant_body<BITS>(a, (int)(b % a.k_blk_x), (int)(b / a.k_blk_x), b);
+  } else {
+    const int wv = threadIdx.x >> 6;
+    const int64_t tok = (b - kn) * 4 + wv;
+    value_wave_body<E, BITS>(a, tok < ntok ? tok : 0, tok < ntok, cbs[wv], &bases[wv]);
+  }
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) last = atomicAdd(&a.ws_ctr[2], 1u) == gridDim.x - 1;
+  __syncthreads();
+  if (last) {
+    __threadfence();
+    place_all(a, kn, ntok);
+  }
 }
 
 // Place the staged side-channel entries in flat order, keys and values in one
@@ -1227,6 +1334,19 @@ hipError_t launch_bits(const NuqArgs &a, int key_cpc, int val_cpc, hipStream_t s
   hipError_t e;
   hipLaunchKernelGGL(nuq_zero, dim3(1), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t ntok = (int64_t)a.BH * a.S;
+  if (val_cpc == 0 && ntok <= 256) {  // decode-sized: one launch for key quant, values and placement
+    if (a.fit_keys && (e = launch_key_fit<L>(a, key_cpc, st)) != hipSuccess) return e;
+    const int64_t kn = a.k_blk_x * (int64_t)a.BH;
+    const dim3 grid((unsigned)(kn + (ntok + 3) / 4));
+    if (a.D <= 64)
+      hipLaunchKernelGGL((nuq_small<1, BITS>), grid, dim3(256), 0, st, a, kn, ntok);
+    else if (a.D == 128)
+      hipLaunchKernelGGL((nuq_small<2, BITS>), grid, dim3(256), 0, st, a, kn, ntok);
+    else
+      hipLaunchKernelGGL((nuq_small<4, BITS>), grid, dim3(256), 0, st, a, kn, ntok);
+    return hipGetLastError();
+  }
   if (val_cpc == 0) {  // few tokens: short kernels, where a cross-stream join costs more than it hides
     if (a.fit_keys && (e = launch_key_fit<L>(a, key_cpc, st)) != hipSuccess) return e;
     hipLaunchKernelGGL((nuq_key_quant<BITS>), dim3((unsigned)a.k_blk_x, a.BH), dim3(256), 0, st, a);
