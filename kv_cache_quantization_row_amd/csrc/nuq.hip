@@ -901,7 +901,10 @@ template <int L>
 __device__ __forceinline__ float pick(const float (&v)[L], int i) {  // v[i] for a lane-varying i
   float r = v[0];
 #pragma unroll
-  for (int j = 1; j < L; ++j) r = i == j ? v[j] : r;
+  for (int j = 1; j < L; ++j) {
+    r = i == j ? v[j] : r;
+    asm volatile("" : "+v"(r));  // keep the select chain in registers (no indexed scratch table)
+  }
   return r;
 }
 template <int J>
@@ -1041,7 +1044,10 @@ __device__ __forceinline__ void value_wave_body(const NuqArgs &a, int64_t tok, b
       const int i = c - 1, sl = i >> 6;
       double w = ps[0];
 #pragma unroll
-      for (int t = 1; t < 2 * R; ++t) w = sl == t ? ps[t] : w;
+      for (int t = 1; t < 2 * R; ++t) {
+        w = sl == t ? ps[t] : w;
+        asm volatile("" : "+v"(w));
+      }
       const uint64_t b = __builtin_bit_cast(uint64_t, w);
       const uint32_t l32 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, i & 63);
       const uint32_t h32 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), i & 63);
