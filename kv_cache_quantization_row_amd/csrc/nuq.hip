@@ -488,10 +488,14 @@ __global__ __launch_bounds__(256) void nuq_zero(NuqArgs a) {
 // CPC*128 tokens x 256/CPC channels is read with coalesced dword loads (two
 // channels of one token each), transposed into the lanes' chunks through
 // LDS, then every lane sorts its chunk in registers and stores it back.
+#ifndef KVQ_NUQ_KF_T
+#define KVQ_NUQ_KF_T 256  // lanes per key-fit workgroup (64 KiB of LDS at 256)
+#endif
+constexpr int KF_T = KVQ_NUQ_KF_T;
 template <int CPC, int L>
-__global__ __launch_bounds__(256) void nuq_key_fit(NuqArgs a) {
+__global__ __launch_bounds__(KF_T) void nuq_key_fit(NuqArgs a) {
   extern __shared__ uint32_t lds[];
-  constexpr int CHANS = 256 / CPC, NP = CHANS / 2;  // channels, channel pairs
+  constexpr int CHANS = KF_T / CPC, NP = CHANS / 2;  // channels, channel pairs
   const int lane = threadIdx.x;
   const int bh = blockIdx.y;
   const int g = lane / CPC, q = lane % CPC;
@@ -506,7 +510,7 @@ __global__ __launch_bounds__(256) void nuq_key_fit(NuqArgs a) {
   {
     const uint16_t *base = a.keys + (size_t)bh * a.S * a.D;
 #pragma unroll 8
-    for (int u = lane; u < 64 * CPC * NP; u += 256) {
+    for (int u = lane; u < 64 * CPC * NP; u += KF_T) {
       const int pp = u % NP, rp = u / NP;  // channel pair, token pair
       const int c = 2 * pp, r = 2 * rp;
       uint32_t x0 = 0x7c007c00u, x1 = 0x7c007c00u;  // +inf padding sorts last
@@ -1273,9 +1277,9 @@ __global__ __launch_bounds__(256) void nuq_place(NuqArgs a, int64_t kn) {
 namespace {
 template <int CPC, int L>
 hipError_t launch_key_fit_cpc(const NuqArgs &a, hipStream_t st) {
-  const int chans = 256 / CPC;
+  const int chans = KF_T / CPC;
   dim3 grid((a.D + chans - 1) / chans, a.BH);
-  hipLaunchKernelGGL((nuq_key_fit<CPC, L>), grid, dim3(256), 256 * 64 * 4, st, a);
+  hipLaunchKernelGGL((nuq_key_fit<CPC, L>), grid, dim3(KF_T), KF_T * 64 * 4, st, a);
   return hipGetLastError();
 }
 template <int L>

@@ -287,7 +287,7 @@ __global__ __launch_bounds__(256) void sym_quant_fast(SymQuantArgs a) {
 // 256-thread workgroup 256/L8 rows. Each lane packs 8 codes into BITS bytes;
 // for q6 the odd lane hands its 6 bytes to the even lane (DPP), which stores
 // 12 bytes.
-template <int BITS, int L8>
+template <int BITS, int L8, int U>
 __global__ __launch_bounds__(256) void sym_quant_v8(SymQuantArgs a) {
   constexpr int D = L8 * 8, RPW = 64 / L8, PD = D * BITS / 8;
   const int side = blockIdx.z;
@@ -300,64 +300,75 @@ __global__ __launch_bounds__(256) void sym_quant_v8(SymQuantArgs a) {
   const int lane = threadIdx.x & 63;
   const uint32_t wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   const int sub = lane / L8, li = lane % L8;
-  const uint32_t row = wave * RPW + sub;
   const uint16_t *xl = x + (size_t)layer * rows * D;
-  uint4 in = make_uint4(0, 0, 0, 0);
-  int64_t slot = -1;
-  if (row < rows) {
-    in = ld_stream(reinterpret_cast<const uint4 *>(xl + (size_t)row * D + li * 8));
-    slot = a.slot_mapping[a.h_shift >= 0 ? (row >> a.h_shift) : row / a.H];
-  }
-  const uint32_t w[4] = {in.x, in.y, in.z, in.w};
-  uint32_t amax = absmax_bits(w, 4);
-  amax = group_max_u32<L8>(amax);
-  uint16_t s16;
-  float r;
-  row_scale<BITS>(amax, s16, r);
-  uint32_t m[8];
-  if (__any(s16 != 0 && s16 < 0x0400u)) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      m[2 * i] = enc_raw<BITS, true>((uint16_t)(w[i] & 0xffffu), r);
-      m[2 * i + 1] = enc_raw<BITS, true>((uint16_t)(w[i] >> 16), r);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      m[2 * i] = enc_raw<BITS, false>((uint16_t)(w[i] & 0xffffu), r);
-      m[2 * i + 1] = enc_raw<BITS, false>((uint16_t)(w[i] >> 16), r);
-    }
-  }
-  constexpr uint32_t K = 0x4b400000u;
   uint8_t *cl = codes + (size_t)(a.layer0 + layer) * a.code_layer_stride;
-  const bool ok = row < rows && slot >= 0 && slot < a.n_slots;
-  const size_t orow = ok ? (size_t)slot * a.H + (row - (a.h_shift >= 0 ? (row >> a.h_shift) : row / a.H) * a.H) : 0;
-  if constexpr (BITS == 8) {
-    const uint32_t o0 = __builtin_amdgcn_perm(m[1], m[0], 0x0c0c0400u) | __builtin_amdgcn_perm(m[3], m[2], 0x04000c0cu);
-    const uint32_t o1 = __builtin_amdgcn_perm(m[5], m[4], 0x0c0c0400u) | __builtin_amdgcn_perm(m[7], m[6], 0x04000c0cu);
-    if (ok) *reinterpret_cast<uint2 *>(cl + orow * PD + li * 8) = make_uint2(o0, o1);
-  } else if constexpr (BITS == 4) {
-    constexpr uint32_t C = K + (K << 4) + (K << 8) + (K << 12) + (K << 16) + (K << 20) + (K << 24) + (K << 28);
-    uint32_t v = m[0];
+  // U consecutive row groups per wave, all loads issued first
+  uint4 in[U];
+  int64_t slot[U];
 #pragma unroll
-    for (int i = 1; i < 8; ++i) v += m[i] << (4 * i);
-    if (ok) *reinterpret_cast<uint32_t *>(cl + orow * PD + li * 4) = v - C;
-  } else {
-    constexpr uint32_t C = K + (K << 6) + (K << 12) + (K << 18);
-    const uint32_t g0 = (m[0] + (m[1] << 6) + (m[2] << 12) + (m[3] << 18)) - C;
-    const uint32_t g1 = (m[4] + (m[5] << 6) + (m[6] << 12) + (m[7] << 18)) - C;
-    // this lane's 6 bytes: g0 (24 bits) then g1 (24 bits)
-    const uint32_t lo = g0 | (g1 << 24), hi = g1 >> 8;  // 48 bits
-    // the odd neighbour's 48 bits, moved to the even lane (quad_perm [1,1,3,3])
-    const uint32_t nlo = dpp<0xf5>(lo), nhi = dpp<0xf5>(hi);
-    if (ok && (li & 1) == 0) {
-      uint32_t *dst = reinterpret_cast<uint32_t *>(cl + orow * PD + li * 6);
-      dst[0] = lo;
-      dst[1] = hi | (nlo << 16);
-      dst[2] = (nlo >> 16) | (nhi << 16);
+  for (int u = 0; u < U; ++u) {
+    const uint32_t row = (wave * U + u) * RPW + sub;
+    in[u] = make_uint4(0, 0, 0, 0);
+    slot[u] = -1;
+    if (row < rows) {
+      in[u] = ld_stream(reinterpret_cast<const uint4 *>(xl + (size_t)row * D + li * 8));
+      slot[u] = a.slot_mapping[a.h_shift >= 0 ? (row >> a.h_shift) : row / a.H];
     }
   }
-  if (ok && li == 0) scales[(size_t)(a.layer0 + layer) * a.scale_layer_stride + orow] = s16;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t row = (wave * U + u) * RPW + sub;
+    const uint32_t w[4] = {in[u].x, in[u].y, in[u].z, in[u].w};
+    uint32_t amax = absmax_bits(w, 4);
+    amax = group_max_u32<L8>(amax);
+    uint16_t s16;
+    float r;
+    row_scale<BITS>(amax, s16, r);
+    uint32_t m[8];
+    if (__any(s16 != 0 && s16 < 0x0400u)) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        m[2 * i] = enc_raw<BITS, true>((uint16_t)(w[i] & 0xffffu), r);
+        m[2 * i + 1] = enc_raw<BITS, true>((uint16_t)(w[i] >> 16), r);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        m[2 * i] = enc_raw<BITS, false>((uint16_t)(w[i] & 0xffffu), r);
+        m[2 * i + 1] = enc_raw<BITS, false>((uint16_t)(w[i] >> 16), r);
+      }
+    }
+    constexpr uint32_t K = 0x4b400000u;
+    const bool ok = row < rows && slot[u] >= 0 && slot[u] < a.n_slots;
+    const size_t orow =
+        ok ? (size_t)slot[u] * a.H + (row - (a.h_shift >= 0 ? (row >> a.h_shift) : row / a.H) * a.H) : 0;
+    if constexpr (BITS == 8) {
+      const uint32_t o0 = __builtin_amdgcn_perm(m[1], m[0], 0x0c0c0400u) | __builtin_amdgcn_perm(m[3], m[2], 0x04000c0cu);
+      const uint32_t o1 = __builtin_amdgcn_perm(m[5], m[4], 0x0c0c0400u) | __builtin_amdgcn_perm(m[7], m[6], 0x04000c0cu);
+      if (ok) *reinterpret_cast<uint2 *>(cl + orow * PD + li * 8) = make_uint2(o0, o1);
+    } else if constexpr (BITS == 4) {
+      constexpr uint32_t C = K + (K << 4) + (K << 8) + (K << 12) + (K << 16) + (K << 20) + (K << 24) + (K << 28);
+      uint32_t v = m[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) v += m[i] << (4 * i);
+      if (ok) *reinterpret_cast<uint32_t *>(cl + orow * PD + li * 4) = v - C;
+    } else {
+      constexpr uint32_t C = K + (K << 6) + (K << 12) + (K << 18);
+      const uint32_t g0 = (m[0] + (m[1] << 6) + (m[2] << 12) + (m[3] << 18)) - C;
+      const uint32_t g1 = (m[4] + (m[5] << 6) + (m[6] << 12) + (m[7] << 18)) - C;
+      // this lane's 6 bytes: g0 (24 bits) then g1 (24 bits)
+      const uint32_t lo = g0 | (g1 << 24), hi = g1 >> 8;  // 48 bits
+      // the odd neighbour's 48 bits, moved to the even lane (quad_perm [1,1,3,3])
+      const uint32_t nlo = dpp<0xf5>(lo), nhi = dpp<0xf5>(hi);
+      if (ok && (li & 1) == 0) {
+        uint32_t *dst = reinterpret_cast<uint32_t *>(cl + orow * PD + li * 6);
+        dst[0] = lo;
+        dst[1] = hi | (nlo << 16);
+        dst[2] = (nlo >> 16) | (nhi << 16);
+      }
+    }
+    if (ok && li == 0) scales[(size_t)(a.layer0 + layer) * a.scale_layer_stride + orow] = s16;
+  }
 }
 
 // Generic write path: one wave per row, any head_dim valid for the width.
@@ -607,10 +618,12 @@ hipError_t launch_quant_u(const SymQuantArgs &a, int n_layers, hipStream_t st) {
 #endif
 template <int BITS, int L8>
 hipError_t launch_quant_v8(const SymQuantArgs &a, int n_layers, hipStream_t st) {
-  constexpr int RPW = 64 / L8;
-  const uint32_t per_block = RPW * 4;
+  // row groups per wave: two loads in flight per lane help q6/q4 (+1.5..3%
+  // measured), q8 is faster with one
+  constexpr int RPW = 64 / L8, U = BITS == 8 ? 1 : 2;
+  const uint32_t per_block = RPW * 4 * U;
   dim3 grid((a.rows_per_layer + per_block - 1) / per_block, n_layers, 2);
-  hipLaunchKernelGGL((sym_quant_v8<BITS, L8>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((sym_quant_v8<BITS, L8, U>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 template <int BITS, int LPR>
