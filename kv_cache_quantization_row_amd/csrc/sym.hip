@@ -29,7 +29,10 @@
 #define KVQ_SYM_QUANT_WPB 4  // waves per workgroup in the write path
 #endif
 #ifndef KVQ_SYM_DEQ_PPB
-#define KVQ_SYM_DEQ_PPB 16  // positions per workgroup in the read path (divides page_size)
+#define KVQ_SYM_DEQ_PPB 16  // most positions per workgroup in the read path (divides page_size)
+#endif
+#ifndef KVQ_SYM_DEQ_UNIT_BYTES
+#define KVQ_SYM_DEQ_UNIT_BYTES 6144  // code bytes staged per read-path workgroup, at most
 #endif
 #ifndef KVQ_NT_LOAD
 #define KVQ_NT_LOAD 0  // 1: non-temporal hint on the streaming fp16 loads (write path)
@@ -668,9 +671,17 @@ hipError_t launch_quant_bits(const SymQuantArgs &a, int n_layers, hipStream_t st
 // tuning target whose codes are whole 16-byte units
 template <int BITS>
 int pick_ppb(const SymDequantArgs &a) {
-  for (int q = min(KVQ_SYM_DEQ_PPB, a.page_size); q >= 1; --q)
-    if (a.page_size % q == 0 && ((int64_t)q * a.H * a.D * BITS / 8) % 16 == 0) return q;
-  return 0;
+  // the largest unit (positions dividing the page) whose codes stay within
+  // KVQ_SYM_DEQ_UNIT_BYTES: 4-6 KiB of staged codes per workgroup measured
+  // best (q8 at D=256: 4 positions, q6 / q4: 8); else the smallest valid unit
+  int fallback = 0;
+  for (int q = min(KVQ_SYM_DEQ_PPB, a.page_size); q >= 1; --q) {
+    const int64_t bytes = (int64_t)q * a.H * a.D * BITS / 8;
+    if (a.page_size % q != 0 || bytes % 16 != 0) continue;
+    if (bytes <= KVQ_SYM_DEQ_UNIT_BYTES) return q;
+    fallback = q;
+  }
+  return fallback;
 }
 
 template <int BITS, int D>
