@@ -621,12 +621,13 @@ hipError_t launch_quant_u(const SymQuantArgs &a, int n_layers, hipStream_t st) {
 #endif
 template <int BITS, int L8>
 hipError_t launch_quant_v8(const SymQuantArgs &a, int n_layers, hipStream_t st) {
-  // row groups per wave: two loads in flight per lane help q6/q4 (+1.5..3%
-  // measured), q8 is faster with one
-  constexpr int RPW = 64 / L8, U = BITS == 8 ? 1 : 2;
-  const uint32_t per_block = RPW * 4 * U;
+  // measured on the paged prefill: q6/q4 run best with two row groups per
+  // wave and two waves per workgroup (+4% over one group and four waves),
+  // q8 with one row group and four waves
+  constexpr int RPW = 64 / L8, U = BITS == 8 ? 1 : 2, WPB = BITS == 8 ? 4 : 2;
+  const uint32_t per_block = RPW * WPB * U;
   dim3 grid((a.rows_per_layer + per_block - 1) / per_block, n_layers, 2);
-  hipLaunchKernelGGL((sym_quant_v8<BITS, L8, U>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((sym_quant_v8<BITS, L8, U>), grid, dim3(64 * WPB), 0, st, a);
   return hipGetLastError();
 }
 template <int BITS, int LPR>
