@@ -397,16 +397,28 @@ __global__ __launch_bounds__(256) void kivi_values_generic(KiviArgs a) {
 
 // ------------------------------------------------------------------ launch
 namespace {
+// workgroup shapes measured on B=128 x 8 heads x 8064 tokens x D=64:
+// keys 2 waves (key groups) per workgroup, values 1 wave with one row
+// group (+4% keys, +10% values over 4 waves / 2 row groups)
+#ifndef KVQ_KIVI_KWPB
+#define KVQ_KIVI_KWPB 2  // waves (key groups) per workgroup
+#endif
+#ifndef KVQ_KIVI_VWPB
+#define KVQ_KIVI_VWPB 1  // waves per workgroup, values
+#endif
+#ifndef KVQ_KIVI_VU
+#define KVQ_KIVI_VU 1  // row groups per wave, values
+#endif
 template <int BITS, int CL>
 hipError_t keys_cl(const KiviArgs &a, int ng, hipStream_t st) {
-  constexpr int TPI = 64 / CL;
-  const dim3 grid((unsigned)((ng + 3) / 4), (unsigned)a.BH);
+  constexpr int TPI = 64 / CL, W = KVQ_KIVI_KWPB;
+  const dim3 grid((unsigned)((ng + W - 1) / W), (unsigned)a.BH), blk(64 * W);
   switch (a.gs / TPI) {  // loads per lane; fast path only when gs % TPI == 0
-    case 1: hipLaunchKernelGGL((kivi_keys_fast<BITS, CL, 1>), grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((kivi_keys_fast<BITS, CL, 2>), grid, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((kivi_keys_fast<BITS, CL, 4>), grid, dim3(256), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((kivi_keys_fast<BITS, CL, 8>), grid, dim3(256), 0, st, a); break;
-    case 16: hipLaunchKernelGGL((kivi_keys_fast<BITS, CL, 16>), grid, dim3(256), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((kivi_keys_fast<BITS, CL, 1>), grid, blk, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((kivi_keys_fast<BITS, CL, 2>), grid, blk, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((kivi_keys_fast<BITS, CL, 4>), grid, blk, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((kivi_keys_fast<BITS, CL, 8>), grid, blk, 0, st, a); break;
+    case 16: hipLaunchKernelGGL((kivi_keys_fast<BITS, CL, 16>), grid, blk, 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -448,10 +460,10 @@ hipError_t launch_keys(const KiviArgs &a, hipStream_t st) {
 
 template <int BITS, int CL, int LPG>
 hipError_t values_cfg(const KiviArgs &a, hipStream_t st) {
-  constexpr int U = 2, RPW = 64 / CL;
+  constexpr int U = KVQ_KIVI_VU, RPW = 64 / CL, W = KVQ_KIVI_VWPB;
   const int64_t waves = ((a.hi - a.lo) + RPW * U - 1) / (RPW * U);  // per (b, h)
-  hipLaunchKernelGGL((kivi_values_fast<BITS, CL, LPG, U>), dim3((unsigned)((waves + 3) / 4), (unsigned)a.BH),
-                     dim3(256), 0, st, a);
+  hipLaunchKernelGGL((kivi_values_fast<BITS, CL, LPG, U>), dim3((unsigned)((waves + W - 1) / W), (unsigned)a.BH),
+                     dim3(64 * W), 0, st, a);
   return hipGetLastError();
 }
 
