@@ -107,6 +107,93 @@ def test_paged_ragged_multilayer(bits, H, D):
     _check_roundtrip(xk, xv, bits, H, D, P, num_pages, 4, 1, slot, bt, lens, 350)
 
 
+@pytest.mark.parametrize("bits", [8, 6, 4])
+@pytest.mark.parametrize("H,D", [(4, 256), (8, 128), (2, 64), (3, 256), (1, 16), (2, 512)])
+def test_paged_large_write(bits, H, D):
+    """More than 16384 (layer, token, head) rows per call: the write path that
+    large prefill chunks take (8 channels per lane), with scattered pages,
+    ragged sequences, skipped slots and a ragged tail of rows."""
+    say("sym paged large", bits, H, D)
+    rng = np.random.default_rng(bits * 7000 + H * 10 + D)
+    P = 16
+    lens = np.array([1, 17, 333, 95, 4100 // H + 7, 2900 // H], np.int32)
+    blocks = (lens + P - 1) // P
+    num_pages = int(blocks.sum()) + 3
+    perm = rng.permutation(num_pages)
+    max_blocks = int(blocks.max()) + 1
+    bt = np.full((len(lens), max_blocks), -1, np.int32)
+    o = 0
+    for s_, b in enumerate(blocks):
+        bt[s_, :b] = perm[o:o + b]
+        o += b
+    slot = np.concatenate([bt[s_, np.arange(n) // P] * P + np.arange(n) % P for s_, n in enumerate(lens)])
+    slot = slot.astype(np.int64)
+    slot[11] = -1
+    slot[40] = num_pages * P + 1
+    T = len(slot)
+    n_layers = 3
+    assert T * H * n_layers > 16384
+    g = torch.Generator().manual_seed(int(rng.integers(1 << 30)))
+    xk = (torch.randn((n_layers, T, H, D), generator=g) * 2).half()
+    xv = torch.randn((n_layers, T, H, D), generator=g).half()
+    xk[1, 5] = 0
+    _check_roundtrip(xk, xv, bits, H, D, P, num_pages, 3, 0, slot, bt, lens, int(lens.max()) + 3)
+
+
+@pytest.mark.parametrize("bits", [8, 6, 4])
+def test_full_size_sampled(bits):
+    """The benchmark's paged workload in its launch configuration: 16 layers x
+    4 KV heads x D=256, page 16, 16 sequences x 32,768-token prefill in one
+    launch over all layers, single-token appends, a full dequant sweep.
+    Compared with the oracle on sampled layers, sequences and positions."""
+    say("sym full size", bits)
+    d = dev()
+    L, H, D, P, S, T, ND = 16, 4, 256, 16, 16, 32768, 3
+    total = T + ND
+    bt, num_pages = inputs.paged_block_table(S, total, P, seed=2002)
+    slot_pf = inputs.slot_mapping_for(bt, P, 0, T)
+    k = torch.empty((L, S * T, H, D), dtype=torch.float16, device=d)
+    v = torch.empty_like(k)
+    for l in range(L):
+        k[l] = inputs.sym_layer(S * T, H, D, seed=2100 + l, device=d, laplace_token_frac=0.05, channel_seed=3100 + l)
+        v[l] = inputs.sym_layer(S * T, H, D, seed=2200 + l, device=d, laplace_token_frac=0.05, channel_seed=3200 + l)
+    kd = inputs.sym_layer(ND * L * S, H, D, seed=2300, device=d, laplace_token_frac=0.05).view(ND, L, S, H, D)
+    pd = kvq.kvq_packed_dim(D, bits)
+    slots = num_pages * P
+    kc = torch.zeros((L, slots, H, pd), dtype=torch.uint8, device=d)
+    vc = torch.zeros_like(kc)
+    ks = torch.zeros((L, slots, H), dtype=torch.int16, device=d)
+    vs = torch.zeros_like(ks)
+    lay = kvq.layout(L, num_pages, P, H, D, bits)
+    kvq.kvq_quant_sym(lay, k, v, slot_pf.to(d), kc, ks, vc, vs)
+    for i in range(ND):
+        kvq.kvq_quant_sym(lay, kd[i], kd[i], inputs.slot_mapping_for(bt, P, T + i, 1).to(d), kc, ks, vc, vs)
+    ko = torch.empty((L, S, total, H, D), dtype=torch.float16, device=d)
+    vo = torch.empty_like(ko)
+    kvq.kvq_dequant_sym(lay, kc, ks, vc, vs, bt.to(d), torch.full((S,), total, dtype=torch.int32, device=d),
+                        ko, vo)
+    torch.cuda.synchronize()
+    pos = np.r_[0:40, 16000:16040, T - 40:T]
+    for l in (0, 9, 15):
+        for s_ in (0, 7, 15):
+            for name, x, cp, sp, out in (("K", k, kc, ks, ko), ("V", v, vc, vs, vo)):
+                rows = u16(x[l, torch.as_tensor(s_ * T + pos, device=d)])  # [n][H][D]
+                rc, rsc = oracle.sym_quant_rows(rows, bits)
+                sl = slot_pf[torch.as_tensor(s_ * T + pos)].to(torch.int64).to(d)
+                got_c = cp[l][sl].cpu().numpy()
+                got_s = u16(sp[l][sl])
+                what = (name, "layer", l, "seq", s_)
+                assert first_diff(got_c, rc) is None, what + ("codes", first_diff(got_c, rc))
+                assert first_diff(got_s, rsc) is None, what + ("scales", first_diff(got_s, rsc))
+                got_o = u16(out[l, s_, torch.as_tensor(pos, device=d)])
+                exp_o = oracle.sym_dequant_rows(rc, rsc, D, bits)
+                assert first_diff(got_o, exp_o) is None, what + ("dequant", first_diff(got_o, exp_o))
+            # the appended tokens (written through the small-write path) and their read-back
+            dc, dsc = oracle.sym_quant_rows(u16(kd[:, l, s_]), bits)   # [ND][H]
+            got_o = u16(ko[l, s_, T:T + ND])
+            assert first_diff(got_o, oracle.sym_dequant_rows(dc, dsc, D, bits)) is None, ("append", l, s_)
+
+
 @pytest.mark.parametrize("bits,D", [(8, 96), (6, 96), (4, 96), (6, 20), (8, 2), (4, 2), (8, 7),
                                     (6, 2048), (4, 80), (8, 200)])
 def test_generic_head_dims(bits, D):
