@@ -1,0 +1,110 @@
+"""GPU cache objects (caches.py over libkvq) against the CPU lifecycle models
+(oracle/caches.py): the same sequence of prefill, decode appends and trims
+(into the residual, into the quantized region, to empty) must leave the same
+buffers bit-for-bit, the same frontiers, frozen tables and counters.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.caches import KiviCacheModel, NuqCacheModel
+from kv_cache_quantization_row_amd import caches, inputs
+from tests.gpu_util import dev, first_diff, say, u16
+
+pytestmark = pytest.mark.gpu
+
+
+def _kivi_inputs(B, H, S, D, seed):
+    k, v = inputs.kivi_kv(B, H, S, D, seed=seed)
+    return k, v
+
+
+def _check_kivi(c, m, what):
+    assert (c.offset, c.n_quantized) == (m.offset, m.nq), what
+    gk = u16(c.keys[:, :, : c.offset])
+    gv = u16(c.values[:, :, : c.offset])
+    assert first_diff(gk, m.k) is None, (what, "keys", first_diff(gk, m.k))
+    assert first_diff(gv, m.v) is None, (what, "values", first_diff(gv, m.v))
+    assert (c.compressed_key_bytes, c.compressed_value_bytes, c.residual_fp16_bytes) == \
+        (m.key_bytes, m.value_bytes, m.residual_bytes), what
+    assert (c.fp16_key_bytes, c.fp16_value_bytes) == (m.key_fp16, m.value_fp16), what
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_kivi_cache_lifecycle(bits):
+    say("kivi cache", bits)
+    d = dev()
+    B, H, D = 2, 4, 64
+    k, v = _kivi_inputs(B, H, 900, D, 20 + bits)
+    kn, vn = k.numpy().view(np.uint16), v.numpy().view(np.uint16)
+    c, m = caches.KiviCache(bits), KiviCacheModel(bits)
+    t = 0
+
+    def push(n, what):
+        nonlocal t
+        kk, vv = c.update_and_fetch(k[:, :, t:t + n].to(d).contiguous(), v[:, :, t:t + n].to(d).contiguous())
+        assert kk.shape[2] == c.offset
+        m.update(kn[:, :, t:t + n], vn[:, :, t:t + n])
+        t += n
+        _check_kivi(c, m, what)
+
+    push(300, "prefill")
+    for i in range(40):
+        push(1, "decode %d" % i)
+    assert c.trim(37) == m.trim(37) == 37
+    _check_kivi(c, m, "trim into the residual")
+    push(20, "append")
+    assert c.trim(200) == m.trim(200) == 200
+    _check_kivi(c, m, "trim into the quantized region")
+    push(150, "re-flush")
+    for i in range(5):
+        push(1, "decode after rollback %d" % i)
+    assert c.trim(10 ** 6) == m.trim(10 ** 6)
+    assert c.offset == 0 and c.n_quantized == 0
+    push(200, "new sequence")
+    ratio = (c.fp16_key_bytes + c.fp16_value_bytes) / (c.compressed_key_bytes + c.compressed_value_bytes +
+                                                        c.residual_fp16_bytes)
+    assert c.effective_compression_ratio == pytest.approx(ratio)
+
+
+def test_nuq_cache_lifecycle():
+    say("nuq cache")
+    d = dev()
+    B, H, D, bits = 1, 4, 128, 3
+    kt = inputs.student_t((B * H, 200, D), 4, seed=31).view(B, H, 200, D)
+    vt = inputs.student_t((B * H, 200, D), 4, seed=32).view(B, H, 200, D)
+    kn, vn = u16(kt), u16(vt)
+    c, m = caches.NuqCache(bits, 0.02, 8, 4), NuqCacheModel(bits, 0.02, 8, 4)
+    t = 0
+
+    def push(n, what):
+        nonlocal t
+        c.update_and_fetch(kt[:, :, t:t + n].to(d).contiguous(), vt[:, :, t:t + n].to(d).contiguous())
+        m.update(kn[:, :, t:t + n], vn[:, :, t:t + n])
+        r = m.last
+        t += n
+        assert c.offset == m.offset, what
+        assert first_diff(u16(c.keys[:, :, : c.offset]), m.k) is None, (what, "keys")
+        assert first_diff(u16(c.values[:, :, : c.offset]), m.v) is None, (what, "values")
+        assert np.array_equal(c.key_levels.cpu().numpy().view(np.uint32), m.key_levels.view(np.uint32)), what
+        assert np.array_equal(u16(c.key_thresh), m.key_thresh), what
+        assert (c.outlier_count, c.sink_kept) == (m.outlier_count, m.sink_kept), what
+        return r
+
+    r = push(120, "prefill")
+    # the byte estimate of a prefill call: codes, the key tables (fp32 levels +
+    # fp16 threshold per channel), 6 bytes per emitted outlier, fp16 sinks
+    BH, L = B * H, 1 << bits
+    exp_k = BH * 120 * D * bits // 8 + len(r["k_out"][0]) * 6 + BH * 4 * D * 2 + BH * D * (L * 4 + 2)
+    assert c.compressed_key_bytes == exp_k
+    assert c.effective_bits == pytest.approx(16.0 * exp_k / (BH * 120 * D * 2))
+    for i in range(6):
+        push(1, "decode %d" % i)
+    assert c.trim(30) == m.trim(30) == 30
+    push(1, "decode after partial trim")
+    assert c.trim(10 ** 6) == m.trim(10 ** 6)
+    assert c.offset == 0 and c.key_levels is None and c.outlier_count == 0
+    t = 130
+    push(60, "second sequence")
+    push(1, "second sequence decode")
