@@ -2,9 +2,10 @@
 decide what to quantize when, and keep the byte accounting.
 
 Every quantization step runs in the HIP kernels (kvq_kivi_quant_dequant,
-kvq_nuq_fit_quant); this module only appends incoming tokens to the
-device-resident fp16 buffers (PyTorch memory), moves the frontiers and
-counts bytes. Tensors are fp16 [B][H][S][D] on the current HIP device.
+kvq_nuq_fit_quant, kvq_quant_sym / kvq_dequant_sym); this module only
+appends incoming tokens to device-resident buffers (PyTorch memory), moves
+frontiers, hands out pages and counts bytes. KIVI / NUQ tensors are fp16
+[B][H][S][D] on the current HIP device.
 
 KiviCache  ["veloxquant_mlx.cache.kivi_cache", class KIVIKVCache:
             update_and_fetch, _quantization_boundary, trim with
@@ -14,6 +15,10 @@ NuqCache   ["veloxquant_mlx.cache.kvquant_cache module", class
             KVQuantKVCache: update_and_fetch, trim, and the outlier_count,
             sink_kept, key_levels, compressed_*_bytes and effective_bits
             properties]
+PagedSymCache [MTPLX pull request #267, "feat(kv-cache): add q6 paged KV
+            quantization": paged q8/q6/q4 storage sized by packed_dim; the
+            page allocator, appends and trims are a reading, the page
+            describes only the storage]
 """
 from __future__ import annotations
 
@@ -264,3 +269,93 @@ class NuqCache:
     def effective_bits(self) -> float:
         """Stored key bits per key element (codes, tables, outliers, sinks)."""
         return 0.0 if self._kf == 0 else 16.0 * self._kc / self._kf
+
+
+class PagedSymCache:
+    """Paged symmetric q8/q6/q4 cache for several sequences: per (layer,
+    K/V) pools of `num_pages` pages of `page_size` token slots (the layout of
+    kvq_quant_sym / kvq_dequant_sym), a free list of pages, and per sequence
+    its page list and length. Appends take pages from the free list as a
+    sequence grows and quantize the new tokens into their slots; trims give
+    back the pages past the new length; fetch dequantizes whole sequences
+    through a block table. Page allocation is host bookkeeping; every byte
+    of the cache is written and read by the kernels."""
+
+    def __init__(self, layers, num_pages, page_size, kv_heads, head_dim, bits, device=None):
+        import torch
+
+        self.lay = kvq.layout(layers, num_pages, page_size, kv_heads, head_dim, bits)
+        self.P, self.H, self.D, self.L, self.bits = page_size, kv_heads, head_dim, layers, bits
+        pd = kvq.kvq_packed_dim(head_dim, bits)
+        if pd <= 0:
+            raise kvq.KvqError(kvq.KVQ_ERR_SHAPE, "head_dim %d is not valid for q%d" % (head_dim, bits))
+        slots = num_pages * page_size
+        dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+        self.device = dev
+        self.k_codes = torch.zeros((layers, slots, kv_heads, pd), dtype=torch.uint8, device=dev)
+        self.v_codes = torch.zeros_like(self.k_codes)
+        self.k_scales = torch.zeros((layers, slots, kv_heads), dtype=torch.int16, device=dev)
+        self.v_scales = torch.zeros_like(self.k_scales)
+        self.free = list(range(num_pages - 1, -1, -1))  # stack: page 0 is handed out first
+        self.pages = {}                                 # seq id -> [page ids]
+        self.lengths = {}                               # seq id -> tokens
+
+    def pages_in_use(self) -> int:
+        return sum(len(p) for p in self.pages.values())
+
+    def append(self, seq_ids, k, v):
+        """k, v: fp16 [layers][n_tokens][kv_heads][head_dim], the new tokens of
+        the listed sequences one after another; seq_ids: [(seq id, count)]."""
+        import torch
+
+        slots = []
+        for sid, n in seq_ids:
+            pages = self.pages.setdefault(sid, [])
+            length = self.lengths.get(sid, 0)
+            need = (length + n + self.P - 1) // self.P - len(pages)
+            if need > len(self.free):
+                raise kvq.KvqError(kvq.KVQ_ERR_CAPACITY, "page pool exhausted (%d free, %d needed)" %
+                                   (len(self.free), need))
+            for _ in range(need):
+                pages.append(self.free.pop())
+            for pos in range(length, length + n):
+                slots.append(pages[pos // self.P] * self.P + pos % self.P)
+            self.lengths[sid] = length + n
+        if len(slots) != int(k.shape[1]):
+            raise kvq.KvqError(kvq.KVQ_ERR_SHAPE, "token count does not match the sequence counts")
+        sm = torch.tensor(slots, dtype=torch.int32).to(self.device)
+        kvq.kvq_quant_sym(self.lay, k, v, sm, self.k_codes, self.k_scales, self.v_codes, self.v_scales)
+
+    def trim(self, sid, n: int) -> int:
+        length = self.lengths.get(sid, 0)
+        t = max(0, min(int(n), length))
+        self.lengths[sid] = length - t
+        keep = (length - t + self.P - 1) // self.P
+        while len(self.pages[sid]) > keep:
+            self.free.append(self.pages[sid].pop())
+        return t
+
+    def release(self, sid):
+        self.trim(sid, self.lengths.get(sid, 0))
+        self.pages.pop(sid, None)
+        self.lengths.pop(sid, None)
+
+    def fetch(self, seq_list, max_len=None):
+        """fp16 (K, V) [layers][len(seq_list)][max_len][kv_heads][head_dim];
+        positions past a sequence's length are +0."""
+        import torch
+
+        lens = [self.lengths.get(s, 0) for s in seq_list]
+        max_len = max(lens + [1]) if max_len is None else max_len
+        mb = max(1, max(len(self.pages.get(s, [])) for s in seq_list))
+        bt = torch.full((len(seq_list), mb), -1, dtype=torch.int32)
+        for i, s in enumerate(seq_list):
+            p = self.pages.get(s, [])
+            if p:
+                bt[i, : len(p)] = torch.tensor(p, dtype=torch.int32)
+        shape = (self.L, len(seq_list), max_len, self.H, self.D)
+        ko = torch.empty(shape, dtype=torch.float16, device=self.device)
+        vo = torch.empty_like(ko)
+        kvq.kvq_dequant_sym(self.lay, self.k_codes, self.k_scales, self.v_codes, self.v_scales,
+                            bt.to(self.device), torch.tensor(lens, dtype=torch.int32).to(self.device), ko, vo)
+        return ko, vo

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 from oracle.caches import KiviCacheModel, NuqCacheModel
-from kv_cache_quantization_row_amd import caches, inputs
+from kv_cache_quantization_row_amd import caches, inputs, kvq
 from tests.gpu_util import dev, first_diff, say, u16
 
 pytestmark = pytest.mark.gpu
@@ -108,3 +108,60 @@ def test_nuq_cache_lifecycle():
     t = 130
     push(60, "second sequence")
     push(1, "second sequence decode")
+
+
+@pytest.mark.parametrize("bits", [6, 8, 4])
+def test_paged_sym_cache_lifecycle(bits):
+    """Three sequences share a small page pool: batched appends, decode steps,
+    trims that free pages, a release and a reuse of the freed pages. Every
+    fetch equals the oracle's quantize -> dequantize of each sequence's rows
+    (a row's result does not depend on the slot it is stored in)."""
+    say("paged sym cache", bits)
+    d = dev()
+    Lyr, P, H, D = 2, 16, 4, 128
+    c = caches.PagedSymCache(Lyr, 40, P, H, D, bits, device=d)
+    g = torch.Generator().manual_seed(bits)
+    hist = {}
+
+    def append(pairs):
+        n = sum(k for _, k in pairs)
+        x = (torch.randn((2, Lyr, n, H, D), generator=g) * 3).half()
+        c.append(pairs, x[0].to(d), x[1].to(d))
+        o = 0
+        for sid, k in pairs:
+            hk, hv = hist.get(sid, (np.zeros((Lyr, 0, H, D), np.uint16), np.zeros((Lyr, 0, H, D), np.uint16)))
+            hist[sid] = (np.concatenate([hk, u16(x[0, :, o:o + k])], 1), np.concatenate([hv, u16(x[1, :, o:o + k])], 1))
+            o += k
+
+    def check(what):
+        sids = sorted(hist)
+        ko, vo = c.fetch(sids)
+        for i, sid in enumerate(sids):
+            n = c.lengths[sid]
+            assert hist[sid][0].shape[1] == n
+            for side, out in ((0, ko), (1, vo)):
+                rc, rs = oracle.sym_quant_rows(hist[sid][side], bits)
+                exp = oracle.sym_dequant_rows(rc, rs, D, bits)
+                assert first_diff(u16(out[:, i, :n]), exp) is None, (what, sid, side)
+                assert not u16(out[:, i, n:]).any(), (what, "tail", sid)
+        used = [p for ps in c.pages.values() for p in ps]
+        assert len(used) == len(set(used)) and not set(used) & set(c.free), what
+        assert all(len(c.pages[s]) == (c.lengths[s] + P - 1) // P for s in c.pages), what
+
+    append([(0, 100), (1, 37), (2, 1)])
+    check("prefill")
+    for step in range(20):
+        append([(0, 1), (1, 1), (2, 1)])
+    check("decode")
+    for sid, t in ((0, 50), (1, 30), (2, 21)):
+        assert c.trim(sid, t) == t
+        hist[sid] = (hist[sid][0][:, : c.lengths[sid]], hist[sid][1][:, : c.lengths[sid]])
+    check("trim")
+    free_before = len(c.free)
+    c.release(1)
+    del hist[1]
+    assert len(c.free) == free_before + 2
+    append([(3, 300), (0, 5)])
+    check("reuse")
+    with pytest.raises(kvq.KvqError):
+        append([(4, 40 * P)])
