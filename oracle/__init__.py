@@ -5,7 +5,9 @@ through ctypes. Only the test suite, the smoke check and the benchmark's
 CPU-baseline leg use it; the product library never imports it. All arrays are
 numpy, host memory, C-contiguous. fp16 data travels as uint16 bit patterns.
 
-Sources are cited per function in kvq_oracle.cpp (page title + section).
+Sources are cited per function in kvq_oracle.cpp (page title + section);
+attn_decode (decode attention over dequantized rows) is plain numpy in
+float64, and caches.py holds CPU models of the cache lifecycles.
 """
 from __future__ import annotations
 
@@ -201,6 +203,26 @@ def kivi_round_trip(x, lo, hi, per_channel, bits, group_size, eps=1e-8, want_par
                                    group_size, eps, _p(codes), _p(scale), _p(mn))
     assert rc == 0, rc
     return x, codes, scale, mn
+
+
+# ------------------------------------------------------------------ decode attention
+def attn_decode(q, k, v, scale):
+    """One decode step of attention over dequantized rows, in float64.
+
+    [MTPLX pull request #267, "feat(kv-cache): add q6 paged KV quantization",
+     PR description: the cache's rows are dequantized and handed to
+     scaled-dot-product attention] out = sum_t softmax_t(scale * q.k_t) v_t,
+    the softmax taken after subtracting the largest score; no rows -> zeros.
+    q: fp16 bits [D]; k, v: fp16 bits [T][D] (the dequantized cache rows).
+    """
+    qf = _u16(q).view(np.float16).astype(np.float64)
+    kf = _u16(k).view(np.float16).astype(np.float64).reshape(-1, qf.size)
+    vf = _u16(v).view(np.float16).astype(np.float64).reshape(-1, qf.size)
+    if kf.shape[0] == 0:
+        return np.zeros(qf.size)
+    s = (kf @ qf) * float(scale)
+    w = np.exp(s - s.max())
+    return (w[:, None] * vf).sum(axis=0) / w.sum()
 
 
 # ------------------------------------------------------------------ NUQ
