@@ -138,6 +138,43 @@ int kvq_dequant_sym(const kvq_paged_layout *layout, const uint8_t *k_codes,
                     int32_t max_blocks, const int32_t *seq_lens, int32_t n_seqs, int32_t max_len,
                     uint16_t *k_out, uint16_t *v_out, void *stream);
 
+/* ------------------------------------------------------------------ decode attention
+ * [MTPLX pull request #267, "feat(kv-cache): add q6 paged KV quantization",
+ *  PR description: the cached rows are dequantized (code x fp16 scale) and
+ *  passed to scaled-dot-product attention] -- here one call reads the packed
+ *  codes and scales directly (no fp16 copy of the cache).
+ */
+
+/* [host] Bytes of device workspace kvq_attn_decode_sym needs:
+ * n_seqs * ceil(max_len / 256) * q_heads * (head_dim + 2) * 4 (one chunk when
+ * max_len is 0). -1 on a negative size or non-positive q_heads / head_dim. */
+int64_t kvq_attn_workspace_bytes(int32_t n_seqs, int32_t q_heads, int32_t head_dim, int32_t max_len);
+
+/* One decode step of attention for one layer of a paged symmetric pool.
+ *   out[s][h][:] = sum_t softmax_t(softmax_scale * q[s][h] . k[s][t]) v[s][t]
+ * over positions t < min(seq_lens[s], max_len) of sequence s, where k, v are
+ * the rows of KV head h / (q_heads / kv_heads) dequantized exactly as
+ * kvq_dequant_sym does; positions p >= max_blocks * page_size and positions
+ * whose block-table entry is outside [0, num_pages) are left out of the
+ * softmax; a sequence with no position left gives 0.
+ * q fp16 [n_seqs][q_heads][head_dim]; out fp16 [n_seqs][q_heads][head_dim];
+ * block_table / seq_lens / pools as in kvq_dequant_sym; layer indexes the
+ * pool. head_dim 64, 128 or 256; q_heads a multiple of kv_heads with at most
+ * 16 query heads per KV head. Scores and the softmax are fp32 (scores from
+ * fp16 products accumulated in fp32), the probabilities are rounded to fp16
+ * for the weighted sum of V, accumulated in fp32; the result is rounded to
+ * fp16 once.
+ * workspace: caller-owned device memory of kvq_attn_workspace_bytes bytes,
+ * 16-byte aligned, contents irrelevant on entry. All pointers device memory,
+ * caller-owned; code pools and q 16-byte aligned. Errors: KVQ_ERR_SHAPE /
+ * _NULL / _ALIGN / _CAPACITY / _ARG as for the other calls. Asynchronous on
+ * `stream`. */
+int kvq_attn_decode_sym(const kvq_paged_layout *layout, const uint8_t *k_codes, const uint16_t *k_scales,
+                        const uint8_t *v_codes, const uint16_t *v_scales, int32_t layer, const uint16_t *q,
+                        int32_t q_heads, const int32_t *block_table, int32_t max_blocks,
+                        const int32_t *seq_lens, int32_t n_seqs, int32_t max_len, float softmax_scale,
+                        uint16_t *out, void *workspace, int64_t workspace_bytes, void *stream);
+
 /* ------------------------------------------------------------------ KIVI
  * ["veloxquant_mlx.cache.kivi_cache", KIVIKVCache._quant_dequant_along]
  * Asymmetric min/max round trip in binary32: for each group,

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvq.so")
 OBJ_DIR = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "sym.hip", "kivi.hip", "nuq.hip"]
+SOURCES = ["api.hip", "sym.hip", "kivi.hip", "nuq.hip", "attn.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -223,6 +223,75 @@ int kvq_dequant_sym(const kvq_paged_layout *layout, const uint8_t *k_codes,
                     "kvq_dequant_sym launch");
 }
 
+int64_t kvq_attn_workspace_bytes(int32_t n_seqs, int32_t q_heads, int32_t head_dim, int32_t max_len) {
+  if (n_seqs < 0 || q_heads <= 0 || head_dim <= 0 || max_len < 0) return -1;
+  const int64_t chunks = max_len > 0 ? ((int64_t)max_len + kvq::ATTN_CHUNK - 1) / kvq::ATTN_CHUNK : 1;
+  return (int64_t)n_seqs * chunks * q_heads * (head_dim + 2) * 4;
+}
+
+int kvq_attn_decode_sym(const kvq_paged_layout *layout, const uint8_t *k_codes, const uint16_t *k_scales,
+                        const uint8_t *v_codes, const uint16_t *v_scales, int32_t layer, const uint16_t *q,
+                        int32_t q_heads, const int32_t *block_table, int32_t max_blocks,
+                        const int32_t *seq_lens, int32_t n_seqs, int32_t max_len, float softmax_scale,
+                        uint16_t *out, void *workspace, int64_t workspace_bytes, void *stream) {
+  int rc = check_layout(layout);
+  if (rc) return rc;
+  const kvq_paged_layout &L = *layout;
+  if (L.head_dim != 64 && L.head_dim != 128 && L.head_dim != 256)
+    return fail(KVQ_ERR_SHAPE, "attention head_dim must be 64, 128 or 256 (got %d)", L.head_dim);
+  if (q_heads <= 0 || q_heads % L.kv_heads != 0 || q_heads / L.kv_heads > 16)
+    return fail(KVQ_ERR_SHAPE, "q_heads=%d must be a multiple of kv_heads=%d, at most 16 per KV head", q_heads,
+                L.kv_heads);
+  if (layer < 0 || layer >= L.layers) return fail(KVQ_ERR_SHAPE, "layer %d outside the pool's %d layers", layer,
+                                                  L.layers);
+  if (n_seqs < 0 || max_len < 0 || max_blocks < 0) return fail(KVQ_ERR_SHAPE, "negative size");
+  if (n_seqs == 0) return ok();
+  if (n_seqs > 65535) return fail(KVQ_ERR_SHAPE, "at most 65535 sequences per call");
+  if (!(softmax_scale == softmax_scale) || softmax_scale == __builtin_inff() || softmax_scale == -__builtin_inff())
+    return fail(KVQ_ERR_ARG, "softmax_scale must be finite");
+  if (!k_codes || !k_scales || !v_codes || !v_scales || !q || !out || !seq_lens || !workspace)
+    return fail(KVQ_ERR_NULL, "a required attention pointer is NULL");
+  if (max_len > 0 && (!block_table || max_blocks == 0))
+    return fail(KVQ_ERR_NULL, "block_table is NULL or max_blocks is 0");
+  for (const void *p : {(const void *)k_codes, (const void *)v_codes, (const void *)q, (const void *)workspace})
+    if (!aligned(p, 16)) return fail(KVQ_ERR_ALIGN, "code pools, q and the workspace need 16-byte alignment");
+  if (!aligned(k_scales, 2) || !aligned(v_scales, 2) || !aligned(out, 2) || !aligned(seq_lens, 4) ||
+      (block_table && !aligned(block_table, 4)))
+    return fail(KVQ_ERR_ALIGN, "misaligned scales, output, block table or lengths");
+  const int64_t need = kvq_attn_workspace_bytes(n_seqs, q_heads, L.head_dim, max_len);
+  if (workspace_bytes < need)
+    return fail(KVQ_ERR_CAPACITY, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
+                (long long)need);
+  const int64_t pd = packed(L.head_dim, L.bits);
+  const int64_t slots = (int64_t)L.num_pages * L.page_size;
+  kvq::AttnArgs a{};
+  a.k_codes = k_codes;
+  a.v_codes = v_codes;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  a.code_layer_stride = slots * L.kv_heads * pd;
+  a.scale_layer_stride = slots * L.kv_heads;
+  a.layer = layer;
+  a.num_pages = L.num_pages;
+  a.page_size = L.page_size;
+  a.kv_heads = L.kv_heads;
+  a.head_dim = L.head_dim;
+  a.bits = L.bits;
+  a.q = q;
+  a.q_heads = q_heads;
+  a.group = q_heads / L.kv_heads;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks;
+  a.seq_lens = seq_lens;
+  a.n_seqs = n_seqs;
+  a.max_len = max_len;
+  a.n_chunks = (int32_t)(max_len > 0 ? ((int64_t)max_len + kvq::ATTN_CHUNK - 1) / kvq::ATTN_CHUNK : 1);
+  a.scale = softmax_scale;
+  a.ws = static_cast<float *>(workspace);
+  a.out = out;
+  return hip_status(kvq::launch_attn_decode(a, (hipStream_t)stream), "kvq_attn_decode_sym launch");
+}
+
 int64_t kvq_kivi_boundary(int64_t offset, int32_t residual_length, int32_t group_size) {
   if (group_size <= 0 || residual_length < 0 || offset < 0) return -1;
   int64_t aged = offset - residual_length;

@@ -67,4 +67,22 @@ struct NuqArgs {
 
 hipError_t launch_nuq(const NuqArgs &a, int key_cpc, int val_cpc, hipStream_t st);
 
+constexpr int ATTN_CHUNK = 256;    // positions per attention workgroup
+struct AttnArgs {
+  const uint8_t *k_codes, *v_codes;      // pools as in SymDequantArgs
+  const uint16_t *k_scales, *v_scales;
+  int64_t code_layer_stride, scale_layer_stride;
+  int32_t layer, num_pages, page_size, kv_heads, head_dim, bits;
+  const uint16_t *q;                     // fp16 [n_seqs][q_heads][D]
+  int32_t q_heads, group;                // group = q_heads / kv_heads (<= 16)
+  const int32_t *block_table;            // [n_seqs][max_blocks]
+  int32_t max_blocks;
+  const int32_t *seq_lens;               // [n_seqs]
+  int32_t n_seqs, max_len, n_chunks;
+  float scale;
+  float *ws;                             // [n_seqs][n_chunks][q_heads][D + 2]
+  uint16_t *out;                         // fp16 [n_seqs][q_heads][D]
+};
+hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t st);
+
 }  // namespace kvq

@@ -45,6 +45,9 @@ _SIGS = {
     "kvq_quant_sym": (C.c_int, [C.POINTER(PagedLayout), _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     "kvq_dequant_sym": (C.c_int, [C.POINTER(PagedLayout), _P, _P, _P, _P, _I, _I, _P, _I, _P, _I, _I,
                                   _P, _P, _P]),
+    "kvq_attn_workspace_bytes": (_L, [_I, _I, _I, _I]),
+    "kvq_attn_decode_sym": (C.c_int, [C.POINTER(PagedLayout), _P, _P, _P, _P, _I, _P, _I, _P, _I, _P, _I, _I,
+                                      _F, _P, _P, _L, _P]),
     "kvq_kivi_boundary": (_L, [_L, _I, _I]),
     "kvq_kivi_quant_dequant": (C.c_int, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F,
                                          _P, _P, _P, _P, _P, _P, _P]),
@@ -156,6 +159,22 @@ def kvq_dequant_sym(lay: PagedLayout, k_codes, k_scales, v_codes, v_scales, bloc
                                _ptr(v_scales), layer0, n_layers, _ptr(block_table),
                                int(block_table.shape[1]), _ptr(seq_lens), n_seqs, max_len,
                                _ptr(k_out), _ptr(v_out), _stream(stream)))
+
+
+# ------------------------------------------------------------------ decode attention
+def kvq_attn_workspace_bytes(n_seqs, q_heads, head_dim, max_len) -> int:
+    return lib().kvq_attn_workspace_bytes(n_seqs, q_heads, head_dim, max_len)
+
+
+def kvq_attn_decode_sym(lay: PagedLayout, k_codes, k_scales, v_codes, v_scales, layer: int, q, block_table,
+                        seq_lens, max_len: int, softmax_scale: float, out, workspace, stream=None):
+    """q, out: fp16 [n_seqs][q_heads][head_dim]; pools as in kvq_dequant_sym."""
+    _dev(k_codes, k_scales, v_codes, v_scales, q, block_table, seq_lens, out, workspace)
+    n_seqs, q_heads = int(q.shape[0]), int(q.shape[1])
+    _err(lib().kvq_attn_decode_sym(C.byref(lay), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales),
+                                   layer, _ptr(q), q_heads, _ptr(block_table), int(block_table.shape[1]),
+                                   _ptr(seq_lens), n_seqs, max_len, softmax_scale, _ptr(out), _ptr(workspace),
+                                   int(workspace.numel() * workspace.element_size()), _stream(stream)))
 
 
 # ------------------------------------------------------------------ KIVI

@@ -101,6 +101,36 @@ def test_sym_dequant_validation_errors():
     assert _dequant(good, max_len=0) == kvq.KVQ_OK
 
 
+def _attn(lay, kc=FAKE, ks=FAKE, vc=FAKE, vs=FAKE, layer=0, q=FAKE, qh=8, bt=FAKE, mb=4, sl=FAKE, n_seqs=2,
+          max_len=64, scale=0.125, out=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return kvq.lib().kvq_attn_decode_sym(C.byref(lay), kc, ks, vc, vs, layer, q, qh, bt, mb, sl, n_seqs, max_len,
+                                         scale, out, ws, ws_bytes, None)
+
+
+def test_attn_workspace_and_validation_errors():
+    ws = kvq.kvq_attn_workspace_bytes
+    assert ws(3, 8, 128, 257) == 3 * 2 * 8 * 130 * 4
+    assert ws(3, 8, 128, 256) == 3 * 1 * 8 * 130 * 4
+    assert ws(1, 4, 64, 0) == 4 * 66 * 4                                    # one chunk when max_len is 0
+    assert ws(-1, 4, 64, 8) == ws(1, 0, 64, 8) == ws(1, 4, 0, 8) == ws(1, 4, 64, -1) == -1
+    good = kvq.layout(2, 8, 16, 4, 128, 6)
+    assert _attn(kvq.layout(2, 8, 16, 4, 96, 6)) == kvq.KVQ_ERR_SHAPE       # head_dim 64/128/256 only
+    assert _attn(kvq.layout(2, 8, 16, 4, 128, 5)) == kvq.KVQ_ERR_BITS
+    assert _attn(good, qh=6) == kvq.KVQ_ERR_SHAPE                           # not a multiple of kv_heads
+    assert _attn(good, qh=4 * 17) == kvq.KVQ_ERR_SHAPE                      # more than 16 per KV head
+    assert _attn(good, layer=2) == kvq.KVQ_ERR_SHAPE
+    assert _attn(good, n_seqs=-1) == kvq.KVQ_ERR_SHAPE
+    assert _attn(good, scale=float("inf")) == kvq.KVQ_ERR_ARG
+    assert _attn(good, scale=float("nan")) == kvq.KVQ_ERR_ARG
+    assert _attn(good, ws=None) == kvq.KVQ_ERR_NULL
+    assert _attn(good, bt=None) == kvq.KVQ_ERR_NULL
+    assert _attn(good, q=FAKE + 8) == kvq.KVQ_ERR_ALIGN
+    assert _attn(good, ws=FAKE + 4) == kvq.KVQ_ERR_ALIGN
+    assert _attn(good, sl=FAKE + 2) == kvq.KVQ_ERR_ALIGN
+    assert _attn(good, ws_bytes=ws(2, 8, 128, 64) - 1) == kvq.KVQ_ERR_CAPACITY
+    assert _attn(good, n_seqs=0) == kvq.KVQ_OK
+
+
 def _kivi(k=FAKE, v=FAKE, B=2, H=2, S=64, D=64, lo=0, hi=32, bits=2, gs=32, eps=1e-8, kc=None,
           ks=None, km=None, vc=None, vs=None, vm=None):
     return kvq.lib().kvq_kivi_quant_dequant(k, v, B, H, S, D, lo, hi, bits, gs, eps, kc, ks, km, vc,
