@@ -11,8 +11,8 @@ drawn from Laplace(0,1). One step = that whole sequence for each width in
 
 Output: one JSON line (metric, value in GB/s of fp16-equivalent KV processed,
 roofline of the dominant kernel, CPU-oracle baseline on a bounded sample).
-Other workloads (--workload kivi | long_context | single_layer | nuq) print a
-line of the same form for their own configuration.
+Other workloads (--workload kivi | long_context | single_layer | nuq |
+attn_decode) print a line of the same form for their own configuration.
 """
 from __future__ import annotations
 
@@ -31,32 +31,39 @@ METRIC = "KV quant+pack / unpack+dequant GB/s (fp16-equiv) and % of HBM peak, 1 
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_sym_kivi.md")
+ATTN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_attn_decode.md")
 CSRC = os.path.join(ROOT, "kv_cache_quantization_row_amd", "csrc")
 
 
 def measured_traffic(kernel_class):
-    """HBM bytes per launch of a kernel class from the committed rocprofv3
-    FETCH_SIZE/WRITE_SIZE summary, or None when there is no entry or the
-    kernel source changed since the counters were taken."""
+    """HBM bytes of one timed span of a kernel class from the committed
+    rocprofv3 FETCH_SIZE/WRITE_SIZE summaries, or None when there is no entry
+    or the kernel source changed since the counters were taken."""
     import hashlib
     import re
 
-    if kernel_class.startswith("quant_prefill_q"):
+    launches, traffic_file = 1, TRAFFIC_FILE
+    if kernel_class.startswith("attn_decode_q"):  # span: one launch pair per layer
+        b = kernel_class.split("_q")[1].split("_")[0]
+        launches = int(kernel_class.rsplit("_x", 1)[1])
+        names, src = ["attn_decode_chunk_pg<%s, 256>" % b, "attn_decode_merge<256>"], "attn.hip"
+        traffic_file = ATTN_TRAFFIC_FILE
+    elif kernel_class.startswith("quant_prefill_q"):
         b = kernel_class[-1]
-        names, src = ["sym_quant_fast<%s, 16, 2>" % b], "sym.hip"
+        names, src = ["sym_quant_v8<%s, 32, %d>" % (b, 1 if b == "8" else 2)], "sym.hip"
     elif kernel_class.startswith("dequant_sweep_q"):
         b = kernel_class[-1]
         names, src = ["sym_dequant_page<%s, 256>" % b], "sym.hip"
     elif kernel_class.startswith("kivi_keys_values_b"):
         b = kernel_class[-1]
-        names, src = ["kivi_keys_fast<%s, 8, 4>" % b, "kivi_values_fast<%s, 8, 4, 2>" % b], "kivi.hip"
+        names, src = ["kivi_keys_fast<%s, 8, 4>" % b, "kivi_values_fast<%s, 8, 4, 1>" % b], "kivi.hip"
     else:
         return None
-    if not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(traffic_file):
         return None
     sha = hashlib.sha1(open(os.path.join(CSRC, src), "rb").read()).hexdigest()
     best = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(traffic_file):
         m = re.match(r"traffic (.+?) grid=(\d+) bytes=(\d+) src_sha1=([0-9a-f]+)", line.strip())
         if m and m.group(1) in names and m.group(4) == sha:
             g = int(m.group(2))
@@ -64,7 +71,7 @@ def measured_traffic(kernel_class):
                 best[m.group(1)] = (g, int(m.group(3)))
     if len(best) != len(names):
         return None
-    return sum(v[1] for v in best.values())
+    return launches * sum(v[1] for v in best.values())
 
 
 def log(*a):
@@ -440,6 +447,114 @@ class LongContext:
         return None
 
 
+# --------------------------------------------------------------------------- decode attention
+class AttnDecode:
+    """Decode attention over the packed pools of the paged configuration:
+    16 layers x 4 KV heads x D=256, page 16, 16 sequences x 33,024 tokens
+    (32,768 prefill + 256 appends) in randomly assigned pages, 4 query heads
+    per KV head; one step = one decode token of every sequence through all 16
+    layers (one launch per layer) for each width in --bits."""
+
+    def __init__(self, torch, args):
+        self.torch = torch
+        self.L, self.H, self.D, self.P, self.G = 16, 4, 256, 16, args.attn_group
+        self.S, self.len = 16, args.prefill_tokens + args.decode_steps
+        self.bits_list = [int(b) for b in args.bits.split(",")]
+        self.name = "attn_decode"
+
+    def setup(self):
+        torch = self.torch
+        from kv_cache_quantization_row_amd import inputs, kvq
+
+        self.kvq = kvq
+        d = torch.device("cuda:0")
+        L, H, D, P, S, T = self.L, self.H, self.D, self.P, self.S, self.len
+        bt, self.num_pages = inputs.paged_block_table(S, T, P, seed=2002)
+        slots = self.num_pages * P
+        slot_map = inputs.slot_mapping_for(bt, P, 0, T).to(d)
+        self.bt = bt.to(d)
+        self.lens = torch.full((S,), T, dtype=torch.int32, device=d)
+        self.pools = {}
+        for b in self.bits_list:
+            pd = kvq.kvq_packed_dim(D, b)
+            lay = kvq.layout(L, self.num_pages, P, H, D, b)
+            kc = torch.empty((L, slots, H, pd), dtype=torch.uint8, device=d)
+            vc = torch.empty_like(kc)
+            ks = torch.empty((L, slots, H), dtype=torch.int16, device=d)
+            vs = torch.empty_like(ks)
+            self.pools[b] = (lay, kc, ks, vc, vs)
+        for l in range(L):
+            log("filling layer %d of the pools (%d tokens)" % (l, S * T))
+            k = inputs.sym_layer(S * T, H, D, seed=2100 + l, device=d, laplace_token_frac=0.05,
+                                 channel_seed=3100 + l)[None]
+            v = inputs.sym_layer(S * T, H, D, seed=2200 + l, device=d, laplace_token_frac=0.05,
+                                 channel_seed=3200 + l)[None]
+            for b, (lay, kc, ks, vc, vs) in self.pools.items():
+                kvq.kvq_quant_sym(lay, k, v, slot_map, kc, ks, vc, vs, layer0=l)
+            del k, v
+        self.q = inputs.sym_layer(L * S, H * self.G, D, seed=2500, device=d, outlier_frac=0).view(L, S, H * self.G, D)
+        self.out = torch.empty((S, H * self.G, D), dtype=torch.float16, device=d)
+        self.ws = torch.empty(kvq.kvq_attn_workspace_bytes(S, H * self.G, D, T), dtype=torch.uint8, device=d)
+        self.scale = 1.0 / D ** 0.5
+        torch.cuda.synchronize()
+
+    def step(self, tm):
+        kvq = self.kvq
+        for b in self.bits_list:
+            lay, kc, ks, vc, vs = self.pools[b]
+            with tm.span("attn_decode_q%d_x%d" % (b, self.L)):
+                for l in range(self.L):
+                    kvq.kvq_attn_decode_sym(lay, kc, ks, vc, vs, l, self.q[l], self.bt, self.lens, self.len,
+                                            self.scale, self.out, self.ws)
+
+    # fp16-equivalent K and V elements read per step
+    def elems(self):
+        return 2 * self.L * self.S * self.len * self.H * self.D * len(self.bits_list)
+
+    def kernel_bytes(self, name):
+        """Algorithmic bytes of the 16 launches of one width: packed codes and
+        fp16 scales of every cached K and V row, the queries and the outputs."""
+        b = int(name.split("_q")[1].split("_")[0])
+        rows = 2 * self.S * self.len * self.H
+        qo = 2 * self.S * self.H * self.G * self.D * 2
+        return self.L * (rows * (self.D * b // 8 + 2) + qo)
+
+    def config(self):
+        return {"workload": "paged decode attention over packed q8/q6/q4 codes: 16 layers x 4 KV heads x D=256, "
+                            "page 16, 16 seqs x %d tokens, %d query heads per KV head, one decode token per "
+                            "sequence through all layers" % (self.len, self.G),
+                "bits": self.bits_list, "layers": self.L, "kv_heads": self.H, "q_heads": self.H * self.G,
+                "head_dim": self.D, "page_size": self.P, "seqs": self.S, "tokens_per_seq": self.len}
+
+    def cpu_baseline(self, budget_tokens):
+        """Oracle on layer 0 of one sequence (budget_tokens/4 tokens): dequantize
+        the rows, then attention for every query head, per width."""
+        import numpy as np
+        import torch as _t
+        import oracle
+        from kv_cache_quantization_row_amd import inputs
+
+        n = max(budget_tokens // 4, 1)
+        H, D, G = self.H, self.D, self.G
+        k = inputs.sym_layer(n, H, D, seed=2100, laplace_token_frac=0.05, channel_seed=3100)
+        v = inputs.sym_layer(n, H, D, seed=2200, laplace_token_frac=0.05, channel_seed=3200)
+        q = inputs.sym_layer(1, H * G, D, seed=2500, outlier_frac=0)[0]
+        kk, vv, qq = (x.contiguous().view(_t.int16).numpy().view(np.uint16) for x in (k, v, q))
+        t0 = time.perf_counter()
+        for b in self.bits_list:
+            for h in range(H):
+                kd = oracle.sym_dequant_rows(*oracle.sym_quant_rows(kk[:, h], b), D, b)
+                vd = oracle.sym_dequant_rows(*oracle.sym_quant_rows(vv[:, h], b), D, b)
+                for j in range(G):
+                    oracle.attn_decode(qq[h * G + j], kd, vd, self.scale)
+        dt = time.perf_counter() - t0
+        elems = 2 * n * H * D * len(self.bits_list)
+        return {"value": round(2 * elems / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": "layer 0, one sequence of %d tokens x 4 KV heads x 256, %d query heads per KV head, "
+                          "quantize + dequantize + attention at q%s (%.1f s; quantization included, so an "
+                          "upper bound on the oracle's time)" % (n, G, "/q".join(map(str, self.bits_list)), dt)}
+
+
 # --------------------------------------------------------------------------- single layer
 class SingleLayer:
     """One layer, K and V each [1024][4][256], q6, 64 pages of 16 (slots in token
@@ -530,7 +645,7 @@ class Copy:
 
 
 WORKLOADS = {"paged_sym": PagedSym, "kivi": Kivi, "nuq": Nuq, "long_context": LongContext,
-             "single_layer": SingleLayer, "copy": Copy}
+             "single_layer": SingleLayer, "attn_decode": AttnDecode, "copy": Copy}
 
 
 def main():
@@ -545,6 +660,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--decode-steps-long", type=int, default=1024)
     ap.add_argument("--cpu-tokens", type=int, default=65536)
+    ap.add_argument("--attn-group", type=int, default=4, help="query heads per KV head (attn_decode)")
     ap.add_argument("--page-order", default="random", choices=["random", "identity"],
                     help="pool page assignment of the paged workload (random = fragmented pool)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -225,7 +225,7 @@ int kvq_dequant_sym(const kvq_paged_layout *layout, const uint8_t *k_codes,
 
 int64_t kvq_attn_workspace_bytes(int32_t n_seqs, int32_t q_heads, int32_t head_dim, int32_t max_len) {
   if (n_seqs < 0 || q_heads <= 0 || head_dim <= 0 || max_len < 0) return -1;
-  const int64_t chunks = max_len > 0 ? ((int64_t)max_len + kvq::ATTN_CHUNK - 1) / kvq::ATTN_CHUNK : 1;
+  const int64_t chunks = max_len > 0 ? ((int64_t)max_len + kvq::ATTN_MIN_CHUNK - 1) / kvq::ATTN_MIN_CHUNK : 1;
   return (int64_t)n_seqs * chunks * q_heads * (head_dim + 2) * 4;
 }
 
@@ -285,8 +285,7 @@ int kvq_attn_decode_sym(const kvq_paged_layout *layout, const uint8_t *k_codes, 
   a.seq_lens = seq_lens;
   a.n_seqs = n_seqs;
   a.max_len = max_len;
-  a.n_chunks = (int32_t)(max_len > 0 ? ((int64_t)max_len + kvq::ATTN_CHUNK - 1) / kvq::ATTN_CHUNK : 1);
-  a.scale = softmax_scale;
+  a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);  // log2(e)
   a.ws = static_cast<float *>(workspace);
   a.out = out;
   return hip_status(kvq::launch_attn_decode(a, (hipStream_t)stream), "kvq_attn_decode_sym launch");

@@ -67,7 +67,10 @@ struct NuqArgs {
 
 hipError_t launch_nuq(const NuqArgs &a, int key_cpc, int val_cpc, hipStream_t st);
 
-constexpr int ATTN_CHUNK = 256;    // positions per attention workgroup
+// Attention chunks are whole blocks of 16 positions and never shorter than
+// ATTN_MIN_CHUNK positions, so a sequence of max_len positions has at most
+// ceil(max_len / ATTN_MIN_CHUNK) chunk partials in the workspace.
+constexpr int ATTN_MIN_CHUNK = 256;
 struct AttnArgs {
   const uint8_t *k_codes, *v_codes;      // pools as in SymDequantArgs
   const uint16_t *k_scales, *v_scales;
@@ -78,11 +81,12 @@ struct AttnArgs {
   const int32_t *block_table;            // [n_seqs][max_blocks]
   int32_t max_blocks;
   const int32_t *seq_lens;               // [n_seqs]
-  int32_t n_seqs, max_len, n_chunks;
-  float scale;
+  int32_t n_seqs, max_len;
+  int32_t n_chunks, chunk_blocks;        // set by launch_attn_decode
+  float scale_log2;                      // softmax scale * log2(e)
   float *ws;                             // [n_seqs][n_chunks][q_heads][D + 2]
   uint16_t *out;                         // fp16 [n_seqs][q_heads][D]
 };
-hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t st);
+hipError_t launch_attn_decode(AttnArgs a, hipStream_t st);
 
 }  // namespace kvq
