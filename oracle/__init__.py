@@ -58,6 +58,8 @@ _SIGS = {
     "orc_nuq_fit": (None, [_P, _I, _I, _I, _P]),
     "orc_nuq_threshold": (C.c_uint16, [_P, _I, _F]),
     "orc_nuq_nearest": (_I, [C.c_uint16, _P, _I]),
+    "orc_kivi_pack": (_I, [_P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P]),
+    "orc_kivi_unpack": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P]),
     "orc_nuq_fit_quant": (_I, [_P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I,
                                _P, _P, _P, _P, _P, _P, _P, _P, _P, _LL, _P, _P, _P]),
 }
@@ -203,6 +205,44 @@ def kivi_round_trip(x, lo, hi, per_channel, bits, group_size, eps=1e-8, want_par
                                    group_size, eps, _p(codes), _p(scale), _p(mn))
     assert rc == 0, rc
     return x, codes, scale, mn
+
+
+def kivi_param_shape(B, H, S_cap, D, per_channel, group_size):
+    """Shape of the fp16 scale / zero arrays of packed KIVI storage."""
+    if per_channel:
+        return (B, H, (S_cap + group_size - 1) // group_size, D)
+    return (B, H, S_cap, (D + group_size - 1) // group_size)
+
+
+def kivi_pack(x, lo, hi, per_channel, bits, group_size, eps=1e-8, into=None):
+    """Packed KIVI storage of tokens [lo, hi) of x (fp16 bits [B][H][S_cap][D]).
+
+    Returns (codes uint8 [B][H][S_cap][D*bits/8], scale uint16, zero uint16)
+    with the parameter shapes of kivi_param_shape; `into` = such a triple to
+    update in place (other tokens kept)."""
+    x = _u16(x)
+    B, H, S_cap, D = x.shape
+    if into is None:
+        shp = kivi_param_shape(B, H, S_cap, D, per_channel, group_size)
+        into = (np.zeros((B, H, S_cap, D * bits // 8), np.uint8), np.zeros(shp, np.uint16),
+                np.zeros(shp, np.uint16))
+    codes, sc, zr = into
+    assert codes.flags.c_contiguous and sc.flags.c_contiguous and zr.flags.c_contiguous
+    rc = lib().orc_kivi_pack(_p(x), B, H, S_cap, D, lo, hi, int(per_channel), bits, group_size, eps,
+                             _p(codes), _p(sc), _p(zr))
+    assert rc == 0, rc
+    return codes, sc, zr
+
+
+def kivi_unpack(codes, scale, zero, lo, hi, per_channel, bits, group_size, D):
+    """fp16 bits [B][H][S_cap][D]: tokens [lo, hi) reconstructed, others 0."""
+    codes = np.ascontiguousarray(codes, np.uint8)
+    B, H, S_cap = codes.shape[:3]
+    out = np.zeros((B, H, S_cap, D), np.uint16)
+    rc = lib().orc_kivi_unpack(_p(codes), _p(_u16(scale)), _p(_u16(zero)), B, H, S_cap, D, lo, hi,
+                               int(per_channel), bits, group_size, _p(out))
+    assert rc == 0, rc
+    return out
 
 
 # ------------------------------------------------------------------ decode attention

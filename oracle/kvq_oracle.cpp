@@ -519,6 +519,123 @@ int orc_kivi_round_trip(uint16_t *x, int B, int H, int S_cap, int D, int lo, int
   return 0;
 }
 
+// ------------------------------------------------------ exported: KIVI packed
+// Packed KIVI storage: b-bit codes plus one fp16 (scale, zero) pair per
+// group, the layout the page's byte accounting charges for
+// ["veloxquant_mlx.cache.kivi_cache", module docstring on per-token storage
+// at bit-width b and group size g, and _quantized_bytes]. The group math is
+// that of _quant_dequant_along with the parameters rounded to fp16 before
+// use, so that the stored pair reproduces the codes:
+//   scale = max(RN32((max - min)/levels), eps) rounded to fp16 toward zero,
+//           so that the top level min + levels*scale never exceeds the
+//           group's max (rounding to nearest can push it past the fp16
+//           range: at b = 8 a group spanning +-65504 would reconstruct its
+//           max as +inf); a result of 0 becomes 2^-24, the smallest positive
+//           fp16 (the page's 1e-8 floor is not representable in fp16);
+//   zero  = min (an fp16 value already, stored exactly; -0 as +0);
+//   code  = clip(round_half_even(RN32(RN32(x - zero) / scale)), 0, levels);
+//   recon = RN16(RN32(code * scale) + zero).
+void kivi_group_p16(const float *vals, int n, int levels, float eps, int *codes, uint16_t *s16,
+                    uint16_t *z16) {
+  float mn = vals[0], mx = vals[0];
+  for (int i = 1; i < n; ++i) {
+    if (vals[i] < mn) mn = vals[i];
+    if (vals[i] > mx) mx = vals[i];
+  }
+  float scale = (mx - mn) / (float)levels;
+  if (scale < eps) scale = eps;
+  uint16_t sh = f2h(scale);
+  if (h2f(sh) > scale) --sh;  // toward zero (scale > 0: one step down the bit pattern)
+  if (sh == 0) sh = 1;        // 2^-24
+  const float s = h2f(sh);
+  for (int i = 0; i < n; ++i) {
+    float t = (vals[i] - mn) / s;
+    float c = std::nearbyint(t);
+    if (c < 0.0f) c = 0.0f;
+    if (c > (float)levels) c = (float)levels;
+    codes[i] = (int)c;
+  }
+  *s16 = sh;
+  *z16 = f2h(mn + 0.0f);
+}
+
+// Quantize tokens [lo, hi) of x, fp16 [B][H][S_cap][D] (not modified), into
+// packed storage indexed by absolute token: codes [B][H][S_cap][D*bits/8]
+// (LSB-first along D), keys (per_channel = 1, groups of gs tokens from token
+// 0; lo must be a multiple of gs) scale/zero fp16 [B][H][ceil(S_cap/gs)][D],
+// values (per_channel = 0, groups of gs channels) scale/zero fp16
+// [B][H][S_cap][ceil(D/gs)]. Codes outside [lo, hi) are left as they are.
+int orc_kivi_pack(const uint16_t *x, int B, int H, int S_cap, int D, int lo, int hi, int per_channel,
+                  int bits, int gs, float eps, uint8_t *codes, uint16_t *scale16, uint16_t *zero16) {
+  if (bits < 1 || bits > 8 || gs <= 0 || lo < 0 || hi < lo || hi > S_cap || D <= 0) return -1;
+  if ((long long)D * bits % 8) return -1;
+  if (per_channel && lo % gs) return -1;
+  const int levels = (1 << bits) - 1;
+  const long long cpr = (long long)D * bits / 8;
+  std::vector<float> buf(std::max(gs, 1));
+  std::vector<int> cbuf(std::max(gs, 1));
+  for (long long bh = 0; bh < (long long)B * H; ++bh) {
+    const uint16_t *base = x + bh * S_cap * D;
+    uint8_t *crow = codes + bh * S_cap * cpr;
+    for (int t = lo; t < hi; ++t) std::memset(crow + (long long)t * cpr, 0, (size_t)cpr);
+    if (per_channel) {
+      const int ngc = (S_cap + gs - 1) / gs;
+      for (int t0 = lo; t0 < hi; t0 += gs) {
+        const int t1 = std::min(t0 + gs, hi);
+        for (int d = 0; d < D; ++d) {
+          for (int t = t0; t < t1; ++t) buf[t - t0] = h2f(base[(long long)t * D + d]);
+          uint16_t sh, zh;
+          kivi_group_p16(buf.data(), t1 - t0, levels, eps, cbuf.data(), &sh, &zh);
+          for (int t = t0; t < t1; ++t) put_code(crow + (long long)t * cpr, d, bits, cbuf[t - t0]);
+          scale16[(bh * ngc + t0 / gs) * D + d] = sh;
+          zero16[(bh * ngc + t0 / gs) * D + d] = zh;
+        }
+      }
+    } else {
+      const int ng = (D + gs - 1) / gs;
+      for (int t = lo; t < hi; ++t) {
+        for (int g = 0; g < ng; ++g) {
+          const int d0 = g * gs, d1 = std::min(d0 + gs, D);
+          for (int d = d0; d < d1; ++d) buf[d - d0] = h2f(base[(long long)t * D + d]);
+          uint16_t sh, zh;
+          kivi_group_p16(buf.data(), d1 - d0, levels, eps, cbuf.data(), &sh, &zh);
+          for (int d = d0; d < d1; ++d) put_code(crow + (long long)t * cpr, d, bits, cbuf[d - d0]);
+          scale16[(bh * S_cap + t) * ng + g] = sh;
+          zero16[(bh * S_cap + t) * ng + g] = zh;
+        }
+      }
+    }
+  }
+  return 0;
+}
+
+// Reconstruct tokens [lo, hi) from packed storage (layouts as above) into
+// out, fp16 [B][H][S_cap][D] at the same token positions:
+// RN16(RN32(code * scale) + zero).
+int orc_kivi_unpack(const uint8_t *codes, const uint16_t *scale16, const uint16_t *zero16, int B, int H,
+                    int S_cap, int D, int lo, int hi, int per_channel, int bits, int gs, uint16_t *out) {
+  if (bits < 1 || bits > 8 || gs <= 0 || lo < 0 || hi < lo || hi > S_cap || D <= 0) return -1;
+  if ((long long)D * bits % 8) return -1;
+  const long long cpr = (long long)D * bits / 8;
+  const int ngc = (S_cap + gs - 1) / gs, ng = (D + gs - 1) / gs;
+  for (long long bh = 0; bh < (long long)B * H; ++bh) {
+    for (int t = lo; t < hi; ++t) {
+      const uint8_t *row = codes + (bh * S_cap + t) * cpr;
+      for (int d = 0; d < D; ++d) {
+        int c = 0;
+        for (int b = 0; b < bits; ++b) {
+          const long bit = (long)d * bits + b;
+          c |= ((row[bit / 8] >> (bit % 8)) & 1) << b;
+        }
+        const long long p = per_channel ? (bh * ngc + t / gs) * D + d : (bh * S_cap + t) * ng + d / gs;
+        const float prod = (float)c * h2f(scale16[p]);
+        out[(bh * S_cap + t) * D + d] = f2h(prod + h2f(zero16[p]));
+      }
+    }
+  }
+  return 0;
+}
+
 // ------------------------------------------------------------ exported: NUQ
 // Lloyd fit of one vector of inlier samples (used directly by the pins).
 void orc_nuq_fit(const uint16_t *u, int m, int L, int iters, float *levels) {
