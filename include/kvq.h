@@ -209,6 +209,46 @@ int kvq_kivi_quant_dequant(uint16_t *keys, uint16_t *values, int32_t B, int32_t 
                            float eps, uint8_t *k_codes, float *k_scale, float *k_min,
                            uint8_t *v_codes, float *v_scale, float *v_min, void *stream);
 
+/* Packed KIVI storage ["veloxquant_mlx.cache.kivi_cache", module docstring
+ * on per-token storage at bit-width b and group size g, and
+ * _quantized_bytes]: b-bit codes plus one fp16 (scale, zero) pair per
+ * group, the storage the page's byte accounting charges for. Group math as
+ * kvq_kivi_quant_dequant with the pair rounded to fp16 before use:
+ * scale = max((max - min)/levels, eps) rounded to fp16 toward zero (so that
+ * zero + levels*scale never exceeds the group's max) and raised to 2^-24 if
+ * that gives 0 (eps = 1e-8 is below the smallest fp16); zero = min (exact,
+ * -0 stored as +0); code = clamp(rint((x - zero)/scale), 0, levels) with the
+ * fp16 scale; reconstruction fp16(code*scale + zero), product then sum.
+ * Storage is indexed by absolute token so that successive flushes fill it in
+ * place:
+ *   codes   uint8 [B][H][S_cap][D*bits/8], LSB-first along D;
+ *   keys    groups of group_size tokens from token 0 (lo must be a multiple
+ *           of group_size): scale, zero fp16 [B][H][ceil(S_cap/group_size)][D];
+ *   values  groups of group_size channels: scale, zero fp16
+ *           [B][H][S_cap][ceil(D/group_size)].
+ * Requires D % 8 == 0 and group_size a positive multiple of 8; bits 2, 4,
+ * 8; all pointers device memory, caller-owned, 16-byte aligned. */
+
+/* Quantize tokens [lo, hi) of keys and/or values (fp16 [B][H][S_cap][D],
+ * not modified) into packed storage; the other tokens' storage is not
+ * touched. keys or values may be NULL to skip that side (its outputs are
+ * then unused); a given side needs all three outputs. hi == lo is a no-op.
+ * Errors: KVQ_ERR_NULL, KVQ_ERR_BITS, KVQ_ERR_SHAPE, KVQ_ERR_ARG (eps),
+ * KVQ_ERR_ALIGN, KVQ_ERR_HIP. Asynchronous on `stream`. */
+int kvq_kivi_pack(const uint16_t *keys, const uint16_t *values, int32_t B, int32_t H, int32_t S_cap, int32_t D,
+                  int32_t lo, int32_t hi, int32_t bits, int32_t group_size, float eps, uint8_t *k_codes,
+                  uint16_t *k_scale, uint16_t *k_zero, uint8_t *v_codes, uint16_t *v_scale, uint16_t *v_zero,
+                  void *stream);
+
+/* Reconstruct tokens [lo, hi) from packed storage into k_out / v_out (fp16
+ * [B][H][S_cap][D], the same token positions; other tokens not written).
+ * Either output may be NULL to skip that side. Errors as kvq_kivi_pack
+ * (no eps). Asynchronous on `stream`. */
+int kvq_kivi_unpack(const uint8_t *k_codes, const uint16_t *k_scale, const uint16_t *k_zero, const uint8_t *v_codes,
+                    const uint16_t *v_scale, const uint16_t *v_zero, int32_t B, int32_t H, int32_t S_cap, int32_t D,
+                    int32_t lo, int32_t hi, int32_t bits, int32_t group_size, uint16_t *k_out, uint16_t *v_out,
+                    void *stream);
+
 /* ------------------------------------------------------------------ NUQ
  * ["veloxquant_mlx.cache.kvquant_cache module", module docstring] KVQuant-style
  * non-uniform quantization. Keys get one table of L = 2^bits levels per

@@ -340,7 +340,104 @@ int kvq_kivi_quant_dequant(uint16_t *keys, uint16_t *values, int32_t B, int32_t 
   a.bits = bits;
   a.gs = group_size;
   a.eps = eps;
+  a.packed = 0;
+  a.code_rows = (int32_t)n;
+  a.code_t0 = lo;
+  a.kgrp_rows = (int32_t)((n + group_size - 1) / group_size);
+  a.kgrp0 = 0;
   return hip_status(kvq::launch_kivi(a, (hipStream_t)stream), "kvq_kivi_quant_dequant launch");
+}
+
+int kvq_kivi_pack(const uint16_t *keys, const uint16_t *values, int32_t B, int32_t H, int32_t S_cap, int32_t D,
+                  int32_t lo, int32_t hi, int32_t bits, int32_t group_size, float eps, uint8_t *k_codes,
+                  uint16_t *k_scale, uint16_t *k_zero, uint8_t *v_codes, uint16_t *v_scale, uint16_t *v_zero,
+                  void *stream) {
+  if (!keys && !values) return fail(KVQ_ERR_NULL, "neither keys nor values given");
+  if (keys && (!k_codes || !k_scale || !k_zero)) return fail(KVQ_ERR_NULL, "key codes, scale and zero are required");
+  if (values && (!v_codes || !v_scale || !v_zero))
+    return fail(KVQ_ERR_NULL, "value codes, scale and zero are required");
+  if (bits != 2 && bits != 4 && bits != 8) return fail(KVQ_ERR_BITS, "bits=%d is not one of 2, 4, 8", bits);
+  if (B < 0 || H < 0 || S_cap < 0 || D <= 0) return fail(KVQ_ERR_SHAPE, "bad B/H/S_cap/D");
+  if (lo < 0 || hi < lo || hi > S_cap) return fail(KVQ_ERR_SHAPE, "need 0 <= lo <= hi <= S_cap");
+  if (group_size <= 0 || group_size % 8 || D % 8)
+    return fail(KVQ_ERR_SHAPE, "packed storage needs D %% 8 == 0 and group_size a positive multiple of 8");
+  if (keys && lo % group_size)
+    return fail(KVQ_ERR_SHAPE, "key groups start at token 0: lo=%d must be a multiple of group_size", lo);
+  if (!(eps > 0.0f) || !(eps < 3.0e38f)) return fail(KVQ_ERR_ARG, "eps must be positive and finite");
+  for (const void *p : {(const void *)keys, (const void *)values, (const void *)k_codes, (const void *)v_codes,
+                        (const void *)k_scale, (const void *)k_zero, (const void *)v_scale, (const void *)v_zero})
+    if (p && !aligned(p, 16)) return fail(KVQ_ERR_ALIGN, "packed KIVI tensors need 16-byte alignment");
+  const int64_t BH = (int64_t)B * H;
+  if (hi == lo || BH == 0) return ok();
+  const int64_t n = hi - lo;
+  if (BH * S_cap * D >= ((int64_t)1 << 46)) return fail(KVQ_ERR_SHAPE, "tensor too large");
+  if ((BH * n + 255) / 256 * 64 >= ((int64_t)1 << 31)) return fail(KVQ_ERR_SHAPE, "too many rows");
+  kvq::KiviArgs a{};
+  a.keys = const_cast<uint16_t *>(keys);  // read only: packed mode writes no reconstruction
+  a.values = const_cast<uint16_t *>(values);
+  a.k_codes = k_codes;
+  a.v_codes = v_codes;
+  a.k_s16 = k_scale;
+  a.k_z16 = k_zero;
+  a.v_s16 = v_scale;
+  a.v_z16 = v_zero;
+  a.BH = BH;
+  a.S_cap = S_cap;
+  a.D = D;
+  a.lo = lo;
+  a.hi = hi;
+  a.bits = bits;
+  a.gs = group_size;
+  a.eps = eps;
+  a.packed = 1;
+  a.code_rows = S_cap;
+  a.code_t0 = 0;
+  a.kgrp_rows = (int32_t)(((int64_t)S_cap + group_size - 1) / group_size);
+  a.kgrp0 = lo / group_size;
+  return hip_status(kvq::launch_kivi(a, (hipStream_t)stream), "kvq_kivi_pack launch");
+}
+
+int kvq_kivi_unpack(const uint8_t *k_codes, const uint16_t *k_scale, const uint16_t *k_zero, const uint8_t *v_codes,
+                    const uint16_t *v_scale, const uint16_t *v_zero, int32_t B, int32_t H, int32_t S_cap, int32_t D,
+                    int32_t lo, int32_t hi, int32_t bits, int32_t group_size, uint16_t *k_out, uint16_t *v_out,
+                    void *stream) {
+  if (!k_out && !v_out) return fail(KVQ_ERR_NULL, "neither key nor value output given");
+  if (k_out && (!k_codes || !k_scale || !k_zero)) return fail(KVQ_ERR_NULL, "key codes, scale and zero are required");
+  if (v_out && (!v_codes || !v_scale || !v_zero))
+    return fail(KVQ_ERR_NULL, "value codes, scale and zero are required");
+  if (bits != 2 && bits != 4 && bits != 8) return fail(KVQ_ERR_BITS, "bits=%d is not one of 2, 4, 8", bits);
+  if (B < 0 || H < 0 || S_cap < 0 || D <= 0) return fail(KVQ_ERR_SHAPE, "bad B/H/S_cap/D");
+  if (lo < 0 || hi < lo || hi > S_cap) return fail(KVQ_ERR_SHAPE, "need 0 <= lo <= hi <= S_cap");
+  if (group_size <= 0 || group_size % 8 || D % 8)
+    return fail(KVQ_ERR_SHAPE, "packed storage needs D %% 8 == 0 and group_size a positive multiple of 8");
+  for (const void *p : {(const void *)k_codes, (const void *)v_codes, (const void *)k_scale, (const void *)k_zero,
+                        (const void *)v_scale, (const void *)v_zero, (const void *)k_out, (const void *)v_out})
+    if (p && !aligned(p, 16)) return fail(KVQ_ERR_ALIGN, "packed KIVI tensors need 16-byte alignment");
+  const int64_t BH = (int64_t)B * H;
+  if (hi == lo || BH == 0) return ok();
+  if (BH * S_cap * D >= ((int64_t)1 << 46)) return fail(KVQ_ERR_SHAPE, "tensor too large");
+  if ((int64_t)(hi - lo) * (D / 8) >= ((int64_t)1 << 31) - 256 || (BH + 65534) / 65535 > 65535)
+    return fail(KVQ_ERR_SHAPE, "too many rows");
+  kvq::KiviUnpackArgs a{};
+  a.BH = BH;
+  a.S_cap = S_cap;
+  a.D = D;
+  a.lo = lo;
+  a.hi = hi;
+  a.bits = bits;
+  a.gs = group_size;
+  for (int side = 0; side < 2; ++side) {
+    uint16_t *out = side ? v_out : k_out;
+    if (!out) continue;
+    a.codes = side ? v_codes : k_codes;
+    a.scale = side ? v_scale : k_scale;
+    a.zero = side ? v_zero : k_zero;
+    a.out = out;
+    a.per_channel = side == 0;
+    const int rc = hip_status(kvq::launch_kivi_unpack(a, (hipStream_t)stream), "kvq_kivi_unpack launch");
+    if (rc) return rc;
+  }
+  return ok();
 }
 
 // ------------------------------------------------------------------ NUQ

@@ -34,15 +34,31 @@ hipError_t launch_sym_quant(const SymQuantArgs &a, int bits, int n_layers, hipSt
 hipError_t launch_sym_dequant(const SymDequantArgs &a, int bits, int n_layers, hipStream_t st);
 
 struct KiviArgs {
-  uint16_t *keys, *values;         // fp16 [B][H][S_cap][D], in place on [lo, hi)
-  uint8_t *k_codes, *v_codes;      // optional
-  float *k_scale, *k_min, *v_scale, *v_min;
+  uint16_t *keys, *values;         // fp16 [B][H][S_cap][D], in place on [lo, hi) (read only when packed)
+  uint8_t *k_codes, *v_codes;      // optional (required when packed)
+  float *k_scale, *k_min, *v_scale, *v_min;        // binary32 parameters (round trip)
+  uint16_t *k_s16, *k_z16, *v_s16, *v_z16;         // fp16 parameters (packed)
   int64_t BH;
   int32_t S_cap, D, lo, hi, bits, gs;
   float eps;
+  int32_t packed;      // 1: fp16 parameters (scale rounded toward zero), no reconstruction written
+  int32_t code_rows;   // code / value-parameter rows per (b, h): hi - lo, or S_cap when packed
+  int32_t code_t0;     // token of row 0: lo, or 0 when packed
+  int32_t kgrp_rows;   // key parameter groups per (b, h): ceil((hi-lo)/gs), or ceil(S_cap/gs)
+  int32_t kgrp0;       // group index of the first group (0, or lo/gs when packed)
 };
 
 hipError_t launch_kivi(const KiviArgs &a, hipStream_t st);
+
+struct KiviUnpackArgs {
+  const uint8_t *codes;            // [BH][S_cap][D*bits/8]
+  const uint16_t *scale, *zero;    // fp16: keys [BH][ceil(S_cap/gs)][D], values [BH][S_cap][ceil(D/gs)]
+  uint16_t *out;                   // fp16 [BH][S_cap][D], tokens [lo, hi) written
+  int64_t BH;
+  int32_t S_cap, D, lo, hi, bits, gs, per_channel;
+  int32_t chunk_shift, gs_shift;   // log2(D/8), log2(gs) when powers of two, else -1 (set by the launcher)
+};
+hipError_t launch_kivi_unpack(KiviUnpackArgs a, hipStream_t st);
 
 struct NuqArgs {
   const uint16_t *keys, *values;   // fp16 [BH][S][D]

@@ -18,6 +18,13 @@
 //  values lane l holds channels 8*(l % CL).. of token row l / CL; a group of
 //         gs channels is gs/8 consecutive lanes, reduced with DPP.
 // Other shapes use one-thread-per-(vector, group) generic kernels.
+//
+// Packed storage (the b-bit codes and fp16 (scale, zero) per group that the
+// page's byte accounting charges, module docstring and _quantized_bytes):
+// the same kernels with `packed` set round each scale toward zero to fp16
+// (at least 2^-24) before computing the codes, write fp16 parameters and
+// codes indexed by absolute token, and leave the fp16 input untouched;
+// kivi_unpack rebuilds fp16(code*scale + zero) from them.
 #include "common.h"
 #include "kernels.h"
 
@@ -85,6 +92,15 @@ __device__ __forceinline__ float recip(float s) {
 template <int BITS>
 __device__ __forceinline__ float kivi_scale_c(float mn, float mx, float eps) {
   return fmaxf(div_levels<BITS>(mx - mn), eps);
+}
+
+// a binary32 scale rounded toward zero to fp16, at least 2^-24 (packed
+// storage: the top level zero + levels*scale stays within the group's max)
+__device__ __forceinline__ float scale_p16(float s) {
+  uint16_t h = f2h(s);
+  if (h2f(h) > s) --h;  // s > 0: one step down the bit pattern
+  if (h == 0) h = 1;
+  return h2f(h);
 }
 
 // Eight elements at a time: the quotients a[i]*inv[i] and their tie flags
@@ -202,10 +218,11 @@ __global__ __launch_bounds__(256) void kivi_keys_fast(KiviArgs a) {
     mn[i] = kunkey_f((kmn[i / 2] >> (16 * (i & 1))) & 0xffffu);
     const float mx = kunkey_f((kmx[i / 2] >> (16 * (i & 1))) & 0xffffu);
     sc[i] = kivi_scale_c<BITS>(mn[i], mx, a.eps);
+    if (a.packed) sc[i] = scale_p16(sc[i]);
     inv[i] = recip(sc[i]);
   }
 
-  const int64_t nrow0 = bh * n + (t0 - a.lo);  // row of token t0 in the [BH][n] code layout
+  const int64_t nrow0 = bh * a.code_rows + (t0 - a.code_t0);  // code row of token t0
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
     if (!ok[j]) continue;
@@ -222,16 +239,27 @@ __global__ __launch_bounds__(256) void kivi_keys_fast(KiviArgs a) {
       if (i & 1) o[i / 2] |= r << 16; else o[i / 2] = r;
     }
     const int t = tr + TPI * j;
-    *reinterpret_cast<uint4 *>(base + (size_t)t * D) = make_uint4(o[0], o[1], o[2], o[3]);
+    if (!a.packed) *reinterpret_cast<uint4 *>(base + (size_t)t * D) = make_uint4(o[0], o[1], o[2], o[3]);
     if (a.k_codes)
       store_codes8<BITS>(a.k_codes + (size_t)(nrow0 + t) * (D * BITS / 8) + ch * BITS, c);
   }
   if (tr == 0) {
-    const size_t p = ((size_t)bh * ng + g) * D + ch * 8;
+    const size_t p = ((size_t)bh * a.kgrp_rows + a.kgrp0 + g) * D + ch * 8;
+    if (a.packed) {
+      uint32_t sw[4], zw[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (a.k_scale) a.k_scale[p + i] = sc[i];
-      if (a.k_min) a.k_min[p + i] = mn[i] + 0.0f;
+      for (int i = 0; i < 4; ++i) {
+        sw[i] = (uint32_t)f2h(sc[2 * i]) | ((uint32_t)f2h(sc[2 * i + 1]) << 16);
+        zw[i] = (uint32_t)f2h(mn[2 * i] + 0.0f) | ((uint32_t)f2h(mn[2 * i + 1] + 0.0f) << 16);
+      }
+      *reinterpret_cast<uint4 *>(a.k_s16 + p) = make_uint4(sw[0], sw[1], sw[2], sw[3]);
+      *reinterpret_cast<uint4 *>(a.k_z16 + p) = make_uint4(zw[0], zw[1], zw[2], zw[3]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (a.k_scale) a.k_scale[p + i] = sc[i];
+        if (a.k_min) a.k_min[p + i] = mn[i] + 0.0f;
+      }
     }
   }
 }
@@ -264,24 +292,33 @@ __global__ __launch_bounds__(256) void kivi_keys_generic(KiviArgs a) {
       mn[i] = fminf(mn[i], x);
       mx[i] = fmaxf(mx[i], x);
     }
-  for (int i = 0; i < C; ++i) sc[i] = kivi_scale(mn[i], mx[i], lev, a.eps);
+  for (int i = 0; i < C; ++i) {
+    sc[i] = kivi_scale(mn[i], mx[i], lev, a.eps);
+    if (a.packed) sc[i] = scale_p16(sc[i]);
+  }
   const int cpr = D * a.bits / 8;
   for (int t = t0; t < t1; ++t) {
     uint64_t packed = 0;
     for (int i = 0; i < C; ++i) {
       uint32_t c;
-      col[(size_t)t * D + i] = kivi_elem(h2f(col[(size_t)t * D + i]), mn[i], sc[i], lev, c);
+      const uint16_t r = kivi_elem(h2f(col[(size_t)t * D + i]), mn[i], sc[i], lev, c);
+      if (!a.packed) col[(size_t)t * D + i] = r;
       packed |= (uint64_t)c << (a.bits * i);
     }
     if (C == 8 && a.k_codes) {
-      uint8_t *dst = a.k_codes + ((size_t)bh * n + (t - a.lo)) * cpr + ck * a.bits;
+      uint8_t *dst = a.k_codes + ((size_t)bh * a.code_rows + (t - a.code_t0)) * cpr + ck * a.bits;
       for (int b = 0; b < a.bits; ++b) dst[b] = (uint8_t)(packed >> (8 * b));
     }
   }
   for (int i = 0; i < C; ++i) {
-    const size_t p = ((size_t)bh * ng + g) * D + ck * C + i;
-    if (a.k_scale) a.k_scale[p] = sc[i];
-    if (a.k_min) a.k_min[p] = mn[i] + 0.0f;  // a zero minimum is exported as +0
+    const size_t p = ((size_t)bh * a.kgrp_rows + a.kgrp0 + g) * D + ck * C + i;
+    if (a.packed) {
+      a.k_s16[p] = f2h(sc[i]);
+      a.k_z16[p] = f2h(mn[i] + 0.0f);
+    } else {
+      if (a.k_scale) a.k_scale[p] = sc[i];
+      if (a.k_min) a.k_min[p] = mn[i] + 0.0f;  // a zero minimum is exported as +0
+    }
   }
 }
 
@@ -326,7 +363,8 @@ __global__ __launch_bounds__(256) void kivi_values_fast(KiviArgs a) {
     kmn = group_min_u32<LPG>(kmn);
     kmx = group_max_u32<LPG>(kmx);
     const float mn = kunkey_f(kmn), mx = kunkey_f(kmx);
-    const float sc = kivi_scale_c<BITS>(mn, mx, a.eps);
+    float sc = kivi_scale_c<BITS>(mn, mx, a.eps);
+    if (a.packed) sc = scale_p16(sc);
     const float inv = recip(sc);
     uint32_t o[4], c[8];
     float ad[8], scv[8], invv[8], cf[8];
@@ -342,14 +380,20 @@ __global__ __launch_bounds__(256) void kivi_values_fast(KiviArgs a) {
       c[i] = (uint32_t)cf[i];
       const uint32_t r = f2h(cf[i] * sc + mn);
       if (i & 1) o[i / 2] |= r << 16; else o[i / 2] = r;
-    }    if (tok[u] < n) {
-      const size_t rowid = (size_t)bh * n + tok[u];  // row of the [BH][n] code layout
-      *reinterpret_cast<uint4 *>(vb + (size_t)tok[u] * D) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+    if (tok[u] < n) {
+      const size_t rowid = (size_t)bh * a.code_rows + (a.lo + tok[u] - a.code_t0);  // code row
+      if (!a.packed) *reinterpret_cast<uint4 *>(vb + (size_t)tok[u] * D) = make_uint4(o[0], o[1], o[2], o[3]);
       if (a.v_codes) store_codes8<BITS>(a.v_codes + rowid * (D * BITS / 8) + ch * BITS, c);
       if (ch % LPG == 0) {
         const size_t p = rowid * ng + ch / LPG;
-        if (a.v_scale) a.v_scale[p] = sc;
-        if (a.v_min) a.v_min[p] = mn + 0.0f;
+        if (a.packed) {
+          a.v_s16[p] = f2h(sc);
+          a.v_z16[p] = f2h(mn + 0.0f);
+        } else {
+          if (a.v_scale) a.v_scale[p] = sc;
+          if (a.v_min) a.v_min[p] = mn + 0.0f;
+        }
       }
     }
   }
@@ -363,9 +407,10 @@ __global__ __launch_bounds__(256) void kivi_values_generic(KiviArgs a) {
   const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (id >= a.BH * n * ng) return;
   const int g = (int)(id % ng);
-  const int64_t row = id / ng;  // bh * n + (t - lo)
-  const int64_t bh = row / n;
-  const int t = a.lo + (int)(row - bh * n);
+  const int64_t row0 = id / ng;  // bh * n + (t - lo)
+  const int64_t bh = row0 / n;
+  const int t = a.lo + (int)(row0 - bh * n);
+  const int64_t row = bh * a.code_rows + (t - a.code_t0);  // code / parameter row
   const int d0 = g * a.gs, d1 = min(d0 + a.gs, D);
   const float lev = (float)((1 << a.bits) - 1);
   uint16_t *r = a.values + ((size_t)bh * a.S_cap + t) * D;
@@ -375,14 +420,16 @@ __global__ __launch_bounds__(256) void kivi_values_generic(KiviArgs a) {
     mn = fminf(mn, x);
     mx = fmaxf(mx, x);
   }
-  const float sc = kivi_scale(mn, mx, lev, a.eps);
+  float sc = kivi_scale(mn, mx, lev, a.eps);
+  if (a.packed) sc = scale_p16(sc);
   // codes (only requested when D % 8 == 0 and gs % 8 == 0): the group covers
   // whole 8-channel chunks, each chunk is `bits` whole bytes
   uint8_t *cr = a.v_codes ? a.v_codes + (size_t)row * (D * a.bits / 8) : nullptr;
   uint64_t packed = 0;
   for (int d = d0; d < d1; ++d) {
     uint32_t c;
-    r[d] = kivi_elem(h2f(r[d]), mn, sc, lev, c);
+    const uint16_t rec = kivi_elem(h2f(r[d]), mn, sc, lev, c);
+    if (!a.packed) r[d] = rec;
     packed |= (uint64_t)c << (a.bits * (d % 8));
     if (cr && (d % 8 == 7 || d == d1 - 1)) {
       uint8_t *dst = cr + (d / 8) * a.bits;
@@ -391,8 +438,84 @@ __global__ __launch_bounds__(256) void kivi_values_generic(KiviArgs a) {
     }
   }
   const size_t p = (size_t)row * ng + g;
-  if (a.v_scale) a.v_scale[p] = sc;
-  if (a.v_min) a.v_min[p] = mn + 0.0f;
+  if (a.packed) {
+    a.v_s16[p] = f2h(sc);
+    a.v_z16[p] = f2h(mn + 0.0f);
+  } else {
+    if (a.v_scale) a.v_scale[p] = sc;
+    if (a.v_min) a.v_min[p] = mn + 0.0f;
+  }
+}
+
+// ------------------------------------------------------------------ unpack
+// One thread per (b, h, 8 consecutive tokens, 8 channels): BITS code bytes
+// per token, the group's fp16 (scale, zero), 8 outputs
+// fp16(RN32(code*scale) + zero) per token in one 16-byte store. Keys
+// reload their group's parameters only when the group changes (never, when
+// lo is a multiple of 8: the group size is); values take one pair per token
+// and 8 channels.
+constexpr int KIVI_UNPACK_ROWS = 8;
+template <int BITS, bool PERCH>
+__global__ __launch_bounds__(256) void kivi_unpack(KiviUnpackArgs a) {
+  // grid: x = (8-token block, chunk) pairs of one (b, h) slice, y (+ 65535 z) = (b, h)
+  const int chunks = a.D / 8, n = a.hi - a.lo;
+  const int nblk = (n + KIVI_UNPACK_ROWS - 1) / KIVI_UNPACK_ROWS;
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (uint32_t)(nblk * chunks)) return;
+  const int64_t bh = (int64_t)blockIdx.z * 65535 + blockIdx.y;
+  if (bh >= a.BH) return;
+  const int k = a.chunk_shift >= 0 ? (int)(i & (uint32_t)(chunks - 1)) : (int)(i % (uint32_t)chunks);
+  const int tb = (int)(a.chunk_shift >= 0 ? i >> a.chunk_shift : i / (uint32_t)chunks);
+  const int t0 = a.lo + tb * KIVI_UNPACK_ROWS;
+  const int rows = min(KIVI_UNPACK_ROWS, a.hi - t0);
+  const int64_t row0 = bh * a.S_cap + t0;
+  const int ngv = (a.D + a.gs - 1) / a.gs;
+  float s[8], z[8];
+  int cur_tg = -1;  // key group whose parameters s, z hold
+  const int64_t kg0 = bh * ((a.S_cap + a.gs - 1) / a.gs);
+  const int vg = a.gs_shift >= 0 ? (8 * k) >> a.gs_shift : (8 * k) / a.gs;
+#pragma unroll
+  for (int r = 0; r < KIVI_UNPACK_ROWS; ++r) {
+    if (r >= rows) break;
+    const int64_t row = row0 + r;
+    if constexpr (PERCH) {  // the 8 tokens share a group unless lo % 8 != 0
+      const int tg = a.gs_shift >= 0 ? (t0 + r) >> a.gs_shift : (t0 + r) / a.gs;
+      if (tg != cur_tg) {
+        cur_tg = tg;
+        const int64_t p = (kg0 + tg) * a.D + 8 * k;
+        const uint4 sv = *reinterpret_cast<const uint4 *>(a.scale + p);
+        const uint4 zv = *reinterpret_cast<const uint4 *>(a.zero + p);
+        const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w}, zw[4] = {zv.x, zv.y, zv.z, zv.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          s[e] = (e & 1) ? hi_h2f(sw[e / 2]) : lo_h2f(sw[e / 2]);
+          z[e] = (e & 1) ? hi_h2f(zw[e / 2]) : lo_h2f(zw[e / 2]);
+        }
+      }
+    }
+    const uint8_t *cp = a.codes + row * (a.D * BITS / 8) + k * BITS;
+    uint64_t cw;
+    if constexpr (BITS == 2) cw = *reinterpret_cast<const uint16_t *>(cp);
+    else if constexpr (BITS == 4) cw = *reinterpret_cast<const uint32_t *>(cp);
+    else cw = *reinterpret_cast<const uint64_t *>(cp);
+    if constexpr (!PERCH) {
+      const float s0 = h2f(a.scale[row * ngv + vg]), z0 = h2f(a.zero[row * ngv + vg]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        s[e] = s0;
+        z[e] = z0;
+      }
+    }
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float c = (float)(uint32_t)((cw >> (BITS * e)) & ((1u << BITS) - 1));
+      const float prod = c * s[e];
+      const uint32_t h = f2h(prod + z[e]);
+      if (e & 1) o[e / 2] |= h << 16; else o[e / 2] = h;
+    }
+    *reinterpret_cast<uint4 *>(a.out + row * a.D + 8 * k) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
 }
 
 // ------------------------------------------------------------------ launch
@@ -524,6 +647,33 @@ hipError_t launch_kivi(const KiviArgs &a, hipStream_t st) {
     case 2: return launch_bits<2>(a, st);
     case 4: return launch_bits<4>(a, st);
     default: return launch_bits<8>(a, st);
+  }
+}
+
+namespace {
+template <int BITS>
+hipError_t unpack_b(const KiviUnpackArgs &a, hipStream_t st) {
+  const int64_t per_bh = (int64_t)((a.hi - a.lo + KIVI_UNPACK_ROWS - 1) / KIVI_UNPACK_ROWS) * (a.D / 8);
+  const dim3 grid((unsigned)((per_bh + 255) / 256), (unsigned)(a.BH < 65535 ? a.BH : 65535),
+                  (unsigned)((a.BH + 65534) / 65535));
+  if (a.per_channel) hipLaunchKernelGGL((kivi_unpack<BITS, true>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((kivi_unpack<BITS, false>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_kivi_unpack(KiviUnpackArgs a, hipStream_t st) {
+  auto log2_or = [](int v) {
+    int s = 0;
+    while ((1 << s) < v) ++s;
+    return (1 << s) == v ? s : -1;
+  };
+  a.chunk_shift = log2_or(a.D / 8);
+  a.gs_shift = log2_or(a.gs);
+  switch (a.bits) {
+    case 2: return unpack_b<2>(a, st);
+    case 4: return unpack_b<4>(a, st);
+    default: return unpack_b<8>(a, st);
   }
 }
 

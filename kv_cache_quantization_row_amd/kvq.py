@@ -51,6 +51,8 @@ _SIGS = {
     "kvq_kivi_boundary": (_L, [_L, _I, _I]),
     "kvq_kivi_quant_dequant": (C.c_int, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F,
                                          _P, _P, _P, _P, _P, _P, _P]),
+    "kvq_kivi_pack": (C.c_int, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _P]),
+    "kvq_kivi_unpack": (C.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
     "kvq_nuq_workspace_bytes": (_L, [_I, _I, _I, _I, _I, _I, _F, _I]),
     "kvq_nuq_outlier_bound": (_L, [_I, _I, _I, _I, _I, _F, _I, _I]),
     "kvq_nuq_fit_quant": (C.c_int, [_P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I,
@@ -188,6 +190,38 @@ def kvq_kivi_quant_dequant(keys, values, lo: int, hi: int, bits: int, group_size
     _err(lib().kvq_kivi_quant_dequant(_ptr(keys), _ptr(values), B, H, S_cap, D, lo, hi, bits,
                                       group_size, eps, _ptr(k_codes), _ptr(k_scale), _ptr(k_min),
                                       _ptr(v_codes), _ptr(v_scale), _ptr(v_min), _stream(stream)))
+
+
+def kivi_param_shape(B, H, S_cap, D, per_channel, group_size):
+    """Shape of the fp16 scale / zero arrays of packed KIVI storage."""
+    if per_channel:
+        return (B, H, (S_cap + group_size - 1) // group_size, D)
+    return (B, H, S_cap, (D + group_size - 1) // group_size)
+
+
+def kvq_kivi_pack(keys, values, lo: int, hi: int, bits: int, group_size: int = 32, eps: float = 1e-8,
+                  k_codes=None, k_scale=None, k_zero=None, v_codes=None, v_scale=None, v_zero=None,
+                  stream=None):
+    """keys/values fp16 [B][H][S_cap][D] (either None); codes uint8
+    [B][H][S_cap][D*bits/8]; scale/zero int16 holding fp16 bits, shapes of
+    kivi_param_shape."""
+    x = keys if keys is not None else values
+    _dev(keys, values, k_codes, k_scale, k_zero, v_codes, v_scale, v_zero)
+    B, H, S_cap, D = (int(s) for s in x.shape)
+    _err(lib().kvq_kivi_pack(_ptr(keys), _ptr(values), B, H, S_cap, D, lo, hi, bits, group_size, eps,
+                             _ptr(k_codes), _ptr(k_scale), _ptr(k_zero), _ptr(v_codes), _ptr(v_scale),
+                             _ptr(v_zero), _stream(stream)))
+
+
+def kvq_kivi_unpack(k_codes, k_scale, k_zero, v_codes, v_scale, v_zero, lo: int, hi: int, bits: int,
+                    group_size: int, k_out, v_out, stream=None):
+    """Tokens [lo, hi) into k_out / v_out, fp16 [B][H][S_cap][D] (either None)."""
+    o = k_out if k_out is not None else v_out
+    _dev(k_codes, k_scale, k_zero, v_codes, v_scale, v_zero, k_out, v_out)
+    B, H, S_cap, D = (int(s) for s in o.shape)
+    _err(lib().kvq_kivi_unpack(_ptr(k_codes), _ptr(k_scale), _ptr(k_zero), _ptr(v_codes), _ptr(v_scale),
+                               _ptr(v_zero), B, H, S_cap, D, lo, hi, bits, group_size, _ptr(k_out),
+                               _ptr(v_out), _stream(stream)))
 
 
 # ------------------------------------------------------------------ NUQ

@@ -157,6 +157,38 @@ def test_kivi_validation_errors():
     assert _kivi(B=0) == kvq.KVQ_OK
 
 
+def _kpack(k=FAKE, v=FAKE, B=2, H=2, S=64, D=64, lo=0, hi=32, bits=2, gs=32, eps=1e-8, kc=FAKE, ks=FAKE,
+           kz=FAKE, vc=FAKE, vs=FAKE, vz=FAKE):
+    return kvq.lib().kvq_kivi_pack(k, v, B, H, S, D, lo, hi, bits, gs, eps, kc, ks, kz, vc, vs, vz, None)
+
+
+def _kunpack(kc=FAKE, ks=FAKE, kz=FAKE, vc=FAKE, vs=FAKE, vz=FAKE, B=2, H=2, S=64, D=64, lo=0, hi=32, bits=4,
+             gs=32, ko=FAKE, vo=FAKE):
+    return kvq.lib().kvq_kivi_unpack(kc, ks, kz, vc, vs, vz, B, H, S, D, lo, hi, bits, gs, ko, vo, None)
+
+
+def test_kivi_packed_validation_errors():
+    assert _kpack(bits=3) == kvq.KVQ_ERR_BITS
+    assert _kpack(k=None, v=None) == kvq.KVQ_ERR_NULL
+    assert _kpack(kz=None) == kvq.KVQ_ERR_NULL
+    assert _kpack(v=FAKE, vc=None) == kvq.KVQ_ERR_NULL
+    assert _kpack(lo=8, hi=40) == kvq.KVQ_ERR_SHAPE            # key groups start at token 0
+    assert _kpack(gs=12) == kvq.KVQ_ERR_SHAPE                  # group size a multiple of 8
+    assert _kpack(D=60) == kvq.KVQ_ERR_SHAPE
+    assert _kpack(hi=65) == kvq.KVQ_ERR_SHAPE
+    assert _kpack(eps=0.0) == kvq.KVQ_ERR_ARG
+    assert _kpack(ks=FAKE + 2) == kvq.KVQ_ERR_ALIGN
+    assert _kpack(lo=32, hi=32) == kvq.KVQ_OK
+    assert _kpack(B=0) == kvq.KVQ_OK
+    assert _kunpack(bits=5) == kvq.KVQ_ERR_BITS
+    assert _kunpack(ko=None, vo=None) == kvq.KVQ_ERR_NULL
+    assert _kunpack(kc=None) == kvq.KVQ_ERR_NULL
+    assert _kunpack(vo=FAKE + 8) == kvq.KVQ_ERR_ALIGN
+    assert _kunpack(lo=40, hi=32) == kvq.KVQ_ERR_SHAPE
+    assert _kunpack(gs=0) == kvq.KVQ_ERR_SHAPE
+    assert _kunpack(hi=16, lo=16) == kvq.KVQ_OK
+
+
 def test_binding_refuses_host_tensors():
     import torch
     lay = kvq.layout(1, 4, 16, 4, 256, 6)
