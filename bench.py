@@ -365,7 +365,7 @@ class Nuq:
     def __init__(self, torch, args):
         self.torch = torch
         self.BH, self.S, self.D, self.bits = 32, 4096, 128, 3
-        self.frac, self.iters, self.ns, self.n_dec = 0.01, 8, 4, 64
+        self.frac, self.iters, self.ns, self.n_dec = 0.01, args.lloyd_iters, 4, 64
         self.copies = 16
         self.name = "nuq"
 
@@ -424,7 +424,7 @@ class Nuq:
 
     def config(self):
         return {"workload": "KVQuant-style NUQ 3-bit: batch 4 x 8 KV heads, D=128, 4096-token prefill "
-                            "(1%% outliers, 8 Lloyd iterations, 4 sinks) + %d decode calls" % self.n_dec,
+                            "(1%% outliers, %d Lloyd iterations, 4 sinks) + %d decode calls" % (self.iters, self.n_dec),
                 "bits": self.bits, "outlier_fraction": self.frac, "lloyd_iters": self.iters,
                 "n_sink": self.ns, "rotation_copies": self.copies}
 
@@ -734,6 +734,7 @@ def main():
     ap.add_argument("--prefill-tokens", type=int, default=32768)
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--decode-steps-long", type=int, default=1024)
+    ap.add_argument("--lloyd-iters", type=int, default=8, help="Lloyd iterations of the NUQ fits (nuq workload)")
     ap.add_argument("--cpu-tokens", type=int, default=65536)
     ap.add_argument("--attn-group", type=int, default=4, help="query heads per KV head (attn_decode)")
     ap.add_argument("--page-order", default="random", choices=["random", "identity"],

@@ -160,15 +160,20 @@ class NuqCache:
     """KVQuant-style NUQ cache: the first call of a sequence fits and freezes
     the per-channel key levels and |key| thresholds (and keeps its first
     n_sink tokens exact); every call fits fresh per-token value levels; the
-    buffers hold the dequantized K/V. Byte accounting (a reading of the
-    page's description): codes at `bits` per element, fp32 level tables,
-    fp16 key thresholds, 6 bytes per outlier (fp16 value + int32 position),
+    buffers hold the dequantized K/V. With refit_interval = N > 0 the key
+    tables are fit again from the tokens of every N-th call after the first
+    ("re-fit every N decode steps from the most recent token",
+    ["veloxquant_mlx.cache.kvquant_cache module", level lifecycle]).
+    Byte accounting (a reading of the page's description): codes at `bits`
+    per element, fp32 level tables and fp16 key thresholds (one key table
+    held at a time), 6 bytes per outlier (fp16 value + int32 position),
     fp16 sink tokens."""
 
     def __init__(self, bits: int = 3, outlier_fraction: float = 0.01, lloyd_iters: int = 8, n_sink: int = 4,
-                 step: int = 256):
+                 step: int = 256, refit_interval: int = 0):
         self.bits, self.outlier_fraction, self.lloyd_iters, self.n_sink, self.step = (
             bits, outlier_fraction, lloyd_iters, n_sink, step)
+        self.refit_interval = int(refit_interval)
         self._reset()
 
     def _reset(self):
@@ -180,6 +185,7 @@ class NuqCache:
         self.sink_kept = 0
         self._kc = self._vc = self._kf = self._vf = 0
         self._shape = None
+        self._since_fit = 0  # calls since the key tables were fit
 
     def update_and_fetch(self, keys, values):
         import torch
@@ -189,8 +195,9 @@ class NuqCache:
             raise kvq.KvqError(kvq.KVQ_ERR_SHAPE, "batch, heads and head_dim are fixed for a cache")
         self._shape = (B, H, D)
         BH, L, d = B * H, 1 << self.bits, keys.device
-        fit = self.key_levels is None
-        if fit:
+        first = self.key_levels is None
+        fit = first or (self.refit_interval > 0 and self._since_fit + 1 >= self.refit_interval)
+        if first:
             self.key_levels = torch.zeros((BH, D, L), dtype=torch.float32, device=d)
             self.key_thresh = torch.zeros((BH, D), dtype=torch.int16, device=d)
         k = keys.reshape(BH, S, D).contiguous()
@@ -217,7 +224,8 @@ class NuqCache:
         self.last_outliers = ((lists[0][: n_out[0]], lists[1][: n_out[0]]), (lists[2][: n_out[1]], lists[3][: n_out[1]]))
         codes = BH * S * D * self.bits // 8
         sink_bytes = BH * sinks * D * 2
-        self._kc += codes + n_out[0] * 6 + sink_bytes + (BH * D * (L * 4 + 2) if fit else 0)
+        self._kc += codes + n_out[0] * 6 + sink_bytes + (BH * D * (L * 4 + 2) if first else 0)
+        self._since_fit = 0 if fit else self._since_fit + 1
         self._vc += codes + n_out[1] * 6 + sink_bytes + BH * S * L * 4
         self._kf += BH * S * D * 2
         self._vf += BH * S * D * 2

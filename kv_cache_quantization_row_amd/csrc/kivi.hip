@@ -506,12 +506,16 @@ __global__ __launch_bounds__(256) void kivi_unpack(KiviUnpackArgs a) {
         z[e] = z0;
       }
     }
+    // code*scale is exact in binary32 (at most 8 + 11 significant bits), so
+    // RN32(RN32(code*scale) + zero) is one fma
+    const uint32_t cw0 = (uint32_t)cw, cw1 = (uint32_t)(cw >> 32);
     uint32_t o[4];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float c = (float)(uint32_t)((cw >> (BITS * e)) & ((1u << BITS) - 1));
-      const float prod = c * s[e];
-      const uint32_t h = f2h(prod + z[e]);
+      float c;
+      if constexpr (BITS == 8) c = (float)(uint32_t)(uint8_t)((e < 4 ? cw0 : cw1) >> (8 * (e % 4)));
+      else c = (float)__builtin_amdgcn_ubfe(cw0, BITS * e, BITS);
+      const uint32_t h = f2h(__builtin_fmaf(c, s[e], z[e]));
       if (e & 1) o[e / 2] |= h << 16; else o[e / 2] = h;
     }
     *reinterpret_cast<uint4 *>(a.out + row * a.D + 8 * k) = make_uint4(o[0], o[1], o[2], o[3]);

@@ -14,8 +14,11 @@ KiviCacheModel: ["veloxquant_mlx.cache.kivi_cache", KIVIKVCache] tokens age
   fp16 (scale, zero) pair per group (_quantized_bytes / _account_bytes).
 NuqCacheModel: ["veloxquant_mlx.cache.kvquant_cache module", KVQuantKVCache]
   the first call of a sequence fits and freezes the key tables and keeps
-  its first n_sink tokens exact; later calls reuse the frozen key state;
-  trimming to empty starts over; a partial trim keeps the key state.
+  its first n_sink tokens exact; later calls reuse the frozen key state,
+  except that with refit_interval = N > 0 every N-th call after the first
+  fits the key tables again from that call's tokens (level lifecycle: levels
+  re-fit every N decode steps from the most recent token); trimming to
+  empty starts over; a partial trim keeps the key state.
 """
 from __future__ import annotations
 
@@ -85,8 +88,9 @@ class KiviCacheModel:
 
 
 class NuqCacheModel:
-    def __init__(self, bits=3, outlier_fraction=0.01, lloyd_iters=8, n_sink=4):
+    def __init__(self, bits=3, outlier_fraction=0.01, lloyd_iters=8, n_sink=4, refit_interval=0):
         self.bits, self.frac, self.iters, self.n_sink = bits, outlier_fraction, lloyd_iters, n_sink
+        self.refit_interval = refit_interval
         self.start()
 
     def start(self):
@@ -95,6 +99,7 @@ class NuqCacheModel:
         self.outlier_count = 0
         self.sink_kept = 0
         self.last = None
+        self.since_fit = 0
 
     @property
     def offset(self):
@@ -103,11 +108,14 @@ class NuqCacheModel:
     def update(self, keys, values):
         B, H, S, D = keys.shape
         first = self.key_levels is None
+        fit = first or (self.refit_interval > 0 and self.since_fit + 1 == self.refit_interval)
         r = nuq_fit_quant(keys.reshape(B * H, S, D), values.reshape(B * H, S, D), self.offset, self.bits,
-                          self.frac, self.iters, self.n_sink, int(first), self.key_levels, self.key_thresh)
-        if first:
+                          self.frac, self.iters, self.n_sink, int(fit), self.key_levels, self.key_thresh)
+        if fit:
             self.key_levels, self.key_thresh = r["key_levels"], r["key_thresh"]
+        if first:
             self.sink_kept += min(self.n_sink, S)
+        self.since_fit = 0 if fit else self.since_fit + 1
         self.outlier_count += len(r["k_out"][0]) + len(r["v_out"][0])
         kr = r["k_recon"].reshape(B, H, S, D)
         vr = r["v_recon"].reshape(B, H, S, D)

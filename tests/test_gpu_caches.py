@@ -165,3 +165,25 @@ def test_paged_sym_cache_lifecycle(bits):
     check("reuse")
     with pytest.raises(kvq.KvqError):
         append([(4, 40 * P)])
+
+
+@pytest.mark.parametrize("interval", [1, 3])
+def test_nuq_cache_refit_interval(interval):
+    """Key tables fit again from every `interval`-th decode call's tokens."""
+    say("nuq cache refit", interval)
+    d = dev()
+    B, H, D, bits = 1, 4, 64, 3
+    kt = inputs.student_t((B * H, 140, D), 4, seed=41).view(B, H, 140, D)
+    vt = inputs.student_t((B * H, 140, D), 4, seed=42).view(B, H, 140, D)
+    kn, vn = u16(kt), u16(vt)
+    c = caches.NuqCache(bits, 0.02, 8, 4, refit_interval=interval)
+    m = NuqCacheModel(bits, 0.02, 8, 4, refit_interval=interval)
+    t = 0
+    for n in [100] + [1] * 7 + [5, 1]:
+        c.update_and_fetch(kt[:, :, t:t + n].to(d).contiguous(), vt[:, :, t:t + n].to(d).contiguous())
+        m.update(kn[:, :, t:t + n], vn[:, :, t:t + n])
+        t += n
+        assert first_diff(u16(c.keys[:, :, : c.offset]), m.k) is None, ("keys", t)
+        assert first_diff(u16(c.values[:, :, : c.offset]), m.v) is None, ("values", t)
+        assert np.array_equal(c.key_levels.cpu().numpy().view(np.uint32), m.key_levels.view(np.uint32)), t
+        assert np.array_equal(u16(c.key_thresh), m.key_thresh), t

@@ -154,6 +154,21 @@ def test_degenerate_data(case, BH):
         compare(g, r, what="%s frac=%g iters=%d" % (case, frac, iters))
 
 
+@pytest.mark.parametrize("iters", [1, 2, 4, 16])
+def test_lloyd_iteration_counts(iters):
+    """The Lloyd iteration count the pages name as the speed / quality lever."""
+    say("nuq iters", iters)
+    BH, S, D = 4, 300, 128
+    k, v = t4((BH, S, D), 60 + iters), t4((BH, S, D), 61 + iters)
+    g = gpu_nuq(k, v, 0, 3, 0.01, iters, 4, 1)
+    r = oracle.nuq_fit_quant(k, v, 0, 3, 0.01, iters, 4, 1)
+    compare(g, r, what="iters=%d" % iters)
+    kd, vd = t4((BH, 1, D), 70), t4((BH, 1, D), 71)
+    g2 = gpu_nuq(kd, vd, S, 3, 0.01, iters, 4, 0, g["key_levels"], g["key_thresh"])
+    r2 = oracle.nuq_fit_quant(kd, vd, S, 3, 0.01, iters, 4, 0, r["key_levels"], r["key_thresh"])
+    compare(g2, r2, what="decode iters=%d" % iters)
+
+
 def test_long_key_fit_64_chunks():
     """8192 non-sink tokens per key channel: 64 lanes per vector."""
     say("nuq 8192-token key fit")

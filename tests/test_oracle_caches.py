@@ -155,3 +155,47 @@ def test_nuq_partial_trim_keeps_frozen_keys():
                              lev, thr)
     assert np.array_equal(m.k[:, :, 50:51].reshape(2, 1, D), r["k_recon"])
     assert m.sink_kept == 4
+
+
+def test_nuq_refit_interval_refits_from_the_latest_call():
+    """["kvquant_cache module", level lifecycle] with a positive refit
+    interval N the key levels are fit again every N decode steps from the
+    most recent token(s): the tables change exactly at decode calls N, 2N,
+    and equal a fit of that call's tokens alone; in between they are reused;
+    interval 0 never refits."""
+    B, H, D, N = 1, 2, 32, 3
+    k, v = _kv(B, H, 90, D, 9)
+    frozen = NuqCacheModel(3, 0.05, 8, 4, refit_interval=0)
+    m = NuqCacheModel(3, 0.05, 8, 4, refit_interval=N)
+    for c in (frozen, m):
+        c.update(k[:, :, :80], v[:, :, :80])
+    lev0 = m.key_levels.copy()
+    for step in range(1, 8):
+        t = 79 + step
+        prev = m.key_levels.copy()
+        for c in (frozen, m):
+            c.update(k[:, :, t:t + 1], v[:, :, t:t + 1])
+        assert np.array_equal(frozen.key_levels.view(np.uint32), lev0.view(np.uint32))
+        if step % N == 0:
+            r = oracle.nuq_fit_quant(k[:, :, t:t + 1].reshape(2, 1, D), v[:, :, t:t + 1].reshape(2, 1, D), t, 3,
+                                     0.05, 8, 4, 1)
+            assert np.array_equal(m.key_levels.view(np.uint32), r["key_levels"].view(np.uint32))
+            assert not np.array_equal(m.key_levels.view(np.uint32), prev.view(np.uint32))
+        else:
+            assert np.array_equal(m.key_levels.view(np.uint32), prev.view(np.uint32))
+    assert m.sink_kept == frozen.sink_kept == 4
+
+
+def test_nuq_refit_from_one_token_reconstructs_it_exactly():
+    """A per-channel fit over a single sample: no outlier (k = floor(frac*1)
+    = 0), every quantile and every Lloyd level equals the sample, so the
+    token's keys reconstruct exactly."""
+    B, H, D = 1, 2, 32
+    k, v = _kv(B, H, 12, D, 10)
+    m = NuqCacheModel(3, 0.05, 8, 4, refit_interval=1)
+    m.update(k[:, :, :10], v[:, :, :10])
+    m.update(k[:, :, 10:11], v[:, :, 10:11])
+    lev = m.key_levels.reshape(2, D, 8)
+    x = k[:, :, 10].reshape(2, D).view(np.float16).astype(np.float32)
+    assert np.array_equal(lev, np.repeat(x[:, :, None], 8, axis=2))
+    assert np.array_equal(m.k[:, :, 10], k[:, :, 10])
