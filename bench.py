@@ -56,7 +56,7 @@ def measured_traffic(kernel_class):
         names, src = ["sym_dequant_page<%s, 256>" % b], "sym.hip"
     elif kernel_class.startswith("kivi_keys_values_b"):
         b = kernel_class[-1]
-        names, src = ["kivi_keys_fast<%s, 8, 4>" % b, "kivi_values_fast<%s, 8, 4, 1>" % b], "kivi.hip"
+        names, src = ["kivi_keys_fast<%s, 8, 4, false>" % b, "kivi_values_fast<%s, 8, 4, 1, false>" % b], "kivi.hip"
     else:
         return None
     if not os.path.exists(traffic_file):

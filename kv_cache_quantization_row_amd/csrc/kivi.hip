@@ -21,7 +21,7 @@
 //
 // Packed storage (the b-bit codes and fp16 (scale, zero) per group that the
 // page's byte accounting charges, module docstring and _quantized_bytes):
-// the same kernels with `packed` set round each scale toward zero to fp16
+// the same kernels instantiated for packed storage round each scale toward zero to fp16
 // (at least 2^-24) before computing the codes, write fp16 parameters and
 // codes indexed by absolute token, and leave the fp16 input untouched;
 // kivi_unpack rebuilds fp16(code*scale + zero) from them.
@@ -147,7 +147,7 @@ __device__ __forceinline__ uint32_t pkmax(uint32_t a, uint32_t b) {
 }
 
 // ------------------------------------------------------------------ keys
-template <int BITS, int CL, int NI>
+template <int BITS, int CL, int NI, bool PK>
 __global__ __launch_bounds__(256) void kivi_keys_fast(KiviArgs a) {
   constexpr int TPI = 64 / CL;  // token rows per load instruction
   const int D = CL * 8;
@@ -218,7 +218,7 @@ __global__ __launch_bounds__(256) void kivi_keys_fast(KiviArgs a) {
     mn[i] = kunkey_f((kmn[i / 2] >> (16 * (i & 1))) & 0xffffu);
     const float mx = kunkey_f((kmx[i / 2] >> (16 * (i & 1))) & 0xffffu);
     sc[i] = kivi_scale_c<BITS>(mn[i], mx, a.eps);
-    if (a.packed) sc[i] = scale_p16(sc[i]);
+    if constexpr (PK) sc[i] = scale_p16(sc[i]);
     inv[i] = recip(sc[i]);
   }
 
@@ -239,13 +239,13 @@ __global__ __launch_bounds__(256) void kivi_keys_fast(KiviArgs a) {
       if (i & 1) o[i / 2] |= r << 16; else o[i / 2] = r;
     }
     const int t = tr + TPI * j;
-    if (!a.packed) *reinterpret_cast<uint4 *>(base + (size_t)t * D) = make_uint4(o[0], o[1], o[2], o[3]);
+    if constexpr (!PK) *reinterpret_cast<uint4 *>(base + (size_t)t * D) = make_uint4(o[0], o[1], o[2], o[3]);
     if (a.k_codes)
       store_codes8<BITS>(a.k_codes + (size_t)(nrow0 + t) * (D * BITS / 8) + ch * BITS, c);
   }
   if (tr == 0) {
     const size_t p = ((size_t)bh * a.kgrp_rows + a.kgrp0 + g) * D + ch * 8;
-    if (a.packed) {
+    if constexpr (PK) {
       uint32_t sw[4], zw[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -323,7 +323,7 @@ __global__ __launch_bounds__(256) void kivi_keys_generic(KiviArgs a) {
 }
 
 // ------------------------------------------------------------------ values
-template <int BITS, int CL, int LPG, int U>
+template <int BITS, int CL, int LPG, int U, bool PK>
 __global__ __launch_bounds__(256) void kivi_values_fast(KiviArgs a) {
   constexpr int RPW = 64 / CL;  // token rows per wave
   const int D = CL * 8;
@@ -364,7 +364,7 @@ __global__ __launch_bounds__(256) void kivi_values_fast(KiviArgs a) {
     kmx = group_max_u32<LPG>(kmx);
     const float mn = kunkey_f(kmn), mx = kunkey_f(kmx);
     float sc = kivi_scale_c<BITS>(mn, mx, a.eps);
-    if (a.packed) sc = scale_p16(sc);
+    if constexpr (PK) sc = scale_p16(sc);
     const float inv = recip(sc);
     uint32_t o[4], c[8];
     float ad[8], scv[8], invv[8], cf[8];
@@ -383,11 +383,11 @@ __global__ __launch_bounds__(256) void kivi_values_fast(KiviArgs a) {
     }
     if (tok[u] < n) {
       const size_t rowid = (size_t)bh * a.code_rows + (a.lo + tok[u] - a.code_t0);  // code row
-      if (!a.packed) *reinterpret_cast<uint4 *>(vb + (size_t)tok[u] * D) = make_uint4(o[0], o[1], o[2], o[3]);
+      if constexpr (!PK) *reinterpret_cast<uint4 *>(vb + (size_t)tok[u] * D) = make_uint4(o[0], o[1], o[2], o[3]);
       if (a.v_codes) store_codes8<BITS>(a.v_codes + rowid * (D * BITS / 8) + ch * BITS, c);
       if (ch % LPG == 0) {
         const size_t p = rowid * ng + ch / LPG;
-        if (a.packed) {
+        if constexpr (PK) {
           a.v_s16[p] = f2h(sc);
           a.v_z16[p] = f2h(mn + 0.0f);
         } else {
@@ -536,16 +536,16 @@ namespace {
 #ifndef KVQ_KIVI_VU
 #define KVQ_KIVI_VU 1  // row groups per wave, values
 #endif
-template <int BITS, int CL>
+template <int BITS, int CL, bool PK>
 hipError_t keys_cl(const KiviArgs &a, int ng, hipStream_t st) {
   constexpr int TPI = 64 / CL, W = KVQ_KIVI_KWPB;
   const dim3 grid((unsigned)((ng + W - 1) / W), (unsigned)a.BH), blk(64 * W);
   switch (a.gs / TPI) {  // loads per lane; fast path only when gs % TPI == 0
-    case 1: hipLaunchKernelGGL((kivi_keys_fast<BITS, CL, 1>), grid, blk, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((kivi_keys_fast<BITS, CL, 2>), grid, blk, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((kivi_keys_fast<BITS, CL, 4>), grid, blk, 0, st, a); break;
-    case 8: hipLaunchKernelGGL((kivi_keys_fast<BITS, CL, 8>), grid, blk, 0, st, a); break;
-    case 16: hipLaunchKernelGGL((kivi_keys_fast<BITS, CL, 16>), grid, blk, 0, st, a); break;
+    case 1: hipLaunchKernelGGL((kivi_keys_fast<BITS, CL, 1, PK>), grid, blk, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((kivi_keys_fast<BITS, CL, 2, PK>), grid, blk, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((kivi_keys_fast<BITS, CL, 4, PK>), grid, blk, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((kivi_keys_fast<BITS, CL, 8, PK>), grid, blk, 0, st, a); break;
+    case 16: hipLaunchKernelGGL((kivi_keys_fast<BITS, CL, 16, PK>), grid, blk, 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -561,18 +561,18 @@ bool keys_fast_ok(const KiviArgs &a) {
   return ni == 1 || ni == 2 || ni == 4 || ni == 8 || ni == 16;
 }
 
-template <int BITS>
+template <int BITS, bool PK>
 hipError_t launch_keys(const KiviArgs &a, hipStream_t st) {
   const int n = a.hi - a.lo;
   const int ng = (n + a.gs - 1) / a.gs;
   if (keys_fast_ok(a)) {
     switch (a.D / 8) {
-      case 1: return keys_cl<BITS, 1>(a, ng, st);
-      case 2: return keys_cl<BITS, 2>(a, ng, st);
-      case 4: return keys_cl<BITS, 4>(a, ng, st);
-      case 8: return keys_cl<BITS, 8>(a, ng, st);
-      case 16: return keys_cl<BITS, 16>(a, ng, st);
-      case 32: return keys_cl<BITS, 32>(a, ng, st);
+      case 1: return keys_cl<BITS, 1, PK>(a, ng, st);
+      case 2: return keys_cl<BITS, 2, PK>(a, ng, st);
+      case 4: return keys_cl<BITS, 4, PK>(a, ng, st);
+      case 8: return keys_cl<BITS, 8, PK>(a, ng, st);
+      case 16: return keys_cl<BITS, 16, PK>(a, ng, st);
+      case 32: return keys_cl<BITS, 32, PK>(a, ng, st);
     }
   }
   if (a.D % 8 == 0) {
@@ -585,25 +585,25 @@ hipError_t launch_keys(const KiviArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int BITS, int CL, int LPG>
+template <int BITS, int CL, int LPG, bool PK>
 hipError_t values_cfg(const KiviArgs &a, hipStream_t st) {
   constexpr int U = KVQ_KIVI_VU, RPW = 64 / CL, W = KVQ_KIVI_VWPB;
   const int64_t waves = ((a.hi - a.lo) + RPW * U - 1) / (RPW * U);  // per (b, h)
-  hipLaunchKernelGGL((kivi_values_fast<BITS, CL, LPG, U>), dim3((unsigned)((waves + W - 1) / W), (unsigned)a.BH),
+  hipLaunchKernelGGL((kivi_values_fast<BITS, CL, LPG, U, PK>), dim3((unsigned)((waves + W - 1) / W), (unsigned)a.BH),
                      dim3(64 * W), 0, st, a);
   return hipGetLastError();
 }
 
-template <int BITS, int CL>
+template <int BITS, int CL, bool PK>
 hipError_t values_cl(const KiviArgs &a, hipStream_t st) {
   switch (a.gs / 8) {
-    case 1: return values_cfg<BITS, CL, 1>(a, st);
-    case 2: if constexpr (CL >= 2) return values_cfg<BITS, CL, 2>(a, st); break;
-    case 4: if constexpr (CL >= 4) return values_cfg<BITS, CL, 4>(a, st); break;
-    case 8: if constexpr (CL >= 8) return values_cfg<BITS, CL, 8>(a, st); break;
-    case 16: if constexpr (CL >= 16) return values_cfg<BITS, CL, 16>(a, st); break;
-    case 32: if constexpr (CL >= 32) return values_cfg<BITS, CL, 32>(a, st); break;
-    case 64: if constexpr (CL >= 64) return values_cfg<BITS, CL, 64>(a, st); break;
+    case 1: return values_cfg<BITS, CL, 1, PK>(a, st);
+    case 2: if constexpr (CL >= 2) return values_cfg<BITS, CL, 2, PK>(a, st); break;
+    case 4: if constexpr (CL >= 4) return values_cfg<BITS, CL, 4, PK>(a, st); break;
+    case 8: if constexpr (CL >= 8) return values_cfg<BITS, CL, 8, PK>(a, st); break;
+    case 16: if constexpr (CL >= 16) return values_cfg<BITS, CL, 16, PK>(a, st); break;
+    case 32: if constexpr (CL >= 32) return values_cfg<BITS, CL, 32, PK>(a, st); break;
+    case 64: if constexpr (CL >= 64) return values_cfg<BITS, CL, 64, PK>(a, st); break;
   }
   return hipErrorInvalidValue;
 }
@@ -617,17 +617,17 @@ bool values_fast_ok(const KiviArgs &a) {
   return (lpg & (lpg - 1)) == 0 && lpg <= CL && a.D % a.gs == 0;
 }
 
-template <int BITS>
+template <int BITS, bool PK>
 hipError_t launch_values(const KiviArgs &a, hipStream_t st) {
   if (values_fast_ok(a)) {
     switch (a.D / 8) {
-      case 1: return values_cl<BITS, 1>(a, st);
-      case 2: return values_cl<BITS, 2>(a, st);
-      case 4: return values_cl<BITS, 4>(a, st);
-      case 8: return values_cl<BITS, 8>(a, st);
-      case 16: return values_cl<BITS, 16>(a, st);
-      case 32: return values_cl<BITS, 32>(a, st);
-      case 64: return values_cl<BITS, 64>(a, st);
+      case 1: return values_cl<BITS, 1, PK>(a, st);
+      case 2: return values_cl<BITS, 2, PK>(a, st);
+      case 4: return values_cl<BITS, 4, PK>(a, st);
+      case 8: return values_cl<BITS, 8, PK>(a, st);
+      case 16: return values_cl<BITS, 16, PK>(a, st);
+      case 32: return values_cl<BITS, 32, PK>(a, st);
+      case 64: return values_cl<BITS, 64, PK>(a, st);
     }
   }
   const int n = a.hi - a.lo;
@@ -637,12 +637,16 @@ hipError_t launch_values(const KiviArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int BITS, bool PK>
+hipError_t launch_bits_p(const KiviArgs &a, hipStream_t st) {
+  hipError_t e = hipSuccess;
+  if (a.keys) e = launch_keys<BITS, PK>(a, st);
+  if (e == hipSuccess && a.values) e = launch_values<BITS, PK>(a, st);
+  return e;
+}
 template <int BITS>
 hipError_t launch_bits(const KiviArgs &a, hipStream_t st) {
-  hipError_t e = hipSuccess;
-  if (a.keys) e = launch_keys<BITS>(a, st);
-  if (e == hipSuccess && a.values) e = launch_values<BITS>(a, st);
-  return e;
+  return a.packed ? launch_bits_p<BITS, true>(a, st) : launch_bits_p<BITS, false>(a, st);
 }
 }  // namespace
 
