@@ -32,6 +32,15 @@
 //     updated by walking the cut from its old to its new position. Sums are
 //     doubles, exact while |sum| < 2^29 (fp16 values are multiples of 2^-24),
 //     so each level is the exact mean rounded once to binary32.
+// Key fits with at least as many lanes per channel as levels (CPC >= L, the
+// many-token prefill) first merge the channel's CPC sorted chunks into one
+// globally sorted sequence (the bitonic network continued across lanes with
+// DPP and swizzle exchanges), which makes the fit cheap: tau is searched over
+// the k+1 smallest and k+1 largest samples only (the k+1 largest |x| lie
+// there), the inlier range and the quantile order statistics are direct
+// reads, and in a Lloyd iteration lane j places cut j (a ballot over the
+// chunks' last keys, then a search inside one chunk) and reads its exact
+// prefix sum from per-lane sums at every 32nd slot plus at most 31 samples.
 // Codes are then #{j : x > T_j}, which equals the first index of the nearest
 // level. The side channel (flat index, fp16 value) is emitted in ascending
 // flat order: each workgroup reserves a staging range with one atomic and
@@ -442,6 +451,196 @@ __device__ void fit_vector(const Chunk &c, int nq, float frac, int iters, float 
   }
 }
 
+// ----------------------------------------------------------------- merged chunks
+// The CPC sorted chunks of one vector are merged into one sorted sequence by
+// continuing the bitonic network across lanes: element e = 128q + s (lane q
+// of the group, slot s) pairs with e ^ (K-1) in the merge of blocks of size K
+// (lane q ^ (K/128 - 1), slot 127 - s) and then with e ^ J for J = K/4 .. 1
+// (lanes q ^ (J/128) for J >= 128; the two halves of a register for J = 64;
+// registers r ^ J below). The smaller element goes to the lower index.
+template <int M>  // value of lane ^ M (M < 64; whole wave active)
+__device__ __forceinline__ uint32_t lane_xor_m(uint32_t v) {
+  if constexpr (M == 1) return dpp<DPP_XOR1>(v);
+  else if constexpr (M == 2) return dpp<DPP_XOR2>(v);
+  else if constexpr (M == 3) return dpp<0x1b>(v);  // quad_perm [3,2,1,0]
+  else if constexpr (M == 7) return dpp<DPP_HALF_MIRROR>(v);
+  else if constexpr (M == 15) return dpp<DPP_MIRROR>(v);
+  else if constexpr (M < 32) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (M << 10) | 0x1f);
+  else return (uint32_t)__shfl_xor((int)v, M);
+}
+__device__ __forceinline__ uint32_t keep(uint32_t a, uint32_t b, bool lower) {
+  const u16x2v x = __builtin_bit_cast(u16x2v, a), y = __builtin_bit_cast(u16x2v, b);
+  return lower ? __builtin_bit_cast(uint32_t, __builtin_elementwise_min(x, y))
+               : __builtin_bit_cast(uint32_t, __builtin_elementwise_max(x, y));
+}
+template <int M>  // flip across lanes q and q ^ M (M = K/128 - 1), slots s and 127 - s
+__device__ __forceinline__ void xflip(uint32_t *v, int q) {
+  const bool lower = (q & ((M + 1) >> 1)) == 0;
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    const uint32_t a = lane_xor_m<M>(v[63 - r]), b = lane_xor_m<M>(v[r]);
+    v[r] = keep(v[r], (a >> 16) | (a << 16), lower);
+    v[63 - r] = keep(v[63 - r], (b >> 16) | (b << 16), lower);
+  }
+}
+template <int DL>  // lanes q and q ^ DL, same slot
+__device__ __forceinline__ void xdisp(uint32_t *v, int q) {
+  const bool lower = (q & DL) == 0;
+#pragma unroll
+  for (int r = 0; r < 64; ++r) v[r] = keep(v[r], lane_xor_m<DL>(v[r]), lower);
+}
+__device__ __forceinline__ void inlane_tail(uint32_t *v) {
+#pragma unroll
+  for (int r = 0; r < 64; ++r) {  // slots r and r + 64
+    const uint32_t lo = v[r] & 0xffffu, hi = v[r] >> 16;
+    v[r] = min(lo, hi) | (max(lo, hi) << 16);
+  }
+  disperse<32>(v);
+  disperse<16>(v);
+  disperse<8>(v);
+  disperse<4>(v);
+  disperse<2>(v);
+  disperse<1>(v);
+}
+template <int CPC>
+__device__ __forceinline__ void merge_lanes(uint32_t *v, int q) {
+  if constexpr (CPC >= 2) { xflip<1>(v, q); inlane_tail(v); }
+  if constexpr (CPC >= 4) { xflip<3>(v, q); xdisp<1>(v, q); inlane_tail(v); }
+  if constexpr (CPC >= 8) { xflip<7>(v, q); xdisp<2>(v, q); xdisp<1>(v, q); inlane_tail(v); }
+  if constexpr (CPC >= 16) {
+    xflip<15>(v, q); xdisp<4>(v, q); xdisp<2>(v, q); xdisp<1>(v, q); inlane_tail(v);
+  }
+  if constexpr (CPC >= 32) {
+    xflip<31>(v, q); xdisp<8>(v, q); xdisp<4>(v, q); xdisp<2>(v, q); xdisp<1>(v, q); inlane_tail(v);
+  }
+  if constexpr (CPC >= 64) {
+    xflip<63>(v, q); xdisp<16>(v, q); xdisp<8>(v, q); xdisp<4>(v, q); xdisp<2>(v, q); xdisp<1>(v, q);
+    inlane_tail(v);
+  }
+}
+
+// Fit of one vector whose n samples are sorted across the CPC lanes of the
+// group (lane q holds positions [128q, 128q + 128), padding sorts last).
+// lds: the chunks of the workgroup's lanes; tbl: per lane, five exact prefix
+// sums B + (sum of its first 32k valid slots), k = 0..4, with B the sum of
+// the chunks before it. CPC >= L: lane q < L does the work of level q. The
+// result equals fit_vector's.
+template <int CPC, int L>
+__device__ void fit_global(const uint32_t *lds, const double *tbl, int lane, int n, uint32_t last, float frac,
+                           int iters, float *lev, FitOut &fo) {
+  const int q = lane % CPC, gb = lane - q;        // group base (workgroup lane)
+  const int wb = (lane & 63) - q;                 // group base inside the wave
+  const uint64_t gmask = (CPC == 64 ? ~0ull : ((1ull << CPC) - 1)) << wb;
+  auto at = [&](int l, int i) -> uint32_t {       // slot i of lane l's chunk
+    const uint32_t x = lds[l * 64 + ((i & 63) ^ (l & 63))];
+    return (i & 64) ? (x >> 16) : (x & 0xffffu);
+  };
+  auto gat = [&](int p) -> uint32_t { return at(gb + (p >> 7), p & 127); };
+  auto pref = [&](int c) -> double {              // exact sum of the c smallest samples, c <= n
+    int cq = c >> 7, s = c & 127;
+    if (cq >= CPC) { cq = CPC - 1; s = 128; }
+    const int kk = s >> 5, l = gb + cq;
+    double r0 = tbl[l * 5 + kk], r1 = 0.0, r2 = 0.0, r3 = 0.0;
+    const int st = kk * 32;
+#pragma unroll
+    for (int t = 0; t < 32; t += 4) {
+      if (st + t < s) r0 += kval(at(l, st + t));
+      if (st + t + 1 < s) r1 += kval(at(l, st + t + 1));
+      if (st + t + 2 < s) r2 += kval(at(l, st + t + 2));
+      if (st + t + 3 < s) r3 += kval(at(l, st + t + 3));
+    }
+    return (r0 + r1) + (r2 + r3);
+  };
+  fo.tau = 0;
+  fo.tau_key = key16(0);
+#pragma unroll
+  for (int j = 0; j < L; ++j) lev[j] = 0.0f;
+  if (n == 0) return;
+  const long long k = (long long)floor((double)frac * (double)n);
+  const int kp1 = (int)k + 1;  // <= n (frac < 1)
+  // ---- tau: the k+1 largest |x| lie among the kp1 smallest and the kp1
+  // largest samples, so the counts of the bitwise search run over those
+  const int cs = min(n, 2 * kp1);
+  int pos = 0;
+#pragma unroll 1
+  for (int sb = 16384; sb >= 1; sb >>= 1) {
+    const int cand = pos + sb - 1;
+    if (cand > 0x7bff) continue;
+    int cnt = 0;
+    for (int i = q; i < cs; i += CPC) {
+      const int p = (cs == n || i < kp1) ? i : n - cs + i;
+      cnt += (int)((unkey16(gat(p)) & 0x7fffu) >= (uint32_t)cand);
+    }
+    if (gsum<CPC>(cnt) >= kp1) pos += sb;
+  }
+  const uint32_t tau = (uint32_t)(pos - 1);
+  fo.tau = (uint16_t)tau;
+  fo.tau_key = key16(tau);
+  // ---- inliers [lo, hi): at most k samples lie outside [-tau, tau], so
+  // both outer runs sit inside the kp1 end positions
+  const uint32_t klo = tau == 0 ? key16(0x8000u) : key16(tau | 0x8000u);
+  const uint32_t khi = key16(tau);
+  int cl = 0, ch = 0;
+  for (int i = q; i < kp1; i += CPC) {
+    cl += (int)(gat(i) < klo);
+    ch += (int)(gat(n - 1 - i) > khi);
+  }
+  const int lo = gsum<CPC>(cl), hi = n - gsum<CPC>(ch);
+  const int m = hi - lo;
+  // ---- quantile initialisation: order statistics are direct reads
+#pragma unroll
+  for (int j = 0; j < L; ++j) {
+    const long long num = (long long)(2 * j + 1) * (long long)(m - 1);
+    const int rk = (int)(num / (2 * L)), rem = (int)(num % (2 * L));
+    double v = kval(gat(lo + rk));
+    if (rem != 0) {
+      const double u1 = kval(gat(lo + rk + 1));
+      v = v + ((double)rem / (double)(2 * L)) * (u1 - v);
+    }
+    lev[j] = (float)v + 0.0f;
+  }
+  // ---- Lloyd iterations: lane q < L-1 places cut q (chunk by ballot, then
+  // a search inside the chunk) and takes its exact prefix sum; lane q < L
+  // updates level q from its cell [cut q-1, cut q)
+  const double p_lo = pref(lo), p_hi = pref(hi);
+  for (int it = 0; it < iters; ++it) {
+    uint32_t T[L];
+    cut_keys<L>(lev, T);
+    int fc = 0;
+    uint32_t tq = 0xffffu;
+#pragma unroll
+    for (int j = 0; j < L - 1; ++j) {
+      const int f = __popcll(__ballot(last <= T[j]) & gmask);
+      fc = q == j ? f : fc;
+      tq = q == j ? T[j] : tq;
+    }
+    int c_me = hi;
+    double p_me = p_hi;
+    if (q < L - 1) {
+      int c = 128 * CPC;
+      if (fc < CPC) {
+        const Chunk cc{lds + (gb + fc) * 64, (gb + fc) & 63};
+        c = 128 * fc + cc.upper(tq);
+      }
+      c_me = min(max(c, lo), hi);
+      p_me = pref(c_me);
+    }
+    int c_prev = __shfl_up(c_me, 1);
+    double p_prev = __shfl_up(p_me, 1);
+    if (q == 0) { c_prev = lo; p_prev = p_lo; }
+    float nl = lev[0];
+#pragma unroll
+    for (int j = 1; j < L; ++j) nl = q == j ? lev[j] : nl;
+    const int cnt = c_me - c_prev;
+    if (q < L && cnt > 0) nl = (float)((p_me - p_prev) / (double)cnt);
+#pragma unroll
+    for (int j = 0; j < L; ++j) lev[j] = __shfl(nl, wb + j);
+    // an empty duplicate keeps its level while its twin moves: keep the table
+    // ordered so the cells stay contiguous ranges
+    sort_levels<L>(lev);
+  }
+}
+
 // load the 128-sample chunk from a register array of fp16 pairs (element i
 // in word i/2) into the sort layout (element i in register i%64, half i/64)
 __device__ __forceinline__ void to_sort_layout(const uint32_t *raw, uint32_t *v) {
@@ -527,6 +726,7 @@ __global__ __launch_bounds__(KF_T) void nuq_key_fit(NuqArgs a) {
   }
   __syncthreads();
   const int nq = active ? max(0, min(CH, nfit - q * CH)) : 0;
+  uint32_t last = 0;  // key of this lane's largest slot (merged path)
   {
     uint32_t raw[64];
     const int sz = 4 * swz(lane);
@@ -538,12 +738,46 @@ __global__ __launch_bounds__(KF_T) void nuq_key_fit(NuqArgs a) {
     uint32_t v[64];
     to_sort_layout(raw, v);
     sort128(v);
-    store_chunk(lds + lane * 64, lane & 63, v);  // this lane's own words only
+    if constexpr (CPC >= L) {
+      // one sorted sequence per channel, then exact prefix sums of every
+      // lane's valid slots at multiples of 32, offset by the chunks before it
+      merge_lanes<CPC>(v, q);
+      store_chunk(lds + lane * 64, lane & 63, v);
+      last = v[63] >> 16;
+      double cs[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int r = 0; r < 64; ++r) {
+        if (r < nq) cs[r >> 5] += kval(v[r] & 0xffffu);
+        if (64 + r < nq) cs[2 + (r >> 5)] += kval(v[r] >> 16);
+      }
+      const double tot = (cs[0] + cs[1]) + (cs[2] + cs[3]);
+      double x = tot;
+#pragma unroll
+      for (int dd = 1; dd < CPC; dd <<= 1) {
+        const double y = __shfl_up(x, dd);
+        if (q >= dd) x += y;
+      }
+      double *tb = reinterpret_cast<double *>(lds + KF_T * 64) + lane * 5;
+      const double b0 = x - tot;
+      tb[0] = b0;
+      tb[1] = b0 + cs[0];
+      tb[2] = b0 + (cs[0] + cs[1]);
+      tb[3] = b0 + ((cs[0] + cs[1]) + cs[2]);
+      tb[4] = b0 + tot;
+    } else {
+      store_chunk(lds + lane * 64, lane & 63, v);  // this lane's own words only
+    }
   }
-  Chunk c{lds + lane * 64, lane & 63};
   float lev[L];
   FitOut fo;
-  fit_vector<CPC, L>(c, nq, a.frac, a.iters, lev, fo);
+  if constexpr (CPC >= L) {
+    __syncthreads();  // the fit reads the other lanes' chunks and sums
+    fit_global<CPC, L>(lds, reinterpret_cast<const double *>(lds + KF_T * 64), lane, active ? nfit : 0, last,
+                       a.frac, a.iters, lev, fo);
+  } else {
+    Chunk c{lds + lane * 64, lane & 63};
+    fit_vector<CPC, L>(c, nq, a.frac, a.iters, lev, fo);
+  }
   if (active && q == 0) {
     float *kl = a.key_levels + ((size_t)bh * a.D + d) * L;
 #pragma unroll
@@ -1279,7 +1513,9 @@ template <int CPC, int L>
 hipError_t launch_key_fit_cpc(const NuqArgs &a, hipStream_t st) {
   const int chans = KF_T / CPC;
   dim3 grid((a.D + chans - 1) / chans, a.BH);
-  hipLaunchKernelGGL((nuq_key_fit<CPC, L>), grid, dim3(KF_T), KF_T * 64 * 4, st, a);
+  // merged path: chunks (64 words per lane) + five prefix sums per lane
+  const size_t lds = (size_t)KF_T * 64 * 4 + (CPC >= L ? (size_t)KF_T * 5 * 8 : 0);
+  hipLaunchKernelGGL((nuq_key_fit<CPC, L>), grid, dim3(KF_T), lds, st, a);
   return hipGetLastError();
 }
 template <int L>

@@ -154,6 +154,53 @@ def test_degenerate_data(case, BH):
         compare(g, r, what="%s frac=%g iters=%d" % (case, frac, iters))
 
 
+# key fits whose lanes per channel reach the level count run on one merged,
+# globally sorted sequence per channel: every width at several lane counts,
+# n = 4096 (no padding: the prefix sum at the very end), and the degenerate
+# data of the test above at merged sizes
+@pytest.mark.parametrize("S,bits", [(600, 1), (600, 2), (1100, 3), (1100, 4), (2500, 4), (4100, 3),
+                                    (4100, 2), (8196, 4)])
+def test_merged_key_fit(S, bits):
+    say("nuq merged key fit", S, bits)
+    BH, D = 2, 32
+    k, v = t4((BH, S, D), 80 + S + bits), t4((BH, S, D), 90 + S + bits)
+    for frac in (0.01, 0.1):
+        g = gpu_nuq(k, v, 0, bits, frac, 8, 4, 1, want_recon=S < 8000)
+        r = oracle.nuq_fit_quant(k, v, 0, bits, frac, 8, 4, 1)
+        keys = None if S < 8000 else ["key_levels", "key_thresh", "k_codes"]
+        compare(g, r, keys=keys, what="S=%d bits=%d frac=%g" % (S, bits, frac))
+
+
+@pytest.mark.parametrize("S,bits", [(1028, 2), (2100, 3)])
+@pytest.mark.parametrize("case", ["ties", "zeros", "signed_zeros", "extremes", "subnormal", "const"])
+def test_merged_key_fit_degenerate(case, S, bits):
+    say("nuq merged degenerate", case, S, bits)
+    BH, D = 2, 32
+    rng = np.random.default_rng(100 + ["ties", "zeros", "signed_zeros", "extremes", "subnormal", "const"].index(case))
+    if case == "ties":
+        x = rng.integers(-3, 4, size=(2, BH, S, D)).astype(np.float16)
+    elif case == "zeros":
+        x = np.zeros((2, BH, S, D), np.float16)
+        x[..., ::7, :] = 1.5
+    elif case == "signed_zeros":
+        x = np.where(rng.random((2, BH, S, D)) < 0.5, np.float16(0.0), np.float16(-0.0)).astype(np.float16)
+        x[:, :, ::3, :] = rng.standard_normal((2, BH, (S + 2) // 3, D)).astype(np.float16)
+    elif case == "extremes":
+        x = (rng.standard_t(4, size=(2, BH, S, D)) * 3000).clip(-65504, 65504).astype(np.float16)
+        x[:, :, 10, :] = 65504
+        x[:, :, 11, :] = -65504
+    elif case == "subnormal":
+        x = (rng.integers(-40, 40, size=(2, BH, S, D)) * 2.0 ** -24).astype(np.float16)
+    else:
+        x = np.full((2, BH, S, D), 0.25, np.float16)
+    k, v = x[0].view(np.uint16), x[1].view(np.uint16)
+    for frac, iters in [(0.05, 8), (0.0, 3), (0.3, 0)]:
+        g = gpu_nuq(k, v, 0, bits, frac, iters, 4, 1, want_recon=False)
+        r = oracle.nuq_fit_quant(k, v, 0, bits, frac, iters, 4, 1)
+        compare(g, r, keys=["key_levels", "key_thresh", "k_codes"],
+                what="%s S=%d bits=%d frac=%g iters=%d" % (case, S, bits, frac, iters))
+
+
 @pytest.mark.parametrize("iters", [1, 2, 4, 16])
 def test_lloyd_iteration_counts(iters):
     """The Lloyd iteration count the pages name as the speed / quality lever."""
