@@ -13,7 +13,9 @@
  *
  * Conventions for every entry point:
  *   - Pointers are DEVICE memory owned by the caller unless marked [host]. The
- *     library allocates nothing on these paths and keeps no device state.
+ *     library allocates no device memory and keeps no device data between
+ *     calls; its only device objects are the auxiliary stream and two events
+ *     that kvq_nuq_fit_quant creates once per device (see there).
  *   - fp16 data is passed as uint16_t bit patterns (IEEE binary16).
  *   - `stream` is a hipStream_t passed as void*; NULL is the null stream. Work
  *     is enqueued on it; no entry point synchronises.
@@ -304,6 +306,13 @@ int64_t kvq_nuq_workspace_bytes(int32_t BH, int32_t S, int32_t D, int32_t bits, 
  *   workspace: device memory of at least kvq_nuq_workspace_bytes, owned by
  *   the caller, 16-byte aligned; its contents on entry do not matter.
  * Calls that share a workspace must not overlap.
+ * Streams: when BH*S > 4096 the value fit runs on a second stream of the
+ * current device, forked from `stream` after the call's first kernel and
+ * joined back into it before the last (event record / stream wait), so the
+ * call stays ordered on `stream` like every other. That stream (non-blocking,
+ * default priority) and its two events are created on the first such call
+ * on each device and kept until the process ends; concurrent host threads
+ * are serialised around the fork and join.
  * Errors: KVQ_ERR_NULL, KVQ_ERR_BITS, KVQ_ERR_SHAPE, KVQ_ERR_ARG (frac,
  * iters), KVQ_ERR_CAPACITY, KVQ_ERR_ALIGN, KVQ_ERR_HIP. */
 int kvq_nuq_fit_quant(const uint16_t *keys, const uint16_t *values, int32_t BH, int32_t S, int32_t D,

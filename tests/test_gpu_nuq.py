@@ -158,7 +158,7 @@ def test_degenerate_data(case, BH):
 # globally sorted sequence per channel: every width at several lane counts,
 # n = 4096 (no padding: the prefix sum at the very end), and the degenerate
 # data of the test above at merged sizes
-@pytest.mark.parametrize("S,bits", [(600, 1), (600, 2), (1100, 3), (1100, 4), (2500, 4), (4100, 3),
+@pytest.mark.parametrize("S,bits", [(400, 2), (600, 1), (600, 2), (1100, 3), (1100, 4), (2500, 4), (4100, 3),
                                     (4100, 2), (8196, 4)])
 def test_merged_key_fit(S, bits):
     say("nuq merged key fit", S, bits)
