@@ -171,6 +171,16 @@ def test_merged_key_fit(S, bits):
         compare(g, r, keys=keys, what="S=%d bits=%d frac=%g" % (S, bits, frac))
 
 
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_merged_key_fit_head_dims(D):
+    say("nuq merged key fit D", D)
+    BH, S, bits = 3, 1500, 3
+    k, v = t4((BH, S, D), 300 + D), t4((BH, S, D), 301 + D)
+    g = gpu_nuq(k, v, 0, bits, 0.01, 8, 4, 1)
+    r = oracle.nuq_fit_quant(k, v, 0, bits, 0.01, 8, 4, 1)
+    compare(g, r, what="D=%d" % D)
+
+
 @pytest.mark.parametrize("S,bits", [(1028, 2), (2100, 3)])
 @pytest.mark.parametrize("case", ["ties", "zeros", "signed_zeros", "extremes", "subnormal", "const"])
 def test_merged_key_fit_degenerate(case, S, bits):
