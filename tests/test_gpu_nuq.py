@@ -171,14 +171,15 @@ def test_merged_key_fit(S, bits):
         compare(g, r, keys=keys, what="S=%d bits=%d frac=%g" % (S, bits, frac))
 
 
-@pytest.mark.parametrize("D", [64, 128, 256])
-def test_merged_key_fit_head_dims(D):
-    say("nuq merged key fit D", D)
-    BH, S, bits = 3, 1500, 3
-    k, v = t4((BH, S, D), 300 + D), t4((BH, S, D), 301 + D)
-    g = gpu_nuq(k, v, 0, bits, 0.01, 8, 4, 1)
+@pytest.mark.parametrize("D,S,BH", [(64, 1500, 3), (128, 1500, 3), (256, 1500, 3), (64, 4100, 2), (256, 8196, 1)])
+def test_merged_key_fit_head_dims(D, S, BH):
+    say("nuq merged key fit D S", D, S)
+    bits = 3
+    k, v = t4((BH, S, D), 300 + D + S), t4((BH, S, D), 301 + D + S)
+    g = gpu_nuq(k, v, 0, bits, 0.01, 8, 4, 1, want_recon=S < 8000)
     r = oracle.nuq_fit_quant(k, v, 0, bits, 0.01, 8, 4, 1)
-    compare(g, r, what="D=%d" % D)
+    keys = None if S < 8000 else ["key_levels", "key_thresh", "k_codes"]
+    compare(g, r, keys=keys, what="D=%d S=%d" % (D, S))
 
 
 @pytest.mark.parametrize("S,bits", [(1028, 2), (2100, 3)])
