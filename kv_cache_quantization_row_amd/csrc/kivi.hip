@@ -212,14 +212,36 @@ __global__ __launch_bounds__(256) void kivi_keys_fast(KiviArgs a) {
       kmx[i] = pkmax(kmx[i], dpp<0x121>(kmx[i]));
     }
   }
-  float mn[8], sc[8], inv[8];
+  // every lane of a channel chunk now holds the same 8 minima and maxima;
+  // lane tr computes the scales of channels tr, tr + TPI, ... once and the
+  // chunk's lanes gather the 8 scales and reciprocals with lane shuffles
+  constexpr int SPL = TPI >= 8 ? 1 : 8 / TPI;  // scales computed per lane
+  float mn[8], mxv[8], sc[8], inv[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     mn[i] = kunkey_f((kmn[i / 2] >> (16 * (i & 1))) & 0xffffu);
-    const float mx = kunkey_f((kmx[i / 2] >> (16 * (i & 1))) & 0xffffu);
-    sc[i] = kivi_scale_c<BITS>(mn[i], mx, a.eps);
-    if constexpr (PK) sc[i] = scale_p16(sc[i]);
-    inv[i] = recip(sc[i]);
+    mxv[i] = kunkey_f((kmx[i / 2] >> (16 * (i & 1))) & 0xffffu);
+  }
+  float s_own[SPL], i_own[SPL];
+#pragma unroll
+  for (int q = 0; q < SPL; ++q) {
+    const int ci = (tr % 8) + q * TPI;  // channel of this lane's q-th scale
+    float cmn = mn[0], cmx = mxv[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) {
+      cmn = ci == i ? mn[i] : cmn;
+      cmx = ci == i ? mxv[i] : cmx;
+    }
+    float sq = kivi_scale_c<BITS>(cmn, cmx, a.eps);
+    if constexpr (PK) sq = scale_p16(sq);
+    s_own[q] = sq;
+    i_own[q] = recip(sq);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int src = ch + CL * (i % (TPI < 8 ? TPI : 8));  // the lane that computed channel i
+    sc[i] = __shfl(s_own[TPI < 8 ? i / TPI : 0], src);
+    inv[i] = __shfl(i_own[TPI < 8 ? i / TPI : 0], src);
   }
 
   const int64_t nrow0 = bh * a.code_rows + (t0 - a.code_t0);  // code row of token t0
