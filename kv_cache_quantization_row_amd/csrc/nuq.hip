@@ -604,8 +604,26 @@ __device__ void fit_global(const uint32_t *lds, const double *tbl, int lane, int
   // updates level q from its cell [cut q-1, cut q)
   const double p_lo = pref(lo), p_hi = pref(hi);
   for (int it = 0; it < iters; ++it) {
+    // cut keys as cut_keys<L> computes them, one threshold per lane: lane
+    // j < L-1 takes levels j, j+1 (0 marks equal levels), then every lane
+    // gathers them and carries the cut above over duplicates
+    float lq = lev[0], lq1 = lev[1];
+#pragma unroll
+    for (int j = 1; j < L - 1; ++j) {
+      lq = q == j ? lev[j] : lq;
+      lq1 = q == j ? lev[j + 1] : lq1;
+    }
+    uint32_t tmine = 0;
+    if (q < L - 1 && lq < lq1) tmine = key16(thr16(lq, lq1));
     uint32_t T[L];
-    cut_keys<L>(lev, T);
+    uint32_t nt = 0xffffu;
+#pragma unroll
+    for (int j = L - 2; j >= 0; --j) {
+      const uint32_t t = (uint32_t)__shfl((int)tmine, wb + j);
+      if (t) nt = t;
+      T[j] = nt;
+    }
+    T[L - 1] = 0xffffu;
     int fc = 0;
     uint32_t tq = 0xffffu;
 #pragma unroll
