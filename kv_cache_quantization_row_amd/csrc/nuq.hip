@@ -539,17 +539,24 @@ __device__ void fit_global(const uint32_t *lds, const double *tbl, int lane, int
   auto pref = [&](int c) -> double {              // exact sum of the c smallest samples, c <= n
     int cq = c >> 7, s = c & 127;
     if (cq >= CPC) { cq = CPC - 1; s = 128; }
-    const int kk = s >> 5, l = gb + cq;
-    double r0 = tbl[l * 5 + kk], r1 = 0.0, r2 = 0.0, r3 = 0.0;
-    const int st = kk * 32;
+    const int l = gb + cq;
+    // from the nearer of the two checkpoints around slot s: add the slots
+    // after the lower one, or subtract those up to the upper one (padding
+    // past n counts as 0, as in the table); at most 16 samples either way
+    const int kk = s >> 5, rem = s & 31;
+    const bool up = rem <= 16;
+    const int st = up ? kk * 32 : s, cnt = up ? rem : 32 - rem;
+    const int lim = n - 128 * cq;                 // valid slots of this chunk
+    double r0 = 0.0, r1 = 0.0, r2 = 0.0, r3 = 0.0;
 #pragma unroll
-    for (int t = 0; t < 32; t += 4) {
-      if (st + t < s) r0 += kval(at(l, st + t));
-      if (st + t + 1 < s) r1 += kval(at(l, st + t + 1));
-      if (st + t + 2 < s) r2 += kval(at(l, st + t + 2));
-      if (st + t + 3 < s) r3 += kval(at(l, st + t + 3));
+    for (int t = 0; t < 16; t += 4) {
+      if (t < cnt && st + t < lim) r0 += kval(at(l, st + t));
+      if (t + 1 < cnt && st + t + 1 < lim) r1 += kval(at(l, st + t + 1));
+      if (t + 2 < cnt && st + t + 2 < lim) r2 += kval(at(l, st + t + 2));
+      if (t + 3 < cnt && st + t + 3 < lim) r3 += kval(at(l, st + t + 3));
     }
-    return (r0 + r1) + (r2 + r3);
+    const double tail = (r0 + r1) + (r2 + r3);
+    return up ? tbl[l * 5 + kk] + tail : tbl[l * 5 + kk + 1] - tail;
   };
   fo.tau = 0;
   fo.tau_key = key16(0);
