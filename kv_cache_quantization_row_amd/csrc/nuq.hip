@@ -60,6 +60,14 @@ constexpr int CH = 128;             // samples per lane chunk
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2v __attribute__((ext_vector_type(2)));
 
+// DPP lane move for patterns whose every source lane lies in its own row
+// (quad permutes, row mirrors): no lane keeps an old value, so none is
+// materialised (the generic helper writes a 0 first, one extra move each)
+template <int CTRL>
+__device__ __forceinline__ uint32_t dppm(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xf, 0xf, true);
+}
+
 // ----------------------------------------------------------------- keys
 __device__ __forceinline__ uint32_t key16(uint32_t h) {  // order-preserving key of an fp16 pattern
   return (h & 0x8000u) ? (~h & 0xffffu) : (h | 0x8000u);
@@ -172,10 +180,10 @@ struct Chunk {
 // a lane swizzle across rows; every lane of the group receives the result
 template <int G, typename Op>
 __device__ __forceinline__ uint32_t gred_u32(uint32_t v, Op op) {
-  if constexpr (G >= 2) v = op(v, dpp<DPP_XOR1>(v));
-  if constexpr (G >= 4) v = op(v, dpp<DPP_XOR2>(v));
-  if constexpr (G >= 8) v = op(v, dpp<DPP_HALF_MIRROR>(v));
-  if constexpr (G >= 16) v = op(v, dpp<DPP_MIRROR>(v));
+  if constexpr (G >= 2) v = op(v, dppm<DPP_XOR1>(v));
+  if constexpr (G >= 4) v = op(v, dppm<DPP_XOR2>(v));
+  if constexpr (G >= 8) v = op(v, dppm<DPP_HALF_MIRROR>(v));
+  if constexpr (G >= 16) v = op(v, dppm<DPP_MIRROR>(v));
   if constexpr (G >= 32) v = op(v, (uint32_t)__shfl_xor((int)v, 16));
   if constexpr (G >= 64) v = op(v, (uint32_t)__shfl_xor((int)v, 32));
   return v;
@@ -191,7 +199,7 @@ __device__ __forceinline__ uint32_t gmin(uint32_t v) {
 template <int CTRL>
 __device__ __forceinline__ double dppd(double v) {
   const uint64_t b = __builtin_bit_cast(uint64_t, v);
-  const uint64_t lo = dpp<CTRL>((uint32_t)b), hi = dpp<CTRL>((uint32_t)(b >> 32));
+  const uint64_t lo = dppm<CTRL>((uint32_t)b), hi = dppm<CTRL>((uint32_t)(b >> 32));
   return __builtin_bit_cast(double, lo | (hi << 32));
 }
 // (the partial sums are exact, so the reduction order does not matter)
@@ -460,11 +468,11 @@ __device__ void fit_vector(const Chunk &c, int nq, float frac, int iters, float 
 // registers r ^ J below). The smaller element goes to the lower index.
 template <int M>  // value of lane ^ M (M < 64; whole wave active)
 __device__ __forceinline__ uint32_t lane_xor_m(uint32_t v) {
-  if constexpr (M == 1) return dpp<DPP_XOR1>(v);
-  else if constexpr (M == 2) return dpp<DPP_XOR2>(v);
-  else if constexpr (M == 3) return dpp<0x1b>(v);  // quad_perm [3,2,1,0]
-  else if constexpr (M == 7) return dpp<DPP_HALF_MIRROR>(v);
-  else if constexpr (M == 15) return dpp<DPP_MIRROR>(v);
+  if constexpr (M == 1) return dppm<DPP_XOR1>(v);
+  else if constexpr (M == 2) return dppm<DPP_XOR2>(v);
+  else if constexpr (M == 3) return dppm<0x1b>(v);  // quad_perm [3,2,1,0]
+  else if constexpr (M == 7) return dppm<DPP_HALF_MIRROR>(v);
+  else if constexpr (M == 15) return dppm<DPP_MIRROR>(v);
   else if constexpr (M < 32) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (M << 10) | 0x1f);
   else return (uint32_t)__shfl_xor((int)v, M);
 }
@@ -921,7 +929,7 @@ __device__ __forceinline__ void key_quant_body(const NuqArgs &a, int bx, int bh,
     }
     omask[it] = valid ? om : 0u;
     // pack: the 4 lanes of a quad hold 32 consecutive codes = 4*BITS bytes
-    const uint32_t n1 = dpp<0x39>(codes), n2 = dpp<0x4e>(codes), n3 = dpp<0x93>(codes);  // lanes +1, +2, +3
+    const uint32_t n1 = dppm<0x39>(codes), n2 = dppm<0x4e>(codes), n3 = dppm<0x93>(codes);  // lanes +1, +2, +3
     if (valid && (ck & 3) == 0) {
       const uint64_t lo = (uint64_t)codes | ((uint64_t)n1 << (8 * BITS));
       const uint64_t hi = (uint64_t)n2 | ((uint64_t)n3 << (8 * BITS));
@@ -1172,8 +1180,8 @@ __device__ __forceinline__ float pick(const float (&v)[L], int i) {  // v[i] for
 }
 template <int J>
 __device__ __forceinline__ uint32_t lane_xor(uint32_t v) {  // value of lane ^ J
-  if constexpr (J == 1) return dpp<DPP_XOR1>(v);
-  else if constexpr (J == 2) return dpp<DPP_XOR2>(v);
+  if constexpr (J == 1) return dppm<DPP_XOR1>(v);
+  else if constexpr (J == 2) return dppm<DPP_XOR2>(v);
   else if constexpr (J < 32) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (J << 10) | 0x1f);
   else return (uint32_t)__shfl_xor((int)v, 32);
 }
