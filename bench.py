@@ -208,17 +208,33 @@ class PagedSym:
         v = inputs.sym_layer(n, self.H, self.D, seed=2200, laplace_token_frac=0.05, channel_seed=3200)
         kk = k.view(__import__("torch").int16).numpy().view(np.uint16)
         vv = v.view(__import__("torch").int16).numpy().view(np.uint16)
+        def run(parts):  # quantize + dequantize every part at every width; fp16-equivalent elements
+            elems = 0
+            for b in self.bits_list:
+                for x in parts:
+                    c, s = oracle.sym_quant_rows(x, b)
+                    oracle.sym_dequant_rows(c, s, self.D, b)
+                    elems += 2 * x.size
+            return elems
+
         t0 = time.perf_counter()
-        elems = 0
-        for b in self.bits_list:
-            for x in (kk, vv):
-                c, s = oracle.sym_quant_rows(x, b)
-                oracle.sym_dequant_rows(c, s, self.D, b)
-                elems += 2 * x.size
-        dt = time.perf_counter() - t0
-        return {"value": round(2 * elems / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-                "sample": "layer 0, %d tokens x 4 heads x 256 of K and V, quantize + dequantize at q%s "
-                          "(%.1f s single-threaded)" % (n, "/q".join(map(str, self.bits_list)), dt)}
+        elems = run((kk, vv))
+        dt1 = time.perf_counter() - t0
+        # all cores: one thread per core over disjoint token ranges, each
+        # calling the unmodified oracle (its C calls release the GIL)
+        from concurrent.futures import ThreadPoolExecutor
+        cores = max(1, min(16, len(os.sched_getaffinity(0))))
+        cut = [n * i // cores for i in range(cores + 1)]
+        parts = [(kk[cut[i]:cut[i + 1]], vv[cut[i]:cut[i + 1]]) for i in range(cores)]
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(cores) as ex:
+            elems_all = sum(ex.map(run, parts))
+        dtn = time.perf_counter() - t0
+        return {"value": round(2 * elems_all / dtn / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+                "value_1core": round(2 * elems / dt1 / 1e9, 4),
+                "sample": "layer 0, %d tokens x 4 heads x 256 of K and V, quantize + dequantize at q%s: "
+                          "%.1f s on one thread, %.2f s on %d threads over disjoint token ranges"
+                          % (n, "/q".join(map(str, self.bits_list)), dt1, dtn, cores)}
 
 
 # --------------------------------------------------------------------------- KIVI
