@@ -147,6 +147,9 @@ class PagedSym:
                                    laplace_token_frac=0.05).view(self.N_DEC, L, S, H, D)
         self.vd = inputs.sym_layer(self.N_DEC * L * S, H, D, seed=2400, device=d,
                                    laplace_token_frac=0.05).view(self.N_DEC, L, S, H, D)
+        # per-step views built here so the timed loop holds only the library calls
+        self.kd_steps = [self.kd[i] for i in range(self.N_DEC)]
+        self.vd_steps = [self.vd[i] for i in range(self.N_DEC)]
         slots = self.num_pages * P
         self.kc = torch.empty((L * slots * H * D,), dtype=torch.uint8, device=d)  # sized for q8
         self.vc = torch.empty_like(self.kc)
@@ -167,7 +170,7 @@ class PagedSym:
                 kvq.kvq_quant_sym(lay, self.k, self.v, self.slot_prefill, self.kc, self.ks, self.vc, self.vs)
             with tm.span("decode_append_q%d_x%d" % (b, self.N_DEC)):
                 for i in range(self.N_DEC):
-                    kvq.kvq_quant_sym(lay, self.kd[i], self.vd[i], self.slot_dec[i], self.kc, self.ks,
+                    kvq.kvq_quant_sym(lay, self.kd_steps[i], self.vd_steps[i], self.slot_dec[i], self.kc, self.ks,
                                       self.vc, self.vs)
             with tm.span("dequant_sweep_q%d" % b):
                 kvq.kvq_dequant_sym(lay, self.kc, self.ks, self.vc, self.vs, self.bt_d, self.lens,
@@ -491,6 +494,10 @@ class LongContext:
             self.v[:, l] = inputs.sym_layer(self.T, H, D, seed=7200 + l, device=d, channel_seed=8200 + l).view(nch, self.CH, H, D)
         self.kd = inputs.sym_layer(self.N_DEC * L, H, D, seed=7300, device=d).view(self.N_DEC, L, 1, H, D)
         self.vd = inputs.sym_layer(self.N_DEC * L, H, D, seed=7400, device=d).view(self.N_DEC, L, 1, H, D)
+        # per-step views built here so the timed loop holds only the library calls
+        self.kd_steps = [self.kd[i] for i in range(self.N_DEC)]
+        self.vd_steps = [self.vd[i] for i in range(self.N_DEC)]
+        self.sm_steps = [self.slot_dec[i:i + 1] for i in range(self.N_DEC)]
         slots = self.num_pages * P
         pd = kvq.kvq_packed_dim(D, self.bits)
         self.kc = torch.empty((L, slots, H, pd), dtype=torch.uint8, device=d)
@@ -511,7 +518,7 @@ class LongContext:
                 kvq.kvq_quant_sym(self.lay, self.k[c], self.v[c], sm, self.kc, self.ks, self.vc, self.vs)
         with tm.span("decode_append_q6_x%d" % self.N_DEC):
             for i in range(self.N_DEC):
-                kvq.kvq_quant_sym(self.lay, self.kd[i], self.vd[i], self.slot_dec[i:i + 1], self.kc, self.ks,
+                kvq.kvq_quant_sym(self.lay, self.kd_steps[i], self.vd_steps[i], self.sm_steps[i], self.kc, self.ks,
                                   self.vc, self.vs)
         with tm.span("dequant_full_q6"):
             kvq.kvq_dequant_sym(self.lay, self.kc, self.ks, self.vc, self.vs, self.bt_d, self.lens, self.ko, self.vo)
