@@ -399,6 +399,8 @@ class Nuq:
         self.v = [inputs.student_t((BH, S, D), 4, seed=1005 + 10 * i, device=d) for i in range(self.copies)]
         self.kd = inputs.student_t((self.n_dec, BH, 1, D), 4, seed=5000, device=d)
         self.vd = inputs.student_t((self.n_dec, BH, 1, D), 4, seed=6000, device=d)
+        self.kd_steps = [self.kd[t] for t in range(self.n_dec)]  # views built before timing
+        self.vd_steps = [self.vd[t] for t in range(self.n_dec)]
         z = lambda *sh, dt=torch.float32: torch.zeros(sh, dtype=dt, device=d)
         self.kl, self.kt = z(BH, D, L), z(BH, D, dt=torch.int16)
         self.vl, self.vl1 = z(BH, S, L), z(BH, 1, L)
@@ -424,7 +426,7 @@ class Nuq:
                                   self.kl, self.kt, self.vl, self.kc, self.vc, *self.lists, self.cnt, self.ws)
         with tm.span("nuq_decode_x%d" % self.n_dec):
             for t in range(self.n_dec):
-                kvq.kvq_nuq_fit_quant(self.kd[t], self.vd[t], self.S + t, self.bits, self.frac, self.iters,
+                kvq.kvq_nuq_fit_quant(self.kd_steps[t], self.vd_steps[t], self.S + t, self.bits, self.frac, self.iters,
                                       self.ns, 0, self.kl, self.kt, self.vl1, self.kc1, self.vc1,
                                       *self.lists1, self.cnt1, self.ws1)
 
