@@ -194,6 +194,59 @@ def test_full_size_sampled(bits):
             assert first_diff(got_o, oracle.sym_dequant_rows(dc, dsc, D, bits)) is None, ("append", l, s_)
 
 
+def test_long_context_sampled():
+    """The long-context workload in its launch configuration: one sequence of
+    262,144 tokens, 16 layers x 4 KV heads x D=256, q6, page 16, quantized in
+    64 launches of 4,096 tokens (all layers each), single-token appends, then
+    one dequant of the whole cache. Compared with the oracle on sampled
+    chunks, layers and positions."""
+    say("sym long context")
+    d = dev()
+    L, H, D, P, bits, T, CH, ND = 16, 4, 256, 16, 6, 262144, 4096, 4
+    total, nch = T + ND, T // CH
+    bt, num_pages = inputs.paged_block_table(1, total, P, seed=5005)
+    k = torch.empty((nch, L, CH, H, D), dtype=torch.float16, device=d)
+    v = torch.empty_like(k)
+    for l in range(L):
+        k[:, l] = inputs.sym_layer(T, H, D, seed=7100 + l, device=d, channel_seed=8100 + l).view(nch, CH, H, D)
+        v[:, l] = inputs.sym_layer(T, H, D, seed=7200 + l, device=d, channel_seed=8200 + l).view(nch, CH, H, D)
+    kd = inputs.sym_layer(ND * L, H, D, seed=7300, device=d).view(ND, L, 1, H, D)
+    pd = kvq.kvq_packed_dim(D, bits)
+    slots = num_pages * P
+    kc = torch.zeros((L, slots, H, pd), dtype=torch.uint8, device=d)
+    vc = torch.zeros_like(kc)
+    ks = torch.zeros((L, slots, H), dtype=torch.int16, device=d)
+    vs = torch.zeros_like(ks)
+    lay = kvq.layout(L, num_pages, P, H, D, bits)
+    slot_ch = [inputs.slot_mapping_for(bt, P, c * CH, CH) for c in range(nch)]
+    for c in range(nch):
+        kvq.kvq_quant_sym(lay, k[c], v[c], slot_ch[c].to(d), kc, ks, vc, vs)
+    slot_dec = inputs.slot_mapping_for(bt, P, T, ND)
+    for i in range(ND):
+        kvq.kvq_quant_sym(lay, kd[i], kd[i], slot_dec[i:i + 1].to(d), kc, ks, vc, vs)
+    ko = torch.empty((L, 1, total, H, D), dtype=torch.float16, device=d)
+    vo = torch.empty_like(ko)
+    kvq.kvq_dequant_sym(lay, kc, ks, vc, vs, bt.to(d), torch.full((1,), total, dtype=torch.int32, device=d), ko, vo)
+    torch.cuda.synchronize()
+    pos = np.r_[0:24, 2040:2056, CH - 24:CH]
+    for c in (0, 31, 63):
+        for l in (0, 7, 15):
+            for name, x, cp, sp, out in (("K", k, kc, ks, ko), ("V", v, vc, vs, vo)):
+                rows = u16(x[c, l, torch.as_tensor(pos, device=d)])  # [n][H][D]
+                rc, rsc = oracle.sym_quant_rows(rows, bits)
+                sl = slot_ch[c][torch.as_tensor(pos)].to(torch.int64).to(d)
+                what = (name, "chunk", c, "layer", l)
+                assert first_diff(cp[l][sl].cpu().numpy(), rc) is None, what + ("codes",)
+                assert first_diff(u16(sp[l][sl]), rsc) is None, what + ("scales",)
+                got_o = u16(out[l, 0, torch.as_tensor(c * CH + pos, device=d)])
+                assert first_diff(got_o, oracle.sym_dequant_rows(rc, rsc, D, bits)) is None, what + ("dequant",)
+    for l in (0, 15):
+        dc, dsc = oracle.sym_quant_rows(u16(kd[:, l, 0]), bits)  # [ND][H]
+        assert first_diff(u16(ko[l, 0, T:T + ND]), oracle.sym_dequant_rows(dc, dsc, D, bits)) is None, ("append", l)
+    del k, v, kc, vc, ko, vo
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("bits,D", [(8, 96), (6, 96), (4, 96), (6, 20), (8, 2), (4, 2), (8, 7),
                                     (6, 2048), (4, 80), (8, 200)])
 def test_generic_head_dims(bits, D):
