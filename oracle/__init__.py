@@ -56,11 +56,11 @@ _SIGS = {
     "orc_kivi_boundary": (_LL, [_LL, _I, _I]),
     "orc_kivi_round_trip": (_I, [_P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P]),
     "orc_nuq_fit": (None, [_P, _I, _I, _I, _P]),
-    "orc_nuq_threshold": (C.c_uint16, [_P, _I, _F]),
+    "orc_nuq_threshold": (C.c_uint16, [_P, _I, C.c_double]),
     "orc_nuq_nearest": (_I, [C.c_uint16, _P, _I]),
     "orc_kivi_pack": (_I, [_P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P]),
     "orc_kivi_unpack": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P]),
-    "orc_nuq_fit_quant": (_I, [_P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I,
+    "orc_nuq_fit_quant": (_I, [_P, _P, _I, _I, _I, _I, _I, C.c_double, _I, _I, _I,
                                _P, _P, _P, _P, _P, _P, _P, _P, _P, _LL, _P, _P, _P]),
 }
 

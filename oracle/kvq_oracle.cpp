@@ -334,9 +334,12 @@ void nuq_fit(const uint16_t *u_bits, int m, int L, int iters, float *lev) {
 // (k+1)-th largest |x| and a sample is an outlier when |x| > tau, so at most k
 // samples per vector are isolated ("nominal" vs "realized" count). n == 0
 // gives tau = 0. Returns tau as an fp16 bit pattern.
-uint16_t nuq_threshold(const uint16_t *x_bits, int n, float frac) {
+// The fraction is a binary64 number: the page's configuration field
+// kvquant_outlier_fraction is a Python float (default 0.01), and f*n is one
+// binary64 product, so 1% of 100 samples is exactly 1.
+uint16_t nuq_threshold(const uint16_t *x_bits, int n, double frac) {
   if (n == 0) return 0;
-  long long k = (long long)std::floor((double)frac * (double)n);
+  long long k = (long long)std::floor(frac * (double)n);
   if (k < 0 || k >= n) std::abort();  // callers keep 0 <= frac < 1
   std::vector<uint16_t> a(n);
   for (int i = 0; i < n; ++i) a[i] = (uint16_t)(x_bits[i] & 0x7fffu);
@@ -641,7 +644,7 @@ int orc_kivi_unpack(const uint8_t *codes, const uint16_t *scale16, const uint16_
 void orc_nuq_fit(const uint16_t *u, int m, int L, int iters, float *levels) {
   nuq_fit(u, m, L, iters, levels);
 }
-uint16_t orc_nuq_threshold(const uint16_t *x, int n, float frac) { return nuq_threshold(x, n, frac); }
+uint16_t orc_nuq_threshold(const uint16_t *x, int n, double frac) { return nuq_threshold(x, n, frac); }
 int orc_nuq_nearest(uint16_t u, const float *levels, int L) {
   return nearest_level((double)h2f(u), levels, L);
 }
@@ -661,14 +664,14 @@ int orc_nuq_nearest(uint16_t u, const float *levels, int L) {
 // exceed out_cap. recon (optional): inliers -> fp16 of their level,
 // outliers and sinks -> x.
 int orc_nuq_fit_quant(const uint16_t *keys, const uint16_t *values, int BH, int S, int D,
-                      int start_pos, int bits, float frac, int iters, int n_sink, int fit_keys,
+                      int start_pos, int bits, double frac, int iters, int n_sink, int fit_keys,
                       float *key_levels, uint16_t *key_thresh, float *value_levels,
                       uint8_t *k_codes, uint8_t *v_codes, int32_t *k_opos, uint16_t *k_oval,
                       int32_t *v_opos, uint16_t *v_oval, long long out_cap,
                       long long *out_counts, uint16_t *k_recon, uint16_t *v_recon) {
   if (bits < 1 || bits > 4 || BH <= 0 || S <= 0 || D <= 0 || ((long long)D * bits) % 8 != 0)
     return -1;
-  if (!(frac >= 0.0f && frac < 1.0f) || iters < 0) return -1;
+  if (!(frac >= 0.0 && frac < 1.0) || iters < 0) return -1;
   const int L = 1 << bits;
   const long long cpr = (long long)D * bits / 8;
   const int n_sink_eff = (start_pos == 0) ? std::min(std::max(n_sink, 0), S) : 0;

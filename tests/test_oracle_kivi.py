@@ -191,3 +191,135 @@ def test_chunking_independence(orc, chunks):
     K2, V2, n2 = run(chunks)
     assert n1 == n2 == (T - R) // gs * gs
     assert np.array_equal(K1, K2) and np.array_equal(V1, V2)
+
+
+# ------------------------------------------------------------------ library cross-check
+def _torch_round_trip(x_u16, lo, hi, per_channel, bits, gs, eps=1e-8):
+    """The kivi_cache page's group round trip (_quant_dequant_along) restated
+    with torch CPU eager operations, one IEEE operation per step: float32
+    cast, edge-replicating pad to whole groups, group min / max, scale =
+    (max - min) / levels then the maximum with eps, (x - min) / scale, round
+    (half to even), clip to [0, levels], then the product and the sum as two
+    separate operations, cast to fp16. Returns (fp16 bits, codes)."""
+    import torch
+
+    x = torch.from_numpy(np.ascontiguousarray(x_u16).view(np.int16).copy()).view(torch.float16)
+    out = x.clone()
+    sl = x[:, :, lo:hi].to(torch.float32)
+    axis = 2 if per_channel else 3
+    n = sl.shape[axis]
+    pad = (-n) % gs
+    if pad:
+        last = sl.narrow(axis, n - 1, 1)
+        reps = [1, 1, 1, 1]
+        reps[axis] = pad
+        sl = torch.cat([sl, last.repeat(*reps)], dim=axis)
+    shp = list(sl.shape)
+    g = sl.reshape(*shp[:axis], shp[axis] // gs, gs, *shp[axis + 1:])
+    gmin = g.amin(dim=axis + 1, keepdim=True)
+    gmax = g.amax(dim=axis + 1, keepdim=True)
+    levels = torch.full_like(gmin, float((1 << bits) - 1))
+    scale = torch.div(torch.sub(gmax, gmin), levels)
+    scale = torch.maximum(scale, torch.full_like(scale, eps))
+    q = torch.round(torch.div(torch.sub(g, gmin), scale))
+    q = torch.clamp(q, torch.zeros_like(q), levels.expand_as(q))
+    prod = torch.mul(q, scale)
+    rec = torch.add(prod, gmin)
+    rec = rec.reshape(shp).narrow(axis, 0, n).to(torch.float16)
+    out[:, :, lo:hi] = rec
+    codes = q.reshape(shp).narrow(axis, 0, n).to(torch.int64).numpy()
+    return out.view(torch.int16).numpy().view(np.uint16), codes
+
+
+def _unpack_codes(codes, D, bits):
+    cb = np.unpackbits(codes, axis=-1, bitorder="little")[..., : D * bits]
+    return (cb.reshape(*cb.shape[:-1], D, bits) * (1 << np.arange(bits))).sum(-1)
+
+
+def _tie_data(rng, B, H, S, D, lo, hi, gs, bits, per_channel):
+    """Groups whose scale is a power of two (max - min = levels * 2^e) and
+    whose other members sit exactly half-way between two codes, so every
+    quotient (x - min)/scale of a non-end member is an exact .5 tie."""
+    m = (1 << bits) - 1
+    x = rng.standard_normal((B, H, S, D))
+    e = -3 if bits < 8 else -7
+    sl = x[:, :, lo:hi]
+    axis = 2 if per_channel else 3
+    n = sl.shape[axis]
+    ng = (n + gs - 1) // gs
+    for gi in range(ng):
+        a, b = gi * gs, min(gi * gs + gs, n)
+        idx = [slice(None)] * 4
+        idx[axis] = slice(a, b)
+        blk = np.moveaxis(sl[tuple(idx)], axis, -1)
+        base = rng.integers(-64, 64, size=blk.shape[:-1] + (1,)) * 2.0 ** (e - 1)
+        half = rng.integers(0, m, size=blk.shape) + 0.5
+        vals = base + half * 2.0 ** e
+        vals[..., 0] = base[..., 0]
+        if b - a > 1:
+            vals[..., -1] = base[..., 0] + m * 2.0 ** e
+        sl[tuple(idx)] = np.moveaxis(vals, -1, axis)
+    xf = x.astype(np.float16)
+    assert np.array_equal(xf[:, :, lo:hi].astype(np.float64), sl)  # every value exact in fp16
+    return xf
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("per_channel", [1, 0])
+def test_matches_torch_transliteration(orc, bits, per_channel):
+    """Bit-for-bit against the torch restatement on random data (ragged last
+    groups on both axes) and on exact-tie data."""
+    rng = np.random.default_rng(40 + bits + 7 * per_channel)
+    B, H, S, D, gs = 2, 3, 150, 72, 32
+    lo, hi = 6, 141                                   # 135 tokens: ragged key group
+    x = rng.standard_normal((B, H, S, D)) * rng.choice([0.01, 1, 30], size=(B, H, 1, D))
+    for data in (x.astype(np.float16), _tie_data(rng, B, H, S, D, lo, hi, gs, bits, per_channel)):
+        rec, codes, _, _ = orc.kivi_round_trip(data.view(np.uint16), lo, hi, per_channel, bits, gs,
+                                               want_params=True)
+        ref, qref = _torch_round_trip(data.view(np.uint16), lo, hi, per_channel, bits, gs)
+        assert np.array_equal(rec, ref)
+        assert np.array_equal(_unpack_codes(codes, D, bits), qref)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("per_channel", [1, 0])
+def test_exact_ties_round_to_even(orc, bits, per_channel):
+    """A member half-way between codes c and c + 1 gets the even one (the page
+    rounds with mx.round, which rounds half to even)."""
+    rng = np.random.default_rng(60 + bits + 7 * per_channel)
+    B, H, S, D, gs = 2, 2, 100, 64, 16
+    lo, hi = 3, 99
+    x = _tie_data(rng, B, H, S, D, lo, hi, gs, bits, per_channel)
+    _, codes, scale, mn = orc.kivi_round_trip(x.view(np.uint16), lo, hi, per_channel, bits, gs, want_params=True)
+    c = _unpack_codes(codes, D, bits)
+    e = -3 if bits < 8 else -7
+    assert np.all(scale == np.float32(2.0 ** e))
+    t = x[:, :, lo:hi].astype(np.float64)
+    if per_channel:
+        g = np.arange(hi - lo) // gs
+        t = (t - mn[:, :, g, :]) / 2.0 ** e
+    else:
+        g = np.arange(D) // gs
+        t = (t - mn[..., g]) / 2.0 ** e
+    tie = (t - np.floor(t)) == 0.5
+    assert tie.sum() > 0.8 * t.size
+    assert np.all(c[tie] % 2 == 0)
+    assert np.all(np.abs(c[tie] - t[tie]) == 0.5)
+
+
+def test_reconstruction_rounds_the_product_before_the_sum(orc):
+    """x' = fp16(RN32(RN32(code * scale) + min)): on data where the fused
+    form RN32(code * scale + min) differs, the oracle gives the unfused one."""
+    rng = np.random.default_rng(77)
+    B, H, S, D, gs, bits = 4, 4, 256, 64, 32, 4
+    x = (rng.standard_normal((B, H, S, D)) * 3).astype(np.float16)
+    rec, codes, scale, mn = orc.kivi_round_trip(x.view(np.uint16), 0, S, 0, bits, gs, want_params=True)
+    c = _unpack_codes(codes, D, bits).astype(np.float32)
+    g = np.arange(D) // gs
+    s32, m32 = scale[..., g], mn[..., g]
+    unfused = (c * s32).astype(np.float32) + m32
+    fused = (c.astype(np.float64) * s32.astype(np.float64) + m32.astype(np.float64)).astype(np.float32)
+    differ = unfused.astype(np.float16) != fused.astype(np.float16)
+    assert differ.sum() > 0                     # the data separates the two forms
+    got = rec.view(np.float16)
+    assert np.array_equal(got[differ], unfused.astype(np.float16)[differ])

@@ -148,7 +148,7 @@ def test_threshold_is_the_k_plus_1_th_largest(orc, frac):
         x = f16(rng.standard_t(4, size=n))
         x[: n // 10] = x[0]  # ties
         tau = np.uint16(orc.nuq_threshold(x, frac)).view(np.float16)
-        k = math.floor(float(np.float32(frac)) * n)
+        k = math.floor(frac * n)
         a = np.abs(x.astype(np.float64))
         assert np.sum(a > tau) <= k < np.sum(a >= tau)
 
@@ -203,13 +203,13 @@ def test_outliers_exact_bounded_and_sorted(orc, prefill):
         flag = flag.reshape(BH, S, D)
         assert not flag[:, :4].any()
         if thr_axis == "k":  # per channel over S-4 tokens
-            kmax = math.floor(float(np.float32(0.05)) * (S - 4))
+            kmax = math.floor(0.05 * (S - 4))
             assert flag.sum(1).max() <= kmax
             tau = r["key_thresh"].view(np.float16).astype(np.float64)
             a = np.abs(x.astype(np.float64))[:, 4:]
             assert np.array_equal(flag[:, 4:], a > tau[:, None, :])
         else:                # per token over D channels
-            assert flag.sum(2).max() <= math.floor(float(np.float32(0.05)) * D)
+            assert flag.sum(2).max() <= math.floor(0.05 * D)
         assert np.all(_codes(r["k_codes" if thr_axis == "k" else "v_codes"], D)[flag] == 0)
 
 
@@ -253,3 +253,76 @@ def test_all_sink_prefill_and_tiny_vectors(orc):
     assert np.all(r["key_levels"] == 0) and np.all(r["key_thresh"] == 0)
     r = orc.nuq_fit_quant(k, v, 0, 2, 0.01, 8, 2, 1)   # one non-sink token per channel
     assert np.array_equal(r["k_recon"][:, 2], k.view(np.uint16)[:, 2])  # single sample is its own level
+
+
+# ------------------------------------------------------------------ outlier count reading
+def _distinct_magnitudes(rng, n):
+    """n fp16 values with pairwise different |x| (distinct positive normal
+    patterns) and random signs."""
+    pats = rng.choice(np.arange(0x2c00, 0x5c00, dtype=np.uint16), size=n, replace=False)
+    sign = rng.integers(0, 2, size=n).astype(np.uint16) << 15
+    return (pats | sign).astype(np.uint16)
+
+
+# The page's kvquant_outlier_fraction is a Python float (binary64, default
+# 0.01); the count is floor(fraction * n) of that binary64 product, so whole
+# percentages of round sample counts give the integer one expects.
+@pytest.mark.parametrize("frac,n,k", [(0.01, 100, 1), (0.01, 200, 2), (0.01, 1000, 10), (0.01, 99, 0),
+                                      (0.01, 128, 1), (0.01, 4092, 40), (0.03, 100, 3), (0.05, 100, 5),
+                                      (0.1, 1000, 100), (0.0, 500, 0), (0.5, 7, 3)])
+def test_outlier_count_at_whole_percentages(orc, frac, n, k):
+    rng = np.random.default_rng(n + int(frac * 1000))
+    x = _distinct_magnitudes(rng, n)
+    tau = np.uint16(orc.nuq_threshold(x, frac)).view(np.float16)
+    a = np.abs(x.view(np.float16).astype(np.float64))
+    assert int(np.sum(a > float(tau))) == k
+
+
+def test_prefill_of_104_tokens_with_4_sinks_isolates_one_key_per_channel(orc):
+    """100 non-sink tokens at 1%: exactly one key outlier per channel, and
+    with D = 200 exactly two value outliers per token."""
+    rng = np.random.default_rng(104)
+    BH, S, D = 2, 104, 200
+    k = np.stack([np.stack([_distinct_magnitudes(rng, S) for _ in range(D)], 1) for _ in range(BH)])
+    v = np.stack([np.stack([_distinct_magnitudes(rng, D) for _ in range(S)], 0) for _ in range(BH)])
+    r = orc.nuq_fit_quant(k, v, 0, 3, 0.01, 8, 4, 1)
+    pos = r["k_out"][0]
+    assert len(pos) == BH * D
+    per_ch = np.bincount((pos // (S * D)) * D + pos % D, minlength=BH * D)
+    assert np.all(per_ch == 1)
+    vpos = r["v_out"][0]
+    assert len(vpos) == BH * (S - 4) * 2
+    assert np.all(np.bincount(vpos // D, minlength=BH * S)[np.arange(BH * S) % S >= 4] == 2)
+
+
+# ------------------------------------------------------------------ outliers are left out of the fit
+def test_outliers_are_excluded_from_the_level_fit(orc):
+    """Dense-and-sparse: the levels are fit on the dense part only. Moving the
+    isolated samples further out (they stay the isolated ones, the threshold
+    does not change) leaves every key and value level unchanged, while a fit
+    that included them would move a level (checked on the same data)."""
+    rng = np.random.default_rng(31)
+    BH, S, D = 2, 204, 64
+    k, v = _t4(rng, (BH, S, D)), _t4(rng, (BH, S, D))
+    frac = 0.02
+    r = orc.nuq_fit_quant(k, v, 0, 3, frac, 8, 4, 1)
+    k2 = k.reshape(-1).copy()
+    v2 = v.reshape(-1).copy()
+    kp, vp = r["k_out"][0], r["v_out"][0]
+    assert len(kp) > 0 and len(vp) > 0
+    k2[kp] = f16(k2[kp].astype(np.float64) * 8)
+    v2[vp] = f16(v2[vp].astype(np.float64) * 8)
+    k2, v2 = k2.reshape(k.shape), v2.reshape(v.shape)
+    r2 = orc.nuq_fit_quant(k2, v2, 0, 3, frac, 8, 4, 1)
+    for name in ("key_levels", "key_thresh", "value_levels", "k_codes", "v_codes"):
+        assert np.array_equal(r[name], r2[name]), name
+    assert np.array_equal(r2["k_out"][0], kp) and np.array_equal(r2["v_out"][0], vp)
+    # the pin has power: fitting all samples of a vector moves at least one level
+    moved = 0
+    for bh in range(BH):
+        for d in range(D):
+            col = k2[bh, 4:, d]
+            moved += int(not np.array_equal(orc.nuq_fit(col, 8, 8), r2["key_levels"][bh, d]))
+        for s in range(4, S):
+            moved += int(not np.array_equal(orc.nuq_fit(v2[bh, s], 8, 8), r2["value_levels"][bh, s]))
+    assert moved > 0.5 * BH * (D + S - 4)
