@@ -222,7 +222,8 @@ int kvq_kivi_quant_dequant(uint16_t *keys, uint16_t *values, int32_t B, int32_t 
  * -0 stored as +0); code = clamp(rint((x - zero)/scale), 0, levels) with the
  * fp16 scale; reconstruction fp16(code*scale + zero), product then sum.
  * Storage is indexed by absolute token so that successive flushes fill it in
- * place:
+ * place (the fp16 side may be a window of the sequence, see x_rows / x_t0
+ * and out_rows / out_t0):
  *   codes   uint8 [B][H][S_cap][D*bits/8], LSB-first along D;
  *   keys    groups of group_size tokens from token 0 (lo must be a multiple
  *           of group_size): scale, zero fp16 [B][H][ceil(S_cap/group_size)][D];
@@ -231,32 +232,39 @@ int kvq_kivi_quant_dequant(uint16_t *keys, uint16_t *values, int32_t B, int32_t 
  * Requires D % 8 == 0 and group_size a positive multiple of 8; bits 2, 4,
  * 8; all pointers device memory, caller-owned, 16-byte aligned. */
 
-/* Quantize tokens [lo, hi) of keys and/or values (fp16 [B][H][S_cap][D],
- * not modified) into packed storage; the other tokens' storage is not
- * touched. keys or values may be NULL to skip that side (its outputs are
- * then unused); a given side needs all three outputs. hi == lo is a no-op.
+/* Quantize tokens [lo, hi) of keys and/or values into packed storage; the
+ * other tokens' storage is not touched. keys / values: fp16
+ * [B][H][x_rows][D], not modified, row r holding token x_t0 + r (so a
+ * residual window can be packed without copying it into a full-length
+ * buffer; x_rows = S_cap, x_t0 = 0 for a full-length buffer); needs
+ * 0 <= x_t0 <= lo and hi <= x_t0 + x_rows. keys or values may be NULL to skip
+ * that side (its outputs are then unused); a given side needs all three
+ * outputs. hi == lo is a no-op.
  * Errors: KVQ_ERR_NULL, KVQ_ERR_BITS, KVQ_ERR_SHAPE, KVQ_ERR_ARG (eps),
  * KVQ_ERR_ALIGN, KVQ_ERR_HIP. Asynchronous on `stream`. */
 int kvq_kivi_pack(const uint16_t *keys, const uint16_t *values, int32_t B, int32_t H, int32_t S_cap, int32_t D,
                   int32_t lo, int32_t hi, int32_t bits, int32_t group_size, float eps, uint8_t *k_codes,
                   uint16_t *k_scale, uint16_t *k_zero, uint8_t *v_codes, uint16_t *v_scale, uint16_t *v_zero,
-                  void *stream);
+                  int32_t x_rows, int32_t x_t0, void *stream);
 
-/* Reconstruct tokens [lo, hi) from packed storage into k_out / v_out (fp16
- * [B][H][S_cap][D], the same token positions; other tokens not written).
+/* Reconstruct tokens [lo, hi) from packed storage into k_out / v_out, fp16
+ * [B][H][out_rows][D] with token t written to row t - out_t0 (needs
+ * 0 <= out_t0 <= lo and hi <= out_t0 + out_rows; other rows not written).
  * Either output may be NULL to skip that side. Errors as kvq_kivi_pack
  * (no eps). Asynchronous on `stream`. */
 int kvq_kivi_unpack(const uint8_t *k_codes, const uint16_t *k_scale, const uint16_t *k_zero, const uint8_t *v_codes,
                     const uint16_t *v_scale, const uint16_t *v_zero, int32_t B, int32_t H, int32_t S_cap, int32_t D,
                     int32_t lo, int32_t hi, int32_t bits, int32_t group_size, uint16_t *k_out, uint16_t *v_out,
-                    void *stream);
+                    int32_t out_rows, int32_t out_t0, void *stream);
 
 /* ------------------------------------------------------------------ NUQ
  * ["veloxquant_mlx.cache.kvquant_cache module", module docstring] KVQuant-style
  * non-uniform quantization. Keys get one table of L = 2^bits levels per
  * channel (samples: the channel's values over tokens), values one table per
  * token (samples: the token's D channels). Per vector of n samples:
- *   k = floor(frac * n) (in double); tau = the (k+1)-th largest |x|; samples
+ *   k = floor(frac * n) with frac a binary64 number and one binary64 product
+ *   (the page's outlier fraction is a Python float: 1% of 100 samples is 1);
+ *   tau = the (k+1)-th largest |x|; samples
  *   with |x| > tau are outliers (at most k), kept exact in a side channel;
  *   the inliers are fit by `lloyd_iters` Lloyd-Max iterations (unweighted
  *   1-D k-means) from linear-interpolated quantiles at probabilities
@@ -284,13 +292,13 @@ int kvq_kivi_unpack(const uint8_t *k_codes, const uint16_t *k_scale, const uint1
  * BH*n_fit*floor(frac*D), with n_fit = S minus the call's sink tokens.
  * -1 on invalid arguments. */
 int64_t kvq_nuq_outlier_bound(int32_t BH, int32_t S, int32_t D, int32_t start_pos, int32_t n_sink,
-                              float frac, int32_t fit_keys, int32_t which);
+                              double frac, int32_t fit_keys, int32_t which);
 
 /* [host] Bytes of device workspace kvq_nuq_fit_quant needs for these sizes
  * (scratch: per-channel thresholds, per-block counters, outlier staging).
  * -1 on invalid arguments. */
 int64_t kvq_nuq_workspace_bytes(int32_t BH, int32_t S, int32_t D, int32_t bits, int32_t start_pos,
-                                int32_t n_sink, float frac, int32_t fit_keys);
+                                int32_t n_sink, double frac, int32_t fit_keys);
 
 /* One NUQ call over fp16 keys and values [BH][S][D] (BH = batch*kv_heads).
  *   bits 1..4 (L = 2^bits); D in {32, 64, 128, 256}; 0 <= frac < 1;
@@ -316,7 +324,7 @@ int64_t kvq_nuq_workspace_bytes(int32_t BH, int32_t S, int32_t D, int32_t bits, 
  * Errors: KVQ_ERR_NULL, KVQ_ERR_BITS, KVQ_ERR_SHAPE, KVQ_ERR_ARG (frac,
  * iters), KVQ_ERR_CAPACITY, KVQ_ERR_ALIGN, KVQ_ERR_HIP. */
 int kvq_nuq_fit_quant(const uint16_t *keys, const uint16_t *values, int32_t BH, int32_t S, int32_t D,
-                      int32_t start_pos, int32_t bits, float frac, int32_t lloyd_iters, int32_t n_sink,
+                      int32_t start_pos, int32_t bits, double frac, int32_t lloyd_iters, int32_t n_sink,
                       int32_t fit_keys, float *key_levels, uint16_t *key_thresh, float *value_levels,
                       uint8_t *k_codes, uint8_t *v_codes, int32_t *k_opos, uint16_t *k_oval,
                       int32_t *v_opos, uint16_t *v_oval, int64_t out_cap, int64_t *out_counts,

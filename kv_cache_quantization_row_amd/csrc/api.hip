@@ -345,13 +345,15 @@ int kvq_kivi_quant_dequant(uint16_t *keys, uint16_t *values, int32_t B, int32_t 
   a.code_t0 = lo;
   a.kgrp_rows = (int32_t)((n + group_size - 1) / group_size);
   a.kgrp0 = 0;
+  a.x_rows = S_cap;
+  a.x_t0 = 0;
   return hip_status(kvq::launch_kivi(a, (hipStream_t)stream), "kvq_kivi_quant_dequant launch");
 }
 
 int kvq_kivi_pack(const uint16_t *keys, const uint16_t *values, int32_t B, int32_t H, int32_t S_cap, int32_t D,
                   int32_t lo, int32_t hi, int32_t bits, int32_t group_size, float eps, uint8_t *k_codes,
                   uint16_t *k_scale, uint16_t *k_zero, uint8_t *v_codes, uint16_t *v_scale, uint16_t *v_zero,
-                  void *stream) {
+                  int32_t x_rows, int32_t x_t0, void *stream) {
   if (!keys && !values) return fail(KVQ_ERR_NULL, "neither keys nor values given");
   if (keys && (!k_codes || !k_scale || !k_zero)) return fail(KVQ_ERR_NULL, "key codes, scale and zero are required");
   if (values && (!v_codes || !v_scale || !v_zero))
@@ -363,6 +365,8 @@ int kvq_kivi_pack(const uint16_t *keys, const uint16_t *values, int32_t B, int32
     return fail(KVQ_ERR_SHAPE, "packed storage needs D %% 8 == 0 and group_size a positive multiple of 8");
   if (keys && lo % group_size)
     return fail(KVQ_ERR_SHAPE, "key groups start at token 0: lo=%d must be a multiple of group_size", lo);
+  if (x_rows < 0 || x_t0 < 0 || (hi > lo && (x_t0 > lo || (int64_t)hi > (int64_t)x_t0 + x_rows)))
+    return fail(KVQ_ERR_SHAPE, "input rows [%d, %d + %d) do not hold tokens [%d, %d)", x_t0, x_t0, x_rows, lo, hi);
   if (!(eps > 0.0f) || !(eps < 3.0e38f)) return fail(KVQ_ERR_ARG, "eps must be positive and finite");
   for (const void *p : {(const void *)keys, (const void *)values, (const void *)k_codes, (const void *)v_codes,
                         (const void *)k_scale, (const void *)k_zero, (const void *)v_scale, (const void *)v_zero})
@@ -370,7 +374,8 @@ int kvq_kivi_pack(const uint16_t *keys, const uint16_t *values, int32_t B, int32
   const int64_t BH = (int64_t)B * H;
   if (hi == lo || BH == 0) return ok();
   const int64_t n = hi - lo;
-  if (BH * S_cap * D >= ((int64_t)1 << 46)) return fail(KVQ_ERR_SHAPE, "tensor too large");
+  if (BH * S_cap * D >= ((int64_t)1 << 46) || BH * x_rows * D >= ((int64_t)1 << 46))
+    return fail(KVQ_ERR_SHAPE, "tensor too large");
   if ((BH * n + 255) / 256 * 64 >= ((int64_t)1 << 31)) return fail(KVQ_ERR_SHAPE, "too many rows");
   kvq::KiviArgs a{};
   a.keys = const_cast<uint16_t *>(keys);  // read only: packed mode writes no reconstruction
@@ -394,13 +399,15 @@ int kvq_kivi_pack(const uint16_t *keys, const uint16_t *values, int32_t B, int32
   a.code_t0 = 0;
   a.kgrp_rows = (int32_t)(((int64_t)S_cap + group_size - 1) / group_size);
   a.kgrp0 = lo / group_size;
+  a.x_rows = x_rows;
+  a.x_t0 = x_t0;
   return hip_status(kvq::launch_kivi(a, (hipStream_t)stream), "kvq_kivi_pack launch");
 }
 
 int kvq_kivi_unpack(const uint8_t *k_codes, const uint16_t *k_scale, const uint16_t *k_zero, const uint8_t *v_codes,
                     const uint16_t *v_scale, const uint16_t *v_zero, int32_t B, int32_t H, int32_t S_cap, int32_t D,
                     int32_t lo, int32_t hi, int32_t bits, int32_t group_size, uint16_t *k_out, uint16_t *v_out,
-                    void *stream) {
+                    int32_t out_rows, int32_t out_t0, void *stream) {
   if (!k_out && !v_out) return fail(KVQ_ERR_NULL, "neither key nor value output given");
   if (k_out && (!k_codes || !k_scale || !k_zero)) return fail(KVQ_ERR_NULL, "key codes, scale and zero are required");
   if (v_out && (!v_codes || !v_scale || !v_zero))
@@ -410,12 +417,16 @@ int kvq_kivi_unpack(const uint8_t *k_codes, const uint16_t *k_scale, const uint1
   if (lo < 0 || hi < lo || hi > S_cap) return fail(KVQ_ERR_SHAPE, "need 0 <= lo <= hi <= S_cap");
   if (group_size <= 0 || group_size % 8 || D % 8)
     return fail(KVQ_ERR_SHAPE, "packed storage needs D %% 8 == 0 and group_size a positive multiple of 8");
+  if (out_rows < 0 || out_t0 < 0 || (hi > lo && (out_t0 > lo || (int64_t)hi > (int64_t)out_t0 + out_rows)))
+    return fail(KVQ_ERR_SHAPE, "output rows [%d, %d + %d) do not hold tokens [%d, %d)", out_t0, out_t0, out_rows, lo,
+                hi);
   for (const void *p : {(const void *)k_codes, (const void *)v_codes, (const void *)k_scale, (const void *)k_zero,
                         (const void *)v_scale, (const void *)v_zero, (const void *)k_out, (const void *)v_out})
     if (p && !aligned(p, 16)) return fail(KVQ_ERR_ALIGN, "packed KIVI tensors need 16-byte alignment");
   const int64_t BH = (int64_t)B * H;
   if (hi == lo || BH == 0) return ok();
-  if (BH * S_cap * D >= ((int64_t)1 << 46)) return fail(KVQ_ERR_SHAPE, "tensor too large");
+  if (BH * S_cap * D >= ((int64_t)1 << 46) || BH * out_rows * D >= ((int64_t)1 << 46))
+    return fail(KVQ_ERR_SHAPE, "tensor too large");
   if ((int64_t)(hi - lo) * (D / 8) >= ((int64_t)1 << 31) - 256 || (BH + 65534) / 65535 > 65535)
     return fail(KVQ_ERR_SHAPE, "too many rows");
   kvq::KiviUnpackArgs a{};
@@ -426,6 +437,8 @@ int kvq_kivi_unpack(const uint8_t *k_codes, const uint16_t *k_scale, const uint1
   a.hi = hi;
   a.bits = bits;
   a.gs = group_size;
+  a.out_rows = out_rows;
+  a.out_t0 = out_t0;
   for (int side = 0; side < 2; ++side) {
     uint16_t *out = side ? v_out : k_out;
     if (!out) continue;
@@ -449,16 +462,17 @@ struct NuqPlan {
   int64_t off_ctr, off_kblk, off_vblk, off_ksup, off_vsup, off_kpos, off_kval, off_vpos, off_vval, total;
 };
 
-int64_t floor_frac(float frac, int64_t n) { return (int64_t)std::floor((double)frac * (double)n); }
+// outliers per vector of n samples: floor(frac * n), one binary64 product
+int64_t floor_frac(double frac, int64_t n) { return (int64_t)std::floor(frac * (double)n); }
 
 int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
 int nuq_plan(int32_t BH, int32_t S, int32_t D, int32_t bits, int32_t start_pos, int32_t n_sink,
-             float frac, int32_t fit_keys, NuqPlan &p) {
+             double frac, int32_t fit_keys, NuqPlan &p) {
   if (bits < 1 || bits > 4) return fail(KVQ_ERR_BITS, "NUQ bits=%d is not in 1..4", bits);
   if (BH <= 0 || S <= 0) return fail(KVQ_ERR_SHAPE, "BH and S must be positive");
   if (D != 32 && D != 64 && D != 128 && D != 256) return fail(KVQ_ERR_SHAPE, "NUQ head_dim must be 32, 64, 128 or 256 (got %d)", D);
-  if (!(frac >= 0.0f && frac < 1.0f)) return fail(KVQ_ERR_ARG, "outlier fraction must be in [0, 1)");
+  if (!(frac >= 0.0 && frac < 1.0)) return fail(KVQ_ERR_ARG, "outlier fraction must be in [0, 1)");
   if (start_pos < 0 || n_sink < 0) return fail(KVQ_ERR_ARG, "start_pos and n_sink must be >= 0");
   if ((int64_t)BH * S * D >= ((int64_t)1 << 31)) return fail(KVQ_ERR_SHAPE, "BH*S*D must be < 2^31 (int32 outlier positions)");
   if (BH > 65535) return fail(KVQ_ERR_SHAPE, "BH must be <= 65535");
@@ -492,21 +506,21 @@ int nuq_plan(int32_t BH, int32_t S, int32_t D, int32_t bits, int32_t start_pos, 
 }  // namespace
 
 int64_t kvq_nuq_outlier_bound(int32_t BH, int32_t S, int32_t D, int32_t start_pos, int32_t n_sink,
-                              float frac, int32_t fit_keys, int32_t which) {
+                              double frac, int32_t fit_keys, int32_t which) {
   NuqPlan p;
   if (nuq_plan(BH, S, D, 1, start_pos, n_sink, frac, fit_keys, p) != KVQ_OK) return -1;
   return which == 0 ? p.kb : (which == 1 ? p.vb : -1);
 }
 
 int64_t kvq_nuq_workspace_bytes(int32_t BH, int32_t S, int32_t D, int32_t bits, int32_t start_pos,
-                                int32_t n_sink, float frac, int32_t fit_keys) {
+                                int32_t n_sink, double frac, int32_t fit_keys) {
   NuqPlan p;
   if (nuq_plan(BH, S, D, bits, start_pos, n_sink, frac, fit_keys, p) != KVQ_OK) return -1;
   return p.total;
 }
 
 int kvq_nuq_fit_quant(const uint16_t *keys, const uint16_t *values, int32_t BH, int32_t S, int32_t D,
-                      int32_t start_pos, int32_t bits, float frac, int32_t lloyd_iters, int32_t n_sink,
+                      int32_t start_pos, int32_t bits, double frac, int32_t lloyd_iters, int32_t n_sink,
                       int32_t fit_keys, float *key_levels, uint16_t *key_thresh, float *value_levels,
                       uint8_t *k_codes, uint8_t *v_codes, int32_t *k_opos, uint16_t *k_oval,
                       int32_t *v_opos, uint16_t *v_oval, int64_t out_cap, int64_t *out_counts,
@@ -543,7 +557,8 @@ int kvq_nuq_fit_quant(const uint16_t *keys, const uint16_t *values, int32_t BH, 
   a.iters = lloyd_iters;
   a.fit_keys = fit_keys ? 1 : 0;
   a.n_sink_eff = p.n_sink_eff;
-  a.frac = frac;
+  a.k_key = (int32_t)floor_frac(frac, p.n_fit);
+  a.k_val = (int32_t)floor_frac(frac, D);
   a.key_levels = key_levels;
   a.key_thresh = key_thresh;
   a.value_levels = value_levels;

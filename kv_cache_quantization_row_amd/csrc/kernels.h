@@ -46,6 +46,8 @@ struct KiviArgs {
   int32_t code_t0;     // token of row 0: lo, or 0 when packed
   int32_t kgrp_rows;   // key parameter groups per (b, h): ceil((hi-lo)/gs), or ceil(S_cap/gs)
   int32_t kgrp0;       // group index of the first group (0, or lo/gs when packed)
+  int32_t x_rows;      // fp16 rows per (b, h) of keys / values (S_cap in place)
+  int32_t x_t0;        // token held by fp16 row 0 (0 in place)
 };
 
 hipError_t launch_kivi(const KiviArgs &a, hipStream_t st);
@@ -53,9 +55,10 @@ hipError_t launch_kivi(const KiviArgs &a, hipStream_t st);
 struct KiviUnpackArgs {
   const uint8_t *codes;            // [BH][S_cap][D*bits/8]
   const uint16_t *scale, *zero;    // fp16: keys [BH][ceil(S_cap/gs)][D], values [BH][S_cap][ceil(D/gs)]
-  uint16_t *out;                   // fp16 [BH][S_cap][D], tokens [lo, hi) written
+  uint16_t *out;                   // fp16 [BH][out_rows][D]: token t in row t - out_t0, tokens [lo, hi) written
   int64_t BH;
   int32_t S_cap, D, lo, hi, bits, gs, per_channel;
+  int32_t out_rows, out_t0;
   int32_t chunk_shift, gs_shift;   // log2(D/8), log2(gs) when powers of two, else -1 (set by the launcher)
 };
 hipError_t launch_kivi_unpack(KiviUnpackArgs a, hipStream_t st);
@@ -63,7 +66,7 @@ hipError_t launch_kivi_unpack(KiviUnpackArgs a, hipStream_t st);
 struct NuqArgs {
   const uint16_t *keys, *values;   // fp16 [BH][S][D]
   int32_t BH, S, D, bits, iters, fit_keys, n_sink_eff;
-  float frac;
+  int32_t k_key, k_val;            // outliers per vector: floor(frac * n) for a key fit (n = non-sink tokens), a value token (n = D)
   float *key_levels;               // [BH][D][L]
   uint16_t *key_thresh;            // [BH][D]
   float *value_levels;             // [BH][S][L]

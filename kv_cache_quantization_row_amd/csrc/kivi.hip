@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void kivi_keys_fast(KiviArgs a) {
   const int t0 = a.lo + g * a.gs;
   const int cnt = min(a.gs, a.hi - t0);
   const int ch = lane % CL, tr = lane / CL;
-  uint16_t *base = a.keys + ((size_t)bh * a.S_cap + t0) * D + ch * 8;
+  uint16_t *base = a.keys + ((size_t)bh * a.x_rows + (t0 - a.x_t0)) * D + ch * 8;
 
   uint4 v[NI];
   bool ok[NI];
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(256) void kivi_keys_generic(KiviArgs a) {
   const int64_t bh = tg / ng;
   const int t0 = a.lo + g * a.gs, t1 = min(t0 + a.gs, a.hi);
   const float lev = (float)((1 << a.bits) - 1);
-  uint16_t *col = a.keys + (size_t)bh * a.S_cap * D + ck * C;
+  uint16_t *col = a.keys + (size_t)bh * a.x_rows * D + ck * C;  // row t - x_t0 holds token t
   float mn[C], mx[C], sc[C];
   for (int i = 0; i < C; ++i) {
     mn[i] = __builtin_inff();
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(256) void kivi_keys_generic(KiviArgs a) {
   }
   for (int t = t0; t < t1; ++t)
     for (int i = 0; i < C; ++i) {
-      const float x = h2f(col[(size_t)t * D + i]);
+      const float x = h2f(col[(size_t)(t - a.x_t0) * D + i]);
       mn[i] = fminf(mn[i], x);
       mx[i] = fmaxf(mx[i], x);
     }
@@ -323,8 +323,8 @@ __global__ __launch_bounds__(256) void kivi_keys_generic(KiviArgs a) {
     uint64_t packed = 0;
     for (int i = 0; i < C; ++i) {
       uint32_t c;
-      const uint16_t r = kivi_elem(h2f(col[(size_t)t * D + i]), mn[i], sc[i], lev, c);
-      if (!a.packed) col[(size_t)t * D + i] = r;
+      const uint16_t r = kivi_elem(h2f(col[(size_t)(t - a.x_t0) * D + i]), mn[i], sc[i], lev, c);
+      if (!a.packed) col[(size_t)(t - a.x_t0) * D + i] = r;
       packed |= (uint64_t)c << (a.bits * i);
     }
     if (C == 8 && a.k_codes) {
@@ -355,7 +355,7 @@ __global__ __launch_bounds__(256) void kivi_values_fast(KiviArgs a) {
   const int64_t bh = blockIdx.y;
   const int ch = lane % CL, tr = lane / CL;
   const int ng = D / (LPG * 8);
-  uint16_t *vb = a.values + ((size_t)bh * a.S_cap + a.lo) * D + ch * 8;
+  uint16_t *vb = a.values + ((size_t)bh * a.x_rows + (a.lo - a.x_t0)) * D + ch * 8;
 
   uint4 v[U];
   int tok[U];  // token offset from lo
@@ -435,7 +435,7 @@ __global__ __launch_bounds__(256) void kivi_values_generic(KiviArgs a) {
   const int64_t row = bh * a.code_rows + (t - a.code_t0);  // code / parameter row
   const int d0 = g * a.gs, d1 = min(d0 + a.gs, D);
   const float lev = (float)((1 << a.bits) - 1);
-  uint16_t *r = a.values + ((size_t)bh * a.S_cap + t) * D;
+  uint16_t *r = a.values + ((size_t)bh * a.x_rows + (t - a.x_t0)) * D;
   float mn = __builtin_inff(), mx = -__builtin_inff();
   for (int d = d0; d < d1; ++d) {
     const float x = h2f(r[d]);
@@ -490,7 +490,8 @@ __global__ __launch_bounds__(256) void kivi_unpack(KiviUnpackArgs a) {
   const int tb = (int)(a.chunk_shift >= 0 ? i >> a.chunk_shift : i / (uint32_t)chunks);
   const int t0 = a.lo + tb * KIVI_UNPACK_ROWS;
   const int rows = min(KIVI_UNPACK_ROWS, a.hi - t0);
-  const int64_t row0 = bh * a.S_cap + t0;
+  const int64_t row0 = bh * a.S_cap + t0;                  // storage row of token t0
+  const int64_t orow0 = bh * a.out_rows + (t0 - a.out_t0);  // output row of token t0
   const int ngv = (a.D + a.gs - 1) / a.gs;
   float s[8], z[8];
   int cur_tg = -1;  // key group whose parameters s, z hold
@@ -540,7 +541,7 @@ __global__ __launch_bounds__(256) void kivi_unpack(KiviUnpackArgs a) {
       const uint32_t h = f2h(__builtin_fmaf(c, s[e], z[e]));
       if (e & 1) o[e / 2] |= h << 16; else o[e / 2] = h;
     }
-    *reinterpret_cast<uint4 *>(a.out + row * a.D + 8 * k) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4 *>(a.out + (orow0 + r) * a.D + 8 * k) = make_uint4(o[0], o[1], o[2], o[3]);
   }
 }
 

@@ -273,14 +273,14 @@ struct FitOut {
 // Fit one vector split over CPC lanes (this lane holds `nq` valid samples in
 // its sorted chunk `c`). Returns levels (identical in all CPC lanes).
 template <int CPC, int L>
-__device__ void fit_vector(const Chunk &c, int nq, float frac, int iters, float *lev, FitOut &fo) {
+__device__ void fit_vector(const Chunk &c, int nq, int kout, int iters, float *lev, FitOut &fo) {
   const int n = gsum<CPC>(nq);
   fo.tau = 0;
   fo.tau_key = key16(0);
 #pragma unroll
   for (int j = 0; j < L; ++j) lev[j] = 0.0f;
   if (n == 0) return;
-  const long long k = (long long)floor((double)frac * (double)n);
+  const long long k = kout;  // floor(frac * n), computed on the host
   // ---- tau: largest non-negative fp16 c with #{|x| >= c} >= k + 1
   uint32_t tau;
   if (CPC == 1) {
@@ -534,7 +534,7 @@ __device__ __forceinline__ void merge_lanes(uint32_t *v, int q) {
 // the chunks before it. CPC >= L: lane q < L does the work of level q. The
 // result equals fit_vector's.
 template <int CPC, int L>
-__device__ void fit_global(const uint32_t *lds, const double *tbl, int lane, int n, uint32_t last, float frac,
+__device__ void fit_global(const uint32_t *lds, const double *tbl, int lane, int n, uint32_t last, int kout,
                            int iters, float *lev, FitOut &fo) {
   const int q = lane % CPC, gb = lane - q;        // group base (workgroup lane)
   const int wb = (lane & 63) - q;                 // group base inside the wave
@@ -571,7 +571,7 @@ __device__ void fit_global(const uint32_t *lds, const double *tbl, int lane, int
 #pragma unroll
   for (int j = 0; j < L; ++j) lev[j] = 0.0f;
   if (n == 0) return;
-  const long long k = (long long)floor((double)frac * (double)n);
+  const long long k = kout;    // floor(frac * n), computed on the host
   const int kp1 = (int)k + 1;  // <= n (frac < 1)
   // ---- tau: the k+1 largest |x| lie among the kp1 smallest and the kp1
   // largest samples, so the counts of the bitwise search run over those
@@ -806,10 +806,10 @@ __global__ __launch_bounds__(KF_T) void nuq_key_fit(NuqArgs a) {
   if constexpr (CPC >= L) {
     __syncthreads();  // the fit reads the other lanes' chunks and sums
     fit_global<CPC, L>(lds, reinterpret_cast<const double *>(lds + KF_T * 64), lane, active ? nfit : 0, last,
-                       a.frac, a.iters, lev, fo);
+                       a.k_key, a.iters, lev, fo);
   } else {
     Chunk c{lds + lane * 64, lane & 63};
-    fit_vector<CPC, L>(c, nq, a.frac, a.iters, lev, fo);
+    fit_vector<CPC, L>(c, nq, a.k_key, a.iters, lev, fo);
   }
   if (active && q == 0) {
     float *kl = a.key_levels + ((size_t)bh * a.D + d) * L;
@@ -1059,7 +1059,7 @@ __global__ __launch_bounds__(64) void nuq_value(NuqArgs a) {
   Chunk c{lds + lane * 64, lane & 63};
   float lev[L];
   FitOut fo;
-  fit_vector<CPC, L>(c, nq, a.frac, a.iters, lev, fo);
+  fit_vector<CPC, L>(c, nq, a.k_val, a.iters, lev, fo);
   uint32_t T[L];
   cut_keys<L>(lev, T);
   if (valid && q == 0) {
@@ -1263,7 +1263,7 @@ __device__ __forceinline__ void value_wave_body(const NuqArgs &a, int64_t tok, b
   for (int j = 0; j < L; ++j) lev[j] = 0.0f;
   uint32_t tau = 0x7fffu;  // no outliers in sink tokens
   if (!sink) {
-    const long long k = (long long)floor((double)a.frac * (double)D);
+    const long long k = a.k_val;  // floor(frac * D), computed on the host
     // ---- tau: largest c with #{|x| >= c} >= k + 1
     int pos = 0;
     for (int sb = 16384; sb >= 1; sb >>= 1) {

@@ -35,6 +35,7 @@ _P = C.c_void_p
 _I = C.c_int32
 _L = C.c_int64
 _F = C.c_float
+_D = C.c_double
 _SIGS = {
     "kvq_last_error": (C.c_char_p, []),
     "kvq_version": (C.c_char_p, []),
@@ -51,11 +52,11 @@ _SIGS = {
     "kvq_kivi_boundary": (_L, [_L, _I, _I]),
     "kvq_kivi_quant_dequant": (C.c_int, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F,
                                          _P, _P, _P, _P, _P, _P, _P]),
-    "kvq_kivi_pack": (C.c_int, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _P]),
-    "kvq_kivi_unpack": (C.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
-    "kvq_nuq_workspace_bytes": (_L, [_I, _I, _I, _I, _I, _I, _F, _I]),
-    "kvq_nuq_outlier_bound": (_L, [_I, _I, _I, _I, _I, _F, _I, _I]),
-    "kvq_nuq_fit_quant": (C.c_int, [_P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I,
+    "kvq_kivi_pack": (C.c_int, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _I, _I, _P]),
+    "kvq_kivi_unpack": (C.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _I, _I, _P]),
+    "kvq_nuq_workspace_bytes": (_L, [_I, _I, _I, _I, _I, _I, _D, _I]),
+    "kvq_nuq_outlier_bound": (_L, [_I, _I, _I, _I, _I, _D, _I, _I]),
+    "kvq_nuq_fit_quant": (C.c_int, [_P, _P, _I, _I, _I, _I, _I, _D, _I, _I, _I,
                                     _P, _P, _P, _P, _P, _P, _P, _P, _P, _L, _P, _P, _P, _P, _L, _P]),
 }
 
@@ -108,6 +109,35 @@ def _dev(*ts):
                 raise KvqError(KVQ_ERR_ARG, "tensors must be contiguous")
 
 
+def _dt(kind):
+    import torch
+    return {"f16": (torch.float16, torch.int16), "f32": (torch.float32,), "u8": (torch.uint8,),
+            "i32": (torch.int32,), "i64": (torch.int64,)}[kind]
+
+
+def _need(t, name, kind, numel=None, ndim=None):
+    """Check a tensor against what the C call will index: element type,
+    rank, and at least `numel` elements (device and layout: _dev, once every
+    argument has passed this)."""
+    if t is None:
+        return
+    if t.dtype not in _dt(kind):
+        raise KvqError(KVQ_ERR_ARG, "%s must be %s (got %s)" % (name, "/".join(str(d) for d in _dt(kind)), t.dtype))
+    if ndim is not None and t.dim() != ndim:
+        raise KvqError(KVQ_ERR_SHAPE, "%s must have %d dimensions (got shape %s)" % (name, ndim, tuple(t.shape)))
+    if numel is not None and t.numel() < numel:
+        raise KvqError(KVQ_ERR_CAPACITY, "%s holds %d elements, %d needed" % (name, t.numel(), numel))
+
+
+def _same(a, b, what):
+    if a is not None and b is not None and tuple(a.shape) != tuple(b.shape):
+        raise KvqError(KVQ_ERR_SHAPE, "%s shapes differ: %s vs %s" % (what, tuple(a.shape), tuple(b.shape)))
+
+
+def _cdiv(a, b):
+    return -(-a // b)
+
+
 # ------------------------------------------------------------------ host helpers
 def kvq_version() -> str:
     return lib().kvq_version().decode()
@@ -140,23 +170,60 @@ def layout(layers, num_pages, page_size, kv_heads, head_dim, bits) -> PagedLayou
     return PagedLayout(layers, num_pages, page_size, kv_heads, head_dim, bits)
 
 
+def _pools(lay, k_codes, k_scales, v_codes, v_scales):
+    pd = kvq_packed_dim(lay.head_dim, lay.bits)
+    if pd <= 0:
+        raise KvqError(KVQ_ERR_SHAPE, "head_dim %d is not valid for q%d" % (lay.head_dim, lay.bits))
+    rows = lay.layers * lay.num_pages * lay.page_size * lay.kv_heads
+    for c, sc, side in ((k_codes, k_scales, "k"), (v_codes, v_scales, "v")):
+        _need(c, side + "_codes", "u8", rows * pd)
+        _need(sc, side + "_scales", "f16", rows)
+
+
 def kvq_quant_sym(lay: PagedLayout, k, v, slot_mapping, k_codes, k_scales, v_codes, v_scales,
                   layer0: int = 0, stream=None):
     """k, v: fp16 [n_layers][n_tokens][kv_heads][head_dim] (either may be None with its pools)."""
     x = k if k is not None else v
-    _dev(k, v, slot_mapping, k_codes, k_scales, v_codes, v_scales)
+    if x is None:
+        raise KvqError(KVQ_ERR_NULL, "neither k nor v given")
+    _same(k, v, "k and v")
+    for t, name in ((k, "k"), (v, "v")):
+        _need(t, name, "f16", ndim=4)
+    if tuple(x.shape[2:]) != (lay.kv_heads, lay.head_dim):
+        raise KvqError(KVQ_ERR_SHAPE, "inputs are [n_layers][n_tokens][%d][%d], got %s" %
+                       (lay.kv_heads, lay.head_dim, tuple(x.shape)))
     n_layers, n_tokens = int(x.shape[0]), int(x.shape[1])
+    _need(slot_mapping, "slot_mapping", "i32", n_tokens)
+    _pools(lay, k_codes, k_scales, v_codes, v_scales)
+    _dev(k, v, slot_mapping, k_codes, k_scales, v_codes, v_scales)
     _err(lib().kvq_quant_sym(C.byref(lay), _ptr(k), _ptr(v), layer0, n_layers, n_tokens,
                              _ptr(slot_mapping), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
                              _ptr(v_scales), _stream(stream)))
+
+
+def _tables(block_table, seq_lens, n_seqs):
+    _need(block_table, "block_table", "i32", ndim=2)
+    if block_table is not None and int(block_table.shape[0]) < n_seqs:
+        raise KvqError(KVQ_ERR_SHAPE, "block_table has %d rows for %d sequences" % (block_table.shape[0], n_seqs))
+    _need(seq_lens, "seq_lens", "i32", n_seqs)
 
 
 def kvq_dequant_sym(lay: PagedLayout, k_codes, k_scales, v_codes, v_scales, block_table, seq_lens,
                     k_out, v_out, layer0: int = 0, stream=None):
     """k_out/v_out: fp16 [n_layers][n_seqs][max_len][kv_heads][head_dim]."""
     o = k_out if k_out is not None else v_out
-    _dev(k_codes, k_scales, v_codes, v_scales, block_table, seq_lens, k_out, v_out)
+    if o is None:
+        raise KvqError(KVQ_ERR_NULL, "neither k_out nor v_out given")
+    _same(k_out, v_out, "k_out and v_out")
+    for t, name in ((k_out, "k_out"), (v_out, "v_out")):
+        _need(t, name, "f16", ndim=5)
+    if tuple(o.shape[3:]) != (lay.kv_heads, lay.head_dim):
+        raise KvqError(KVQ_ERR_SHAPE, "outputs are [n_layers][n_seqs][max_len][%d][%d], got %s" %
+                       (lay.kv_heads, lay.head_dim, tuple(o.shape)))
     n_layers, n_seqs, max_len = int(o.shape[0]), int(o.shape[1]), int(o.shape[2])
+    _tables(block_table, seq_lens, n_seqs)
+    _pools(lay, k_codes, k_scales, v_codes, v_scales)
+    _dev(k_codes, k_scales, v_codes, v_scales, block_table, seq_lens, k_out, v_out)
     _err(lib().kvq_dequant_sym(C.byref(lay), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
                                _ptr(v_scales), layer0, n_layers, _ptr(block_table),
                                int(block_table.shape[1]), _ptr(seq_lens), n_seqs, max_len,
@@ -171,12 +238,20 @@ def kvq_attn_workspace_bytes(n_seqs, q_heads, head_dim, max_len) -> int:
 def kvq_attn_decode_sym(lay: PagedLayout, k_codes, k_scales, v_codes, v_scales, layer: int, q, block_table,
                         seq_lens, max_len: int, softmax_scale: float, out, workspace, stream=None):
     """q, out: fp16 [n_seqs][q_heads][head_dim]; pools as in kvq_dequant_sym."""
-    _dev(k_codes, k_scales, v_codes, v_scales, q, block_table, seq_lens, out, workspace)
+    _need(q, "q", "f16", ndim=3)
+    _need(out, "out", "f16", ndim=3)
+    _same(q, out, "q and out")
+    if int(q.shape[2]) != lay.head_dim:
+        raise KvqError(KVQ_ERR_SHAPE, "q is [n_seqs][q_heads][%d], got %s" % (lay.head_dim, tuple(q.shape)))
     n_seqs, q_heads = int(q.shape[0]), int(q.shape[1])
+    _tables(block_table, seq_lens, n_seqs)
+    _pools(lay, k_codes, k_scales, v_codes, v_scales)
+    _need(workspace, "workspace", "u8")
+    _dev(k_codes, k_scales, v_codes, v_scales, q, block_table, seq_lens, out, workspace)
     _err(lib().kvq_attn_decode_sym(C.byref(lay), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales),
                                    layer, _ptr(q), q_heads, _ptr(block_table), int(block_table.shape[1]),
                                    _ptr(seq_lens), n_seqs, max_len, softmax_scale, _ptr(out), _ptr(workspace),
-                                   int(workspace.numel() * workspace.element_size()), _stream(stream)))
+                                   int(workspace.numel()), _stream(stream)))
 
 
 # ------------------------------------------------------------------ KIVI
@@ -185,8 +260,21 @@ def kvq_kivi_quant_dequant(keys, values, lo: int, hi: int, bits: int, group_size
                            v_codes=None, v_scale=None, v_min=None, stream=None):
     """In place on fp16 [B][H][S_cap][D] keys/values (either may be None)."""
     x = keys if keys is not None else values
-    _dev(keys, values, k_codes, k_scale, k_min, v_codes, v_scale, v_min)
+    if x is None:
+        raise KvqError(KVQ_ERR_NULL, "neither keys nor values given")
+    _same(keys, values, "keys and values")
+    for t, name in ((keys, "keys"), (values, "values")):
+        _need(t, name, "f16", ndim=4)
     B, H, S_cap, D = (int(s) for s in x.shape)
+    n = max(0, hi - lo)
+    if group_size > 0:
+        _need(k_codes, "k_codes", "u8", B * H * n * _cdiv(D * bits, 8))
+        _need(v_codes, "v_codes", "u8", B * H * n * _cdiv(D * bits, 8))
+        for t, name in ((k_scale, "k_scale"), (k_min, "k_min")):
+            _need(t, name, "f32", B * H * _cdiv(n, group_size) * D)
+        for t, name in ((v_scale, "v_scale"), (v_min, "v_min")):
+            _need(t, name, "f32", B * H * n * _cdiv(D, group_size))
+    _dev(keys, values, k_codes, k_scale, k_min, v_codes, v_scale, v_min)
     _err(lib().kvq_kivi_quant_dequant(_ptr(keys), _ptr(values), B, H, S_cap, D, lo, hi, bits,
                                       group_size, eps, _ptr(k_codes), _ptr(k_scale), _ptr(k_min),
                                       _ptr(v_codes), _ptr(v_scale), _ptr(v_min), _stream(stream)))
@@ -199,29 +287,73 @@ def kivi_param_shape(B, H, S_cap, D, per_channel, group_size):
     return (B, H, S_cap, (D + group_size - 1) // group_size)
 
 
+def _packed_store(codes, scale, zero, B, H, S_cap, D, bits, group_size, per_channel, side):
+    import math
+    _need(codes, side + "_codes", "u8", B * H * S_cap * D * bits // 8)
+    if group_size > 0:
+        n = math.prod(kivi_param_shape(B, H, S_cap, D, per_channel, group_size))
+        _need(scale, side + "_scale", "f16", n)
+        _need(zero, side + "_zero", "f16", n)
+
+
 def kvq_kivi_pack(keys, values, lo: int, hi: int, bits: int, group_size: int = 32, eps: float = 1e-8,
                   k_codes=None, k_scale=None, k_zero=None, v_codes=None, v_scale=None, v_zero=None,
-                  stream=None):
-    """keys/values fp16 [B][H][S_cap][D] (either None); codes uint8
-    [B][H][S_cap][D*bits/8]; scale/zero int16 holding fp16 bits, shapes of
+                  x_t0: int = 0, stream=None):
+    """keys/values fp16 [B][H][x_rows][D] (either None), row r holding token
+    x_t0 + r; storage: codes uint8 [B][H][S_cap][D*bits/8] (S_cap is taken
+    from it), scale/zero int16 or fp16 holding fp16 bits, shapes of
     kivi_param_shape."""
     x = keys if keys is not None else values
+    if x is None:
+        raise KvqError(KVQ_ERR_NULL, "neither keys nor values given")
+    _same(keys, values, "keys and values")
+    for t, name in ((keys, "keys"), (values, "values")):
+        _need(t, name, "f16", ndim=4)
+    B, H, x_rows, D = (int(s) for s in x.shape)
+    store = k_codes if keys is not None else v_codes
+    _need(store, "codes", "u8", ndim=4)
+    if store is None:
+        raise KvqError(KVQ_ERR_NULL, "packed storage not given")
+    if (int(store.shape[0]), int(store.shape[1])) != (B, H):
+        raise KvqError(KVQ_ERR_SHAPE, "storage is [%d][%d][S_cap][...], got %s" % (B, H, tuple(store.shape)))
+    S_cap = int(store.shape[2])
+    if keys is not None:
+        _packed_store(k_codes, k_scale, k_zero, B, H, S_cap, D, bits, group_size, True, "k")
+    if values is not None:
+        _packed_store(v_codes, v_scale, v_zero, B, H, S_cap, D, bits, group_size, False, "v")
     _dev(keys, values, k_codes, k_scale, k_zero, v_codes, v_scale, v_zero)
-    B, H, S_cap, D = (int(s) for s in x.shape)
     _err(lib().kvq_kivi_pack(_ptr(keys), _ptr(values), B, H, S_cap, D, lo, hi, bits, group_size, eps,
                              _ptr(k_codes), _ptr(k_scale), _ptr(k_zero), _ptr(v_codes), _ptr(v_scale),
-                             _ptr(v_zero), _stream(stream)))
+                             _ptr(v_zero), x_rows, x_t0, _stream(stream)))
 
 
 def kvq_kivi_unpack(k_codes, k_scale, k_zero, v_codes, v_scale, v_zero, lo: int, hi: int, bits: int,
-                    group_size: int, k_out, v_out, stream=None):
-    """Tokens [lo, hi) into k_out / v_out, fp16 [B][H][S_cap][D] (either None)."""
+                    group_size: int, k_out, v_out, out_t0: int = 0, stream=None):
+    """Tokens [lo, hi) of packed storage (codes [B][H][S_cap][D*bits/8]) into
+    k_out / v_out, fp16 [B][H][out_rows][D] (either None), token t in row
+    t - out_t0."""
     o = k_out if k_out is not None else v_out
+    if o is None:
+        raise KvqError(KVQ_ERR_NULL, "neither k_out nor v_out given")
+    _same(k_out, v_out, "k_out and v_out")
+    for t, name in ((k_out, "k_out"), (v_out, "v_out")):
+        _need(t, name, "f16", ndim=4)
+    B, H, out_rows, D = (int(s) for s in o.shape)
+    store = k_codes if k_out is not None else v_codes
+    _need(store, "codes", "u8", ndim=4)
+    if store is None:
+        raise KvqError(KVQ_ERR_NULL, "packed storage not given")
+    if (int(store.shape[0]), int(store.shape[1])) != (B, H):
+        raise KvqError(KVQ_ERR_SHAPE, "storage is [%d][%d][S_cap][...], got %s" % (B, H, tuple(store.shape)))
+    S_cap = int(store.shape[2])
+    if k_out is not None:
+        _packed_store(k_codes, k_scale, k_zero, B, H, S_cap, D, bits, group_size, True, "k")
+    if v_out is not None:
+        _packed_store(v_codes, v_scale, v_zero, B, H, S_cap, D, bits, group_size, False, "v")
     _dev(k_codes, k_scale, k_zero, v_codes, v_scale, v_zero, k_out, v_out)
-    B, H, S_cap, D = (int(s) for s in o.shape)
     _err(lib().kvq_kivi_unpack(_ptr(k_codes), _ptr(k_scale), _ptr(k_zero), _ptr(v_codes), _ptr(v_scale),
                                _ptr(v_zero), B, H, S_cap, D, lo, hi, bits, group_size, _ptr(k_out),
-                               _ptr(v_out), _stream(stream)))
+                               _ptr(v_out), out_rows, out_t0, _stream(stream)))
 
 
 # ------------------------------------------------------------------ NUQ
@@ -233,17 +365,44 @@ def kvq_nuq_workspace_bytes(BH, S, D, bits, start_pos, n_sink, frac, fit_keys) -
     return lib().kvq_nuq_workspace_bytes(BH, S, D, bits, start_pos, n_sink, frac, int(fit_keys))
 
 
+def _nuq_check(keys, values, bits, key_levels, key_thresh, value_levels, k_codes, v_codes, k_opos, k_oval,
+               v_opos, v_oval, out_counts, k_recon, v_recon):
+    _need(keys, "keys", "f16", ndim=3)
+    _need(values, "values", "f16", ndim=3)
+    if keys is None or values is None:
+        raise KvqError(KVQ_ERR_NULL, "keys and values are required")
+    _same(keys, values, "keys and values")
+    BH, S, D = (int(x) for x in keys.shape)
+    L = 1 << bits if 1 <= bits <= 4 else 0
+    _need(key_levels, "key_levels", "f32", BH * D * L)
+    _need(key_thresh, "key_thresh", "f16", BH * D)
+    _need(value_levels, "value_levels", "f32", BH * S * L)
+    _need(k_codes, "k_codes", "u8", BH * S * _cdiv(D * bits, 8))
+    _need(v_codes, "v_codes", "u8", BH * S * _cdiv(D * bits, 8))
+    for t, name in ((k_opos, "k_opos"), (v_opos, "v_opos")):
+        _need(t, name, "i32")
+    for t, name in ((k_oval, "k_oval"), (v_oval, "v_oval")):
+        _need(t, name, "f16")
+    _need(out_counts, "out_counts", "i64", 2)
+    _need(k_recon, "k_recon", "f16", BH * S * D)
+    _need(v_recon, "v_recon", "f16", BH * S * D)
+    out_cap = min(int(t.numel()) for t in (k_opos, k_oval, v_opos, v_oval) if t is not None) \
+        if all(t is not None for t in (k_opos, k_oval, v_opos, v_oval)) else 0
+    return BH, S, D, out_cap
+
+
 def kvq_nuq_fit_quant(keys, values, start_pos, bits, frac, lloyd_iters, n_sink, fit_keys,
                       key_levels, key_thresh, value_levels, k_codes, v_codes, k_opos, k_oval,
                       v_opos, v_oval, out_counts, workspace, k_recon=None, v_recon=None, stream=None):
     """keys/values fp16 [BH][S][D]; all outputs preallocated device tensors (see include/kvq.h)."""
-    _dev(keys, values, key_levels, key_thresh, value_levels, k_codes, v_codes, k_opos, k_oval,
-         v_opos, v_oval, out_counts, workspace, k_recon, v_recon)
-    BH, S, D = (int(x) for x in keys.shape)
-    out_cap = min(int(k_opos.numel()), int(k_oval.numel()), int(v_opos.numel()), int(v_oval.numel()))
+    BH, S, D, out_cap = _nuq_check(keys, values, bits, key_levels, key_thresh, value_levels, k_codes, v_codes,
+                                   k_opos, k_oval, v_opos, v_oval, out_counts, k_recon, v_recon)
+    _need(workspace, "workspace", "u8")
+    _dev(keys, values, key_levels, key_thresh, value_levels, k_codes, v_codes, k_opos, k_oval, v_opos, v_oval,
+         out_counts, workspace, k_recon, v_recon)
     _err(lib().kvq_nuq_fit_quant(_ptr(keys), _ptr(values), BH, S, D, start_pos, bits, frac,
                                  lloyd_iters, n_sink, int(fit_keys), _ptr(key_levels),
                                  _ptr(key_thresh), _ptr(value_levels), _ptr(k_codes), _ptr(v_codes),
                                  _ptr(k_opos), _ptr(k_oval), _ptr(v_opos), _ptr(v_oval), out_cap,
                                  _ptr(out_counts), _ptr(k_recon), _ptr(v_recon), _ptr(workspace),
-                                 int(workspace.numel() * workspace.element_size()), _stream(stream)))
+                                 int(workspace.numel()) if workspace is not None else 0, _stream(stream)))

@@ -12,6 +12,14 @@ KiviCacheModel: ["veloxquant_mlx.cache.kivi_cache", KIVIKVCache] tokens age
   pulls the flush frontier down to the group boundary at or below the new
   length; bytes of a quantized stretch of n tokens are b-bit codes plus one
   fp16 (scale, zero) pair per group (_quantized_bytes / _account_bytes).
+KiviPackedCacheModel: the same lifecycle with the quantized tokens held only
+  as packed storage (b-bit codes plus one fp16 (scale, zero) pair per group,
+  kivi_pack), the memory the page's byte accounting charges for (module
+  docstring, memory-savings caveat). fp16 is kept for the residual window
+  only; the fp16 view is rebuilt with kivi_unpack. A trim below the frontier
+  brings the tokens between the new frontier and the new length back into
+  the window as their packed reconstructions (they were quantized once and
+  are quantized again when they age out).
 NuqCacheModel: ["veloxquant_mlx.cache.kvquant_cache module", KVQuantKVCache]
   the first call of a sequence fits and freezes the key tables and keeps
   its first n_sink tokens exact; later calls reuse the frozen key state,
@@ -24,7 +32,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import kivi_round_trip, nuq_fit_quant
+from . import kivi_pack, kivi_param_shape, kivi_round_trip, kivi_unpack, nuq_fit_quant
 
 
 class KiviCacheModel:
@@ -85,6 +93,93 @@ class KiviCacheModel:
         self.value_fp16 = max(0, self.value_fp16 - B * H * t * D * 2)
         self.residual_bytes = (self.offset - self.nq) * B * H * D * 2 * 2
         return t
+
+
+class KiviPackedCacheModel:
+    def __init__(self, bits=2, group_size=32, residual_length=128):
+        self.b, self.gs, self.R = bits, group_size, residual_length
+        self.n = 0            # tokens held
+        self.nq = 0           # quantized prefix
+        self.win = None       # (keys, values) fp16 bits [B][H][n - nq][D]
+        self.store = None     # (key (codes, scale, zero), value (codes, scale, zero)), S_cap = self.cap
+        self.cap = 0
+
+    def _grow(self, need, B, H, D):
+        if need <= self.cap:
+            return
+        new = []
+        for per_channel in (1, 0):
+            shp = kivi_param_shape(B, H, need, D, per_channel, self.gs)
+            arrs = (np.zeros((B, H, need, D * self.b // 8), np.uint8), np.zeros(shp, np.uint16),
+                    np.zeros(shp, np.uint16))
+            if self.store is not None:
+                for a, o in zip(arrs, self.store[1 - per_channel]):
+                    a[:, :, : o.shape[2]] = o
+            new.append(arrs)
+        self.store, self.cap = new, need
+
+    def update(self, keys, values):
+        B, H, S, D = keys.shape
+        if self.win is None:
+            self.win = (keys.copy(), values.copy())
+        else:
+            self.win = (np.concatenate([self.win[0], keys], 2), np.concatenate([self.win[1], values], 2))
+        self.n += S
+        eligible = max(0, self.n - self.R)
+        frontier = eligible - eligible % self.gs
+        if frontier > self.nq:
+            self._grow(frontier, B, H, D)
+            for side, per_channel in ((0, 1), (1, 0)):
+                full = np.zeros((B, H, self.cap, D), np.uint16)   # token t in row t
+                full[:, :, self.nq:frontier] = self.win[side][:, :, : frontier - self.nq]
+                kivi_pack(full, self.nq, frontier, per_channel, self.b, self.gs, into=self.store[side])
+            self.win = tuple(w[:, :, frontier - self.nq:].copy() for w in self.win)
+            self.nq = frontier
+        return self.fetch()
+
+    def fetch(self):
+        B, H, _, D = self.win[0].shape
+        out = []
+        for side, per_channel in ((0, 1), (1, 0)):
+            x = np.zeros((B, H, self.n, D), np.uint16)
+            if self.nq:
+                codes, sc, zr = self.store[side]
+                x[:, :, : self.nq] = kivi_unpack(codes, sc, zr, 0, self.nq, per_channel, self.b, self.gs, D)[
+                    :, :, : self.nq]
+            x[:, :, self.nq:] = self.win[side]
+            out.append(x)
+        return out[0], out[1]
+
+    def trim(self, n):
+        t = min(max(n, 0), self.n)
+        if t == 0:
+            return 0
+        keep = self.n - t
+        back = min(self.nq, keep - keep % self.gs)
+        if back < self.nq:
+            B, H, _, D = self.win[0].shape
+            upto = min(self.nq, keep)
+            win = []
+            for side, per_channel in ((0, 1), (1, 0)):
+                codes, sc, zr = self.store[side]
+                rec = kivi_unpack(codes, sc, zr, back, upto, per_channel, self.b, self.gs, D)[:, :, back:upto]
+                win.append(np.concatenate([rec, self.win[side][:, :, : max(0, keep - self.nq)]], 2))
+            self.win = tuple(win)
+            self.nq = back
+        else:
+            self.win = tuple(w[:, :, : keep - self.nq].copy() for w in self.win)
+        self.n = keep
+        return t
+
+    def packed_bytes(self):
+        """(key, value) bytes of the packed rows that hold the quantized prefix."""
+        if self.nq == 0:
+            return 0, 0
+        (kc, ks, kz), (vc, vs, vz) = self.store
+        ng = -(-self.nq // self.gs)
+        kb = kc[:, :, : self.nq].nbytes + ks[:, :, :ng].nbytes + kz[:, :, :ng].nbytes
+        vb = vc[:, :, : self.nq].nbytes + vs[:, :, : self.nq].nbytes + vz[:, :, : self.nq].nbytes
+        return kb, vb
 
 
 class NuqCacheModel:

@@ -158,13 +158,15 @@ def test_kivi_validation_errors():
 
 
 def _kpack(k=FAKE, v=FAKE, B=2, H=2, S=64, D=64, lo=0, hi=32, bits=2, gs=32, eps=1e-8, kc=FAKE, ks=FAKE,
-           kz=FAKE, vc=FAKE, vs=FAKE, vz=FAKE):
-    return kvq.lib().kvq_kivi_pack(k, v, B, H, S, D, lo, hi, bits, gs, eps, kc, ks, kz, vc, vs, vz, None)
+           kz=FAKE, vc=FAKE, vs=FAKE, vz=FAKE, xr=None, x0=0):
+    xr = S if xr is None else xr
+    return kvq.lib().kvq_kivi_pack(k, v, B, H, S, D, lo, hi, bits, gs, eps, kc, ks, kz, vc, vs, vz, xr, x0, None)
 
 
 def _kunpack(kc=FAKE, ks=FAKE, kz=FAKE, vc=FAKE, vs=FAKE, vz=FAKE, B=2, H=2, S=64, D=64, lo=0, hi=32, bits=4,
-             gs=32, ko=FAKE, vo=FAKE):
-    return kvq.lib().kvq_kivi_unpack(kc, ks, kz, vc, vs, vz, B, H, S, D, lo, hi, bits, gs, ko, vo, None)
+             gs=32, ko=FAKE, vo=FAKE, orows=None, o0=0):
+    orows = S if orows is None else orows
+    return kvq.lib().kvq_kivi_unpack(kc, ks, kz, vc, vs, vz, B, H, S, D, lo, hi, bits, gs, ko, vo, orows, o0, None)
 
 
 def test_kivi_packed_validation_errors():
@@ -187,6 +189,15 @@ def test_kivi_packed_validation_errors():
     assert _kunpack(lo=40, hi=32) == kvq.KVQ_ERR_SHAPE
     assert _kunpack(gs=0) == kvq.KVQ_ERR_SHAPE
     assert _kunpack(hi=16, lo=16) == kvq.KVQ_OK
+    # windows: the fp16 side holds tokens [t0, t0 + rows) only (B = 0: valid
+    # calls stop before any launch, the pointers here are fake)
+    assert _kpack(B=0, lo=32, hi=64, xr=32, x0=32) == kvq.KVQ_OK
+    assert _kpack(lo=32, hi=64, xr=31, x0=32) == kvq.KVQ_ERR_SHAPE
+    assert _kpack(lo=32, hi=64, xr=40, x0=33) == kvq.KVQ_ERR_SHAPE
+    assert _kpack(xr=-1) == kvq.KVQ_ERR_SHAPE
+    assert _kunpack(B=0, lo=8, hi=40, orows=32, o0=8) == kvq.KVQ_OK
+    assert _kunpack(lo=8, hi=40, orows=32, o0=9) == kvq.KVQ_ERR_SHAPE
+    assert _kunpack(lo=8, hi=41, orows=32, o0=8) == kvq.KVQ_ERR_SHAPE
 
 
 def test_binding_refuses_host_tensors():
@@ -213,12 +224,16 @@ def _nuq(k=FAKE, v=FAKE, BH=2, S=64, D=128, sp=0, bits=3, frac=0.01, iters=8, ns
 def test_nuq_host_helpers():
     import math
     f = 0.01
-    for BH, S, D, sp, ns, fk in [(32, 4096, 128, 0, 4, 1), (32, 1, 128, 4096, 4, 0), (3, 70, 64, 0, 4, 1),
-                                 (2, 3, 32, 0, 4, 1), (1, 100, 256, 5, 4, 1)]:
+    # (k per key channel, k per value token) at a 1% fraction: floor of the
+    # binary64 product, so 100 samples give 1 and 256 give 2
+    for BH, S, D, sp, ns, fk, kk, kv in [(32, 4096, 128, 0, 4, 1, 40, 1), (32, 1, 128, 4096, 4, 0, 0, 1),
+                                         (3, 70, 64, 0, 4, 1, 0, 0), (2, 3, 32, 0, 4, 1, 0, 0),
+                                         (1, 100, 256, 5, 4, 1, 1, 2), (2, 104, 128, 0, 4, 1, 1, 1),
+                                         (2, 204, 64, 0, 4, 1, 2, 0)]:
         nse = min(ns, S) if sp == 0 else 0
         nf = S - nse
-        kb = BH * D * math.floor(float(__import__("numpy").float32(f)) * nf) if fk else BH * nf * D
-        vb = BH * nf * math.floor(float(__import__("numpy").float32(f)) * D)
+        kb = BH * D * kk if fk else BH * nf * D
+        vb = BH * nf * kv
         assert kvq.kvq_nuq_outlier_bound(BH, S, D, sp, ns, f, fk, 0) == kb
         assert kvq.kvq_nuq_outlier_bound(BH, S, D, sp, ns, f, fk, 1) == vb
         assert kvq.kvq_nuq_workspace_bytes(BH, S, D, 3, sp, ns, f, fk) >= 6 * (kb + vb)
@@ -242,3 +257,93 @@ def test_nuq_validation_errors():
     assert _nuq(k=FAKE + 8) == kvq.KVQ_ERR_ALIGN
     assert _nuq(ws=FAKE + 4) == kvq.KVQ_ERR_ALIGN
     assert _nuq(recon=FAKE + 2) == kvq.KVQ_ERR_ALIGN
+
+
+def _raises(fn, text):
+    with pytest.raises(kvq.KvqError) as e:
+        fn()
+    assert text in str(e.value), str(e.value)
+
+
+def test_binding_checks_types_and_sizes_before_the_call():
+    """The wrappers check element types and sizes against what the C call
+    will index and raise before calling it (host tensors here: a call whose
+    arguments all pass these checks stops at the device check)."""
+    import torch
+    lay = kvq.layout(2, 4, 16, 4, 256, 6)
+    x = torch.zeros((2, 8, 4, 256), dtype=torch.float16)
+    codes = torch.zeros(2 * 4 * 16 * 4 * 192, dtype=torch.uint8)
+    sc = torch.zeros(2 * 4 * 16 * 4, dtype=torch.int16)
+    sm = torch.zeros(8, dtype=torch.int32)
+    q = lambda **kw: kvq.kvq_quant_sym(lay, kw.get("k", x), kw.get("v", x), kw.get("sm", sm), kw.get("kc", codes),
+                                       kw.get("ks", sc), kw.get("vc", codes), kw.get("vs", sc))
+    _raises(lambda: q(sm=torch.zeros(8, dtype=torch.int64)), "slot_mapping must be")
+    _raises(lambda: q(sm=torch.zeros(7, dtype=torch.int32)), "slot_mapping holds 7")
+    _raises(lambda: q(kc=codes[:-1]), "k_codes holds")
+    _raises(lambda: q(vs=sc[:-1]), "v_scales holds")
+    _raises(lambda: q(v=x[:, :4]), "k and v shapes differ")
+    _raises(lambda: q(k=torch.zeros((2, 8, 4, 128), dtype=torch.float16), v=None), "inputs are")
+    _raises(lambda: q(k=x.float(), v=None), "k must be")
+    _raises(lambda: q(), "on the GPU")
+    out = torch.zeros((2, 3, 32, 4, 256), dtype=torch.float16)
+    bt = torch.zeros((3, 2), dtype=torch.int32)
+    sl = torch.zeros(3, dtype=torch.int32)
+    dq = lambda **kw: kvq.kvq_dequant_sym(lay, codes, sc, codes, sc, kw.get("bt", bt), kw.get("sl", sl),
+                                          kw.get("ko", out), kw.get("vo", out))
+    _raises(lambda: dq(bt=bt.long()), "block_table must be")
+    _raises(lambda: dq(bt=bt[:2]), "block_table has 2 rows")
+    _raises(lambda: dq(sl=sl[:2]), "seq_lens holds 2")
+    _raises(lambda: dq(vo=out[:, :2]), "k_out and v_out shapes differ")
+    _raises(lambda: dq(), "on the GPU")
+    # KIVI: a shorter value tensor would be written past its end
+    k4 = torch.zeros((2, 2, 64, 64), dtype=torch.float16)
+    _raises(lambda: kvq.kvq_kivi_quant_dequant(k4, k4[:, :, :32].contiguous(), 0, 32, 2), "keys and values shapes")
+    _raises(lambda: kvq.kvq_kivi_quant_dequant(k4, None, 0, 64, 2, 32, k_codes=torch.zeros(10, dtype=torch.uint8)),
+            "k_codes holds")
+    _raises(lambda: kvq.kvq_kivi_quant_dequant(k4, None, 0, 64, 2, 32, k_scale=torch.zeros(2 * 2 * 2 * 64)),
+            "on the GPU")
+    _raises(lambda: kvq.kvq_kivi_quant_dequant(k4, None, 0, 64, 2, 32, k_scale=torch.zeros(2 * 2 * 2 * 64 - 1)),
+            "k_scale holds")
+    st = torch.zeros((2, 2, 64, 16), dtype=torch.uint8)
+    par = torch.zeros(kvq.kivi_param_shape(2, 2, 64, 64, 1, 32), dtype=torch.int16)
+    _raises(lambda: kvq.kvq_kivi_pack(k4, None, 0, 32, 2, 32, k_codes=st, k_scale=par, k_zero=par[:, :, :1]),
+            "k_zero holds")
+    _raises(lambda: kvq.kvq_kivi_pack(k4, None, 0, 32, 2, 32, k_codes=st[:1], k_scale=par, k_zero=par),
+            "storage is")
+    _raises(lambda: kvq.kvq_kivi_unpack(st, par, par, None, None, None, 0, 32, 2, 32, k4.float(), None), "k_out must be")
+    # NUQ: every output sized from BH, S, D and bits
+    BH, S, D, bits = 2, 16, 64, 3
+    kk = torch.zeros((BH, S, D), dtype=torch.float16)
+    f32 = lambda n: torch.zeros(n, dtype=torch.float32)
+    i16 = lambda n: torch.zeros(n, dtype=torch.int16)
+    u8 = lambda n: torch.zeros(n, dtype=torch.uint8)
+    args = dict(key_levels=f32(BH * D * 8), key_thresh=i16(BH * D), value_levels=f32(BH * S * 8),
+                k_codes=u8(BH * S * 24), v_codes=u8(BH * S * 24), k_opos=torch.zeros(4, dtype=torch.int32),
+                k_oval=i16(4), v_opos=torch.zeros(4, dtype=torch.int32), v_oval=i16(4),
+                out_counts=torch.zeros(2, dtype=torch.int64), workspace=u8(1024))
+    nuq = lambda **kw: kvq.kvq_nuq_fit_quant(kw.pop("keys", kk), kw.pop("values", kk), 0, bits, 0.01, 8, 4, 1,
+                                             **{**args, **kw})
+    _raises(lambda: nuq(key_levels=f32(BH * D * 8 - 1)), "key_levels holds")
+    _raises(lambda: nuq(value_levels=f32(BH * 8)), "value_levels holds")
+    _raises(lambda: nuq(v_codes=u8(BH * S * 24 - 1)), "v_codes holds")
+    _raises(lambda: nuq(k_recon=torch.zeros((BH, S, D - 1), dtype=torch.float16)), "k_recon holds")
+    _raises(lambda: nuq(k_opos=torch.zeros(4, dtype=torch.int64)), "k_opos must be")
+    _raises(lambda: nuq(out_counts=torch.zeros(1, dtype=torch.int64)), "out_counts holds")
+    _raises(lambda: nuq(values=kk[:, :8].contiguous()), "keys and values shapes")
+    _raises(lambda: nuq(), "on the GPU")
+
+
+def test_paged_cache_append_is_all_or_nothing():
+    """A failed append leaves pages, lengths and the free list as they were."""
+    import torch
+    from kv_cache_quantization_row_amd import caches
+    c = caches.PagedSymCache(1, 8, 16, 2, 64, 8, device=torch.device("cpu"))
+    free0 = list(c.free)
+    x = torch.zeros((1, 20, 2, 64), dtype=torch.float16)
+    with pytest.raises(kvq.KvqError):
+        c.append([(0, 10), (1, 11)], x, x)          # 21 tokens listed, 20 given
+    with pytest.raises(kvq.KvqError):
+        c.append([(0, 10), (1, 10)], x, x)          # host tensors: the kernel call refuses them
+    with pytest.raises(kvq.KvqError):
+        c.append([(0, 200)], torch.zeros((1, 200, 2, 64), dtype=torch.float16), None)  # pool exhausted
+    assert c.free == free0 and c.pages == {} and c.lengths == {} and c.rows == {}

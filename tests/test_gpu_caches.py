@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import oracle
-from oracle.caches import KiviCacheModel, NuqCacheModel
+from oracle.caches import KiviCacheModel, KiviPackedCacheModel, NuqCacheModel
 from kv_cache_quantization_row_amd import caches, inputs, kvq
 from tests.gpu_util import dev, first_diff, say, u16
 
@@ -66,6 +66,67 @@ def test_kivi_cache_lifecycle(bits):
     ratio = (c.fp16_key_bytes + c.fp16_value_bytes) / (c.compressed_key_bytes + c.compressed_value_bytes +
                                                         c.residual_fp16_bytes)
     assert c.effective_compression_ratio == pytest.approx(ratio)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_kivi_packed_cache_lifecycle(bits):
+    """KiviCache(storage="packed") against its CPU model: fetched K/V, the
+    packed rows of the quantized prefix, frontiers and byte counts agree
+    bit-for-bit through prefill, decode, trims into the window, into the
+    quantized region and to empty; the bytes reported as compressed are the
+    bytes of the packed rows, and no fp16 copy of the quantized region is
+    kept."""
+    say("kivi packed cache", bits)
+    d = dev()
+    B, H, D, g = 2, 4, 64, 32
+    k, v = _kivi_inputs(B, H, 900, D, 60 + bits)
+    kn, vn = k.numpy().view(np.uint16), v.numpy().view(np.uint16)
+    c, m = caches.KiviCache(bits, storage="packed"), KiviPackedCacheModel(bits)
+    t = 0
+
+    def check(what, fk=None, fv=None):
+        assert (c.offset, c.n_quantized) == (m.n, m.nq), what
+        if fk is None:
+            fk, fv = c.fetch()
+        mk, mv = m.fetch()
+        assert first_diff(u16(fk), mk) is None, (what, "keys", first_diff(u16(fk), mk))
+        assert first_diff(u16(fv), mv) is None, (what, "values", first_diff(u16(fv), mv))
+        if m.nq:
+            ng = -(-m.nq // g)
+            for side in range(2):
+                gc, gs_, gz = c._store[side]
+                mc, ms, mz = m.store[side]
+                r = ng if side == 0 else m.nq
+                assert np.array_equal(gc[:, :, :m.nq].cpu().numpy(), mc[:, :, :m.nq]), (what, side, "codes")
+                assert np.array_equal(u16(gs_[:, :, :r]), ms[:, :, :r]), (what, side, "scale")
+                assert np.array_equal(u16(gz[:, :, :r]), mz[:, :, :r]), (what, side, "zero")
+        assert (c.compressed_key_bytes, c.compressed_value_bytes) == m.packed_bytes(), what
+        assert c.stored_quantized_bytes() == sum(m.packed_bytes()), what
+        assert c.residual_fp16_bytes == B * H * (m.n - m.nq) * D * 4, what
+        assert c.keys is None and c.values is None, what  # no full-length fp16 buffers
+
+    def push(n, what):
+        nonlocal t
+        fk, fv = c.update_and_fetch(k[:, :, t:t + n].to(d).contiguous(), v[:, :, t:t + n].to(d).contiguous())
+        m.update(kn[:, :, t:t + n], vn[:, :, t:t + n])
+        t += n
+        check(what, fk, fv)
+
+    push(300, "prefill")
+    for i in range(40):
+        push(1, "decode %d" % i)
+    assert c.trim(37) == m.trim(37) == 37
+    check("trim into the window")
+    push(20, "append")
+    assert c.trim(200) == m.trim(200) == 200
+    check("trim into the quantized region")
+    push(150, "re-flush")
+    for i in range(5):
+        push(1, "decode after rollback %d" % i)
+    assert c.trim(10 ** 6) == m.trim(10 ** 6)
+    assert c.offset == 0 and c.n_quantized == 0 and c.device_bytes() == 0
+    m = KiviPackedCacheModel(bits)
+    push(200, "new sequence")
 
 
 def test_nuq_cache_lifecycle():
@@ -148,19 +209,30 @@ def test_paged_sym_cache_lifecycle(bits):
         assert len(used) == len(set(used)) and not set(used) & set(c.free), what
         assert all(len(c.pages[s]) == (c.lengths[s] + P - 1) // P for s in c.pages), what
 
+    def decode(sids):
+        x = (torch.randn((2, Lyr, len(sids), H, D), generator=g) * 3).half()
+        c.append_decode(sids, x[0].to(d), x[1].to(d))
+        for i, sid in enumerate(sids):
+            hk, hv = hist[sid]
+            hist[sid] = (np.concatenate([hk, u16(x[0, :, i:i + 1])], 1),
+                         np.concatenate([hv, u16(x[1, :, i:i + 1])], 1))
+
     append([(0, 100), (1, 37), (2, 1)])
     check("prefill")
     for step in range(20):
         append([(0, 1), (1, 1), (2, 1)])
     check("decode")
+    for step in range(20):  # slots from the device block table (new pages through the host path)
+        decode([2, 0, 1])
+    check("device-side decode appends")
     for sid, t in ((0, 50), (1, 30), (2, 21)):
         assert c.trim(sid, t) == t
         hist[sid] = (hist[sid][0][:, : c.lengths[sid]], hist[sid][1][:, : c.lengths[sid]])
     check("trim")
-    free_before = len(c.free)
+    free_before, n_rel = len(c.free), len(c.pages[1])
     c.release(1)
     del hist[1]
-    assert len(c.free) == free_before + 2
+    assert n_rel == 3 and len(c.free) == free_before + n_rel
     append([(3, 300), (0, 5)])
     check("reuse")
     with pytest.raises(kvq.KvqError):

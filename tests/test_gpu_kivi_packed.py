@@ -132,3 +132,39 @@ def test_packed_full_size_sampled():
             _check("v recon", u16(vo[b:b + 1, h:h + 1])[:, :, :hi],
                    oracle.kivi_unpack(*ev, 0, hi, 0, bits, gs, D)[:, :, :hi])
         del kc, ks, kz, vc, vs, vz, ko, vo
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_windowed_pack_and_unpack(bits):
+    """Packing from an fp16 window that holds tokens [t0, t0 + rows) only,
+    and unpacking into such a window, give the full-buffer results; rows
+    outside the range are not written (guard rows hold a sentinel)."""
+    say("kivi packed windows", bits)
+    d = dev()
+    B, H, S, D, gs = 2, 3, 256, 64, 32
+    k, v = inputs.kivi_kv(B, H, S, D, seed=90 + bits)
+    lo, hi = 96, 224                       # key flushes start at a group boundary
+    t0, rows = 96, 150                     # window: tokens [96, 246)
+    kw = k[:, :, t0:t0 + rows].to(d).contiguous()
+    vw = v[:, :, t0:t0 + rows].to(d).contiguous()
+    kc, ks, kz, vc, vs, vz = _storage(B, H, S, D, bits, gs, d)
+    kvq.kvq_kivi_pack(kw, vw, lo, hi, bits, gs, k_codes=kc, k_scale=ks, k_zero=kz, v_codes=vc, v_scale=vs,
+                      v_zero=vz, x_t0=t0)
+    ek = oracle.kivi_pack(u16(k), lo, hi, 1, bits, gs)
+    ev = oracle.kivi_pack(u16(v), lo, hi, 0, bits, gs)
+    o0, orows = 90, 160                    # output window: tokens [90, 250), guard rows around [lo, hi)
+    ko = torch.full((B, H, orows, D), 7.0, dtype=torch.float16, device=d)
+    vo = torch.full_like(ko, 7.0)
+    kvq.kvq_kivi_unpack(kc, ks, kz, vc, vs, vz, lo, hi, bits, gs, ko, vo, out_t0=o0)
+    torch.cuda.synchronize()
+    for tag, got, exp in (("k codes", kc.cpu().numpy(), ek[0]), ("k scale", u16(ks), ek[1]), ("k zero", u16(kz), ek[2]),
+                          ("v codes", vc.cpu().numpy(), ev[0]), ("v scale", u16(vs), ev[1]),
+                          ("v zero", u16(vz), ev[2])):
+        _check(tag, got, exp)
+    rk = oracle.kivi_unpack(*ek, lo, hi, 1, bits, gs, D)
+    rv = oracle.kivi_unpack(*ev, lo, hi, 0, bits, gs, D)
+    _check("k recon", u16(ko)[:, :, lo - o0:hi - o0], rk[:, :, lo:hi])
+    _check("v recon", u16(vo)[:, :, lo - o0:hi - o0], rv[:, :, lo:hi])
+    seven = np.float16(7.0).view(np.uint16)
+    for o in (ko, vo):
+        assert (u16(o)[:, :, :lo - o0] == seven).all() and (u16(o)[:, :, hi - o0:] == seven).all()

@@ -125,6 +125,21 @@ def test_ragged_lengths_and_sinks(S):
         compare(g, r, what="S=%d start=%d sinks=%d" % (S, sp, ns))
 
 
+@pytest.mark.parametrize("S", [104, 204, 1004])
+def test_outlier_count_at_whole_percentages(S):
+    """S - 4 non-sink tokens at a 1% fraction: 1, 2 and 10 key outliers per
+    channel (floor of the binary64 product), as in the oracle."""
+    say("nuq whole-percentage counts", S)
+    BH, D, bits = 3, 128, 3
+    k, v = t4((BH, S, D), 70 + S), t4((BH, S, D), 71 + S)
+    g = gpu_nuq(k, v, 0, bits, 0.01, 8, 4, 1)
+    r = oracle.nuq_fit_quant(k, v, 0, bits, 0.01, 8, 4, 1)
+    compare(g, r, what="S=%d" % S)
+    pos = g["k_out"][0]
+    per_ch = np.bincount((pos // (S * D)) * D + pos % D, minlength=BH * D)
+    assert per_ch.max() <= (S - 4) // 100 and len(pos) > 0
+
+
 @pytest.mark.parametrize("BH", [2, 48])  # 48 x 90 tokens: the lane-per-token value path
 @pytest.mark.parametrize("case", ["ties", "zeros", "signed_zeros", "extremes", "subnormal", "const"])
 def test_degenerate_data(case, BH):

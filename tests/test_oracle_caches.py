@@ -199,3 +199,81 @@ def test_nuq_refit_from_one_token_reconstructs_it_exactly():
     x = k[:, :, 10].reshape(2, D).view(np.float16).astype(np.float32)
     assert np.array_equal(lev, np.repeat(x[:, :, None], 8, axis=2))
     assert np.array_equal(m.k[:, :, 10], k[:, :, 10])
+
+
+# ------------------------------------------------------------------ packed KIVI cache model
+from oracle.caches import KiviPackedCacheModel  # noqa: E402
+
+
+def _store_rows(m):
+    (kc, ks, kz), (vc, vs, vz) = m.store
+    ng = -(-m.nq // m.gs)
+    return [kc[:, :, :m.nq], ks[:, :, :ng], kz[:, :, :ng], vc[:, :, :m.nq], vs[:, :, :m.nq], vz[:, :, :m.nq]]
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_kivi_packed_cache_reduces_to_one_pack(bits):
+    """Without trims, the cache's fp16 view is the packed round trip of the
+    quantized prefix done in one go (flushes are group-aligned, so they cut
+    the same key groups) followed by the untouched residual window; and the
+    flush sizes do not matter."""
+    B, H, D = 2, 2, 64
+    k, v = _kv(B, H, 700, D, 11 + bits)
+    a = _feed(KiviPackedCacheModel(bits), k, v, [700])
+    b = _feed(KiviPackedCacheModel(bits), k, v, [300, 1, 1, 33, 64, 1, 300])
+    c = _feed(KiviPackedCacheModel(bits), k, v, [1] * 700)
+    nq = (700 - 128) // 32 * 32
+    assert a.nq == b.nq == c.nq == nq
+    for m in (b, c):
+        for x, y in zip(_store_rows(a), _store_rows(m)):
+            assert np.array_equal(x, y)
+    fk, fv = c.fetch()
+    for x, f, per_channel in ((k, fk, 1), (v, fv, 0)):
+        codes, sc, zr = oracle.kivi_pack(x, 0, nq, per_channel, bits, 32)
+        rec = oracle.kivi_unpack(codes, sc, zr, 0, nq, per_channel, bits, 32, D)
+        assert np.array_equal(f[:, :, :nq], rec[:, :, :nq])
+        assert np.array_equal(f[:, :, nq:], x[:, :, nq:])
+
+
+def test_kivi_packed_cache_bytes_are_the_stored_rows():
+    """The page's byte formula for the quantized prefix equals the rows of
+    the packed arrays that hold it, at every step."""
+    B, H, D, bits = 1, 3, 64, 2
+    k, v = _kv(B, H, 900, D, 21)
+    m, ref = KiviPackedCacheModel(bits), KiviCacheModel(bits)
+    t = 0
+    for n in (200, 1, 31, 1, 64, 300, 3, 300):
+        m.update(k[:, :, t:t + n], v[:, :, t:t + n])
+        ref.update(k[:, :, t:t + n], v[:, :, t:t + n])
+        t += n
+        assert m.nq == ref.nq
+        assert m.packed_bytes() == (ref.key_bytes, ref.value_bytes)
+        assert m.win[0].shape[2] == ref.offset - ref.nq <= 128 + 32 - 1
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_kivi_packed_cache_trim(bits):
+    """A trim changes no value that is kept; below the frontier the tokens
+    between the new frontier and the new length return to the window as
+    their packed reconstructions; trimming to empty leaves nothing."""
+    B, H, D = 1, 2, 64
+    k, v = _kv(B, H, 800, D, 31 + bits)
+    m = KiviPackedCacheModel(bits)
+    m.update(k[:, :, :400], v[:, :, :400])
+    assert m.nq == 256
+    before = m.fetch()
+    assert m.trim(30) == 30 and (m.n, m.nq) == (370, 256)        # into the window
+    after = m.fetch()
+    assert all(np.array_equal(x[:, :, :370], y) for x, y in zip(before, after))
+    assert m.trim(140) == 140 and (m.n, m.nq) == (230, 224)      # into the quantized region
+    after = m.fetch()
+    assert all(np.array_equal(x[:, :, :230], y) for x, y in zip(before, after))
+    assert np.array_equal(m.win[0], before[0][:, :, 224:230])
+    m.update(k[:, :, 230:600], v[:, :, 230:600])
+    assert m.nq == (600 - 128) // 32 * 32
+    straight = _feed(KiviPackedCacheModel(bits), k[:, :, :600], v[:, :, :600], [600])
+    assert m.packed_bytes() == straight.packed_bytes()
+    # rows quantized before the trim keep their stored values
+    f, g = m.fetch(), straight.fetch()
+    assert all(np.array_equal(x[:, :, :224], y[:, :, :224]) for x, y in zip(f, g))
+    assert m.trim(10 ** 6) == 600 and m.n == 0 and m.win[0].shape[2] == 0
