@@ -331,6 +331,29 @@ int kvq_nuq_fit_quant(const uint16_t *keys, const uint16_t *values, int32_t BH, 
                       uint16_t *k_recon, uint16_t *v_recon, void *workspace, int64_t workspace_bytes,
                       void *stream);
 
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, serving loops that forbid allocation, harnesses that do not allow
+ * hipMalloc: kvq_nuq_fit_quant without the workspace argument. The workspace
+ * is a static device array of KVQ_NUQ_NOALLOC_WORKSPACE_BYTES (32 MiB) built
+ * into the library: every device the library runs on holds one copy until
+ * the process ends, looked up (hipGetSymbolAddress) on the first call made
+ * with that device current. The call allocates nothing, creates no stream or
+ * event, and runs every kernel on `stream` (no auxiliary stream); counters
+ * in the array are cleared by the call's first kernel. Arguments, outputs and
+ * errors as kvq_nuq_fit_quant, plus KVQ_ERR_CAPACITY when the call needs more
+ * workspace than the array holds (kvq_nuq_workspace_bytes gives the need:
+ * e.g. 32 (batch, head) vectors x 4096 tokens x D = 128 need about 2 MiB).
+ * All calls on one device share the one array: calls that overlap on a
+ * device (other streams, other host threads) race and must be serialised by
+ * the caller. */
+#define KVQ_NUQ_NOALLOC_WORKSPACE_BYTES (32u << 20)
+int kvq_nuq_fit_quant_noalloc(const uint16_t *keys, const uint16_t *values, int32_t BH, int32_t S, int32_t D,
+                              int32_t start_pos, int32_t bits, double frac, int32_t lloyd_iters, int32_t n_sink,
+                              int32_t fit_keys, float *key_levels, uint16_t *key_thresh, float *value_levels,
+                              uint8_t *k_codes, uint8_t *v_codes, int32_t *k_opos, uint16_t *k_oval,
+                              int32_t *v_opos, uint16_t *v_oval, int64_t out_cap, int64_t *out_counts,
+                              uint16_t *k_recon, uint16_t *v_recon, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

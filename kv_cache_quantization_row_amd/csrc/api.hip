@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/kvq.h"
@@ -519,16 +520,16 @@ int64_t kvq_nuq_workspace_bytes(int32_t BH, int32_t S, int32_t D, int32_t bits, 
   return p.total;
 }
 
-int kvq_nuq_fit_quant(const uint16_t *keys, const uint16_t *values, int32_t BH, int32_t S, int32_t D,
-                      int32_t start_pos, int32_t bits, double frac, int32_t lloyd_iters, int32_t n_sink,
-                      int32_t fit_keys, float *key_levels, uint16_t *key_thresh, float *value_levels,
-                      uint8_t *k_codes, uint8_t *v_codes, int32_t *k_opos, uint16_t *k_oval,
-                      int32_t *v_opos, uint16_t *v_oval, int64_t out_cap, int64_t *out_counts,
-                      uint16_t *k_recon, uint16_t *v_recon, void *workspace, int64_t workspace_bytes,
-                      void *stream) {
-  NuqPlan p;
-  int rc = nuq_plan(BH, S, D, bits, start_pos, n_sink, frac, fit_keys, p);
-  if (rc) return rc;
+}  // extern "C"
+
+namespace {
+// One NUQ call with a given workspace: host validation, then the launches.
+int nuq_call(const uint16_t *keys, const uint16_t *values, int32_t BH, int32_t S, int32_t D, int32_t start_pos,
+             int32_t bits, double frac, int32_t lloyd_iters, int32_t n_sink, int32_t fit_keys, float *key_levels,
+             uint16_t *key_thresh, float *value_levels, uint8_t *k_codes, uint8_t *v_codes, int32_t *k_opos,
+             uint16_t *k_oval, int32_t *v_opos, uint16_t *v_oval, int64_t out_cap, int64_t *out_counts,
+             uint16_t *k_recon, uint16_t *v_recon, const NuqPlan &p, void *workspace, bool fork, void *stream,
+             const char *what) {
   if (lloyd_iters < 0 || lloyd_iters > 1000) return fail(KVQ_ERR_ARG, "lloyd_iters must be in [0, 1000]");
   if (!keys || !values || !key_levels || !key_thresh || !value_levels || !k_codes || !v_codes ||
       !k_opos || !k_oval || !v_opos || !v_oval || !out_counts || !workspace)
@@ -536,9 +537,6 @@ int kvq_nuq_fit_quant(const uint16_t *keys, const uint16_t *values, int32_t BH, 
   if (out_cap < p.kb || out_cap < p.vb)
     return fail(KVQ_ERR_CAPACITY, "out_cap=%lld below the outlier bound (keys %lld, values %lld)",
                 (long long)out_cap, (long long)p.kb, (long long)p.vb);
-  if (workspace_bytes < p.total)
-    return fail(KVQ_ERR_CAPACITY, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
-                (long long)p.total);
   for (const void *q : {(const void *)keys, (const void *)values, (const void *)k_codes, (const void *)v_codes,
                         (const void *)k_recon, (const void *)v_recon, (const void *)workspace})
     if (q && !aligned(q, 16)) return fail(KVQ_ERR_ALIGN, "fp16 tensors, code buffers and the workspace need 16-byte alignment");
@@ -582,7 +580,79 @@ int kvq_nuq_fit_quant(const uint16_t *keys, const uint16_t *values, int32_t BH, 
   a.ws_vval = reinterpret_cast<uint16_t *>(ws + p.off_vval);
   a.k_blk_x = p.k_blk_x;
   a.v_nblk = p.v_nblk;
-  return hip_status(kvq::launch_nuq(a, p.key_cpc, p.val_cpc, (hipStream_t)stream), "kvq_nuq_fit_quant launch");
+  return hip_status(kvq::launch_nuq(a, p.key_cpc, p.val_cpc, fork, (hipStream_t)stream), what);
+}
+
+// Workspace of kvq_nuq_fit_quant_noalloc: a file-scope device array, one copy
+// per device, addressed through the pointer hipGetSymbolAddress gives for it
+// on that device (the array's name in host code is a host-side stand-in, not
+// a device address, and is never passed to a kernel or a copy).
+static __device__ __align__(256) uint8_t scratch[KVQ_NUQ_NOALLOC_WORKSPACE_BYTES];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64];  // address of `scratch` on device i, looked up once with that device current
+
+int scratch_on_current_device(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(KVQ_ERR_HIP, "device %d is outside the 64 devices supported", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (ptr == nullptr) return fail(KVQ_ERR_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return KVQ_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int kvq_nuq_fit_quant(const uint16_t *keys, const uint16_t *values, int32_t BH, int32_t S, int32_t D,
+                      int32_t start_pos, int32_t bits, double frac, int32_t lloyd_iters, int32_t n_sink,
+                      int32_t fit_keys, float *key_levels, uint16_t *key_thresh, float *value_levels,
+                      uint8_t *k_codes, uint8_t *v_codes, int32_t *k_opos, uint16_t *k_oval,
+                      int32_t *v_opos, uint16_t *v_oval, int64_t out_cap, int64_t *out_counts,
+                      uint16_t *k_recon, uint16_t *v_recon, void *workspace, int64_t workspace_bytes,
+                      void *stream) {
+  NuqPlan p;
+  int rc = nuq_plan(BH, S, D, bits, start_pos, n_sink, frac, fit_keys, p);
+  if (rc) return rc;
+  if (workspace && workspace_bytes < p.total)
+    return fail(KVQ_ERR_CAPACITY, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
+                (long long)p.total);
+  return nuq_call(keys, values, BH, S, D, start_pos, bits, frac, lloyd_iters, n_sink, fit_keys, key_levels,
+                  key_thresh, value_levels, k_codes, v_codes, k_opos, k_oval, v_opos, v_oval, out_cap, out_counts,
+                  k_recon, v_recon, p, workspace, true, stream, "kvq_nuq_fit_quant launch");
+}
+
+int kvq_nuq_fit_quant_noalloc(const uint16_t *keys, const uint16_t *values, int32_t BH, int32_t S, int32_t D,
+                              int32_t start_pos, int32_t bits, double frac, int32_t lloyd_iters, int32_t n_sink,
+                              int32_t fit_keys, float *key_levels, uint16_t *key_thresh, float *value_levels,
+                              uint8_t *k_codes, uint8_t *v_codes, int32_t *k_opos, uint16_t *k_oval,
+                              int32_t *v_opos, uint16_t *v_oval, int64_t out_cap, int64_t *out_counts,
+                              uint16_t *k_recon, uint16_t *v_recon, void *stream) {
+  NuqPlan p;
+  int rc = nuq_plan(BH, S, D, bits, start_pos, n_sink, frac, fit_keys, p);
+  if (rc) return rc;
+  if (p.total > (int64_t)KVQ_NUQ_NOALLOC_WORKSPACE_BYTES)
+    return fail(KVQ_ERR_CAPACITY,
+                "this call needs %lld bytes of workspace, above the %lld bytes of the built-in one "
+                "(use kvq_nuq_fit_quant with a workspace)",
+                (long long)p.total, (long long)KVQ_NUQ_NOALLOC_WORKSPACE_BYTES);
+  if (lloyd_iters < 0 || lloyd_iters > 1000) return fail(KVQ_ERR_ARG, "lloyd_iters must be in [0, 1000]");
+  if (!keys || !values || !key_levels || !key_thresh || !value_levels || !k_codes || !v_codes || !k_opos ||
+      !k_oval || !v_opos || !v_oval || !out_counts)
+    return fail(KVQ_ERR_NULL, "a required NUQ pointer is NULL");
+  void *ws = nullptr;
+  if ((rc = scratch_on_current_device(&ws)) != KVQ_OK) return rc;
+  return nuq_call(keys, values, BH, S, D, start_pos, bits, frac, lloyd_iters, n_sink, fit_keys, key_levels,
+                  key_thresh, value_levels, k_codes, v_codes, k_opos, k_oval, v_opos, v_oval, out_cap, out_counts,
+                  k_recon, v_recon, p, ws, false, stream, "kvq_nuq_fit_quant_noalloc launch");
 }
 
 }  // extern "C"

@@ -84,7 +84,9 @@ struct NuqArgs {
   int64_t k_blk_x, v_nblk;         // key-quant workgroups along S (16384/D rows each); value workgroups
 };
 
-hipError_t launch_nuq(const NuqArgs &a, int key_cpc, int val_cpc, hipStream_t st);
+// fork: run a many-token value fit on the device's auxiliary stream (false:
+// every kernel on `st`, no stream or event is created)
+hipError_t launch_nuq(const NuqArgs &a, int key_cpc, int val_cpc, bool fork, hipStream_t st);
 
 // Attention chunks are whole blocks of 16 positions and never shorter than
 // ATTN_MIN_CHUNK positions, so a sequence of max_len positions has at most

@@ -1608,7 +1608,7 @@ hipError_t launch_values(const NuqArgs &a, int val_cpc, hipStream_t st) {
 }
 
 template <int BITS>
-hipError_t launch_bits(const NuqArgs &a, int key_cpc, int val_cpc, hipStream_t st) {
+hipError_t launch_bits(const NuqArgs &a, int key_cpc, int val_cpc, bool fork, hipStream_t st) {
   constexpr int L = 1 << BITS;
   hipError_t e;
   hipLaunchKernelGGL(nuq_zero, dim3(1), dim3(256), 0, st, a);
@@ -1626,7 +1626,7 @@ hipError_t launch_bits(const NuqArgs &a, int key_cpc, int val_cpc, hipStream_t s
       hipLaunchKernelGGL((nuq_small<4, BITS>), grid, dim3(256), 0, st, a, kn, ntok);
     return hipGetLastError();
   }
-  if (val_cpc == 0) {  // few tokens: short kernels, where a cross-stream join costs more than it hides
+  if (val_cpc == 0 || !fork) {  // few tokens (a cross-stream join costs more than it hides), or one stream asked for
     if (a.fit_keys && (e = launch_key_fit<L>(a, key_cpc, st)) != hipSuccess) return e;
     hipLaunchKernelGGL((nuq_key_quant<BITS>), dim3((unsigned)a.k_blk_x, a.BH), dim3(256), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1650,12 +1650,12 @@ hipError_t launch_bits(const NuqArgs &a, int key_cpc, int val_cpc, hipStream_t s
 }
 }  // namespace
 
-hipError_t launch_nuq(const NuqArgs &a, int key_cpc, int val_cpc, hipStream_t st) {
+hipError_t launch_nuq(const NuqArgs &a, int key_cpc, int val_cpc, bool fork, hipStream_t st) {
   switch (a.bits) {
-    case 1: return launch_bits<1>(a, key_cpc, val_cpc, st);
-    case 2: return launch_bits<2>(a, key_cpc, val_cpc, st);
-    case 3: return launch_bits<3>(a, key_cpc, val_cpc, st);
-    default: return launch_bits<4>(a, key_cpc, val_cpc, st);
+    case 1: return launch_bits<1>(a, key_cpc, val_cpc, fork, st);
+    case 2: return launch_bits<2>(a, key_cpc, val_cpc, fork, st);
+    case 3: return launch_bits<3>(a, key_cpc, val_cpc, fork, st);
+    default: return launch_bits<4>(a, key_cpc, val_cpc, fork, st);
   }
 }
 

@@ -58,6 +58,8 @@ _SIGS = {
     "kvq_nuq_outlier_bound": (_L, [_I, _I, _I, _I, _I, _D, _I, _I]),
     "kvq_nuq_fit_quant": (C.c_int, [_P, _P, _I, _I, _I, _I, _I, _D, _I, _I, _I,
                                     _P, _P, _P, _P, _P, _P, _P, _P, _P, _L, _P, _P, _P, _P, _L, _P]),
+    "kvq_nuq_fit_quant_noalloc": (C.c_int, [_P, _P, _I, _I, _I, _I, _I, _D, _I, _I, _I,
+                                            _P, _P, _P, _P, _P, _P, _P, _P, _P, _L, _P, _P, _P, _P]),
 }
 
 _lib = None
@@ -406,3 +408,22 @@ def kvq_nuq_fit_quant(keys, values, start_pos, bits, frac, lloyd_iters, n_sink, 
                                  _ptr(k_opos), _ptr(k_oval), _ptr(v_opos), _ptr(v_oval), out_cap,
                                  _ptr(out_counts), _ptr(k_recon), _ptr(v_recon), _ptr(workspace),
                                  int(workspace.numel()) if workspace is not None else 0, _stream(stream)))
+
+
+NUQ_NOALLOC_WORKSPACE_BYTES = 32 << 20  # KVQ_NUQ_NOALLOC_WORKSPACE_BYTES in include/kvq.h
+
+
+def kvq_nuq_fit_quant_noalloc(keys, values, start_pos, bits, frac, lloyd_iters, n_sink, fit_keys,
+                              key_levels, key_thresh, value_levels, k_codes, v_codes, k_opos, k_oval,
+                              v_opos, v_oval, out_counts, k_recon=None, v_recon=None, stream=None):
+    """kvq_nuq_fit_quant with the library's built-in device workspace (no
+    allocation; calls on one device must not overlap)."""
+    BH, S, D, out_cap = _nuq_check(keys, values, bits, key_levels, key_thresh, value_levels, k_codes, v_codes,
+                                   k_opos, k_oval, v_opos, v_oval, out_counts, k_recon, v_recon)
+    _dev(keys, values, key_levels, key_thresh, value_levels, k_codes, v_codes, k_opos, k_oval, v_opos, v_oval,
+         out_counts, k_recon, v_recon)
+    _err(lib().kvq_nuq_fit_quant_noalloc(_ptr(keys), _ptr(values), BH, S, D, start_pos, bits, frac,
+                                         lloyd_iters, n_sink, int(fit_keys), _ptr(key_levels),
+                                         _ptr(key_thresh), _ptr(value_levels), _ptr(k_codes), _ptr(v_codes),
+                                         _ptr(k_opos), _ptr(k_oval), _ptr(v_opos), _ptr(v_oval), out_cap,
+                                         _ptr(out_counts), _ptr(k_recon), _ptr(v_recon), _stream(stream)))
