@@ -74,8 +74,48 @@ def measured_traffic(kernel_class):
     return launches * sum(v[1] for v in best.values())
 
 
+VALU_FILE = os.path.join(ROOT, "profiles", "valu_nuq_3bit_BH32_S4096_D128.md")
+# VALU issue peak: each CU issues one wave64 VALU instruction per clock (4
+# SIMDs, each taking 4 clocks for the 64 lanes of a wave on its 16 lanes):
+# 256 CUs x 64 lanes x 2.4 GHz = 39.3 T lane-instructions per second
+# (the 157.3 TFLOP/s fp32 figure counts an fma as 2 and packed fp32 as 2 more).
+VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
+
+
+def measured_valu(call):
+    """VALU instructions (SQ_INSTS_VALU, summed over the kernels of one call)
+    from the committed rocprofv3 counter summary, or None when absent or when
+    the kernel source changed since the counters were taken."""
+    import hashlib
+    import re
+
+    if not os.path.exists(VALU_FILE):
+        return None
+    sha = hashlib.sha1(open(os.path.join(CSRC, "nuq.hip"), "rb").read()).hexdigest()
+    for line in open(VALU_FILE):
+        m = re.match(r"valu_call (\S+) insts=(\d+) src_sha1=([0-9a-f]+)", line.strip())
+        if m and m.group(1) == call and m.group(3) == sha:
+            return int(m.group(2))
+    return None
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+CPU_SHARE = 16  # host cores the GPU box gives one GPU's jobs, whatever the machine has
+CPU_CAP_NOTE = "threads = min(cores available to the process, 16): the host's CPU share for one GPU"
+
+
+def cpu_threads():
+    return max(1, min(CPU_SHARE, len(os.sched_getaffinity(0))))
+
+
+def run_threads(fn, parts):
+    """fn over parts, one thread each (the oracle's C calls release the GIL)."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(len(parts)) as ex:
+        return list(ex.map(fn, parts))
 
 
 class Timers:
@@ -226,7 +266,7 @@ class PagedSym:
         # all cores: one thread per core over disjoint token ranges, each
         # calling the unmodified oracle (its C calls release the GIL)
         from concurrent.futures import ThreadPoolExecutor
-        cores = max(1, min(16, len(os.sched_getaffinity(0))))
+        cores = cpu_threads()
         cut = [n * i // cores for i in range(cores + 1)]
         parts = [(kk[cut[i]:cut[i + 1]], vv[cut[i]:cut[i + 1]]) for i in range(cores)]
         t0 = time.perf_counter()
@@ -236,8 +276,8 @@ class PagedSym:
         return {"value": round(2 * elems_all / dtn / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
                 "value_1core": round(2 * elems / dt1 / 1e9, 4),
                 "sample": "layer 0, %d tokens x 4 heads x 256 of K and V, quantize + dequantize at q%s: "
-                          "%.1f s on one thread, %.2f s on %d threads over disjoint token ranges"
-                          % (n, "/q".join(map(str, self.bits_list)), dt1, dtn, cores)}
+                          "%.1f s on one thread, %.2f s on %d threads over disjoint token ranges (%s)"
+                          % (n, "/q".join(map(str, self.bits_list)), dt1, dtn, cores, CPU_CAP_NOTE)}
 
 
 # --------------------------------------------------------------------------- KIVI
@@ -248,6 +288,7 @@ class Kivi:
         self.torch = torch
         self.B, self.H, self.S, self.D, self.gs = 128, 8, 8192, 64, 32
         self.bits_list = [int(b) for b in args.kivi_bits.split(",")]
+        self.steps, self.warmup = args.steps, args.warmup
         self.name = "kivi"
 
     def setup(self):
@@ -257,17 +298,23 @@ class Kivi:
         self.kvq = kvq
         d = torch.device("cuda:0")
         self.hi = kvq.kvq_kivi_boundary(self.S, 128, self.gs)
-        self.k0, self.v0 = inputs.kivi_kv(self.B, self.H, self.S, self.D, seed=1003, device=d)
-        self.k = self.k0.clone()
-        self.v = self.v0.clone()
+        k0, v0 = inputs.kivi_kv(self.B, self.H, self.S, self.D, seed=1003, device=d)
+        # the round trip is in place and its output sits on the quantization
+        # grid (where the near-tie division fallback never fires), so every
+        # timed call gets its own fresh copy of the input: 2 GiB per call
+        n = len(self.bits_list) * (self.steps + self.warmup)
+        log("KIVI: %d fresh input copies (%.0f GiB)" % (n, n * 2 * k0.numel() * 2 / 2 ** 30))
+        self.copies = [(k0.clone(), v0.clone()) for _ in range(n)]
+        del k0, v0
+        self.i = 0
         torch.cuda.synchronize()
 
     def step(self, tm):
         for b in self.bits_list:
-            # the round trip is in place: re-running it on its own output is the
-            # same work (same groups, same bytes); the data stays resident
+            k, v = self.copies[self.i % len(self.copies)]
+            self.i += 1
             with tm.span("kivi_keys_values_b%d" % b):
-                self.kvq.kvq_kivi_quant_dequant(self.k, self.v, 0, self.hi, b, self.gs)
+                self.kvq.kvq_kivi_quant_dequant(k, v, 0, self.hi, b, self.gs)
 
     def elems(self):
         return 2 * self.B * self.H * self.hi * self.D * len(self.bits_list)
@@ -443,6 +490,21 @@ class Nuq:
         return self.n_dec * (2 * 2 * BH * D + 2 * BH * D * self.bits / 8 + BH * D * (4 * L + 2)
                              + BH * 4 * L + 6 * n_out1)
 
+    def roofline(self, dom, kernels, means):
+        """The prefill call is bound by the fits' VALU work, not by HBM: report
+        its VALU issue rate (counted instructions x 64 lanes over the live call
+        time) against the VALU peak; the HBM fraction stays beside it."""
+        if dom != "nuq_prefill":
+            return None
+        insts = measured_valu("nuq_prefill")
+        if insts is None:
+            return None
+        achieved = insts * 64 / (means[dom] / 1e3) / 1e12
+        return {"bound": "alu", "kernel": dom, "achieved": round(achieved, 3), "peak": round(VALU_PEAK_TOPS, 2),
+                "unit": "TOP/s (VALU lane-instructions)", "frac": round(achieved / VALU_PEAK_TOPS, 4),
+                "traffic": None, "valu_instructions": insts, "frac_hbm": kernels[dom]["frac_hbm"],
+                "algorithmic_bytes": int(self.kernel_bytes(dom))}
+
     def config(self):
         return {"workload": "KVQuant-style NUQ 3-bit: batch 4 x 8 KV heads, D=128, 4096-token prefill "
                             "(1%% outliers, %d Lloyd iterations, 4 sinks) + %d decode calls" % (self.iters, self.n_dec),
@@ -544,7 +606,38 @@ class LongContext:
                 "packed_GiB": round(self.kvq.kvq_sym_cache_bytes(self.T, 16, 4, 256, 6) / 2 ** 30, 4)}
 
     def cpu_baseline(self, budget_tokens):
-        return None
+        """Oracle on chunks 0-3 of layer 0 (16,384 tokens: quantize into pages,
+        then dequantize them), on all CPU_SHARE threads over disjoint token
+        ranges; extrapolated linearly to the whole workload."""
+        import numpy as np
+        import oracle
+        from kv_cache_quantization_row_amd import inputs
+
+        n = 4 * self.CH
+        k = inputs.sym_layer(n, self.H, self.D, seed=7100, channel_seed=8100)
+        v = inputs.sym_layer(n, self.H, self.D, seed=7200, channel_seed=8200)
+        kk = k.view(__import__("torch").int16).numpy().view(np.uint16)
+        vv = v.view(__import__("torch").int16).numpy().view(np.uint16)
+
+        def run(part):
+            elems = 0
+            for x in part:
+                c, sc = oracle.sym_quant_rows(x, self.bits)
+                oracle.sym_dequant_rows(c, sc, self.D, self.bits)
+                elems += 2 * x.size
+            return elems
+
+        cores = cpu_threads()
+        cut = [n * i // cores for i in range(cores + 1)]
+        t0 = time.perf_counter()
+        elems = sum(run_threads(run, [(kk[cut[i]:cut[i + 1]], vv[cut[i]:cut[i + 1]]) for i in range(cores)]))
+        dt = time.perf_counter() - t0
+        rate = 2 * elems / dt / 1e9
+        whole_s = 2 * self.elems() / (rate * 1e9)
+        return {"value": round(rate, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+                "sample": "chunks 0-3 of layer 0 (16,384 tokens x 4 heads x 256, K and V): quantize + dequantize, "
+                          "%.2f s on %d threads (%s); extrapolated linearly: %.0f s for the whole workload"
+                          % (dt, cores, CPU_CAP_NOTE, whole_s)}
 
 
 # --------------------------------------------------------------------------- decode attention
@@ -708,6 +801,105 @@ class SingleLayer:
                             "%d resident copies" % self.copies, "bits": self.bits}
 
     def cpu_baseline(self, budget_tokens):
+        """The oracle on the whole configuration (one layer, K and V [1024][4][256]:
+        quantize into pages, dequantize back), single thread, repeated."""
+        import numpy as np
+        import torch as _t
+        import oracle
+        from kv_cache_quantization_row_amd import inputs
+
+        T, H, D, P = self.T, self.H, self.D, self.P
+        k = inputs.sym_layer(T, H, D, seed=1001).view(_t.int16).numpy().view(np.uint16)
+        v = inputs.sym_layer(T, H, D, seed=1002).view(_t.int16).numpy().view(np.uint16)
+        pd = oracle.packed_dim(D, self.bits)
+        slot = np.arange(T, dtype=np.int32)
+        bt = np.arange(T // P, dtype=np.int32)[None]
+        reps, t0 = 0, time.perf_counter()
+        while reps < 3 or time.perf_counter() - t0 < 2.0:
+            for x in (k, v):
+                codes = np.zeros((T, H, pd), np.uint8)
+                sc = np.zeros((T, H), np.uint16)
+                oracle.sym_quant_paged(x, self.bits, slot, codes, sc)
+                oracle.sym_dequant_paged(codes, sc, P, D, self.bits, bt, np.array([T], np.int32), T)
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
+        return {"value": round(2 * 2 * 2 * T * H * D / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": "the whole configuration (quantize into 64 pages + dequantize, K and V), %d repetitions, "
+                          "%.1f ms each, one thread" % (reps, dt * 1e3)}
+
+
+class Caches:
+    """The cache objects over the kernels, in decode: a NuqCache with a
+    4096-token prefill (batch 4 x 8 KV heads, D=128, 3 bits, 1% outliers, 8
+    Lloyd iterations, 4 sinks) takes 64 one-token decode steps
+    (update_and_fetch: fit, quantize, reconstruction appended; no host sync);
+    a packed KiviCache on the KIVI shape (batch 8 x 16 layers folded, 8 KV
+    heads, D=64, b=2, group 32, residual 128) with an 8192-token prefill
+    takes 32 one-token decode steps, each returning the whole fp16 K/V
+    (kvq_kivi_unpack of the packed prefix plus the fp16 window; one step in
+    32 also packs a new group)."""
+
+    def __init__(self, torch, args):
+        self.torch = torch
+        self.name = "caches"
+        self.n_nuq, self.n_kivi = 64, 32
+
+    def setup(self):
+        torch = self.torch
+        from kv_cache_quantization_row_amd import caches, inputs
+
+        d = torch.device("cuda:0")
+        self.caches = caches
+        B, H, D = 4, 8, 128
+        self.nk = inputs.student_t((B * H, 4096, D), 4, seed=1004, device=d).view(B, H, 4096, D)
+        self.nv = inputs.student_t((B * H, 4096, D), 4, seed=1005, device=d).view(B, H, 4096, D)
+        n_dec = self.n_nuq * 64
+        self.nkd = inputs.student_t((B * H, n_dec, D), 4, seed=5000, device=d).view(B, H, n_dec, D)
+        self.nvd = inputs.student_t((B * H, n_dec, D), 4, seed=6000, device=d).view(B, H, n_dec, D)
+        self.nuq_steps = [(self.nkd[:, :, t:t + 1].contiguous(), self.nvd[:, :, t:t + 1].contiguous())
+                          for t in range(n_dec)]
+        Bk, Hk, Dk = 128, 8, 64
+        self.kk, self.kv = inputs.kivi_kv(Bk, Hk, 8192 + 64 * self.n_kivi, Dk, seed=1003, device=d)
+        self.kivi_steps = [(self.kk[:, :, 8192 + t:8193 + t].contiguous(), self.kv[:, :, 8192 + t:8193 + t].contiguous())
+                           for t in range(64 * self.n_kivi)]
+        self._fresh()
+        torch.cuda.synchronize()
+
+    def _fresh(self):
+        self.nuq = self.caches.NuqCache(3, 0.01, 8, 4)
+        self.nuq.update_and_fetch(self.nk, self.nv)
+        self.kivi = self.caches.KiviCache(2, 32, 128, storage="packed")
+        self.kivi.update_and_fetch(self.kk[:, :, :8192].contiguous(), self.kv[:, :, :8192].contiguous())
+        self.t_nuq = self.t_kivi = 0
+
+    def step(self, tm):
+        if self.t_nuq + self.n_nuq > len(self.nuq_steps) or self.t_kivi + self.n_kivi > len(self.kivi_steps):
+            self._fresh()
+        with tm.span("nuq_cache_decode_x%d" % self.n_nuq):
+            for i in range(self.n_nuq):
+                self.nuq.update_and_fetch(*self.nuq_steps[self.t_nuq + i])
+        self.t_nuq += self.n_nuq
+        with tm.span("kivi_packed_cache_decode_x%d" % self.n_kivi):
+            for i in range(self.n_kivi):
+                self.kivi.update_and_fetch(*self.kivi_steps[self.t_kivi + i])
+        self.t_kivi += self.n_kivi
+
+    def elems(self):  # fp16 K and V elements handed back by the KIVI fetches
+        return 2 * 128 * 8 * 8200 * 64 * self.n_kivi
+
+    def kernel_bytes(self, name):
+        if name.startswith("kivi"):  # per step: packed prefix read, fp16 K/V written, window copied
+            BH, n, D = 128 * 8, 8200, 64
+            return self.n_kivi * 2 * BH * (n * D * 2 + n * D * 2 / 8 + (n // 32) * D * 4 / 2 + n * 4)
+        BH, D, L = 32, 128, 8
+        return self.n_nuq * (2 * 2 * BH * D + 2 * BH * D * 3 / 8 + BH * D * (4 * L + 2) + BH * 4 * L)
+
+    def config(self):
+        return {"workload": "cache objects in decode: NuqCache (batch 4 x 8 KV heads, D=128, 3 bits, 4096-token "
+                            "prefill) 64 one-token steps; packed KiviCache (B=128, 8 KV heads, D=64, b=2, group 32, "
+                            "8192-token prefill) 32 one-token steps returning the whole fp16 K/V"}
+
+    def cpu_baseline(self, budget_tokens):
         return None
 
 
@@ -745,7 +937,8 @@ class Copy:
 
 
 WORKLOADS = {"paged_sym": PagedSym, "kivi": Kivi, "nuq": Nuq, "long_context": LongContext,
-             "single_layer": SingleLayer, "attn_decode": AttnDecode, "kivi_packed": KiviPacked, "copy": Copy}
+             "single_layer": SingleLayer, "attn_decode": AttnDecode, "kivi_packed": KiviPacked, "copy": Copy,
+             "caches": Caches}
 
 
 def main():
@@ -807,12 +1000,16 @@ def main():
         nbytes = wl.kernel_bytes(name)
         gbs = nbytes / (ms / 1e3) / 1e9
         kernels[name] = {"avg_ms": round(ms, 4), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+        if "_x" in name and name.rsplit("_x", 1)[1].isdigit():  # a span of N launches or steps
+            kernels[name]["us_per_call"] = round(ms * 1e3 / int(name.rsplit("_x", 1)[1]), 2)
     totals = {n: means[n] * c for n, c in tm.count().items()}
     cands = [n for n in totals if "decode" not in n] or list(totals)
     dom = max(cands, key=lambda n: totals[n])
-    roof = {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["GB/s"], "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": kernels[dom]["frac_hbm"], "traffic": measured_traffic(dom),
-            "algorithmic_bytes": int(wl.kernel_bytes(dom))}
+    roof = wl.roofline(dom, kernels, means) if hasattr(wl, "roofline") else None
+    if roof is None:
+        roof = {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["GB/s"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": kernels[dom]["frac_hbm"], "traffic": measured_traffic(dom),
+                "algorithmic_bytes": int(wl.kernel_bytes(dom))}
 
     cpu = None
     if not args.no_cpu_baseline:

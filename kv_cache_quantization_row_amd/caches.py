@@ -162,11 +162,19 @@ class KiviCache:
         (kc, ks, kz), (vc, vs, vz) = self._store
         kvq.kvq_kivi_pack(self._win[0], self._win[1], lo, hi, self.bits, self.group_size, k_codes=kc, k_scale=ks,
                           k_zero=kz, v_codes=vc, v_scale=vs, v_zero=vz, x_t0=self._front)
-        # the window keeps tokens [hi, len): move them to its first rows
-        keep = self._len - hi
-        for w in self._win:
-            if keep:
-                w[:, :, :keep].copy_(w[:, :, hi - self._front: hi - self._front + keep].clone())
+        # the window keeps tokens [hi, len): move them to its first rows, into
+        # a smaller buffer when a long prefill left it far larger than the
+        # residual window needs
+        keep, off = self._len - hi, hi - self._front
+        B, H, D, dev = self._geom
+        small = -(-(self.residual_length + self.group_size) // self.step) * self.step + self.step
+        for i, w in enumerate(self._win):
+            if w.shape[2] > 2 * small:
+                nw = _fp16_buffer(None, B, H, max(keep, small), D, self.step, dev)
+                nw[:, :, :keep].copy_(w[:, :, off:off + keep])
+                self._win[i] = nw
+            elif keep:
+                w[:, :, :keep].copy_(w[:, :, off:off + keep].clone())
 
     def _unpack_into(self, out_k, out_v, lo, hi, out_t0):
         (kc, ks, kz), (vc, vs, vz) = self._store
