@@ -529,8 +529,9 @@ class Nuq:
 # --------------------------------------------------------------------------- long context
 class LongContext:
     """One 262,144-token sequence, 16 layers x 4 KV heads x D=256, q6, page 16:
-    quantized in 64 chunks of 4096 tokens (one launch per chunk, all layers),
-    1,024 single-token appends, then a full dequant of 263,168 tokens."""
+    quantized in 64 chunks of 4096 tokens (one launch per chunk, all layers,
+    alternating over two streams), 1,024 single-token appends, then a full
+    dequant of 263,168 tokens."""
 
     def __init__(self, torch, args):
         self.torch = torch
@@ -573,13 +574,26 @@ class LongContext:
         self.bt_d = self.bt.to(d)
         self.lens = torch.full((1,), self.total, dtype=torch.int32, device=d)
         self.lay = kvq.layout(L, self.num_pages, P, H, D, self.bits)
+        self.side = torch.cuda.Stream()  # default priority
         torch.cuda.synchronize()
 
     def step(self, tm):
-        kvq = self.kvq
+        kvq, torch = self.kvq, self.torch
         with tm.span("quant_chunks_q6_x%d" % len(self.slots)):
+            # consecutive chunks are independent: even chunks on the timing
+            # stream, odd ones on a second stream of the same (default)
+            # priority, so one launch's drain overlaps the next one's ramp;
+            # the second stream is forked from and joined back into the first
+            main = torch.cuda.current_stream()
+            fork = torch.cuda.Event()
+            fork.record(main)
+            self.side.wait_event(fork)
             for c, sm in enumerate(self.slots):
-                kvq.kvq_quant_sym(self.lay, self.k[c], self.v[c], sm, self.kc, self.ks, self.vc, self.vs)
+                st = main if c % 2 == 0 else self.side
+                kvq.kvq_quant_sym(self.lay, self.k[c], self.v[c], sm, self.kc, self.ks, self.vc, self.vs, stream=st)
+            join = torch.cuda.Event()
+            join.record(self.side)
+            main.wait_event(join)
         with tm.span("decode_append_q6_x%d" % self.N_DEC):
             for i in range(self.N_DEC):
                 kvq.kvq_quant_sym(self.lay, self.kd_steps[i], self.vd_steps[i], self.sm_steps[i], self.kc, self.ks,

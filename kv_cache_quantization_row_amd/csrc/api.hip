@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 #include <string>
 
@@ -36,6 +37,15 @@ int hip_status(hipError_t e, const char *what) {
 }
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// product of non-negative sizes is below `limit` (false also when the product
+// does not fit in 64 bits)
+bool product_below(std::initializer_list<int64_t> factors, int64_t limit) {
+  int64_t r = 1;
+  for (const int64_t f : factors)
+    if (__builtin_mul_overflow(r, f, &r)) return false;
+  return r < limit;
+}
 
 int32_t qmax_of(int32_t bits) {
   switch (bits) {  // explicit table; unknown widths are not mapped to a neighbour
@@ -70,7 +80,8 @@ int check_layout(const kvq_paged_layout *L) {
     return fail(KVQ_ERR_SHAPE, "layout sizes must be positive (layers=%d pages=%d page_size=%d heads=%d)",
                 L->layers, L->num_pages, L->page_size, L->kv_heads);
   const int64_t slots = (int64_t)L->num_pages * L->page_size;
-  if (slots * L->kv_heads >= ((int64_t)1 << 40))
+  int64_t rows = 0;
+  if (__builtin_mul_overflow(slots, (int64_t)L->kv_heads, &rows) || rows >= ((int64_t)1 << 40))
     return fail(KVQ_ERR_SHAPE, "pool too large");
   return KVQ_OK;
 }
@@ -113,7 +124,10 @@ int64_t kvq_sym_cache_bytes(int64_t tokens, int32_t layers, int32_t kv_heads, in
     if (pd < 0) return -1;
     row = pd + 2;
   }
-  return 2 * tokens * layers * kv_heads * row;
+  int64_t r = 2 * row;
+  for (const int64_t f : {tokens, (int64_t)layers, (int64_t)kv_heads})
+    if (__builtin_mul_overflow(r, f, &r)) return -1;  // not representable
+  return r;
 }
 
 int kvq_quant_sym(const kvq_paged_layout *layout, const uint16_t *k, const uint16_t *v,
@@ -125,8 +139,8 @@ int kvq_quant_sym(const kvq_paged_layout *layout, const uint16_t *k, const uint1
   const kvq_paged_layout &L = *layout;
   if (n_tokens < 0 || n_layers < 0) return fail(KVQ_ERR_SHAPE, "negative n_tokens/n_layers");
   if (layer0 < 0 || (int64_t)layer0 + n_layers > L.layers)
-    return fail(KVQ_ERR_SHAPE, "layers [%d, %d) outside the pool's %d layers", layer0,
-                layer0 + n_layers, L.layers);
+    return fail(KVQ_ERR_SHAPE, "layers [%d, %lld) outside the pool's %d layers", layer0,
+                (long long)layer0 + n_layers, L.layers);
   const bool do_k = k || k_codes || k_scales, do_v = v || v_codes || v_scales;
   if (do_k && (!k || !k_codes || !k_scales))
     return fail(KVQ_ERR_NULL, "K side needs k, k_codes and k_scales together");
@@ -176,8 +190,8 @@ int kvq_dequant_sym(const kvq_paged_layout *layout, const uint8_t *k_codes,
   if (n_seqs < 0 || n_layers < 0 || max_len < 0 || max_blocks < 0)
     return fail(KVQ_ERR_SHAPE, "negative size");
   if (layer0 < 0 || (int64_t)layer0 + n_layers > L.layers)
-    return fail(KVQ_ERR_SHAPE, "layers [%d, %d) outside the pool's %d layers", layer0,
-                layer0 + n_layers, L.layers);
+    return fail(KVQ_ERR_SHAPE, "layers [%d, %lld) outside the pool's %d layers", layer0,
+                (long long)layer0 + n_layers, L.layers);
   const bool do_k = k_out || k_codes || k_scales, do_v = v_out || v_codes || v_scales;
   if (do_k && (!k_out || !k_codes || !k_scales))
     return fail(KVQ_ERR_NULL, "K side needs k_codes, k_scales and k_out together");
@@ -227,7 +241,10 @@ int kvq_dequant_sym(const kvq_paged_layout *layout, const uint8_t *k_codes,
 int64_t kvq_attn_workspace_bytes(int32_t n_seqs, int32_t q_heads, int32_t head_dim, int32_t max_len) {
   if (n_seqs < 0 || q_heads <= 0 || head_dim <= 0 || max_len < 0) return -1;
   const int64_t chunks = max_len > 0 ? ((int64_t)max_len + kvq::ATTN_MIN_CHUNK - 1) / kvq::ATTN_MIN_CHUNK : 1;
-  return (int64_t)n_seqs * chunks * q_heads * (head_dim + 2) * 4;
+  int64_t r = 4 * ((int64_t)head_dim + 2);  // fp32 partial output + running max and sum per chunk and head
+  for (const int64_t f : {(int64_t)n_seqs, chunks, (int64_t)q_heads})
+    if (__builtin_mul_overflow(r, f, &r)) return -1;  // not representable: no valid call has these sizes
+  return r;
 }
 
 int kvq_attn_decode_sym(const kvq_paged_layout *layout, const uint8_t *k_codes, const uint16_t *k_scales,
@@ -322,7 +339,7 @@ int kvq_kivi_quant_dequant(uint16_t *keys, uint16_t *values, int32_t B, int32_t 
   const int64_t BH = (int64_t)B * H;
   if (hi == lo || BH == 0) return ok();
   const int64_t n = hi - lo;
-  if (BH * n * D >= ((int64_t)1 << 46)) return fail(KVQ_ERR_SHAPE, "tensor too large");
+  if (!product_below({BH, n, (int64_t)D}, (int64_t)1 << 46)) return fail(KVQ_ERR_SHAPE, "tensor too large");
   if ((BH * n + 255) / 256 * 64 >= ((int64_t)1 << 31)) return fail(KVQ_ERR_SHAPE, "too many rows");
   kvq::KiviArgs a{};
   a.keys = keys;
@@ -375,7 +392,8 @@ int kvq_kivi_pack(const uint16_t *keys, const uint16_t *values, int32_t B, int32
   const int64_t BH = (int64_t)B * H;
   if (hi == lo || BH == 0) return ok();
   const int64_t n = hi - lo;
-  if (BH * S_cap * D >= ((int64_t)1 << 46) || BH * x_rows * D >= ((int64_t)1 << 46))
+  if (!product_below({BH, (int64_t)S_cap, (int64_t)D}, (int64_t)1 << 46) ||
+      !product_below({BH, (int64_t)x_rows, (int64_t)D}, (int64_t)1 << 46))
     return fail(KVQ_ERR_SHAPE, "tensor too large");
   if ((BH * n + 255) / 256 * 64 >= ((int64_t)1 << 31)) return fail(KVQ_ERR_SHAPE, "too many rows");
   kvq::KiviArgs a{};
@@ -426,7 +444,8 @@ int kvq_kivi_unpack(const uint8_t *k_codes, const uint16_t *k_scale, const uint1
     if (p && !aligned(p, 16)) return fail(KVQ_ERR_ALIGN, "packed KIVI tensors need 16-byte alignment");
   const int64_t BH = (int64_t)B * H;
   if (hi == lo || BH == 0) return ok();
-  if (BH * S_cap * D >= ((int64_t)1 << 46) || BH * out_rows * D >= ((int64_t)1 << 46))
+  if (!product_below({BH, (int64_t)S_cap, (int64_t)D}, (int64_t)1 << 46) ||
+      !product_below({BH, (int64_t)out_rows, (int64_t)D}, (int64_t)1 << 46))
     return fail(KVQ_ERR_SHAPE, "tensor too large");
   if ((int64_t)(hi - lo) * (D / 8) >= ((int64_t)1 << 31) - 256 || (BH + 65534) / 65535 > 65535)
     return fail(KVQ_ERR_SHAPE, "too many rows");
@@ -475,8 +494,8 @@ int nuq_plan(int32_t BH, int32_t S, int32_t D, int32_t bits, int32_t start_pos, 
   if (D != 32 && D != 64 && D != 128 && D != 256) return fail(KVQ_ERR_SHAPE, "NUQ head_dim must be 32, 64, 128 or 256 (got %d)", D);
   if (!(frac >= 0.0 && frac < 1.0)) return fail(KVQ_ERR_ARG, "outlier fraction must be in [0, 1)");
   if (start_pos < 0 || n_sink < 0) return fail(KVQ_ERR_ARG, "start_pos and n_sink must be >= 0");
-  if ((int64_t)BH * S * D >= ((int64_t)1 << 31)) return fail(KVQ_ERR_SHAPE, "BH*S*D must be < 2^31 (int32 outlier positions)");
   if (BH > 65535) return fail(KVQ_ERR_SHAPE, "BH must be <= 65535");
+  if ((int64_t)BH * S * D >= ((int64_t)1 << 31)) return fail(KVQ_ERR_SHAPE, "BH*S*D must be < 2^31 (int32 outlier positions)");
   p.n_sink_eff = start_pos == 0 ? (n_sink < S ? n_sink : S) : 0;
   p.n_fit = S - p.n_sink_eff;
   if (fit_keys && p.n_fit > 8192) return fail(KVQ_ERR_SHAPE, "a key fit covers at most 8192 non-sink tokens per call (got %d)", p.n_fit);

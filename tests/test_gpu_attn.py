@@ -19,7 +19,7 @@ import torch
 
 import oracle
 from kv_cache_quantization_row_amd import kvq
-from tests.gpu_util import dev, say, u16
+from tests.gpu_util import Guarded, dev, say, u16
 
 pytestmark = pytest.mark.gpu
 
@@ -59,11 +59,12 @@ def _run(bits, H, G, D, lens, *, P=16, seed=0, max_len=None, bad_block=None, sca
         bt[s, b] = num_pages + 5          # out of range: those positions are left out
     ml = int(lens.max(initial=0)) if max_len is None else max_len
     scale = float(np.float32(1.0 / np.sqrt(D) if scale is None else scale))   # the kernel takes fp32
-    out = torch.full((n_seqs, H * G, D), 7, dtype=torch.float16, device=d)
-    ws = torch.empty(kvq.kvq_attn_workspace_bytes(n_seqs, H * G, D, ml), dtype=torch.uint8, device=d)
+    guard = Guarded(d)  # sentinel bands around the output and the workspace
+    out = guard.empty((n_seqs, H * G, D), torch.float16, 7)
+    ws = guard.empty((kvq.kvq_attn_workspace_bytes(n_seqs, H * G, D, ml),), torch.uint8)
     kvq.kvq_attn_decode_sym(lay, kc, ks, vc, vs, 1, q.to(d), torch.as_tensor(bt).to(d),
                             torch.as_tensor(lens).to(d), ml, float(scale), out, ws)
-    torch.cuda.synchronize()
+    guard.check("attention")
     got = out.cpu().float().numpy().astype(np.float64)
     xk_u, xv_u, q_u = u16(xk[0]), u16(xv[0]), u16(q)
     o = 0

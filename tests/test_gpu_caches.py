@@ -129,6 +129,30 @@ def test_kivi_packed_cache_lifecycle(bits):
     push(200, "new sequence")
 
 
+def test_kivi_packed_cache_long_prefill():
+    """A prefill far longer than the residual window (the window buffer
+    shrinks after the flush), then decode steps and a trim, against the model."""
+    say("kivi packed cache long prefill")
+    d = dev()
+    B, H, D, bits = 1, 2, 64, 4
+    k, v = _kivi_inputs(B, H, 2200, D, 77)
+    kn, vn = k.numpy().view(np.uint16), v.numpy().view(np.uint16)
+    c, m = caches.KiviCache(bits, storage="packed", step=64), KiviPackedCacheModel(bits)
+    t = 0
+    for n in [2000] + [1] * 70 + [-100] + [50]:
+        if n < 0:
+            assert c.trim(-n) == m.trim(-n)
+            fk, fv = c.fetch()
+        else:
+            fk, fv = c.update_and_fetch(k[:, :, t:t + n].to(d).contiguous(), v[:, :, t:t + n].to(d).contiguous())
+            m.update(kn[:, :, t:t + n], vn[:, :, t:t + n])
+            t += n
+        mk, mv = m.fetch()
+        assert (c.offset, c.n_quantized) == (m.n, m.nq)
+        assert first_diff(u16(fk), mk) is None and first_diff(u16(fv), mv) is None, (t, n)
+        assert c._win[0].shape[2] <= 256, c._win[0].shape  # window buffer sized for the residual, not the prefill
+
+
 def test_nuq_cache_lifecycle():
     say("nuq cache")
     d = dev()

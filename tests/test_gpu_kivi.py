@@ -12,7 +12,7 @@ import torch
 
 import oracle
 from kv_cache_quantization_row_amd import inputs, kvq
-from tests.gpu_util import dev, first_diff, say, u16
+from tests.gpu_util import Guarded, dev, first_diff, say, u16
 
 pytestmark = pytest.mark.gpu
 
@@ -20,21 +20,22 @@ pytestmark = pytest.mark.gpu
 def _run(k, v, lo, hi, bits, gs, want):
     """k, v fp16 CPU [B][H][S][D]; returns GPU results as numpy."""
     d = dev()
+    g = Guarded(d)  # sentinel bands around the in-place tensors and every output
     B, H, S, D = k.shape
     n = hi - lo
-    kg, vg = k.to(d), v.to(d)
+    kg, vg = g.like(k.to(d)), g.like(v.to(d))
     outs = {}
     if want:
         cpr = D * bits // 8
         outs = dict(
-            k_codes=torch.zeros((B, H, n, cpr), dtype=torch.uint8, device=d),
-            k_scale=torch.zeros((B, H, (n + gs - 1) // gs, D), dtype=torch.float32, device=d),
-            k_min=torch.zeros((B, H, (n + gs - 1) // gs, D), dtype=torch.float32, device=d),
-            v_codes=torch.zeros((B, H, n, cpr), dtype=torch.uint8, device=d),
-            v_scale=torch.zeros((B, H, n, (D + gs - 1) // gs), dtype=torch.float32, device=d),
-            v_min=torch.zeros((B, H, n, (D + gs - 1) // gs), dtype=torch.float32, device=d))
+            k_codes=g.empty((B, H, n, cpr), torch.uint8, 0),
+            k_scale=g.empty((B, H, (n + gs - 1) // gs, D), torch.float32, 0.0),
+            k_min=g.empty((B, H, (n + gs - 1) // gs, D), torch.float32, 0.0),
+            v_codes=g.empty((B, H, n, cpr), torch.uint8, 0),
+            v_scale=g.empty((B, H, n, (D + gs - 1) // gs), torch.float32, 0.0),
+            v_min=g.empty((B, H, n, (D + gs - 1) // gs), torch.float32, 0.0))
     kvq.kvq_kivi_quant_dequant(kg, vg, lo, hi, bits, gs, **outs)
-    torch.cuda.synchronize()
+    g.check("kivi round trip")
     return u16(kg), u16(vg), {n_: t.cpu().numpy() for n_, t in outs.items()}
 
 

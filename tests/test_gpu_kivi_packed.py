@@ -7,12 +7,17 @@ import torch
 
 import oracle
 from kv_cache_quantization_row_amd import inputs, kvq
-from tests.gpu_util import dev, first_diff, say, u16
+from tests.gpu_util import Guarded, dev, first_diff, say, u16
 
 pytestmark = pytest.mark.gpu
 
 
-def _storage(B, H, S, D, bits, gs, d):
+def _storage(B, H, S, D, bits, gs, d, guard=None):
+    if guard is not None:  # sentinel bands around every array
+        kshp, vshp = kvq.kivi_param_shape(B, H, S, D, 1, gs), kvq.kivi_param_shape(B, H, S, D, 0, gs)
+        return (guard.empty((B, H, S, D * bits // 8), torch.uint8, 0), guard.empty(kshp, torch.int16, 0),
+                guard.empty(kshp, torch.int16, 0), guard.empty((B, H, S, D * bits // 8), torch.uint8, 0),
+                guard.empty(vshp, torch.int16, 0), guard.empty(vshp, torch.int16, 0))
     kc = torch.zeros((B, H, S, D * bits // 8), dtype=torch.uint8, device=d)
     vc = torch.zeros_like(kc)
     ks = torch.zeros(kvq.kivi_param_shape(B, H, S, D, 1, gs), dtype=torch.int16, device=d)
@@ -30,7 +35,8 @@ def _run(k, v, flushes_k, flushes_v, bits, gs):
     d = dev()
     B, H, S, D = k.shape
     kd, vd = k.to(d).contiguous(), v.to(d).contiguous()
-    st = _storage(B, H, S, D, bits, gs, d)
+    guard = Guarded(d)
+    st = _storage(B, H, S, D, bits, gs, d, guard)
     kc, ks, kz, vc, vs, vz = st
     kn, vn = u16(k), u16(v)
     ok_ = (np.zeros(kc.shape, np.uint8), np.zeros(ks.shape, np.uint16), np.zeros(ks.shape, np.uint16))
@@ -51,11 +57,11 @@ def _run(k, v, flushes_k, flushes_v, bits, gs):
     assert np.array_equal(u16(kd), kn) and np.array_equal(u16(vd), vn)  # inputs untouched
     klo, khi = flushes_k[0][0], flushes_k[-1][1]
     vlo, vhi = flushes_v[0][0], flushes_v[-1][1]
-    ko = torch.full_like(kd, 7.0)
-    vo = torch.full_like(vd, 7.0)
+    ko = guard.like(kd, 7.0)
+    vo = guard.like(vd, 7.0)
     kvq.kvq_kivi_unpack(kc, ks, kz, None, None, None, klo, khi, bits, gs, ko, None)
     kvq.kvq_kivi_unpack(None, None, None, vc, vs, vz, vlo, vhi, bits, gs, None, vo)
-    torch.cuda.synchronize()
+    guard.check("kivi pack / unpack")
     ek = oracle.kivi_unpack(ok_[0], ok_[1], ok_[2], klo, khi, 1, bits, gs, D)
     ev = oracle.kivi_unpack(ov_[0], ov_[1], ov_[2], vlo, vhi, 0, bits, gs, D)
     _check("k recon", u16(ko)[:, :, klo:khi], ek[:, :, klo:khi])

@@ -16,7 +16,7 @@ import torch
 
 import oracle
 from kv_cache_quantization_row_amd import inputs, kvq
-from tests.gpu_util import dev, first_diff, say, u16
+from tests.gpu_util import Guarded, dev, first_diff, say, u16
 
 pytestmark = pytest.mark.gpu
 
@@ -24,31 +24,33 @@ pytestmark = pytest.mark.gpu
 def gpu_nuq(k, v, start_pos, bits, frac, iters, n_sink, fit_keys, key_levels=None, key_thresh=None,
             want_recon=True):
     d = dev()
+    g = Guarded(d)  # sentinel bands around every output and the workspace
     BH, S, D = k.shape
     L = 1 << bits
-    kl = torch.zeros((BH, D, L), dtype=torch.float32, device=d) if key_levels is None else \
-        torch.from_numpy(np.ascontiguousarray(key_levels)).to(d)
-    kt = torch.zeros((BH, D), dtype=torch.int16, device=d) if key_thresh is None else \
-        torch.from_numpy(np.ascontiguousarray(key_thresh).view(np.int16)).to(d)
-    vl = torch.full((BH, S, L), 7.0, dtype=torch.float32, device=d)
-    kc = torch.full((BH, S, D * bits // 8), 0xA5, dtype=torch.uint8, device=d)
-    vc = torch.full_like(kc, 0x5A)
+    kl = g.empty((BH, D, L), torch.float32, 0.0)
+    kt = g.empty((BH, D), torch.int16, 0)
+    if key_levels is not None:
+        kl.copy_(torch.from_numpy(np.ascontiguousarray(key_levels)))
+        kt.copy_(torch.from_numpy(np.ascontiguousarray(key_thresh).view(np.int16)))
+    vl = g.empty((BH, S, L), torch.float32, 7.0)
+    kc = g.empty((BH, S, D * bits // 8), torch.uint8, 0xA5)
+    vc = g.empty((BH, S, D * bits // 8), torch.uint8, 0x5A)
     cap = max(kvq.kvq_nuq_outlier_bound(BH, S, D, start_pos, n_sink, frac, fit_keys, 0),
               kvq.kvq_nuq_outlier_bound(BH, S, D, start_pos, n_sink, frac, fit_keys, 1), 1)
-    kp = torch.full((cap,), -1, dtype=torch.int32, device=d)
-    kvv = torch.zeros((cap,), dtype=torch.int16, device=d)
-    vp = torch.full((cap,), -1, dtype=torch.int32, device=d)
-    vvv = torch.zeros((cap,), dtype=torch.int16, device=d)
-    cnt = torch.full((2,), -1, dtype=torch.int64, device=d)
+    kp = g.empty((cap,), torch.int32, -1)
+    kvv = g.empty((cap,), torch.int16, 0)
+    vp = g.empty((cap,), torch.int32, -1)
+    vvv = g.empty((cap,), torch.int16, 0)
+    cnt = g.empty((2,), torch.int64, -1)
     wsb = kvq.kvq_nuq_workspace_bytes(BH, S, D, bits, start_pos, n_sink, frac, fit_keys)
-    ws = torch.full((wsb,), 0xEE, dtype=torch.uint8, device=d)  # contents on entry must not matter
-    kr = torch.zeros((BH, S, D), dtype=torch.float16, device=d) if want_recon else None
-    vr = torch.zeros_like(kr) if want_recon else None
+    ws = g.empty((wsb,), torch.uint8, 0xEE)  # contents on entry must not matter
+    kr = g.empty((BH, S, D), torch.float16, 0.0) if want_recon else None
+    vr = g.empty((BH, S, D), torch.float16, 0.0) if want_recon else None
     kg = torch.from_numpy(np.ascontiguousarray(k).view(np.int16)).to(d).view(torch.float16)
     vg = torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).to(d).view(torch.float16)
     kvq.kvq_nuq_fit_quant(kg, vg, start_pos, bits, frac, iters, n_sink, fit_keys, kl, kt, vl, kc, vc,
                           kp, kvv, vp, vvv, cnt, ws, kr, vr)
-    torch.cuda.synchronize()
+    g.check("nuq call")
     c = cnt.cpu().numpy()
     out = dict(key_levels=kl.cpu().numpy(), key_thresh=u16(kt), value_levels=vl.cpu().numpy(),
                k_codes=kc.cpu().numpy(), v_codes=vc.cpu().numpy(),

@@ -12,14 +12,17 @@ import torch
 
 import oracle
 from kv_cache_quantization_row_amd import inputs, kvq
-from tests.gpu_util import dev, first_diff, say, u16
+from tests.gpu_util import Guarded, dev, first_diff, say, u16
 
 pytestmark = pytest.mark.gpu
 SENT = 0xA5
 
 
-def _pools(L, num_pages, P, H, D, bits, device):
+def _pools(L, num_pages, P, H, D, bits, device, guard=None):
     pd = kvq.kvq_packed_dim(D, bits)
+    if guard is not None:
+        return (guard.empty((L, num_pages * P, H, pd), torch.uint8, SENT),
+                guard.empty((L, num_pages * P, H), torch.int16, 0x3C01))
     codes = torch.full((L, num_pages * P, H, pd), SENT, dtype=torch.uint8, device=device)
     scales = torch.full((L, num_pages * P, H), 0x3C01, dtype=torch.int16, device=device)
     return codes, scales
@@ -31,19 +34,20 @@ def _check_roundtrip(x_k, x_v, bits, H, D, P, num_pages, n_pool_layers, layer0, 
     d = dev()
     n_layers = x_k.shape[0]
     lay = kvq.layout(n_pool_layers, num_pages, P, H, D, bits)
-    kc, ks = _pools(n_pool_layers, num_pages, P, H, D, bits, d)
-    vc, vs = _pools(n_pool_layers, num_pages, P, H, D, bits, d)
+    g = Guarded(d)  # sentinel bands around every pool and output
+    kc, ks = _pools(n_pool_layers, num_pages, P, H, D, bits, d, g)
+    vc, vs = _pools(n_pool_layers, num_pages, P, H, D, bits, d, g)
     ref = {n: t.cpu().numpy().copy() for n, t in (("kc", kc), ("ks", ks), ("vc", vc), ("vs", vs))}
     ref["ks"] = ref["ks"].view(np.uint16)
     ref["vs"] = ref["vs"].view(np.uint16)
     sm = torch.as_tensor(slot, dtype=torch.int32)
     kvq.kvq_quant_sym(lay, x_k.to(d), x_v.to(d), sm.to(d), kc, ks, vc, vs, layer0=layer0)
     n_seqs = bt.shape[0]
-    ko = torch.full((n_layers, n_seqs, max_len, H, D), 7, dtype=torch.float16, device=d)
-    vo = torch.full_like(ko, 7)
+    ko = g.empty((n_layers, n_seqs, max_len, H, D), torch.float16, 7)
+    vo = g.empty((n_layers, n_seqs, max_len, H, D), torch.float16, 7)
     kvq.kvq_dequant_sym(lay, kc, ks, vc, vs, torch.as_tensor(bt, dtype=torch.int32).to(d),
                         torch.as_tensor(lens, dtype=torch.int32).to(d), ko, vo, layer0=layer0)
-    torch.cuda.synchronize()
+    g.check("sym round trip")
     for name, x, oc, os_, out in (("K", x_k, "kc", "ks", ko), ("V", x_v, "vc", "vs", vo)):
         for l in range(n_layers):
             pl = layer0 + l
@@ -197,7 +201,8 @@ def test_full_size_sampled(bits):
 def test_long_context_sampled():
     """The long-context workload in its launch configuration: one sequence of
     262,144 tokens, 16 layers x 4 KV heads x D=256, q6, page 16, quantized in
-    64 launches of 4,096 tokens (all layers each), single-token appends, then
+    64 launches of 4,096 tokens (all layers each, alternating over two
+    streams), single-token appends, then
     one dequant of the whole cache. Compared with the oracle on sampled
     chunks, layers and positions."""
     say("sym long context")
@@ -219,8 +224,17 @@ def test_long_context_sampled():
     vs = torch.zeros_like(ks)
     lay = kvq.layout(L, num_pages, P, H, D, bits)
     slot_ch = [inputs.slot_mapping_for(bt, P, c * CH, CH) for c in range(nch)]
+    slot_dev = [sm.to(d) for sm in slot_ch]
+    # as timed: chunks alternate between the current stream and a second one
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    fork = torch.cuda.Event()
+    fork.record(main)
+    side.wait_event(fork)
     for c in range(nch):
-        kvq.kvq_quant_sym(lay, k[c], v[c], slot_ch[c].to(d), kc, ks, vc, vs)
+        kvq.kvq_quant_sym(lay, k[c], v[c], slot_dev[c], kc, ks, vc, vs, stream=main if c % 2 == 0 else side)
+    join = torch.cuda.Event()
+    join.record(side)
+    main.wait_event(join)
     slot_dec = inputs.slot_mapping_for(bt, P, T, ND)
     for i in range(ND):
         kvq.kvq_quant_sym(lay, kd[i], kd[i], slot_dec[i:i + 1].to(d), kc, ks, vc, vs)
