@@ -270,7 +270,8 @@ int kvq_kivi_unpack(const uint8_t *k_codes, const uint16_t *k_scale, const uint1
  *   1-D k-means) from linear-interpolated quantiles at probabilities
  *   (j + 1/2)/L; a sample's code is its nearest level (ties to the lower
  *   index); an empty cell keeps its level; a level is the binary32 rounding
- *   of its cell's exact mean (exact while a cell's |sum| < 2^29); after each
+ *   of its cell's exact mean (sums are exact: int64 in 2^-24 units for key
+ *   fits, double for value fits of at most 256 samples); after each
  *   update the table is sorted ascending (an ordered "signpost" table).
  * Attention sinks: when start_pos == 0 the first n_sink tokens of the call
  * are sinks: exact, code 0, excluded from every fit and threshold, and their
@@ -302,8 +303,9 @@ int64_t kvq_nuq_workspace_bytes(int32_t BH, int32_t S, int32_t D, int32_t bits, 
 
 /* One NUQ call over fp16 keys and values [BH][S][D] (BH = batch*kv_heads).
  *   bits 1..4 (L = 2^bits); D in {32, 64, 128, 256}; 0 <= frac < 1;
- *   lloyd_iters >= 0; a key fit (fit_keys = 1) covers at most 8192 non-sink
- *   tokens per call.
+ *   0 <= lloyd_iters <= 1000; a key fit (fit_keys = 1) covers at most
+ *   1,048,576 (2^20) non-sink tokens per call (its per-bucket significand
+ *   sums stay below 2^32); BH*S*D < 2^31 (int32 outlier positions).
  *   key_levels fp32 [BH][D][L] and key_thresh fp16 [BH][D]: written when
  *   fit_keys = 1, read otherwise (each channel's table ascending, as a fit
  *   leaves it). value_levels fp32 [BH][S][L] (written).

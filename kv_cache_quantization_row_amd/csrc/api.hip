@@ -479,7 +479,7 @@ struct NuqPlan {
   int n_sink_eff, n_fit, key_cpc, val_cpc;
   int64_t kb, vb;  // outlier bounds
   int64_t k_blk_x, v_nblk;
-  int64_t off_ctr, off_kblk, off_vblk, off_ksup, off_vsup, off_kpos, off_kval, off_vpos, off_vval, total;
+  int64_t off_ctr, off_kblk, off_vblk, off_ksup, off_vsup, off_kpos, off_kval, off_vpos, off_vval, off_kdat, total;
 };
 
 // outliers per vector of n samples: floor(frac * n), one binary64 product
@@ -498,7 +498,9 @@ int nuq_plan(int32_t BH, int32_t S, int32_t D, int32_t bits, int32_t start_pos, 
   if ((int64_t)BH * S * D >= ((int64_t)1 << 31)) return fail(KVQ_ERR_SHAPE, "BH*S*D must be < 2^31 (int32 outlier positions)");
   p.n_sink_eff = start_pos == 0 ? (n_sink < S ? n_sink : S) : 0;
   p.n_fit = S - p.n_sink_eff;
-  if (fit_keys && p.n_fit > 8192) return fail(KVQ_ERR_SHAPE, "a key fit covers at most 8192 non-sink tokens per call (got %d)", p.n_fit);
+  if (fit_keys && p.n_fit > kvq::NUQ_KFIT_MAX_N)
+    return fail(KVQ_ERR_SHAPE, "a key fit covers at most %d non-sink tokens per call (got %d)", kvq::NUQ_KFIT_MAX_N,
+                p.n_fit);
   int chunks = (p.n_fit + 127) / 128, cpc = 1;
   while (cpc < chunks) cpc <<= 1;
   p.key_cpc = cpc;
@@ -520,6 +522,9 @@ int nuq_plan(int32_t BH, int32_t S, int32_t D, int32_t bits, int32_t start_pos, 
   p.off_kval = o; o = align256(o + p.kb * 2);
   p.off_vpos = o; o = align256(o + p.vb * 4);
   p.off_vval = o; o = align256(o + p.vb * 2);
+  // a key fit over more tokens than fit in LDS keeps its bucketed samples here
+  const int64_t kdat = fit_keys && p.n_fit > kvq::NUQ_KFIT_LDS_N ? (int64_t)BH * D * ((p.n_fit + 15) / 16 * 16) : 0;
+  p.off_kdat = o; o = align256(o + kdat);
   p.total = o;
   return KVQ_OK;
 }
@@ -597,6 +602,9 @@ int nuq_call(const uint16_t *keys, const uint16_t *values, int32_t BH, int32_t S
   a.ws_kval = reinterpret_cast<uint16_t *>(ws + p.off_kval);
   a.ws_vpos = reinterpret_cast<int32_t *>(ws + p.off_vpos);
   a.ws_vval = reinterpret_cast<uint16_t *>(ws + p.off_vval);
+  a.ws_kdat = ws + p.off_kdat;
+  a.k_cap = p.kb;
+  a.v_cap = p.vb;
   a.k_blk_x = p.k_blk_x;
   a.v_nblk = p.v_nblk;
   return hip_status(kvq::launch_nuq(a, p.key_cpc, p.val_cpc, fork, (hipStream_t)stream), what);

@@ -80,12 +80,20 @@ struct NuqArgs {
   uint32_t *ws_kblk, *ws_vblk;     // per workgroup (staging base, count)
   uint32_t *ws_ksup, *ws_vsup;     // per 64 workgroups: sum of their counts
   int32_t *ws_kpos, *ws_vpos;      // staging
+  uint8_t *ws_kdat;                // key fit over more than 8192 tokens: bucketed key bytes [BH][D][round16(n)]
+  int64_t k_cap, v_cap;            // staging and list entries (the outlier bounds): writes past them are dropped
   uint16_t *ws_kval, *ws_vval;
   int64_t k_blk_x, v_nblk;         // key-quant workgroups along S (16384/D rows each); value workgroups
 };
 
 // fork: run a many-token value fit on the device's auxiliary stream (false:
 // every kernel on `st`, no stream or event is created)
+// Key fit: channels of at most NUQ_KFIT_LDS_N non-sink tokens keep their
+// bucketed samples in LDS, longer ones in the workspace; a key fit covers at
+// most NUQ_KFIT_MAX_N tokens (its per-bucket significand sums stay below 2^32
+// and its exact sums below 2^63).
+constexpr int NUQ_KFIT_LDS_N = 8192;
+constexpr int NUQ_KFIT_MAX_N = 1 << 20;
 hipError_t launch_nuq(const NuqArgs &a, int key_cpc, int val_cpc, bool fork, hipStream_t st);
 
 // Attention chunks are whole blocks of 16 positions and never shorter than

@@ -18,30 +18,26 @@
 // their level; levels are binary32 roundings of exact cell means; the table
 // is kept in ascending order after every update (an ordered signpost table).
 //
-// GPU formulation. A vector of n samples is split over CPC lanes, 128
-// samples per lane. Each lane sorts its chunk in registers (a bitonic network
-// on packed 16-bit order keys, all compare-exchanges ascending) and keeps it
-// in LDS. Everything the fit needs then comes from binary searches in those
-// sorted chunks plus sums over CPC lanes:
-//   - tau: binary search on |x| for the largest c with #{|x| >= c} >= k+1;
+// GPU formulation.
+// Values (and short vectors): a vector of n samples is split over CPC lanes,
+// 128 samples per lane. Each lane sorts its chunk in registers (a bitonic
+// network on packed 16-bit order keys, all compare-exchanges ascending) and
+// keeps it in LDS. Everything the fit needs then comes from binary searches in
+// those sorted chunks plus sums over CPC lanes:
+//   - tau: the (k+1)-th largest |x|, walked in from both ends of the chunk;
 //   - the inliers of a chunk are a contiguous index range [lo, hi);
-//   - quantile order statistics: binary search over fp16 order keys;
+//   - quantile order statistics: direct reads (one lane) or a bitwise search
+//     over fp16 order keys;
 //   - a Lloyd iteration: the nearest-level cells are contiguous index ranges
 //     cut at exact fp16 thresholds T_j (largest fp16 t with 2t <= l_j +
 //     l_{j+1}); cell sums are kept as prefix sums P_j at the cut points and
 //     updated by walking the cut from its old to its new position. Sums are
 //     doubles, exact while |sum| < 2^29 (fp16 values are multiples of 2^-24),
 //     so each level is the exact mean rounded once to binary32.
-// Key fits with at least as many lanes per channel as levels (CPC >= L, the
-// many-token prefill) first merge the channel's CPC sorted chunks into one
-// globally sorted sequence (the bitonic network continued across lanes with
-// DPP and swizzle exchanges), which makes the fit cheap: tau is searched over
-// the k+1 smallest and k+1 largest samples only (the k+1 largest |x| lie
-// there), the inlier range and the quantile order statistics are direct
-// reads, and in a Lloyd iteration lane j places cut j (a ballot over the
-// chunks' last keys, then a search inside one chunk) and reads its exact
-// prefix sum from per-lane sums at every 32nd slot plus at most 31 samples.
-// Codes are then #{j : x > T_j}, which equals the first index of the nearest
+// Keys at prefill: a counting sort of each channel's samples by the high byte
+// of their order key, then every query of the fit is a table read plus one
+// bucket scan (the "bucketed key fit" section below); sums there are int64.
+// Codes are #{j : x > T_j}, which equals the first index of the nearest
 // level. The side channel (flat index, fp16 value) is emitted in ascending
 // flat order: each workgroup reserves a staging range with one atomic and
 // adds its count to a per-64-workgroup sum; one placement kernel then puts
@@ -459,221 +455,6 @@ __device__ void fit_vector(const Chunk &c, int nq, int kout, int iters, float *l
   }
 }
 
-// ----------------------------------------------------------------- merged chunks
-// The CPC sorted chunks of one vector are merged into one sorted sequence by
-// continuing the bitonic network across lanes: element e = 128q + s (lane q
-// of the group, slot s) pairs with e ^ (K-1) in the merge of blocks of size K
-// (lane q ^ (K/128 - 1), slot 127 - s) and then with e ^ J for J = K/4 .. 1
-// (lanes q ^ (J/128) for J >= 128; the two halves of a register for J = 64;
-// registers r ^ J below). The smaller element goes to the lower index.
-template <int M>  // value of lane ^ M (M < 64; whole wave active)
-__device__ __forceinline__ uint32_t lane_xor_m(uint32_t v) {
-  if constexpr (M == 1) return dppm<DPP_XOR1>(v);
-  else if constexpr (M == 2) return dppm<DPP_XOR2>(v);
-  else if constexpr (M == 3) return dppm<0x1b>(v);  // quad_perm [3,2,1,0]
-  else if constexpr (M == 7) return dppm<DPP_HALF_MIRROR>(v);
-  else if constexpr (M == 15) return dppm<DPP_MIRROR>(v);
-  else if constexpr (M < 32) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (M << 10) | 0x1f);
-  else return (uint32_t)__shfl_xor((int)v, M);
-}
-__device__ __forceinline__ uint32_t keep(uint32_t a, uint32_t b, bool lower) {
-  const u16x2v x = __builtin_bit_cast(u16x2v, a), y = __builtin_bit_cast(u16x2v, b);
-  return lower ? __builtin_bit_cast(uint32_t, __builtin_elementwise_min(x, y))
-               : __builtin_bit_cast(uint32_t, __builtin_elementwise_max(x, y));
-}
-template <int M>  // flip across lanes q and q ^ M (M = K/128 - 1), slots s and 127 - s
-__device__ __forceinline__ void xflip(uint32_t *v, int q) {
-  const bool lower = (q & ((M + 1) >> 1)) == 0;
-#pragma unroll
-  for (int r = 0; r < 32; ++r) {
-    const uint32_t a = lane_xor_m<M>(v[63 - r]), b = lane_xor_m<M>(v[r]);
-    v[r] = keep(v[r], (a >> 16) | (a << 16), lower);
-    v[63 - r] = keep(v[63 - r], (b >> 16) | (b << 16), lower);
-  }
-}
-template <int DL>  // lanes q and q ^ DL, same slot
-__device__ __forceinline__ void xdisp(uint32_t *v, int q) {
-  const bool lower = (q & DL) == 0;
-#pragma unroll
-  for (int r = 0; r < 64; ++r) v[r] = keep(v[r], lane_xor_m<DL>(v[r]), lower);
-}
-__device__ __forceinline__ void inlane_tail(uint32_t *v) {
-#pragma unroll
-  for (int r = 0; r < 64; ++r) {  // slots r and r + 64
-    const uint32_t lo = v[r] & 0xffffu, hi = v[r] >> 16;
-    v[r] = min(lo, hi) | (max(lo, hi) << 16);
-  }
-  disperse<32>(v);
-  disperse<16>(v);
-  disperse<8>(v);
-  disperse<4>(v);
-  disperse<2>(v);
-  disperse<1>(v);
-}
-template <int CPC>
-__device__ __forceinline__ void merge_lanes(uint32_t *v, int q) {
-  if constexpr (CPC >= 2) { xflip<1>(v, q); inlane_tail(v); }
-  if constexpr (CPC >= 4) { xflip<3>(v, q); xdisp<1>(v, q); inlane_tail(v); }
-  if constexpr (CPC >= 8) { xflip<7>(v, q); xdisp<2>(v, q); xdisp<1>(v, q); inlane_tail(v); }
-  if constexpr (CPC >= 16) {
-    xflip<15>(v, q); xdisp<4>(v, q); xdisp<2>(v, q); xdisp<1>(v, q); inlane_tail(v);
-  }
-  if constexpr (CPC >= 32) {
-    xflip<31>(v, q); xdisp<8>(v, q); xdisp<4>(v, q); xdisp<2>(v, q); xdisp<1>(v, q); inlane_tail(v);
-  }
-  if constexpr (CPC >= 64) {
-    xflip<63>(v, q); xdisp<16>(v, q); xdisp<8>(v, q); xdisp<4>(v, q); xdisp<2>(v, q); xdisp<1>(v, q);
-    inlane_tail(v);
-  }
-}
-
-// Fit of one vector whose n samples are sorted across the CPC lanes of the
-// group (lane q holds positions [128q, 128q + 128), padding sorts last).
-// lds: the chunks of the workgroup's lanes; tbl: per lane, five exact prefix
-// sums B + (sum of its first 32k valid slots), k = 0..4, with B the sum of
-// the chunks before it. CPC >= L: lane q < L does the work of level q. The
-// result equals fit_vector's.
-template <int CPC, int L>
-__device__ void fit_global(const uint32_t *lds, const double *tbl, int lane, int n, uint32_t last, int kout,
-                           int iters, float *lev, FitOut &fo) {
-  const int q = lane % CPC, gb = lane - q;        // group base (workgroup lane)
-  const int wb = (lane & 63) - q;                 // group base inside the wave
-  const uint64_t gmask = (CPC == 64 ? ~0ull : ((1ull << CPC) - 1)) << wb;
-  auto at = [&](int l, int i) -> uint32_t {       // slot i of lane l's chunk
-    const uint32_t x = lds[l * 64 + ((i & 63) ^ (l & 63))];
-    return (i & 64) ? (x >> 16) : (x & 0xffffu);
-  };
-  auto gat = [&](int p) -> uint32_t { return at(gb + (p >> 7), p & 127); };
-  auto pref = [&](int c) -> double {              // exact sum of the c smallest samples, c <= n
-    int cq = c >> 7, s = c & 127;
-    if (cq >= CPC) { cq = CPC - 1; s = 128; }
-    const int l = gb + cq;
-    // from the nearer of the two checkpoints around slot s: add the slots
-    // after the lower one, or subtract those up to the upper one (padding
-    // past n counts as 0, as in the table); at most 16 samples either way
-    const int kk = s >> 5, rem = s & 31;
-    const bool up = rem <= 16;
-    const int st = up ? kk * 32 : s, cnt = up ? rem : 32 - rem;
-    const int lim = n - 128 * cq;                 // valid slots of this chunk
-    double r0 = 0.0, r1 = 0.0, r2 = 0.0, r3 = 0.0;
-#pragma unroll
-    for (int t = 0; t < 16; t += 4) {
-      if (t < cnt && st + t < lim) r0 += kval(at(l, st + t));
-      if (t + 1 < cnt && st + t + 1 < lim) r1 += kval(at(l, st + t + 1));
-      if (t + 2 < cnt && st + t + 2 < lim) r2 += kval(at(l, st + t + 2));
-      if (t + 3 < cnt && st + t + 3 < lim) r3 += kval(at(l, st + t + 3));
-    }
-    const double tail = (r0 + r1) + (r2 + r3);
-    return up ? tbl[l * 5 + kk] + tail : tbl[l * 5 + kk + 1] - tail;
-  };
-  fo.tau = 0;
-  fo.tau_key = key16(0);
-#pragma unroll
-  for (int j = 0; j < L; ++j) lev[j] = 0.0f;
-  if (n == 0) return;
-  const long long k = kout;    // floor(frac * n), computed on the host
-  const int kp1 = (int)k + 1;  // <= n (frac < 1)
-  // ---- tau: the k+1 largest |x| lie among the kp1 smallest and the kp1
-  // largest samples, so the counts of the bitwise search run over those
-  const int cs = min(n, 2 * kp1);
-  int pos = 0;
-#pragma unroll 1
-  for (int sb = 16384; sb >= 1; sb >>= 1) {
-    const int cand = pos + sb - 1;
-    if (cand > 0x7bff) continue;
-    int cnt = 0;
-    for (int i = q; i < cs; i += CPC) {
-      const int p = (cs == n || i < kp1) ? i : n - cs + i;
-      cnt += (int)((unkey16(gat(p)) & 0x7fffu) >= (uint32_t)cand);
-    }
-    if (gsum<CPC>(cnt) >= kp1) pos += sb;
-  }
-  const uint32_t tau = (uint32_t)(pos - 1);
-  fo.tau = (uint16_t)tau;
-  fo.tau_key = key16(tau);
-  // ---- inliers [lo, hi): at most k samples lie outside [-tau, tau], so
-  // both outer runs sit inside the kp1 end positions
-  const uint32_t klo = tau == 0 ? key16(0x8000u) : key16(tau | 0x8000u);
-  const uint32_t khi = key16(tau);
-  int cl = 0, ch = 0;
-  for (int i = q; i < kp1; i += CPC) {
-    cl += (int)(gat(i) < klo);
-    ch += (int)(gat(n - 1 - i) > khi);
-  }
-  const int lo = gsum<CPC>(cl), hi = n - gsum<CPC>(ch);
-  const int m = hi - lo;
-  // ---- quantile initialisation: order statistics are direct reads
-#pragma unroll
-  for (int j = 0; j < L; ++j) {
-    const long long num = (long long)(2 * j + 1) * (long long)(m - 1);
-    const int rk = (int)(num / (2 * L)), rem = (int)(num % (2 * L));
-    double v = kval(gat(lo + rk));
-    if (rem != 0) {
-      const double u1 = kval(gat(lo + rk + 1));
-      v = v + ((double)rem / (double)(2 * L)) * (u1 - v);
-    }
-    lev[j] = (float)v + 0.0f;
-  }
-  // ---- Lloyd iterations: lane q < L-1 places cut q (chunk by ballot, then
-  // a search inside the chunk) and takes its exact prefix sum; lane q < L
-  // updates level q from its cell [cut q-1, cut q)
-  const double p_lo = pref(lo), p_hi = pref(hi);
-  for (int it = 0; it < iters; ++it) {
-    // cut keys as cut_keys<L> computes them, one threshold per lane: lane
-    // j < L-1 takes levels j, j+1 (0 marks equal levels), then every lane
-    // gathers them and carries the cut above over duplicates
-    float lq = lev[0], lq1 = lev[1];
-#pragma unroll
-    for (int j = 1; j < L - 1; ++j) {
-      lq = q == j ? lev[j] : lq;
-      lq1 = q == j ? lev[j + 1] : lq1;
-    }
-    uint32_t tmine = 0;
-    if (q < L - 1 && lq < lq1) tmine = key16(thr16(lq, lq1));
-    uint32_t T[L];
-    uint32_t nt = 0xffffu;
-#pragma unroll
-    for (int j = L - 2; j >= 0; --j) {
-      const uint32_t t = (uint32_t)__shfl((int)tmine, wb + j);
-      if (t) nt = t;
-      T[j] = nt;
-    }
-    T[L - 1] = 0xffffu;
-    int fc = 0;
-    uint32_t tq = 0xffffu;
-#pragma unroll
-    for (int j = 0; j < L - 1; ++j) {
-      const int f = __popcll(__ballot(last <= T[j]) & gmask);
-      fc = q == j ? f : fc;
-      tq = q == j ? T[j] : tq;
-    }
-    int c_me = hi;
-    double p_me = p_hi;
-    if (q < L - 1) {
-      int c = 128 * CPC;
-      if (fc < CPC) {
-        const Chunk cc{lds + (gb + fc) * 64, (gb + fc) & 63};
-        c = 128 * fc + cc.upper(tq);
-      }
-      c_me = min(max(c, lo), hi);
-      p_me = pref(c_me);
-    }
-    int c_prev = __shfl_up(c_me, 1);
-    double p_prev = __shfl_up(p_me, 1);
-    if (q == 0) { c_prev = lo; p_prev = p_lo; }
-    float nl = lev[0];
-#pragma unroll
-    for (int j = 1; j < L; ++j) nl = q == j ? lev[j] : nl;
-    const int cnt = c_me - c_prev;
-    if (q < L && cnt > 0) nl = (float)((p_me - p_prev) / (double)cnt);
-#pragma unroll
-    for (int j = 0; j < L; ++j) lev[j] = __shfl(nl, wb + j);
-    // an empty duplicate keeps its level while its twin moves: keep the table
-    // ordered so the cells stay contiguous ranges
-    sort_levels<L>(lev);
-  }
-}
-
 // load the 128-sample chunk from a register array of fp16 pairs (element i
 // in word i/2) into the sort layout (element i in register i%64, half i/64)
 __device__ __forceinline__ void to_sort_layout(const uint32_t *raw, uint32_t *v) {
@@ -704,6 +485,418 @@ __device__ __forceinline__ int wave_excl(int v, int &total) {
   return x - v;
 }
 
+// ================================================================== bucketed key fit
+// Prefill key fit without a sort. Each channel's non-sink samples are
+// counting-sorted by the high byte of their 16-bit order key (sign, exponent,
+// two significand bits): a workgroup of KB_CH waves covers KB_CH consecutive
+// channels of one (b, h); its threads read token rows of those channels (one
+// 16-byte load per row) and, per sample, add one to its bucket's count and the
+// sample's integer significand to the bucket's significand sum (one 64-bit LDS
+// atomic); after the exclusive prefix of the counts they store each key's low
+// byte at its bucket's cursor (unordered inside a bucket). The members of a
+// bucket share sign and binade, so the bucket's exact sum in 2^-24 units is
+// its significand sum shifted by the exponent; exclusive prefixes of counts and
+// sums over the buckets then give the exact count and sum below every bucket.
+// Each fit query is a table read plus a scan of one bucket by the channel's
+// wave (one wave per channel):
+//  - count and exact sum of the samples with key <= T: the prefixes at T's
+//    bucket plus that bucket's members whose low byte is <= T's;
+//  - the r-th smallest key: the bucket whose range holds rank r (ballot over
+//    the bucket ends), then a 256-bin histogram of that bucket's low bytes;
+//  - tau: the |x| bin (the two buckets of opposite sign with the same
+//    magnitude byte) holding the (k+1)-th largest |x|, then a histogram of the
+//    two buckets' |x| low bytes.
+// Sums are int64 in 2^-24 units: fp16 magnitudes are below 2^40 units and a
+// fit covers at most NUQ_KFIT_MAX_N (2^20) samples, so every sum is exact, and a level is
+// the binary32 rounding of the exact mean. A Lloyd iteration that leaves the
+// ordered table unchanged is a fixed point (every later iteration would
+// repeat it), so the loop stops there with the same result.
+constexpr int KB_CH = 8;                // channels per workgroup (one 16-byte row load)
+constexpr int KB_T = 64 * KB_CH;        // threads: one wave per channel in the fit
+constexpr int KB_LDS_MAX_N = NUQ_KFIT_LDS_N;  // bucketed samples per channel kept in LDS (beyond: in the workspace)
+
+// sign, exponent shift and significand base of the members of bucket b
+__device__ __forceinline__ void kb_bucket(int b, bool &neg, int &sh, uint32_t &mbase) {
+  const int hh = b >= 0x80 ? b - 0x80 : 0x7f - b;  // bits 8..14 of the fp16 pattern
+  const int e = hh >> 2;
+  neg = b < 0x80;
+  sh = e > 0 ? e - 1 : 0;                          // units per significand step: 2^(e-1), subnormals 1
+  mbase = (e > 0 ? 0x400u : 0u) + ((uint32_t)(hh & 3) << 8);
+}
+
+// fp16 pattern of channel ch (0..7, may differ per lane) of a 16-byte row:
+// byte permutes pick half ch & 3 of (x, y) and of (z, w), without an
+// indexed access
+__device__ __forceinline__ uint32_t kb_pick(const uint4 &q, int ch) {
+  const uint32_t h = (uint32_t)(ch & 3);
+  const uint32_t sel = (2 * h) | ((2 * h + 1) << 8) | 0x0c0c0000u;  // bytes 2h, 2h+1, then zeros
+  const uint32_t lo = __builtin_amdgcn_perm(q.y, q.x, sel);
+  const uint32_t hi = __builtin_amdgcn_perm(q.w, q.z, sel);
+  return (ch & 4) ? hi : lo;
+}
+
+// binary32 rounding of (s / c) * 2^-24 for an exact int64 sum s in 2^-24
+// units and a count c (round to nearest even, as the exact quotient would)
+__device__ __forceinline__ float kb_mean(int64_t s, uint32_t c) {
+  const uint64_t a = s < 0 ? (uint64_t)(-s) : (uint64_t)s;
+  float f;
+  if (a < (1ull << 53)) {
+    f = (float)((double)a / (double)c);  // a exact; 53 >= 2*24 + 2: the double rounding is innocuous
+  } else {
+    const uint64_t q = a / c, r = a % c;
+    if (q < (1ull << 24)) {
+      // q + r/c below 2^24: the double sum errs by < 2^-29, and a tie point
+      // of the 24-bit grid is at least 2^-24/c... away unless hit exactly
+      f = (float)((double)q + (double)r / (double)c);
+    } else {
+      const int sh = 64 - __builtin_clzll(q) - 24;
+      uint64_t qh = q >> sh;
+      const uint64_t rb = q & ((1ull << sh) - 1), half = 1ull << (sh - 1);
+      const uint64_t lhs = rb * c + r, rhs = half * c;
+      if (lhs > rhs || (lhs == rhs && (qh & 1))) ++qh;
+      f = __builtin_ldexpf((float)qh, sh);
+    }
+  }
+  f *= 0x1p-24f;
+  return s < 0 ? -f : f;
+}
+
+// exclusive prefix over the 64 lanes of a wave, of a count and an int64 sum
+// (once per channel, in the table set-up)
+__device__ __forceinline__ void kb_excl(uint32_t c, int64_t u, uint32_t &ce, int64_t &ue) {
+  const int lane = threadIdx.x & 63;
+  uint32_t xc = c;
+  int64_t xu = u;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t yc = (uint32_t)__shfl_up((int)xc, d);
+    const int64_t yu = __shfl_up(xu, d);
+    if (lane >= d) {
+      xc += yc;
+      xu += yu;
+    }
+  }
+  ce = xc - c;
+  ue = xu - u;
+}
+
+// DPP move with a fill value for lanes without a source (row shifts,
+// broadcasts; rows outside ROWMASK keep the fill)
+template <int CTRL, int ROWMASK = 0xf>
+__device__ __forceinline__ uint32_t kb_dpp(uint32_t v, uint32_t fill) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)fill, (int)v, CTRL, ROWMASK, 0xf, false);
+}
+constexpr int DPP_ROW_SHL1 = 0x101, DPP_ROW_SHR1 = 0x111, DPP_ROW_SHR2 = 0x112, DPP_ROW_SHR4 = 0x114,
+              DPP_ROW_SHR8 = 0x118, DPP_ROW_BCAST15 = 0x142, DPP_ROW_BCAST31 = 0x143;
+
+// inclusive prefix sum over the wave (Hillis-Steele inside each 16-lane row,
+// then the row totals carried by row broadcasts): no LDS round trips
+__device__ __forceinline__ uint32_t kb_wscan(uint32_t x) {
+  x += kb_dpp<DPP_ROW_SHR1>(x, 0);
+  x += kb_dpp<DPP_ROW_SHR2>(x, 0);
+  x += kb_dpp<DPP_ROW_SHR4>(x, 0);
+  x += kb_dpp<DPP_ROW_SHR8>(x, 0);
+  x += kb_dpp<DPP_ROW_BCAST15, 0xa>(x, 0);
+  x += kb_dpp<DPP_ROW_BCAST31, 0xc>(x, 0);
+  return x;
+}
+
+// wave-uniform sum: DPP inside the rows, then the four row totals
+__device__ __forceinline__ uint32_t kb_wsum(uint32_t v) {
+  v += dppm<DPP_XOR1>(v);
+  v += dppm<DPP_XOR2>(v);
+  v += dppm<DPP_HALF_MIRROR>(v);
+  v += dppm<DPP_MIRROR>(v);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 0) + (uint32_t)__builtin_amdgcn_readlane((int)v, 16) +
+         (uint32_t)__builtin_amdgcn_readlane((int)v, 32) + (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+}
+
+__device__ __forceinline__ uint32_t kb_rl(uint32_t v, int lane) { return (uint32_t)__builtin_amdgcn_readlane((int)v, lane); }
+
+template <typename DatPtr>
+struct KbView {
+  const uint64_t *pre;  // [257] exclusive prefix sums (2^-24 units, int64 bits); [256] = total
+  const uint32_t *end;  // [256] bucket ends (exclusive prefix of the counts, shifted by one bucket)
+  DatPtr dat;           // bucketed key low bytes: bucket b at [start(b), end(b))
+  uint32_t *hist;       // [256] wave scratch
+  __device__ __forceinline__ uint32_t start(int b) const { return b == 0 ? 0u : end[b - 1]; }
+};
+
+// count and exact sum of the samples with key <= T[j], for every cut j whose
+// bit is set in `need` (T[j] wave-uniform): one interleaved pass over all the
+// cuts' buckets, then one wave sum per count and per low-byte sum
+template <int NC, typename V>
+__device__ __forceinline__ void kb_le_many(const V &v, const uint32_t *T, uint32_t need, uint32_t *cnt,
+                                           int64_t *sum) {
+  const int lane = threadIdx.x & 63;
+  uint32_t s0[NC], e0[NC], c[NC], sl[NC];
+  uint32_t maxsz = 0;
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    c[j] = sl[j] = 0;
+    s0[j] = e0[j] = 0;
+    if ((need >> j) & 1u) {
+      const int b = (int)(T[j] >> 8);
+      s0[j] = v.start(b);
+      e0[j] = v.end[b];
+      maxsz = max(maxsz, e0[j] - s0[j]);
+    }
+  }
+  for (uint32_t i = lane; i < maxsz; i += 64) {
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const uint32_t idx = s0[j] + i;
+      if (idx < e0[j]) {
+        const uint32_t kl = v.dat[idx];
+        const bool p = kl <= (T[j] & 0xffu);
+        c[j] += p ? 1u : 0u;
+        sl[j] += p ? kl : 0u;
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    if (!((need >> j) & 1u)) continue;
+    const uint32_t cc = kb_wsum(c[j]), ss = kb_wsum(sl[j]);
+    const int b = (int)(T[j] >> 8);
+    bool neg;
+    int sh;
+    uint32_t mbase;
+    kb_bucket(b, neg, sh, mbase);
+    const uint64_t hl = neg ? (uint64_t)cc * 255u - ss : (uint64_t)ss;  // sum of the fp16 low bytes
+    const int64_t u = (int64_t)(((uint64_t)cc * mbase + hl) << sh);
+    cnt[j] = s0[j] + cc;
+    sum[j] = (int64_t)v.pre[b] + (neg ? -u : u);
+  }
+}
+
+template <typename V>
+__device__ __forceinline__ void kb_le(const V &v, uint32_t T, uint32_t &cnt, int64_t &sum) {
+  kb_le_many<1>(v, &T, 1u, &cnt, &sum);
+}
+
+// the smallest e with (hist[0] + ... + hist[e]) > q, every lane holding
+// entries 4*lane .. 4*lane+3 and the count below them
+__device__ __forceinline__ uint32_t kb_hist_rank(const uint32_t *h4, uint32_t excl, uint32_t q) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t c0 = excl + h4[0], c1 = c0 + h4[1], c2 = c1 + h4[2], c3 = c2 + h4[3];
+  const int i = c0 > q ? 0 : c1 > q ? 1 : c2 > q ? 2 : 3;
+  const uint64_t bal = __ballot(c3 > q);
+  return kb_rl((uint32_t)(4 * lane + i), __ffsll((unsigned long long)bal) - 1);
+}
+
+// the bucket holding rank r (the first b with end(b) > r) and the histogram
+// of its key low bytes (the wave's scratch); returns b
+template <typename V>
+__device__ __forceinline__ int kb_bucket_hist(const V &v, uint32_t r, uint32_t *h4, uint32_t &excl) {
+  const int lane = threadIdx.x & 63;
+  const uint4 e4 = *reinterpret_cast<const uint4 *>(v.end + 4 * lane);
+  const int i = e4.x > r ? 0 : e4.y > r ? 1 : e4.z > r ? 2 : 3;
+  const uint64_t bal = __ballot(e4.w > r);
+  const int b = (int)kb_rl((uint32_t)(4 * lane + i), __ffsll((unsigned long long)bal) - 1);
+  const uint32_t s0 = v.start(b), e0 = v.end[b];
+  *reinterpret_cast<uint4 *>(v.hist + 4 * lane) = make_uint4(0, 0, 0, 0);
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  for (uint32_t j = s0 + lane; j < e0; j += 64) atomicAdd(&v.hist[v.dat[j]], 1u);
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  const uint4 hv = *reinterpret_cast<const uint4 *>(v.hist + 4 * lane);
+  h4[0] = hv.x; h4[1] = hv.y; h4[2] = hv.z; h4[3] = hv.w;
+  const uint32_t t = h4[0] + h4[1] + h4[2] + h4[3];
+  excl = kb_wscan(t) - t;
+  return b;
+}
+
+// keys of the r-th and (want_next) the (r+1)-th smallest samples (0-based;
+// r + want_next < n)
+template <typename V>
+__device__ __forceinline__ void kb_kth2(const V &v, uint32_t r, bool want_next, uint32_t &k1, uint32_t &k2) {
+  uint32_t h4[4], excl;
+  const int b = kb_bucket_hist(v, r, h4, excl);
+  const uint32_t s0 = v.start(b);
+  k1 = ((uint32_t)b << 8) | kb_hist_rank(h4, excl, r - s0);
+  k2 = k1;
+  if (want_next) {
+    if (r + 1 < v.end[b]) {
+      k2 = ((uint32_t)b << 8) | kb_hist_rank(h4, excl, r + 1 - s0);
+    } else {  // rank r + 1 opens the next non-empty bucket
+      const int b2 = kb_bucket_hist(v, r + 1, h4, excl);
+      k2 = ((uint32_t)b2 << 8) | kb_hist_rank(h4, excl, r + 1 - v.start(b2));
+    }
+  }
+}
+
+// (k+1)-th largest |x| (as a non-negative fp16 pattern) among the samples
+template <typename V>
+__device__ __forceinline__ uint32_t kb_tau(const V &v, uint32_t kp1) {
+  const int lane = threadIdx.x & 63;
+  // |x| bins a = 2*lane, 2*lane+1: buckets 0x80+a (x >= 0) and 0x7f-a (x < 0)
+  uint32_t A[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int a = 2 * lane + j;
+    const int bp = 0x80 + a, bn = 0x7f - a;
+    A[j] = (v.end[bp] - v.start(bp)) + (v.end[bn] - v.start(bn));
+  }
+  const uint32_t incl = kb_wscan(A[0] + A[1]);
+  const uint32_t total = kb_rl(incl, 63);
+  const uint32_t above1 = total - incl;  // samples in bins > 2*lane+1
+  const uint32_t above0 = above1 + A[1];
+  // the bin a* with above(a*) < kp1 <= above(a*) + A(a*)
+  const bool f1 = above1 < kp1 && above1 + A[1] >= kp1;
+  const bool f0 = above0 < kp1 && above0 + A[0] >= kp1;
+  const uint64_t bal = __ballot(f0 || f1);
+  const int src = __ffsll((unsigned long long)bal) - 1;
+  const int astar = (int)kb_rl((uint32_t)(f1 ? 2 * lane + 1 : 2 * lane), src);
+  const uint32_t q = kp1 - kb_rl(f1 ? above1 : above0, src);  // 1-based, from the top
+  // histogram of the |x| low bytes of the bin's two buckets
+  *reinterpret_cast<uint4 *>(v.hist + 4 * lane) = make_uint4(0, 0, 0, 0);
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  {
+    const int bp = 0x80 + astar, bn = 0x7f - astar;
+    for (uint32_t j = v.start(bp) + lane; j < v.end[bp]; j += 64) atomicAdd(&v.hist[v.dat[j]], 1u);
+    for (uint32_t j = v.start(bn) + lane; j < v.end[bn]; j += 64) atomicAdd(&v.hist[255u - v.dat[j]], 1u);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  const uint4 hv = *reinterpret_cast<const uint4 *>(v.hist + 4 * lane);
+  // largest low byte w with #{|x| low >= w} >= q
+  const uint32_t t4 = hv.x + hv.y + hv.z + hv.w;
+  const uint32_t inc2 = kb_wscan(t4);
+  const uint32_t ge0 = kb_rl(inc2, 63) - (inc2 - t4);  // #{>= 4*lane}
+  const uint32_t ge1 = ge0 - hv.x, ge2 = ge1 - hv.y, ge3 = ge2 - hv.z;
+  const int last = ge3 >= q ? 3 : ge2 >= q ? 2 : ge1 >= q ? 1 : 0;
+  const uint64_t b2 = __ballot(ge0 >= q);
+  const uint32_t w = kb_rl((uint32_t)(4 * lane + last), 63 - __clzll((long long)b2));
+  return ((uint32_t)astar << 8) | w;
+}
+
+// the fit of one channel by one wave. Lane j < L holds level j and lane
+// j < L-1 cut j (its key and the count and exact sum at it).
+template <int L, typename V>
+__device__ void kb_fit(const V &v, uint32_t n, int kout, int iters, float &lev_me, uint16_t &tau_out) {
+  const int lane = threadIdx.x & 63;
+  lev_me = 0.0f;
+  tau_out = 0;
+  if (n == 0) return;
+  const uint32_t tau = kb_tau(v, (uint32_t)kout + 1u);
+  tau_out = (uint16_t)tau;
+  // inliers: keys in [klo, khi] (with tau == 0 both zeros count)
+  const uint32_t klo = tau == 0 ? key16(0x8000u) : key16(tau | 0x8000u);
+  const uint32_t khi = key16(tau);
+  uint32_t lohi[2];
+  int64_t slohi[2];
+  {
+    const uint32_t T2[2] = {klo - 1, khi};
+    kb_le_many<2>(v, T2, 3u, lohi, slohi);
+  }
+  const uint32_t lo = lohi[0], hi = lohi[1];
+  const int64_t s_lo = slohi[0], s_hi = slohi[1];
+  const uint32_t m = hi - lo;
+  // quantile initialisation: level j interpolates between the r_j-th and
+  // (r_j+1)-th smallest inliers with r_j + f_j = (j + 1/2)(m - 1)/L
+#pragma unroll 1
+  for (int j = 0; j < L; ++j) {
+    const long long num = (long long)(2 * j + 1) * (long long)(m - 1);
+    const uint32_t rk = (uint32_t)(num / (2 * L));
+    const int rem = (int)(num % (2 * L));
+    uint32_t k1, k2;
+    kb_kth2(v, lo + rk, rem != 0, k1, k2);
+    double x = kval(k1);
+    if (rem != 0) {
+      const double u1 = kval(k2);
+      x = x + ((double)rem / (double)(2 * L)) * (u1 - x);
+    }
+    if (lane == j) lev_me = (float)x + 0.0f;
+  }
+  // Lloyd iterations: cells are key ranges cut at exact fp16 thresholds
+  uint32_t t_me = 0xffffffffu, c_me = hi;  // this lane's cut (none yet) and the count / sum at it
+  int64_t s_me = s_hi;
+  const float inf = __builtin_inff();
+  if (lane >= L) lev_me = inf;  // lanes above the table sort last
+#pragma unroll 1
+  for (int it = 0; it < iters; ++it) {
+    // thresholds between neighbouring levels (0 marks equal levels, whose
+    // cut is the one above: the first copy wins ties)
+    const float lnext = __uint_as_float(kb_dpp<DPP_ROW_SHL1>(__float_as_uint(lev_me), __float_as_uint(inf)));
+    uint32_t tmine = 0;
+    if (lane < L - 1 && lev_me < lnext) tmine = key16(thr16(lev_me, lnext));
+    // the cuts from the top, clamped to the inliers; a cut where it was last
+    // iteration, or where the cut above it is, keeps that result
+    uint32_t T[L - 1];
+    uint32_t need = 0, nt = 0xffffu;
+#pragma unroll
+    for (int j = L - 2; j >= 0; --j) {
+      const uint32_t t = kb_rl(tmine, j);
+      if (t) nt = t;
+      T[j] = min(max(nt, klo - 1), khi);
+      const bool same_up = j < L - 2 && T[j] == T[j + 1];
+      if (T[j] != kb_rl(t_me, j) && !same_up) need |= 1u << j;
+    }
+    uint32_t qc[L - 1];
+    int64_t qs[L - 1];
+    kb_le_many<L - 1>(v, T, need, qc, qs);
+    uint32_t c_up = hi;
+    int64_t s_up = s_hi;
+#pragma unroll
+    for (int j = L - 2; j >= 0; --j) {
+      uint32_t cj;
+      int64_t sj;
+      if ((need >> j) & 1u) {
+        cj = qc[j];
+        sj = qs[j];
+      } else if (T[j] == kb_rl(t_me, j)) {
+        cj = kb_rl(c_me, j);
+        sj = (int64_t)(((uint64_t)kb_rl((uint32_t)((uint64_t)s_me >> 32), j) << 32) | kb_rl((uint32_t)s_me, j));
+      } else {
+        cj = c_up;
+        sj = s_up;
+      }
+      if (lane == j) {
+        t_me = T[j];
+        c_me = cj;
+        s_me = sj;
+      }
+      c_up = cj;
+      s_up = sj;
+    }
+    // lane j < L updates level j from its cell (cut j-1, cut j]
+    uint32_t c_lo = kb_dpp<DPP_ROW_SHR1>(c_me, lo);
+    const uint32_t slo_l = kb_dpp<DPP_ROW_SHR1>((uint32_t)s_me, (uint32_t)s_lo);
+    const uint32_t slo_h = kb_dpp<DPP_ROW_SHR1>((uint32_t)((uint64_t)s_me >> 32), (uint32_t)((uint64_t)s_lo >> 32));
+    int64_t s_below = (int64_t)(((uint64_t)slo_h << 32) | slo_l);
+    if (lane == 0) {
+      c_lo = lo;
+      s_below = s_lo;
+    }
+    const uint32_t c_top = lane < L - 1 ? c_me : hi;
+    const int64_t s_top = lane < L - 1 ? s_me : s_hi;
+    float nl = lev_me;
+    if (lane < L && c_top > c_lo) nl = kb_mean(s_top - s_below, c_top - c_lo);
+    // an empty duplicate keeps its level while its twin moves: keep the table
+    // ordered so the cells stay contiguous ranges (odd-even transposition
+    // sort over lanes 0..L-1 with DPP moves; lanes above hold +inf)
+#pragma unroll
+    for (int p = 0; p < L; ++p) {
+      const uint32_t x = __float_as_uint(nl);
+      if ((p & 1) == 0) {  // pairs (0,1), (2,3), ...
+        const float o = __uint_as_float(dppm<DPP_XOR1>(x));
+        nl = (lane & 1) ? fmaxf(nl, o) : fminf(nl, o);
+      } else {             // pairs (1,2), (3,4), ...; lane 0 and lane 15 of the row sit out
+        const float up = __uint_as_float(kb_dpp<DPP_ROW_SHL1>(x, __float_as_uint(inf)));
+        const float dn = __uint_as_float(kb_dpp<DPP_ROW_SHR1>(x, __float_as_uint(-inf)));
+        nl = (lane & 1) ? fminf(nl, up) : fmaxf(nl, dn);
+      }
+    }
+    const bool changed = lane < L && __float_as_uint(nl) != __float_as_uint(lev_me);
+    lev_me = lane < L ? nl : inf;
+    if (__ballot(changed) == 0) break;  // a fixed point: every remaining iteration would repeat it
+  }
+  if (lane >= L) lev_me = 0.0f;
+}
+
 }  // namespace
 
 // ================================================================== kernels
@@ -713,110 +906,6 @@ __global__ __launch_bounds__(256) void nuq_zero(NuqArgs a) {
   const int64_t ks = (a.k_blk_x * a.BH + 63) >> 6, vs = (a.v_nblk + 63) >> 6;
   for (int64_t i = threadIdx.x; i < ks; i += 256) a.ws_ksup[i] = 0;
   for (int64_t i = threadIdx.x; i < vs; i += 256) a.ws_vsup[i] = 0;
-}
-
-// Key fit: lanes (channel g, chunk q) with CPC chunks per channel; a
-// workgroup of 256 lanes covers 256/CPC channels of one (b,h). The tile of
-// CPC*128 tokens x 256/CPC channels is read with coalesced dword loads (two
-// channels of one token each), transposed into the lanes' chunks through
-// LDS, then every lane sorts its chunk in registers and stores it back.
-#ifndef KVQ_NUQ_KF_T
-#define KVQ_NUQ_KF_T 256  // lanes per key-fit workgroup (64 KiB of LDS at 256)
-#endif
-constexpr int KF_T = KVQ_NUQ_KF_T;
-template <int CPC, int L>
-__global__ __launch_bounds__(KF_T) void nuq_key_fit(NuqArgs a) {
-  extern __shared__ uint32_t lds[];
-  constexpr int CHANS = KF_T / CPC, NP = CHANS / 2;  // channels, channel pairs
-  const int lane = threadIdx.x;
-  const int bh = blockIdx.y;
-  const int g = lane / CPC, q = lane % CPC;
-  const int d0 = blockIdx.x * CHANS;
-  const int d = d0 + g;
-  const bool active = d < a.D;
-  const int t0 = a.n_sink_eff;
-  const int nfit = a.S - t0;
-  // raw staging: word k (tokens 2k, 2k+1 of the chunk) of lane l at
-  // l*64 + (k ^ 4*swz(l)); groups of 4 words stay contiguous
-  auto swz = [](int l) { return ((l % CPC) + 5 * (l / CPC)) & 15; };
-  {
-    const uint16_t *base = a.keys + (size_t)bh * a.S * a.D;
-#pragma unroll 8
-    for (int u = lane; u < 64 * CPC * NP; u += KF_T) {
-      const int pp = u % NP, rp = u / NP;  // channel pair, token pair
-      const int c = 2 * pp, r = 2 * rp;
-      uint32_t x0 = 0x7c007c00u, x1 = 0x7c007c00u;  // +inf padding sorts last
-      if (d0 + c < a.D) {
-        const uint32_t *src = reinterpret_cast<const uint32_t *>(base + (size_t)(t0 + r) * a.D + d0 + c);
-        if (r < nfit) x0 = src[0];
-        if (r + 1 < nfit) x1 = src[a.D / 2];
-      }
-      const int l0 = c * CPC + r / 128, l1 = l0 + CPC;  // lanes of channels c, c+1
-      const int k = (r % 128) / 2;
-      lds[l0 * 64 + (k ^ (4 * swz(l0)))] = (x0 & 0xffffu) | (x1 << 16);
-      lds[l1 * 64 + (k ^ (4 * swz(l1)))] = (x0 >> 16) | (x1 & 0xffff0000u);
-    }
-  }
-  __syncthreads();
-  const int nq = active ? max(0, min(CH, nfit - q * CH)) : 0;
-  uint32_t last = 0;  // key of this lane's largest slot (merged path)
-  {
-    uint32_t raw[64];
-    const int sz = 4 * swz(lane);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const uint4 w4 = *reinterpret_cast<const uint4 *>(lds + lane * 64 + ((4 * j) ^ sz));
-      raw[4 * j] = w4.x; raw[4 * j + 1] = w4.y; raw[4 * j + 2] = w4.z; raw[4 * j + 3] = w4.w;
-    }
-    uint32_t v[64];
-    to_sort_layout(raw, v);
-    sort128(v);
-    if constexpr (CPC >= L) {
-      // one sorted sequence per channel, then exact prefix sums of every
-      // lane's valid slots at multiples of 32, offset by the chunks before it
-      merge_lanes<CPC>(v, q);
-      store_chunk(lds + lane * 64, lane & 63, v);
-      last = v[63] >> 16;
-      double cs[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-      for (int r = 0; r < 64; ++r) {
-        if (r < nq) cs[r >> 5] += kval(v[r] & 0xffffu);
-        if (64 + r < nq) cs[2 + (r >> 5)] += kval(v[r] >> 16);
-      }
-      const double tot = (cs[0] + cs[1]) + (cs[2] + cs[3]);
-      double x = tot;
-#pragma unroll
-      for (int dd = 1; dd < CPC; dd <<= 1) {
-        const double y = __shfl_up(x, dd);
-        if (q >= dd) x += y;
-      }
-      double *tb = reinterpret_cast<double *>(lds + KF_T * 64) + lane * 5;
-      const double b0 = x - tot;
-      tb[0] = b0;
-      tb[1] = b0 + cs[0];
-      tb[2] = b0 + (cs[0] + cs[1]);
-      tb[3] = b0 + ((cs[0] + cs[1]) + cs[2]);
-      tb[4] = b0 + tot;
-    } else {
-      store_chunk(lds + lane * 64, lane & 63, v);  // this lane's own words only
-    }
-  }
-  float lev[L];
-  FitOut fo;
-  if constexpr (CPC >= L) {
-    __syncthreads();  // the fit reads the other lanes' chunks and sums
-    fit_global<CPC, L>(lds, reinterpret_cast<const double *>(lds + KF_T * 64), lane, active ? nfit : 0, last,
-                       a.k_key, a.iters, lev, fo);
-  } else {
-    Chunk c{lds + lane * 64, lane & 63};
-    fit_vector<CPC, L>(c, nq, a.k_key, a.iters, lev, fo);
-  }
-  if (active && q == 0) {
-    float *kl = a.key_levels + ((size_t)bh * a.D + d) * L;
-#pragma unroll
-    for (int j = 0; j < L; ++j) kl[j] = lev[j];
-    a.key_thresh[(size_t)bh * a.D + d] = fo.tau;
-  }
 }
 
 // Key quantize against the (frozen or just fitted) per-channel tables. A
@@ -1005,8 +1094,10 @@ __device__ __forceinline__ void key_quant_body(const NuqArgs &a, int bx, int bh,
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         if (m & (1u << e)) {
-          a.ws_kpos[slot] = fpos + e;
-          a.ws_kval[slot] = (uint16_t)(wd[e / 2] >> (16 * (e & 1)));
+          if (slot < a.k_cap) {  // holds by the outlier bound; never written past otherwise
+            a.ws_kpos[slot] = fpos + e;
+            a.ws_kval[slot] = (uint16_t)(wd[e / 2] >> (16 * (e & 1)));
+          }
           ++slot;
         }
     }
@@ -1142,8 +1233,10 @@ __global__ __launch_bounds__(64) void nuq_value(NuqArgs a) {
       for (int e = 0; e < 8; ++e) {
         const uint32_t x = (wd[e / 2] >> (16 * (e & 1))) & 0xffffu;
         if ((x & 0x7fffu) > tau_abs) {
-          a.ws_vpos[slot] = (int32_t)((size_t)tok * D + c0 + g * 8 + e);
-          a.ws_vval[slot] = (uint16_t)x;
+          if (slot < a.v_cap) {
+            a.ws_vpos[slot] = (int32_t)((size_t)tok * D + c0 + g * 8 + e);
+            a.ws_vval[slot] = (uint16_t)x;
+          }
           ++slot;
         }
       }
@@ -1425,8 +1518,10 @@ __device__ __forceinline__ void value_wave_body(const NuqArgs &a, int64_t tok, b
 #pragma unroll
   for (int e = 0; e < E; ++e)
     if (out[e]) {
-      a.ws_vpos[slot] = (int32_t)((size_t)tok * D + lane * E + e);
-      a.ws_vval[slot] = (uint16_t)x[e];
+      if (slot < a.v_cap) {
+        a.ws_vpos[slot] = (int32_t)((size_t)tok * D + lane * E + e);
+        a.ws_vval[slot] = (uint16_t)x[e];
+      }
       ++slot;
     }
 }
@@ -1466,7 +1561,9 @@ __device__ void place_all(const NuqArgs &a, int64_t kn, int64_t vn) {
       }
       if (b < nblk) {
         const uint32_t off = running + before + (uint32_t)ex, base = info[2 * b];
+        const int64_t cap = side ? a.v_cap : a.k_cap;
         for (uint32_t i = 0; i < cnt; ++i) {
+          if ((int64_t)off + i >= cap || (int64_t)base + i >= cap) break;
           opos[off + i] = spos[base + i];
           oval[off + i] = sval[base + i];
         }
@@ -1533,35 +1630,136 @@ __global__ __launch_bounds__(256) void nuq_place(NuqArgs a, int64_t kn) {
   const uint16_t *sval = isv ? a.ws_vval : a.ws_kval;
   int32_t *opos = isv ? a.v_opos : a.k_opos;
   uint16_t *oval = isv ? a.v_oval : a.k_oval;
+  const int64_t cap = isv ? a.v_cap : a.k_cap;
   for (uint32_t i = threadIdx.x; i < cnt; i += 256) {
+    if ((int64_t)off + i >= cap || (int64_t)base + i >= cap) break;
     opos[off + i] = spos[base + i];
     oval[off + i] = sval[base + i];
   }
   if (b == nblk - 1 && threadIdx.x == 0) a.out_counts[isv ? 1 : 0] = (int64_t)off + cnt;
 }
 
+template <int L, bool LDS_DAT>
+__global__ __launch_bounds__(KB_T) void nuq_key_fit_bk(NuqArgs a) {
+  extern __shared__ uint64_t kb_lds[];
+  uint64_t *tab = kb_lds;                                            // [KB_CH][257]
+  uint32_t *cur = reinterpret_cast<uint32_t *>(tab + KB_CH * 257);   // [KB_CH][256]
+  uint32_t *hist = cur + KB_CH * 256;                                // [KB_CH][256]
+  const int bh = blockIdx.y, d0 = blockIdx.x * KB_CH;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int t0 = a.n_sink_eff;
+  const int n = a.S - t0;
+  const int npad = (n + 15) & ~15;
+  uint8_t *dat = LDS_DAT ? reinterpret_cast<uint8_t *>(hist + KB_CH * 256)
+                         : a.ws_kdat + ((size_t)bh * a.D + d0) * (size_t)npad;
+  for (int i = tid; i < KB_CH * 257; i += KB_T) tab[i] = 0;
+  __syncthreads();
+  const uint16_t *kin = a.keys + ((size_t)bh * a.S + t0) * a.D + d0;
+  // ---- bucket counts and significand sums (high word: count, low: sum).
+  // KB_R row loads are in flight before their atomics; at step c lane l works
+  // on channel (c + l) mod 8 of its row, so one instruction's atomics spread
+  // over all eight channels' tables instead of piling onto one. With one
+  // batch of rows per thread (n <= KB_T * KB_R) the rows stay in registers
+  // for the scatter.
+  constexpr int KB_R = 8;
+  const int rot = lane & 7;
+  const bool one_batch = n <= KB_T * KB_R;
+  uint4 w4[KB_R];
+  for (int tb = 0; tb < n; tb += KB_T * KB_R) {
+#pragma unroll
+    for (int r = 0; r < KB_R; ++r) {
+      const int t = tb + tid + r * KB_T;
+      w4[r] = t < n ? *reinterpret_cast<const uint4 *>(kin + (size_t)t * a.D) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < KB_R; ++r) {
+      if (tb + tid + r * KB_T >= n) continue;
+#pragma unroll
+      for (int c = 0; c < KB_CH; ++c) {
+        const uint32_t h = kb_pick(w4[r], (c + rot) & 7);
+        const uint32_t e = (h >> 10) & 31u;
+        const uint32_t m = (h & 0x3ffu) | (e ? 0x400u : 0u);
+        atomicAdd(&tab[((c + rot) & 7) * 257 + (key16(h) >> 8)], (1ull << 32) | m);
+      }
+    }
+  }
+  __syncthreads();
+  // ---- per channel (wave w): exclusive prefixes of counts and exact sums
+  {
+    uint64_t *tb = tab + w * 257;
+    uint32_t cnt[4];
+    int64_t un[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = 4 * lane + i;
+      const uint64_t x = tb[b];
+      bool neg;
+      int sh;
+      uint32_t mbase;
+      kb_bucket(b, neg, sh, mbase);
+      cnt[i] = (uint32_t)(x >> 32);
+      const int64_t u = (int64_t)((uint64_t)(uint32_t)x << sh);
+      un[i] = neg ? -u : u;
+    }
+    uint32_t ce;
+    int64_t ue;
+    kb_excl(cnt[0] + cnt[1] + cnt[2] + cnt[3], (un[0] + un[1]) + (un[2] + un[3]), ce, ue);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = 4 * lane + i;
+      cur[w * 256 + b] = ce;           // scatter cursor: starts at the bucket's first slot
+      tb[b] = (uint64_t)ue;            // exact sum of the buckets below b
+      ce += cnt[i];
+      ue += un[i];
+    }
+    if (lane == 63) tb[256] = (uint64_t)ue;
+  }
+  __syncthreads();
+  // ---- scatter the key low bytes (cursors end as bucket ends)
+  for (int tb = 0; tb < n; tb += KB_T * KB_R) {
+    if (!one_batch) {
+#pragma unroll
+      for (int r = 0; r < KB_R; ++r) {
+        const int t = tb + tid + r * KB_T;
+        w4[r] = t < n ? *reinterpret_cast<const uint4 *>(kin + (size_t)t * a.D) : make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < KB_R; ++r) {
+      if (tb + tid + r * KB_T >= n) continue;
+#pragma unroll
+      for (int c = 0; c < KB_CH; ++c) {
+        const int ch = (c + rot) & 7;
+        const uint32_t k = key16(kb_pick(w4[r], ch));
+        const uint32_t pos = atomicAdd(&cur[ch * 256 + (k >> 8)], 1u);
+        dat[(size_t)ch * npad + pos] = (uint8_t)k;
+      }
+    }
+  }
+  __syncthreads();
+  // ---- the fit of channel d0 + w by wave w
+  KbView<const uint8_t *> v{tab + w * 257, cur + w * 256, dat + (size_t)w * npad, hist + w * 256};
+  float mine;
+  uint16_t tau;
+  kb_fit<L>(v, (uint32_t)n, a.k_key, a.iters, mine, tau);
+  const size_t ch = (size_t)bh * a.D + d0 + w;
+  if (lane < L) a.key_levels[ch * L + lane] = mine;
+  if (lane == 0) a.key_thresh[ch] = tau;
+}
+
 // ================================================================== launch
 namespace {
-template <int CPC, int L>
-hipError_t launch_key_fit_cpc(const NuqArgs &a, hipStream_t st) {
-  const int chans = KF_T / CPC;
-  dim3 grid((a.D + chans - 1) / chans, a.BH);
-  // merged path: chunks (64 words per lane) + five prefix sums per lane
-  const size_t lds = (size_t)KF_T * 64 * 4 + (CPC >= L ? (size_t)KF_T * 5 * 8 : 0);
-  hipLaunchKernelGGL((nuq_key_fit<CPC, L>), grid, dim3(KF_T), lds, st, a);
-  return hipGetLastError();
-}
 template <int L>
-hipError_t launch_key_fit(const NuqArgs &a, int cpc, hipStream_t st) {
-  switch (cpc) {
-    case 1: return launch_key_fit_cpc<1, L>(a, st);
-    case 2: return launch_key_fit_cpc<2, L>(a, st);
-    case 4: return launch_key_fit_cpc<4, L>(a, st);
-    case 8: return launch_key_fit_cpc<8, L>(a, st);
-    case 16: return launch_key_fit_cpc<16, L>(a, st);
-    case 32: return launch_key_fit_cpc<32, L>(a, st);
-    default: return launch_key_fit_cpc<64, L>(a, st);
+hipError_t launch_key_fit(const NuqArgs &a, int /*cpc*/, hipStream_t st) {
+  const int n = a.S - a.n_sink_eff;
+  const dim3 grid((unsigned)(a.D / KB_CH), (unsigned)a.BH);
+  const size_t tables = (size_t)KB_CH * 257 * 8 + (size_t)KB_CH * 256 * 4 * 2;
+  if (n <= KB_LDS_MAX_N) {  // bucketed samples in LDS
+    hipLaunchKernelGGL((nuq_key_fit_bk<L, true>), grid, dim3(KB_T), tables + (size_t)KB_CH * ((n + 15) & ~15), st, a);
+  } else {                  // in the workspace
+    hipLaunchKernelGGL((nuq_key_fit_bk<L, false>), grid, dim3(KB_T), tables, st, a);
   }
+  return hipGetLastError();
 }
 // The value fit reads nothing the key kernels write, so for many tokens it
 // runs on a second stream of the device, forked from the caller's stream

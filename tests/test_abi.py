@@ -246,7 +246,7 @@ def test_nuq_validation_errors():
     assert _nuq(bits=0) == kvq.KVQ_ERR_BITS
     assert _nuq(D=96) == kvq.KVQ_ERR_SHAPE
     assert _nuq(S=0) == kvq.KVQ_ERR_SHAPE
-    assert _nuq(S=8197, ns=4) == kvq.KVQ_ERR_SHAPE          # key fit over 8193 tokens
+    assert _nuq(S=(1 << 20) + 5, BH=1, D=32, ns=4) == kvq.KVQ_ERR_SHAPE  # key fit over 2^20 + 1 tokens
     assert _nuq(frac=1.0) == kvq.KVQ_ERR_ARG
     assert _nuq(frac=-0.1) == kvq.KVQ_ERR_ARG
     assert _nuq(iters=-1) == kvq.KVQ_ERR_ARG

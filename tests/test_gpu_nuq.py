@@ -283,3 +283,33 @@ def test_full_size_sampled():
         if step % 16 == 0:
             rd = oracle.nuq_fit_quant(kd, vd, S + step, bits, 0.01, 8, 4, 0, kl, kth)
             compare(gd, rd, what="decode %d" % step)
+
+
+@pytest.mark.parametrize("S,D,bits", [(16388, 32, 3), (32772, 32, 4), (16388, 128, 2)])
+def test_key_fit_beyond_the_lds_limit(S, D, bits):
+    """Key fits over 16,384 and 32,768 non-sink tokens (the bucketed samples
+    live in the workspace): levels, thresholds and codes of sampled channels
+    against the oracle's threshold and Lloyd fit on each channel's samples."""
+    say("nuq long key fit", S, D, bits)
+    BH, L, frac = 2, 1 << bits, 0.01
+    k, v = t4((BH, S, D), 700 + S + D), t4((BH, S, D), 701 + S + D)
+    g = gpu_nuq(k, v, 0, bits, frac, 8, 4, 1, want_recon=False)
+    rng = np.random.default_rng(S + D)
+    for bh in range(BH):
+        for d in rng.choice(D, size=6, replace=False):
+            col = np.ascontiguousarray(k[bh, 4:, d])
+            tau = oracle.nuq_threshold(col, frac)
+            a = np.abs(col.view(np.float16).astype(np.float64))
+            inl = col[a <= float(np.uint16(tau).view(np.float16))]
+            lev = oracle.nuq_fit(inl, L, 8)
+            assert g["key_thresh"][bh, d] == tau, (bh, d)
+            assert np.array_equal(g["key_levels"][bh, d].view(np.uint32), lev.view(np.uint32)), (bh, d)
+            # codes of the channel's inliers: the nearest level (ties to the lower index)
+            codes = np.unpackbits(g["k_codes"][bh], axis=-1, bitorder="little")[:, : D * bits]
+            codes = (codes.reshape(S, D, bits) * (1 << np.arange(bits))).sum(-1)[:, d]
+            for s in rng.choice(np.arange(4, S), size=40, replace=False):
+                x = k[bh, s, d]
+                if abs(float(np.uint16(x).view(np.float16))) <= float(np.uint16(tau).view(np.float16)):
+                    assert codes[s] == oracle.nuq_nearest(x, lev), (bh, d, s)
+                else:
+                    assert codes[s] == 0, (bh, d, s)
