@@ -478,6 +478,7 @@ namespace {
 struct NuqPlan {
   int n_sink_eff, n_fit, key_cpc, val_cpc;
   int64_t kb, vb;  // outlier bounds
+  int64_t vs;      // value staging slots: k_val per token of every value workgroup
   int64_t k_blk_x, v_nblk;
   int64_t off_ctr, off_kblk, off_vblk, off_ksup, off_vsup, off_kpos, off_kval, off_vpos, off_vval, off_kdat, total;
 };
@@ -520,8 +521,11 @@ int nuq_plan(int32_t BH, int32_t S, int32_t D, int32_t bits, int32_t start_pos, 
   p.off_vsup = o; o = align256(o + (p.v_nblk + 63) / 64 * 4);
   p.off_kpos = o; o = align256(o + p.kb * 4);
   p.off_kval = o; o = align256(o + p.kb * 2);
-  p.off_vpos = o; o = align256(o + p.vb * 4);
-  p.off_vval = o; o = align256(o + p.vb * 2);
+  // value workgroups stage their outliers at fixed offsets (no shared
+  // counter): k_val slots for each token they cover, sinks and padding too
+  p.vs = (p.val_cpc == 0 ? (int64_t)BH * S : p.v_nblk * (64 / p.val_cpc)) * floor_frac(frac, D);
+  p.off_vpos = o; o = align256(o + p.vs * 4);
+  p.off_vval = o; o = align256(o + p.vs * 2);
   // a key fit over more tokens than fit in LDS keeps its bucketed samples here
   const int64_t kdat = fit_keys && p.n_fit > kvq::NUQ_KFIT_LDS_N ? (int64_t)BH * D * ((p.n_fit + 15) / 16 * 16) : 0;
   p.off_kdat = o; o = align256(o + kdat);
@@ -605,6 +609,7 @@ int nuq_call(const uint16_t *keys, const uint16_t *values, int32_t BH, int32_t S
   a.ws_kdat = ws + p.off_kdat;
   a.k_cap = p.kb;
   a.v_cap = p.vb;
+  a.v_scap = p.vs;
   a.k_blk_x = p.k_blk_x;
   a.v_nblk = p.v_nblk;
   return hip_status(kvq::launch_nuq(a, p.key_cpc, p.val_cpc, fork, (hipStream_t)stream), what);

@@ -81,7 +81,9 @@ struct NuqArgs {
   uint32_t *ws_ksup, *ws_vsup;     // per 64 workgroups: sum of their counts
   int32_t *ws_kpos, *ws_vpos;      // staging
   uint8_t *ws_kdat;                // key fit over more than 8192 tokens: bucketed key bytes [BH][D][round16(n)]
-  int64_t k_cap, v_cap;            // staging and list entries (the outlier bounds): writes past them are dropped
+  int64_t k_cap, v_cap;            // list entries (the outlier bounds); key staging is k_cap entries too
+  int64_t v_scap;                  // value staging entries: k_val slots for every token of every value workgroup
+                                   // (writes past any of these bounds are dropped)
   uint16_t *ws_kval, *ws_vval;
   int64_t k_blk_x, v_nblk;         // key-quant workgroups along S (16384/D rows each); value workgroups
 };

@@ -78,6 +78,72 @@ __device__ __forceinline__ uint32_t key_pair(uint32_t w) {
 }
 __device__ __forceinline__ double kval(uint32_t k) { return (double)h2f((uint16_t)unkey16(k)); }
 
+// ----------------------------------------------------------------- packed codes
+// Per 16-bit half: 1 where a > b (unsigned), else 0. A saturating subtract
+// then a minimum with 1, both packed (two VALU instructions for two
+// samples); written out because the compiler rewrites the pattern into
+// per-half compares through the scalar condition registers.
+__device__ __forceinline__ uint32_t pk_gt01(uint32_t a, uint32_t b) {
+  uint32_t r;
+  const uint32_t one = 0x00010001u;
+  asm("v_pk_sub_u16 %0, %1, %2 clamp\n\tv_pk_min_u16 %0, %0, %3" : "=&v"(r) : "v"(a), "v"(b), "v"(one));
+  return r;
+}
+// 0xffff in each half that holds 1 (halves hold 0 or 1: a 24-bit product)
+__device__ __forceinline__ uint32_t pk_mask01(uint32_t g) { return __umul24(g, 0xffffu); }
+// select per half: (m & a) | (~m & b)
+__device__ __forceinline__ uint32_t bsel(uint32_t m, uint32_t a, uint32_t b) { return (m & a) | (~m & b); }
+// codes #{j : key > T_j} of two keys (packed halves) for ascending thresholds
+// T2[j] (each repeated in both halves): a binary search, one code bit per
+// step from the top; the threshold a step tests is picked by the bits above
+// it (bit-select on the masks of the steps before)
+template <int BITS>
+__device__ __forceinline__ uint32_t code_pair(uint32_t kx, const uint32_t *T2) {
+  uint32_t code = 0, msk[BITS];
+#pragma unroll
+  for (int s = BITS - 1; s >= 0; --s) {
+    constexpr int MAXC = 1 << (BITS - 1);
+    uint32_t cand[MAXC];
+    const int nc = 1 << (BITS - 1 - s);  // candidates: one per value of the bits above s
+#pragma unroll
+    for (int p = 0; p < MAXC; ++p)
+      if (p < nc) cand[p] = T2[(p << (s + 1)) + (1 << s) - 1];
+#pragma unroll
+    for (int r = 0; r < BITS - 1 - s; ++r) {  // fold by code bit s + 1 + r
+#pragma unroll
+      for (int p = 0; p < MAXC / 2; ++p)
+        if (p < (nc >> (r + 1))) cand[p] = bsel(msk[s + 1 + r], cand[2 * p + 1], cand[2 * p]);
+    }
+    const uint32_t g = pk_gt01(kx, cand[0]);
+    code |= g << s;
+    msk[s] = pk_mask01(g);
+  }
+  return code;
+}
+// fp16 reconstructions of two codes (packed halves) from the level table as
+// fp16 pairs LH[i] = lev[2i] | lev[2i+1] << 16: byte permutes over pairs of
+// table words, then a bit-select per higher code bit
+template <int L>
+__device__ __forceinline__ uint32_t pick_lev16(const uint32_t *LH, uint32_t code) {
+  const uint32_t sel = (code & 0x00030003u) * 0x0202u + 0x01000100u;  // bytes 2c, 2c+1 of each half
+  if constexpr (L == 2) {
+    return __builtin_amdgcn_perm(LH[0], LH[0], sel);
+  } else if constexpr (L == 4) {
+    return __builtin_amdgcn_perm(LH[1], LH[0], sel);
+  } else {
+    uint32_t w[L / 4];
+#pragma unroll
+    for (int i = 0; i < L / 4; ++i) w[i] = __builtin_amdgcn_perm(LH[2 * i + 1], LH[2 * i], sel);
+    const uint32_t m2 = pk_mask01((code >> 2) & 0x00010001u);
+    if constexpr (L == 8) {
+      return bsel(m2, w[1], w[0]);
+    } else {
+      const uint32_t m3 = pk_mask01((code >> 3) & 0x00010001u);
+      return bsel(m3, bsel(m2, w[3], w[2]), bsel(m2, w[1], w[0]));
+    }
+  }
+}
+
 // ----------------------------------------------------------------- sorting
 __device__ __forceinline__ void ce(uint32_t &a, uint32_t &b) {
   const u16x2v x = __builtin_bit_cast(u16x2v, a), y = __builtin_bit_cast(u16x2v, b);
@@ -402,14 +468,31 @@ __device__ void fit_vector(const Chunk &c, int nq, int kout, int iters, float *l
   for (int it = 0; it < iters; ++it) {
     cut_keys<L>(lev, T);
     if (it == 0) {
-      // one pass over the inliers, cell by cell, recording the running sum at every cut
-      // (four independent partial sums; every partial sum is exact, so the
-      // order of the additions does not matter)
+      // the cut positions clamp(#{keys <= T_q}, lo, hi): the L-1 binary
+      // searches run side by side (independent reads)
+      int pos[L - 1];
+#pragma unroll
+      for (int q = 0; q < L - 1; ++q) pos[q] = 0;
+#pragma unroll
+      for (int sb = 64; sb >= 1; sb >>= 1) {
+#pragma unroll
+        for (int q = 0; q < L - 1; ++q)
+          if (c.at(pos[q] + sb - 1) <= T[q]) pos[q] += sb;
+      }
+#pragma unroll
+      for (int q = 0; q < L - 1; ++q) {
+        if (pos[q] < CH && c.at(pos[q]) <= T[q]) ++pos[q];
+        cut[q] = min(max(pos[q], lo), hi);
+      }
+      cut[L - 1] = hi;
+      // one pass over the inliers, cell by cell, recording the running sum at
+      // every cut (four independent partial sums; every partial sum is exact,
+      // so the order of the additions does not matter)
       double acc = 0.0;
       int prev = lo;
 #pragma unroll
       for (int q = 0; q < L; ++q) {
-        const int nc = q < L - 1 ? min(max(c.upper(T[q]), lo), hi) : hi;
+        const int nc = cut[q];
         double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
         int i = prev;
         for (; i + 4 <= nc; i += 4) {
@@ -421,7 +504,6 @@ __device__ void fit_vector(const Chunk &c, int nq, int kout, int iters, float *l
         for (; i < nc; ++i) a0 += kval(c.at(i));
         acc += (a0 + a1) + (a2 + a3);
         P[q] = acc;
-        cut[q] = nc;
         prev = max(prev, nc);
       }
     } else {
@@ -969,17 +1051,16 @@ __device__ __forceinline__ void key_quant_body(const NuqArgs &a, int bx, int bh,
   }
   __syncthreads();
   // ---- this lane's 8 channels: cut keys and thresholds as channel pairs
-  u16x2v cutp[4][L - 1], taup[4];
+  uint32_t cutp[4][L - 1], taup[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int c = ck * 8 + 2 * p;
 #pragma unroll
-    for (int j = 0; j < L - 1; ++j) cutp[p][j] = u16x2v{cut_s[c * 16 + j], cut_s[(c + 1) * 16 + j]};
-    taup[p] = u16x2v{tau_s[c], tau_s[c + 1]};
+    for (int j = 0; j < L - 1; ++j) cutp[p][j] = (uint32_t)cut_s[c * 16 + j] | ((uint32_t)cut_s[(c + 1) * 16 + j] << 16);
+    taup[p] = (uint32_t)tau_s[c] | ((uint32_t)tau_s[c + 1] << 16);
   }
   uint8_t *kout = a.k_codes + (size_t)bh * a.S * (D * BITS / 8);
   uint32_t omask[KQ_NIT];  // bit e: channel ck*8+e of step it is an outlier
-  const u16x2v one = {1, 1};
 #pragma unroll
   for (int it = 0; it < KQ_NIT; ++it) {
     const int row = row_w + it * RPW;
@@ -991,21 +1072,16 @@ __device__ __forceinline__ void key_quant_body(const NuqArgs &a, int bx, int bh,
       if (valid) in = *reinterpret_cast<const uint4 *>(kin + (size_t)row * D);
     }
     const uint32_t wd[4] = {in.x, in.y, in.z, in.w};
+    const uint32_t live = sink ? 0u : 0xffffffffu;  // sinks: code 0, no outliers
     uint32_t codes = 0, om = 0;
     uint32_t rec[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const u16x2v kx = __builtin_bit_cast(u16x2v, key_pair(wd[p]));
-      const u16x2v ax = __builtin_bit_cast(u16x2v, wd[p] & 0x7fff7fffu);
-      // outlier: |x| > tau (non-negative fp16 patterns order as integers)
-      const u16x2v isout = __builtin_elementwise_min(__builtin_elementwise_sub_sat(ax, taup[p]), one);
-      u16x2v code = {0, 0};
-#pragma unroll
-      for (int j = 0; j < L - 1; ++j)
-        code += __builtin_elementwise_min(__builtin_elementwise_sub_sat(kx, cutp[p][j]), one);
-      code *= (one - isout);  // outliers get code 0
-      uint32_t c0 = code.x, c1 = code.y, o0 = isout.x, o1 = isout.y;
-      if (sink) { c0 = c1 = 0; o0 = o1 = 0; }
+      // two channels at a time in packed 16-bit arithmetic. Outlier: |x| >
+      // tau (non-negative fp16 patterns order as integers); outliers get code 0
+      const uint32_t isout = pk_gt01(wd[p] & 0x7fff7fffu, taup[p]) & live;
+      const uint32_t code = code_pair<BITS>(key_pair(wd[p]), cutp[p]) & ~pk_mask01(isout) & live;
+      const uint32_t c0 = code & 0xffffu, c1 = code >> 16, o0 = isout & 1u, o1 = isout >> 16;
       codes |= (c0 | (c1 << BITS)) << (2 * p * BITS);
       om |= (o0 | (o1 << 1)) << (2 * p);
       if (want_rec) {
@@ -1158,50 +1234,54 @@ __global__ __launch_bounds__(64) void nuq_value(NuqArgs a) {
 #pragma unroll
     for (int j = 0; j < L; ++j) vl[j] = sink ? 0.0f : lev[j];
   }
-  // quantize this lane's channels, 8 at a time: the row is read again
-  // (16-byte loads, L2 hits) rather than kept in registers across the sort
-  // and the fit; codes are packed LSB-first along D
-  const uint32_t tau_abs = sink ? 0x7fffu : fo.tau;  // no outliers in sink tokens
-  int nout = 0;
+  // ---- quantize this lane's channels. The row is read again with all its
+  // 16-byte loads in flight at once and kept in registers. Two samples (one
+  // word) at a time in packed 16-bit arithmetic: outlier flags, codes by a
+  // binary search over the cut keys, reconstructions by byte permutes of the
+  // fp16 level table. Sinks get all-ones cut keys and an unreachable tau
+  // (code 0, no outliers) and keep their input as reconstruction.
+  uint4 rw[CH / 8];
+#pragma unroll
+  for (int g = 0; g < CH / 8; ++g)
+    rw[g] = (valid && g * 8 < nch) ? *reinterpret_cast<const uint4 *>(row + c0 + g * 8) : make_uint4(0, 0, 0, 0);
+  uint32_t T2[L - 1];
+#pragma unroll
+  for (int j = 0; j < L - 1; ++j) T2[j] = sink ? 0xffffffffu : T[j] * 0x10001u;
+  const uint32_t tau2 = (sink ? 0x7fffu : (uint32_t)fo.tau) * 0x10001u;
+  const uint32_t keep_in = sink ? 0xffffffffu : 0u;
+  uint32_t LH[L / 2];
+#pragma unroll
+  for (int i = 0; i < L / 2; ++i) LH[i] = (uint32_t)f2h(lev[2 * i]) | ((uint32_t)f2h(lev[2 * i + 1]) << 16);
+  const bool want_rec = valid && a.v_recon != nullptr;
   constexpr int OBW = CH * BITS / 32;  // dwords of packed codes for 128 channels
-  uint32_t ob[OBW + 1];
+  uint32_t ob[OBW + 1], om[CH / 32];   // codes LSB-first along D; outlier bit per channel
 #pragma unroll
   for (int i = 0; i <= OBW; ++i) ob[i] = 0;
-  const bool want_rec = valid && a.v_recon != nullptr;
+#pragma unroll
+  for (int i = 0; i < CH / 32; ++i) om[i] = 0;
+  uint32_t onum = 0;  // outlier counts per half
 #pragma unroll
   for (int g = 0; g < CH / 8; ++g) {
-    if (g * 8 >= nch) break;
-    uint4 in = make_uint4(0, 0, 0, 0);
-    if (valid) in = *reinterpret_cast<const uint4 *>(row + c0 + g * 8);
-    const uint32_t wd[4] = {in.x, in.y, in.z, in.w};
-    uint32_t rw[4];
+    const uint32_t wd[4] = {rw[g].x, rw[g].y, rw[g].z, rw[g].w};
+    uint32_t rec[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int i = g * 8 + e;
-      const uint32_t x = (wd[e / 2] >> (16 * (e & 1))) & 0xffffu;
+    for (int w = 0; w < 4; ++w) {
+      const int e = g * 8 + 2 * w;  // channel (within the lane) of the low half
+      const uint32_t x = wd[w];
       // |x| > tau on non-negative fp16 patterns is an integer comparison
-      const bool o = (x & 0x7fffu) > tau_abs;
-      uint32_t code = 0;
-      if (!sink) {
-        const uint32_t kx = key16(x);
-#pragma unroll
-        for (int j = 0; j < L - 1; ++j) code += kx > T[j];
-        code = o ? 0u : code;
-      }
-      nout += o ? 1 : 0;
-      const int bit = i * BITS;
-      ob[bit / 32] |= code << (bit % 32);
-      if (bit % 32 + BITS > 32) ob[bit / 32 + 1] |= code >> (32 - bit % 32);
-      if (want_rec) {
-        float lv = lev[0];
-#pragma unroll
-        for (int j = 1; j < L; ++j) lv = code == (uint32_t)j ? lev[j] : lv;
-        const uint32_t r16 = (sink || o) ? x : (uint32_t)f2h(lv);
-        if (e & 1) rw[e / 2] |= r16 << 16; else rw[e / 2] = r16;
-      }
+      const uint32_t o = pk_gt01(x & 0x7fff7fffu, tau2);
+      onum += o;
+      om[e / 32] |= ((o & 1u) | (o >> 15)) << (e % 32);
+      const uint32_t omask = pk_mask01(o);
+      const uint32_t code = code_pair<BITS>(key_pair(x), T2) & ~omask;
+      const uint32_t pc = (code & 0xffffu) | (code >> (16 - BITS));  // codes of channels e, e + 1
+      const int bit = e * BITS;
+      ob[bit / 32] |= pc << (bit % 32);
+      if (bit % 32 + 2 * BITS > 32) ob[bit / 32 + 1] |= pc >> (32 - bit % 32);
+      rec[w] = bsel(omask | keep_in, x, pick_lev16<L>(LH, code));
     }
-    if (want_rec)
-      *reinterpret_cast<uint4 *>(a.v_recon + (size_t)tok * D + c0 + g * 8) = make_uint4(rw[0], rw[1], rw[2], rw[3]);
+    if (want_rec && g * 8 < nch)
+      *reinterpret_cast<uint4 *>(a.v_recon + (size_t)tok * D + c0 + g * 8) = make_uint4(rec[0], rec[1], rec[2], rec[3]);
   }
   if (valid) {
     // the lane's code bytes start on a dword boundary (D >= 32, 128-channel chunks)
@@ -1212,33 +1292,33 @@ __global__ __launch_bounds__(64) void nuq_value(NuqArgs a) {
     for (int j = 0; j < OBW; ++j)
       if (j < ndw) crow[j] = ob[j];
   }
-  // ordered compaction (lanes are in flat order)
+  // ---- side channel in flat order (lanes are in flat order). A token has at
+  // most k_val outliers, so the workgroup's entries go to its own fixed
+  // staging range (k_val slots per token it covers) at the exclusive prefix of
+  // the lane counts; the placement kernel reads the range and the count.
+  const int nout = (int)((onum & 0xffffu) + (onum >> 16));
   int tot;
   const int pre = wave_excl(nout, tot);
-  __shared__ uint32_t base_s;
+  const int64_t base = (int64_t)blockIdx.x * (64 / CPC) * a.k_val;
   if (lane == 0) {
-    const uint32_t base = tot ? atomicAdd(&a.ws_ctr[1], (uint32_t)tot) : 0u;
     if (tot) atomicAdd(&a.ws_vsup[blockIdx.x >> 6], (uint32_t)tot);
-    base_s = base;
-    a.ws_vblk[blockIdx.x * 2] = base;
+    a.ws_vblk[blockIdx.x * 2] = (uint32_t)base;
     a.ws_vblk[blockIdx.x * 2 + 1] = (uint32_t)tot;
   }
-  __syncthreads();
   if (nout) {
-    int slot = base_s + pre;
-    for (int g = 0; g < CH / 8 && g * 8 < nch; ++g) {
-      const uint4 in = *reinterpret_cast<const uint4 *>(row + c0 + g * 8);
-      const uint32_t wd[4] = {in.x, in.y, in.z, in.w};
+    int64_t slot = base + pre;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t x = (wd[e / 2] >> (16 * (e & 1))) & 0xffffu;
-        if ((x & 0x7fffu) > tau_abs) {
-          if (slot < a.v_cap) {
-            a.ws_vpos[slot] = (int32_t)((size_t)tok * D + c0 + g * 8 + e);
-            a.ws_vval[slot] = (uint16_t)x;
-          }
-          ++slot;
+    for (int d = 0; d < CH / 32; ++d) {
+      uint32_t m = om[d];
+      while (m) {
+        const int b = __builtin_ctz(m);
+        m &= m - 1;
+        const int ch = c0 + d * 32 + b;
+        if (slot < a.v_scap) {
+          a.ws_vpos[slot] = (int32_t)((size_t)tok * D + ch);
+          a.ws_vval[slot] = row[ch];
         }
+        ++slot;
       }
     }
   }
@@ -1320,11 +1400,9 @@ __device__ __forceinline__ void bsort(uint32_t (&v)[R], int lane) {
   }
 }
 // one token per wave; every wave of the workgroup runs the body (inactive
-// waves too: the body's barriers are workgroup-wide), cb / base_s are the
-// wave's own LDS
+// waves too: the body's barriers are workgroup-wide), cb is the wave's own LDS
 template <int E, int BITS>
-__device__ __forceinline__ void value_wave_body(const NuqArgs &a, int64_t tok, bool active, uint8_t *cb,
-                                                uint32_t *base_s) {
+__device__ __forceinline__ void value_wave_body(const NuqArgs &a, int64_t tok, bool active, uint8_t *cb) {
   constexpr int L = 1 << BITS;
   constexpr int R = E == 4 ? 2 : 1;  // packed sort registers per lane
   const int lane = threadIdx.x & 63;
@@ -1499,26 +1577,25 @@ __device__ __forceinline__ void value_wave_body(const NuqArgs &a, int64_t tok, b
     reinterpret_cast<uint32_t *>(a.v_codes + (size_t)tok * (D * BITS / 8))[lane] = acc;
   }
   // ---- side channel: flat order is (lane, e)
+  // (at most k_val outliers: the token's fixed staging range of k_val slots)
   const int nout = wave_count<E>(out);
+  const int64_t base = tok * a.k_val;
   if (active && lane == 0) {
-    const uint32_t base = nout ? atomicAdd(&a.ws_ctr[1], (uint32_t)nout) : 0u;
     if (nout) atomicAdd(&a.ws_vsup[tok >> 6], (uint32_t)nout);
-    *base_s = base;
-    a.ws_vblk[tok * 2] = base;
+    a.ws_vblk[tok * 2] = (uint32_t)base;
     a.ws_vblk[tok * 2 + 1] = (uint32_t)nout;
   }
-  __syncthreads();
   int nb = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const uint64_t b = __ballot(out[e]);
     nb += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
   }
-  int slot = (int)*base_s + nb;
+  int64_t slot = base + nb;
 #pragma unroll
   for (int e = 0; e < E; ++e)
     if (out[e]) {
-      if (slot < a.v_cap) {
+      if (slot < a.v_scap) {
         a.ws_vpos[slot] = (int32_t)((size_t)tok * D + lane * E + e);
         a.ws_vval[slot] = (uint16_t)x[e];
       }
@@ -1529,8 +1606,7 @@ __device__ __forceinline__ void value_wave_body(const NuqArgs &a, int64_t tok, b
 template <int E, int BITS>
 __global__ __launch_bounds__(64) void nuq_value_wave(NuqArgs a) {
   __shared__ uint8_t cb[256];  // one code per channel
-  __shared__ uint32_t base_s;
-  value_wave_body<E, BITS>(a, blockIdx.x, true, cb, &base_s);
+  value_wave_body<E, BITS>(a, blockIdx.x, true, cb);
 }
 
 // Both side-channel lists placed by one workgroup: exclusive scans of the
@@ -1561,9 +1637,9 @@ __device__ void place_all(const NuqArgs &a, int64_t kn, int64_t vn) {
       }
       if (b < nblk) {
         const uint32_t off = running + before + (uint32_t)ex, base = info[2 * b];
-        const int64_t cap = side ? a.v_cap : a.k_cap;
+        const int64_t cap = side ? a.v_cap : a.k_cap, scap = side ? a.v_scap : a.k_cap;
         for (uint32_t i = 0; i < cnt; ++i) {
-          if ((int64_t)off + i >= cap || (int64_t)base + i >= cap) break;
+          if ((int64_t)off + i >= cap || (int64_t)base + i >= scap) break;
           opos[off + i] = spos[base + i];
           oval[off + i] = sval[base + i];
         }
@@ -1583,7 +1659,6 @@ __device__ void place_all(const NuqArgs &a, int64_t kn, int64_t vn) {
 template <int E, int BITS>
 __global__ __launch_bounds__(256) void nuq_small(NuqArgs a, int64_t kn, int64_t ntok) {
   __shared__ uint8_t cbs[4][256];
-  __shared__ uint32_t bases[4];
   __shared__ int last;
   const int64_t b = blockIdx.x;
   if (b < kn) {
@@ -1591,7 +1666,7 @@ __global__ __launch_bounds__(256) void nuq_small(NuqArgs a, int64_t kn, int64_t 
   } else {
     const int wv = threadIdx.x >> 6;
     const int64_t tok = (b - kn) * 4 + wv;
-    value_wave_body<E, BITS>(a, tok < ntok ? tok : 0, tok < ntok, cbs[wv], &bases[wv]);
+    value_wave_body<E, BITS>(a, tok < ntok ? tok : 0, tok < ntok, cbs[wv]);
   }
   __threadfence();
   __syncthreads();
@@ -1630,9 +1705,9 @@ __global__ __launch_bounds__(256) void nuq_place(NuqArgs a, int64_t kn) {
   const uint16_t *sval = isv ? a.ws_vval : a.ws_kval;
   int32_t *opos = isv ? a.v_opos : a.k_opos;
   uint16_t *oval = isv ? a.v_oval : a.k_oval;
-  const int64_t cap = isv ? a.v_cap : a.k_cap;
+  const int64_t cap = isv ? a.v_cap : a.k_cap, scap = isv ? a.v_scap : a.k_cap;
   for (uint32_t i = threadIdx.x; i < cnt; i += 256) {
-    if ((int64_t)off + i >= cap || (int64_t)base + i >= cap) break;
+    if ((int64_t)off + i >= cap || (int64_t)base + i >= scap) break;
     opos[off + i] = spos[base + i];
     oval[off + i] = sval[base + i];
   }

@@ -24,8 +24,9 @@ NuqCacheModel: ["veloxquant_mlx.cache.kvquant_cache module", KVQuantKVCache]
   the first call of a sequence fits and freezes the key tables and keeps
   its first n_sink tokens exact; later calls reuse the frozen key state,
   except that with refit_interval = N > 0 every N-th call after the first
-  fits the key tables again from that call's tokens (level lifecycle: levels
-  re-fit every N decode steps from the most recent token); trimming to
+  fits the key tables again from that call's tokens (level lifecycle: the
+  page's periodic re-fit on recent tokens, read as a re-fit on the
+  tokens of every N-th call); trimming to
   empty starts over; a partial trim keeps the key state.
 """
 from __future__ import annotations
