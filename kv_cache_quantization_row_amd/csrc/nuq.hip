@@ -277,27 +277,28 @@ __device__ __forceinline__ double gsum(double v) {
 }
 
 // ----------------------------------------------------------------- exact thresholds
+// the next fp16 value below a finite h (-inf below -65504)
 __device__ __forceinline__ uint16_t prev16(uint16_t h) {
   if ((h & 0x7fffu) == 0) return 0x8001u;
-  if (h & 0x8000u) return h == 0xfbffu ? h : (uint16_t)(h + 1);
+  if (h & 0x8000u) return (uint16_t)(h + 1);
   return (uint16_t)(h - 1);
 }
-// largest finite fp16 t with 2t <= a + b, for levels a < b (the smallest
-// finite fp16 if there is none). With s + e == a + b exactly (TwoSum) and
-// m = s/2, no fp16 value lies strictly between m and the true midpoint
-// m + e/2 (their distance is below one double ulp of m), so the answer is
-// the largest fp16 <= m, stepped down once more when m is itself an fp16
-// value and e < 0. c = fp16(m) is one of the two fp16 neighbours of m.
+// largest fp16 t with 2t <= a + b, for levels a < b: finite, or -inf when
+// a + b < -131008 (every finite input then lies above the cut). TwoSum in
+// binary32 gives s + e == a + b exactly, |e| <= ulp(s)/2. c = fp16(s/2),
+// clamped to the finite range, is the largest fp16 <= a + b or the next one
+// up (fp16 values are 13 bits coarser than binary32 rounding, and a halving
+// that underflows keeps the sign); 2c is exact, and two different floats are
+// at least one ulp of s apart, so 2c > a + b exactly when 2c > s, or 2c == s
+// and e < 0. That case steps c down once.
 __device__ __forceinline__ uint16_t thr16(float a, float b) {
-  const double da = a, db = b;
-  const double s = da + db;
-  const double bb = s - da;
-  const double e = (da - (s - bb)) + (db - bb);
-  const double m = s * 0.5;
-  uint16_t c = f2h((float)m);
+  const float s = a + b;
+  const float bb = s - a;
+  const float e = (a - (s - bb)) + (b - bb);
+  uint16_t c = f2h(s * 0.5f);
   if ((c & 0x7fffu) > 0x7bffu) c = (uint16_t)((c & 0x8000u) | 0x7bffu);
-  const double hc = (double)h2f(c);
-  if (hc > m || (hc == m && e < 0.0)) c = prev16(c);
+  const float c2 = 2.0f * h2f(c);
+  if (c2 > s || (c2 == s && e < 0.0f)) c = prev16(c);
   return c == 0x8000u ? (uint16_t)0 : c;
 }
 // cut keys for sorted levels: cell j is (T[j-1], T[j]] on the key line;
@@ -1714,13 +1715,26 @@ __global__ __launch_bounds__(256) void nuq_place(NuqArgs a, int64_t kn) {
   if (b == nblk - 1 && threadIdx.x == 0) a.out_counts[isv ? 1 : 0] = (int64_t)off + cnt;
 }
 
+// Workgroups go to the eight XCDs (each with its own L2) in turn by linear
+// id. xcd_tile maps the id to a tile index such that consecutive tiles run
+// on one XCD: XCD x = id % 8 takes tiles [x*q + min(x, r), ...) in order,
+// q = n / 8, r = n % 8 (a bijection on [0, n)).
+__device__ __forceinline__ uint32_t xcd_tile(uint32_t id, uint32_t n) {
+  const uint32_t x = id & 7u, q = n >> 3, r = n & 7u;
+  return x * q + min(x, r) + (id >> 3);
+}
+
 template <int L, bool LDS_DAT>
 __global__ __launch_bounds__(KB_T) void nuq_key_fit_bk(NuqArgs a) {
   extern __shared__ uint64_t kb_lds[];
   uint64_t *tab = kb_lds;                                            // [KB_CH][257]
   uint32_t *cur = reinterpret_cast<uint32_t *>(tab + KB_CH * 257);   // [KB_CH][256]
   uint32_t *hist = cur + KB_CH * 256;                                // [KB_CH][256]
-  const int bh = blockIdx.y, d0 = blockIdx.x * KB_CH;
+  // the channel groups of one (b, h) read the same token rows: keep them on
+  // one XCD so that its L2 fetches each row once
+  const int ngrp = a.D / KB_CH;
+  const int t = (int)xcd_tile(blockIdx.x, gridDim.x);
+  const int bh = t / ngrp, d0 = (t - bh * ngrp) * KB_CH;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int t0 = a.n_sink_eff;
   const int n = a.S - t0;
@@ -1827,7 +1841,7 @@ namespace {
 template <int L>
 hipError_t launch_key_fit(const NuqArgs &a, int /*cpc*/, hipStream_t st) {
   const int n = a.S - a.n_sink_eff;
-  const dim3 grid((unsigned)(a.D / KB_CH), (unsigned)a.BH);
+  const dim3 grid((unsigned)(a.D / KB_CH) * (unsigned)a.BH);
   const size_t tables = (size_t)KB_CH * 257 * 8 + (size_t)KB_CH * 256 * 4 * 2;
   if (n <= KB_LDS_MAX_N) {  // bucketed samples in LDS
     hipLaunchKernelGGL((nuq_key_fit_bk<L, true>), grid, dim3(KB_T), tables + (size_t)KB_CH * ((n + 15) & ~15), st, a);

@@ -313,3 +313,82 @@ def test_key_fit_beyond_the_lds_limit(S, D, bits):
                     assert codes[s] == oracle.nuq_nearest(x, lev), (bh, d, s)
                 else:
                     assert codes[s] == 0, (bh, d, s)
+
+
+def _adversarial_level_tables(L):
+    """Ascending binary32 level tables whose neighbour midpoints sit on fp16
+    values, just off them by less than a binary32 rounding of the sum (a tiny
+    level next to a large one), on duplicates (empty cells), on signed zeros,
+    in the fp16 subnormal range and near the top of the fp16 range."""
+    t = 2.0 ** -40
+    pats = [
+        [-3.0, -1.0, -0.5, 0.25, 0.75, 1.25, 2.0, 4.0],
+        [-100.0, -t, 1.5 * t, 1 - 2.0 ** -24, 3.0, 3 + 2.0 ** -20, 6.0, 6 + 2.0 ** -21],
+        [-1.0, -1.0, 0.0, 0.0, 0.0, 2.0, 2.0, 3.0],
+        [-(2.0 ** -20), -0.0, 0.0, 2.0 ** -24, 2.0 ** -23, 1e-3, 5e-3, 1.0],
+        [-60000.0, -59999.99, -1000.5, -1000.25, -3.3, -3.2999, -0.1, -0.05],
+        [1e-3, 1e-3 + 2.0 ** -30, 0.5, 0.5 + 2.0 ** -25, 65000.0, 65503.0, 65504.0, 65504.0],
+    ]
+    out = []
+    for p in range(len(pats)):
+        a = np.array(pats[p], np.float32)
+        if L == 16:
+            a = np.sort(np.concatenate([a, np.array(pats[(p + 1) % len(pats)], np.float32)]), kind="stable")
+        elif L == 4:
+            a = a[[0, 2, 4, 6]] if p % 2 == 0 else a[[1, 3, 5, 7]]
+        elif L == 2:
+            a = a[[1, 4]]
+        assert np.all(a[1:] >= a[:-1])
+        out.append(a)
+    return out
+
+
+def _fp16_sweep(x, n=2):
+    """fp16 patterns of the n finite fp16 values on each side of fp16(x) and fp16(x) itself."""
+    with np.errstate(over="ignore"):  # sweeps past the top of the range are dropped below
+        g = np.float16(x)
+        vals = [g]
+        lo = hi = g
+        for _ in range(n):
+            lo = np.nextafter(lo, np.float16(-np.inf))
+            hi = np.nextafter(hi, np.float16(np.inf))
+            vals += [lo, hi]
+        v = np.array(vals, np.float16)
+    return v[np.isfinite(v)].view(np.uint16)
+
+
+@pytest.mark.parametrize("bits", [3, 2, 4, 1])
+def test_frozen_levels_at_adversarial_midpoints(bits):
+    """Quantization against frozen key levels whose cut points are decided by
+    the last bit: every input lies on or next to a midpoint of neighbouring
+    levels, including midpoints that binary32 cannot hold. Codes, outliers and
+    reconstructions must match the oracle's exact nearest-level rule."""
+    say("nuq adversarial frozen levels", bits)
+    L = 1 << bits
+    BH, S, D = 2, 96, 128
+    tables = _adversarial_level_tables(L)
+    scales = [1.0, 8.0, 0.125]
+    kl = np.zeros((BH, D, L), np.float32)
+    kt = np.full((BH, D), 0x7bff, np.uint16)
+    k = np.zeros((BH, S, D), np.uint16)
+    rng = np.random.default_rng(77 + bits)
+    for b in range(BH):
+        for c in range(D):
+            p = (c + b) % len(tables)
+            sc = scales[(c // len(tables)) % 3]
+            if p == 5 and sc > 1:
+                sc = 1.0  # keep the top pattern inside the fp16 range
+            lev = (tables[p].astype(np.float64) * sc).astype(np.float32)
+            kl[b, c] = lev
+            if c % 7 == 3:
+                kt[b, c] = np.float16(2.0 * sc).view(np.uint16)  # some channels keep |x| > 2 sc exact
+            cand = [_fp16_sweep((float(lev[j]) + float(lev[j + 1])) / 2) for j in range(L - 1)]
+            cand += [_fp16_sweep(float(x), 1) for x in lev]
+            cand = np.unique(np.concatenate(cand + [np.array([0x0000, 0x8000], np.uint16)]))
+            col = np.resize(cand, S)
+            rng.shuffle(col)
+            k[b, :, c] = col
+    v = t4((BH, S, D), 31 + bits)
+    g = gpu_nuq(k, v, 300, bits, 0.01, 8, 4, 0, kl, kt)
+    r = oracle.nuq_fit_quant(k, v, 300, bits, 0.01, 8, 4, 0, kl, kt)
+    compare(g, r, what="adversarial frozen levels")
