@@ -695,6 +695,27 @@ __device__ __forceinline__ uint32_t kb_wsum(uint32_t v) {
 }
 
 __device__ __forceinline__ uint32_t kb_rl(uint32_t v, int lane) { return (uint32_t)__builtin_amdgcn_readlane((int)v, lane); }
+__device__ __forceinline__ double rl_d(double v, int lane) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  return __builtin_bit_cast(double, (uint64_t)kb_rl((uint32_t)b, lane) | ((uint64_t)kb_rl((uint32_t)(b >> 32), lane) << 32));
+}
+// a DPP move of a double (0.0 in lanes without a source)
+template <int CTRL, int ROWMASK = 0xf>
+__device__ __forceinline__ double kb_dppd0(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = kb_dpp<CTRL, ROWMASK>((uint32_t)b, 0u), hi = kb_dpp<CTRL, ROWMASK>((uint32_t)(b >> 32), 0u);
+  return __builtin_bit_cast(double, (uint64_t)lo | ((uint64_t)hi << 32));
+}
+// inclusive prefix sum of doubles over the wave, the pattern of kb_wscan
+__device__ __forceinline__ double wscan_d(double x) {
+  x += kb_dppd0<DPP_ROW_SHR1>(x);
+  x += kb_dppd0<DPP_ROW_SHR2>(x);
+  x += kb_dppd0<DPP_ROW_SHR4>(x);
+  x += kb_dppd0<DPP_ROW_SHR8>(x);
+  x += kb_dppd0<DPP_ROW_BCAST15, 0xa>(x);
+  x += kb_dppd0<DPP_ROW_BCAST31, 0xc>(x);
+  return x;
+}
 
 template <typename DatPtr>
 struct KbView {
@@ -1400,12 +1421,70 @@ __device__ __forceinline__ void bsort(uint32_t (&v)[R], int lane) {
     bsort<R, 2 * K>(v, lane);
   }
 }
-// one token per wave; every wave of the workgroup runs the body (inactive
-// waves too: the body's barriers are workgroup-wide), cb is the wave's own LDS
+// per-wave LDS of the one-wave-per-token value fit
+struct WaveLds {
+  double pre[257];    // pre[i]: exact sum of the i smallest samples
+  uint16_t key[256];  // the token's order keys, ascending (absent channels 0xffff, last)
+  uint8_t cb[256];    // one code per channel
+};
+
+// #{i < N : key[i] <= t} over an ascending LDS array of N (a power of two) keys
+template <int N>
+__device__ __forceinline__ int lds_upper(const uint16_t *key, uint32_t t) {
+  int pos = 0;
+#pragma unroll
+  for (int s_ = N / 2; s_ >= 1; s_ >>= 1)
+    if (key[pos + s_ - 1] <= t) pos += s_;
+  if (pos < N && key[pos] <= t) ++pos;
+  return pos;
+}
+
+// lane j < L-1: cut key j between levels j and j+1 of the lane-distributed
+// table (lane j holds level j, lanes >= L hold +inf); equal neighbours take
+// the cut above them (the first copy wins ties), the last cut is above every
+// finite key. Lanes >= L-1 return 0xffff.
+template <int L>
+__device__ __forceinline__ uint32_t lane_cut_key(float lev_me, int lane) {
+  const float inf = __builtin_inff();
+  const float lnext = __uint_as_float(kb_dpp<DPP_ROW_SHL1>(__float_as_uint(lev_me), __float_as_uint(inf)));
+  uint32_t t = 0xffffu;
+  if (lane < L - 1) t = lev_me < lnext ? key16(thr16(lev_me, lnext)) : 0u;
+  // a 0 takes the first nonzero key above it (lane L-1 holds 0xffff)
+  // (row shifts by 1, 2, 4, 8: after the shift by s a lane holds the first
+  // nonzero key among its next 2s - 1 neighbours). Each move runs in every
+  // lane before the select: a DPP read from a lane that is switched off
+  // returns the fill value.
+  uint32_t u = kb_dpp<0x101>(t, 0xffffu);
+  t = t ? t : u;
+  if constexpr (L > 2) { u = kb_dpp<0x102>(t, 0xffffu); t = t ? t : u; }
+  if constexpr (L > 4) { u = kb_dpp<0x104>(t, 0xffffu); t = t ? t : u; }
+  if constexpr (L > 8) { u = kb_dpp<0x108>(t, 0xffffu); t = t ? t : u; }
+  return t;
+}
+
+// One token per wave (E channels per lane). The token's keys are sorted
+// across the wave (bitonic network on packed 16-bit keys) and kept in the
+// wave's LDS with their exact prefix sums (DPP scans), so that every query
+// of the fit is a read or a binary search there. Level j lives in lane j:
+//  - tau, the (k+1)-th largest |x|: the largest samples by |x| are the two
+//    ends of the sorted row (negatives from the front, the rest from the
+//    back); taking a from the front and k+1-a from the back, the answer is
+//    the largest min(front_a, back_(k+1-a)) over the splits, one split per
+//    lane;
+//  - the inliers are the sorted range [lo, hi) (ballot counts);
+//  - quantile initialisation: lane j reads its two order statistics;
+//  - a Lloyd iteration: lane j < L-1 computes cut key j from its neighbour
+//    level (DPP), binary-searches it in the sorted keys and reads the prefix
+//    sum there; lane q takes cut q-1 from its neighbour (DPP) and divides its
+//    cell's exact sum by its count; an odd-even transposition over lanes
+//    keeps the table ordered.
+// The arithmetic is the same as in nuq_value. Every wave of the workgroup runs
+// the body (inactive waves too); wl is the wave's own LDS.
 template <int E, int BITS>
-__device__ __forceinline__ void value_wave_body(const NuqArgs &a, int64_t tok, bool active, uint8_t *cb) {
+__device__ __forceinline__ void value_wave_body(const NuqArgs &a, int64_t tok, bool active, WaveLds &wl) {
   constexpr int L = 1 << BITS;
   constexpr int R = E == 4 ? 2 : 1;  // packed sort registers per lane
+  constexpr int N = 64 * E;          // sorted slots
   const int lane = threadIdx.x & 63;
   const bool sink = !active || (int)(tok % a.S) < a.n_sink_eff;
   const int D = a.D;
@@ -1430,23 +1509,47 @@ __device__ __forceinline__ void value_wave_body(const NuqArgs &a, int64_t tok, b
   uint32_t ky[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) ky[e] = key16(x[e]);
-  float lev[L];
-#pragma unroll
-  for (int j = 0; j < L; ++j) lev[j] = 0.0f;
-  uint32_t tau = 0x7fffu;  // no outliers in sink tokens
+  const float inf = __builtin_inff();
+  float lev_me = lane < L ? 0.0f : inf;  // level `lane` (lanes >= L: +inf)
+  uint32_t tau = 0x7fffu;                // no outliers in sink tokens
   if (!sink) {
-    const long long k = a.k_val;  // floor(frac * D), computed on the host
-    // ---- tau: largest c with #{|x| >= c} >= k + 1
-    int pos = 0;
-    for (int sb = 16384; sb >= 1; sb >>= 1) {
-      const int cand = pos + sb - 1;
-      if (cand > 0x7bff) continue;
-      bool p[E];
+    // ---- sort the keys across the wave (absent channels are 0xffff and sort last)
+    uint32_t v[R];
+    if constexpr (E == 1) v[0] = (ok[0] ? ky[0] : 0xffffu) | 0xffff0000u;
+    else if constexpr (E == 2) v[0] = ky[0] | (ky[1] << 16);
+    else { v[0] = ky[0] | (ky[1] << 16); v[1] = ky[2] | (ky[3] << 16); }
+    bsort<R, 2>(v, lane);
+    // sorted element i sits in lane i % 64, slot i / 64 (slot s: register
+    // s / 2, half s % 2); keys and exact prefix sums go to the wave's LDS
+    double carry = 0.0;
+    if (lane == 0) wl.pre[0] = 0.0;
 #pragma unroll
-      for (int e = 0; e < E; ++e) p[e] = ok[e] && (x[e] & 0x7fffu) >= (uint32_t)cand;
-      if (wave_count<E>(p) >= k + 1) pos += sb;
+    for (int sl = 0; sl < 2 * R; ++sl) {
+      if (sl >= E && E < 2) break;  // E = 1: the high halves are padding
+      const uint32_t kk = (sl & 1) ? (v[sl >> 1] >> 16) : (v[sl >> 1] & 0xffffu);
+      wl.key[sl * 64 + lane] = (uint16_t)kk;
+      const double inc = wscan_d(kk == 0xffffu ? 0.0 : kval(kk)) + carry;
+      wl.pre[sl * 64 + lane + 1] = inc;
+      carry = rl_d(inc, 63);
     }
-    tau = (uint32_t)(pos - 1);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    // ---- tau: the (k+1)-th largest |x| (k = floor(frac * D) < D, computed on the host)
+    const int kp1 = a.k_val + 1;
+    bool neg[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) neg[e] = ok[e] && ky[e] < 0x8000u;  // x < 0 or x = -0
+    const int nneg = wave_count<E>(neg);
+    uint32_t best = 0;
+    for (int a0 = 0; a0 <= kp1; a0 += 64) {
+      const int fa = a0 + lane, fb = kp1 - fa;  // fa from the front, fb from the back
+      if (fa <= kp1 && fa <= nneg && fb <= D - nneg) {
+        const uint32_t af = fa > 0 ? unkey16(wl.key[fa - 1]) & 0x7fffu : 0x8000u;
+        const uint32_t ab = fb > 0 ? unkey16(wl.key[D - fb]) & 0x7fffu : 0x8000u;
+        best = max(best, min(af, ab));
+      }
+    }
+    tau = min(gred_u32<64>(best, [](uint32_t p_, uint32_t q_) { return max(p_, q_); }), 0x7bffu);
     const uint32_t klo = tau == 0 ? key16(0x8000u) : key16(tau | 0x8000u);
     bool inl[E], below[E];
 #pragma unroll
@@ -1456,97 +1559,61 @@ __device__ __forceinline__ void value_wave_body(const NuqArgs &a, int64_t tok, b
     }
     const int m = wave_count<E>(inl);
     const int lo = wave_count<E>(below), hi = lo + m;  // inliers: sorted positions [lo, hi)
-    // ---- sort the keys across the wave (absent channels are 0xffff and sort last)
-    uint32_t v[R];
-    if constexpr (E == 1) v[0] = (ok[0] ? ky[0] : 0xffffu) | 0xffff0000u;
-    else if constexpr (E == 2) v[0] = ky[0] | (ky[1] << 16);
-    else { v[0] = ky[0] | (ky[1] << 16); v[1] = ky[2] | (ky[3] << 16); }
-    bsort<R, 2>(v, lane);
-    auto key_at = [&](int i) -> uint32_t {  // sorted key i (uniform i)
-      const int s_ = i >> 6;
-      const uint32_t w = (uint32_t)__builtin_amdgcn_readlane((int)((s_ >> 1) ? v[R - 1] : v[0]), i & 63);
-      return (s_ & 1) ? (w >> 16) : (w & 0xffffu);
-    };
-    // ---- exact inclusive prefix sums of the sorted values, slot by slot
-    double ps[2 * R];
-    double carry = 0.0;
-#pragma unroll
-    for (int sl = 0; sl < 2 * R; ++sl) {
-      const uint32_t kk = (sl & 1) ? (v[sl >> 1] >> 16) : (v[sl >> 1] & 0xffffu);
-      double t = kk == 0xffffu ? 0.0 : kval(kk);
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const double y = __shfl_up(t, d);
-        t += lane >= d ? y : 0.0;
-      }
-      ps[sl] = t + carry;
-      carry = __shfl(ps[sl], 63);
-    }
-    auto pref = [&](int c) -> double {  // sum of the c smallest values (uniform c)
-      if (c == 0) return 0.0;
-      const int i = c - 1, sl = i >> 6;
-      double w = ps[0];
-#pragma unroll
-      for (int t = 1; t < 2 * R; ++t) {
-        w = sl == t ? ps[t] : w;
-        asm volatile("" : "+v"(w));
-      }
-      const uint64_t b = __builtin_bit_cast(uint64_t, w);
-      const uint32_t l32 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, i & 63);
-      const uint32_t h32 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), i & 63);
-      return __builtin_bit_cast(double, (uint64_t)l32 | ((uint64_t)h32 << 32));
-    };
-    // ---- quantile initialisation
-#pragma unroll
-    for (int j = 0; j < L; ++j) {
-      const long long num = (long long)(2 * j + 1) * (long long)(m - 1);
+    // ---- quantile initialisation: lane j interpolates between the r-th and
+    // (r+1)-th smallest inliers, r + f = (j + 1/2)(m - 1)/L
+    if (lane < L) {
+      const long long num = (long long)(2 * lane + 1) * (long long)(m - 1);
       const int r = (int)(num / (2 * L));
       const int rem = (int)(num % (2 * L));
-      double val = kval(key_at(lo + r));
-      if (rem != 0) val = val + ((double)rem / (double)(2 * L)) * (kval(key_at(lo + r + 1)) - val);
-      lev[j] = (float)val + 0.0f;
+      double val = kval(wl.key[lo + r]);
+      if (rem != 0) val = val + ((double)rem / (double)(2 * L)) * (kval(wl.key[lo + r + 1]) - val);
+      lev_me = (float)val + 0.0f;
     }
-    // ---- Lloyd iterations: cells are sorted ranges cut at the threshold keys
+    const double p_lo = wl.pre[lo], p_hi = wl.pre[hi];
+    // ---- Lloyd iterations
     for (int it = 0; it < a.iters; ++it) {
-      uint32_t tj = 0;  // lane j < L-1: cut key between levels j and j+1 (0: equal levels)
+      const uint32_t t = lane_cut_key<L>(lev_me, lane);
+      int cut = hi;
+      double pc = p_hi;
       if (lane < L - 1) {
-        const float l0 = pick<L>(lev, lane), l1 = pick<L>(lev, lane + 1);
-        if (l0 < l1) tj = key16(thr16(l0, l1));
+        cut = min(max(lds_upper<N>(wl.key, t), lo), hi);
+        pc = wl.pre[cut];
       }
-      uint32_t nt = 0xffffu;
-      int cut[L];
-      cut[L - 1] = hi;
+      // cell q = (cut q-1, cut q]; lane 0 starts at lo
+      const int c_lo = (int)kb_dpp<DPP_ROW_SHR1>((uint32_t)cut, (uint32_t)lo);
+      const uint64_t pb = __builtin_bit_cast(uint64_t, pc), plb = __builtin_bit_cast(uint64_t, p_lo);
+      const uint32_t pl_lo = kb_dpp<DPP_ROW_SHR1>((uint32_t)pb, (uint32_t)plb);
+      const uint32_t pl_hi = kb_dpp<DPP_ROW_SHR1>((uint32_t)(pb >> 32), (uint32_t)(plb >> 32));
+      const double p_below = __builtin_bit_cast(double, (uint64_t)pl_lo | ((uint64_t)pl_hi << 32));
+      const int cnt = cut - c_lo;
+      float nl = lev_me;
+      if (lane < L && cnt > 0) nl = (float)((pc - p_below) / (double)cnt);
+      // an empty duplicate keeps its level while its twin moves: keep the
+      // table ordered (odd-even transposition over lanes 0..L-1 with DPP
+      // moves; lane 0 and lane 15 of the row sit out of the odd phases)
 #pragma unroll
-      for (int j = L - 2; j >= 0; --j) {
-        const uint32_t r = (uint32_t)__builtin_amdgcn_readlane((int)tj, j);
-        if (r) nt = r;
-        bool p[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) p[e] = ok[e] && ky[e] <= nt;
-        cut[j] = min(max(wave_count<E>(p), lo), hi);
+      for (int ph = 0; ph < L; ++ph) {
+        const uint32_t xb = __float_as_uint(nl);
+        if ((ph & 1) == 0) {  // pairs (0,1), (2,3), ...
+          const float o = __uint_as_float(dppm<DPP_XOR1>(xb));
+          nl = (lane & 1) ? fmaxf(nl, o) : fminf(nl, o);
+        } else {              // pairs (1,2), (3,4), ...
+          const float up = __uint_as_float(kb_dpp<DPP_ROW_SHL1>(xb, __float_as_uint(inf)));
+          const float dn = __uint_as_float(kb_dpp<DPP_ROW_SHR1>(xb, __float_as_uint(-inf)));
+          nl = (lane & 1) ? fminf(nl, up) : fmaxf(nl, dn);
+        }
       }
-      // lane q: cell q's count and exact sum
-      int my_cnt = 0;
-      double my_sum = 0.0;
-      int prev = lo;
-      double pprev = pref(lo);
-#pragma unroll
-      for (int q = 0; q < L; ++q) {
-        const double pc = pref(cut[q]);
-        if (lane == q) { my_cnt = cut[q] - prev; my_sum = pc - pprev; }
-        prev = cut[q];
-        pprev = pc;
-      }
-      const float cur = pick<L>(lev, lane);
-      const float nl = my_cnt > 0 ? (float)(my_sum / (double)my_cnt) : cur;
-#pragma unroll
-      for (int q = 0; q < L; ++q) lev[q] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, nl), q));
-      sort_levels<L>(lev);
+      lev_me = lane < L ? nl : inf;
     }
   }
   // ---- codes, reconstruction, level row
-  uint32_t T[L];
-  cut_keys<L>(lev, T);
+  const uint32_t t_me = lane_cut_key<L>(lev_me, lane);
+  uint32_t T[L - 1];
+  float lev[L];
+#pragma unroll
+  for (int j = 0; j < L - 1; ++j) T[j] = kb_rl(t_me, j);
+#pragma unroll
+  for (int j = 0; j < L; ++j) lev[j] = __uint_as_float(kb_rl(__float_as_uint(lev_me), j));
   bool out[E];
   uint32_t code[E];
 #pragma unroll
@@ -1556,7 +1623,7 @@ __device__ __forceinline__ void value_wave_body(const NuqArgs &a, int64_t tok, b
 #pragma unroll
     for (int j = 0; j < L - 1; ++j) c += ky[e] > T[j];
     code[e] = (sink || out[e]) ? 0u : c;
-    if (ok[e]) cb[lane * E + e] = (uint8_t)code[e];
+    if (ok[e]) wl.cb[lane * E + e] = (uint8_t)code[e];
   }
   if (a.v_recon) {
 #pragma unroll
@@ -1565,15 +1632,16 @@ __device__ __forceinline__ void value_wave_body(const NuqArgs &a, int64_t tok, b
         a.v_recon[(size_t)tok * D + lane * E + e] =
             (sink || out[e]) ? (uint16_t)x[e] : f2h(pick<L>(lev, (int)code[e]));
   }
-  if (active && lane < L) a.value_levels[(size_t)tok * L + lane] = sink ? 0.0f : pick<L>(lev, lane);
-  __syncthreads();
+  if (active && lane < L) a.value_levels[(size_t)tok * L + lane] = lev_me;  // 0 for sinks
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
   // codes LSB-first along D: lane w builds dword w of the row
   if (active && lane < D * BITS / 32) {
     const int bit0 = 32 * lane;
     uint32_t acc = 0;
     for (int c = bit0 / BITS; c * BITS < bit0 + 32; ++c) {
       const int sh = c * BITS - bit0;
-      acc |= sh >= 0 ? (uint32_t)cb[c] << sh : (uint32_t)cb[c] >> -sh;
+      acc |= sh >= 0 ? (uint32_t)wl.cb[c] << sh : (uint32_t)wl.cb[c] >> -sh;
     }
     reinterpret_cast<uint32_t *>(a.v_codes + (size_t)tok * (D * BITS / 8))[lane] = acc;
   }
@@ -1606,8 +1674,8 @@ __device__ __forceinline__ void value_wave_body(const NuqArgs &a, int64_t tok, b
 
 template <int E, int BITS>
 __global__ __launch_bounds__(64) void nuq_value_wave(NuqArgs a) {
-  __shared__ uint8_t cb[256];  // one code per channel
-  value_wave_body<E, BITS>(a, blockIdx.x, true, cb);
+  __shared__ WaveLds wl;
+  value_wave_body<E, BITS>(a, blockIdx.x, true, wl);
 }
 
 // Both side-channel lists placed by one workgroup: exclusive scans of the
@@ -1659,7 +1727,7 @@ __device__ void place_all(const NuqArgs &a, int64_t kn, int64_t vn) {
 // done, and the one that finishes last places the lists. Nothing waits.
 template <int E, int BITS>
 __global__ __launch_bounds__(256) void nuq_small(NuqArgs a, int64_t kn, int64_t ntok) {
-  __shared__ uint8_t cbs[4][256];
+  __shared__ WaveLds wls[4];
   __shared__ int last;
   const int64_t b = blockIdx.x;
   if (b < kn) {
@@ -1667,7 +1735,7 @@ __global__ __launch_bounds__(256) void nuq_small(NuqArgs a, int64_t kn, int64_t 
   } else {
     const int wv = threadIdx.x >> 6;
     const int64_t tok = (b - kn) * 4 + wv;
-    value_wave_body<E, BITS>(a, tok < ntok ? tok : 0, tok < ntok, cbs[wv]);
+    value_wave_body<E, BITS>(a, tok < ntok ? tok : 0, tok < ntok, wls[wv]);
   }
   __threadfence();
   __syncthreads();
