@@ -479,6 +479,8 @@ struct NuqPlan {
   int n_sink_eff, n_fit, key_cpc, val_cpc;
   int64_t kb, vb;  // outlier bounds
   int64_t vs;      // value staging slots: k_val per token of every value workgroup
+  int64_t ks;      // key staging slots: kb, or BH*S*D for a small call
+  bool small;      // at most 256 (batch, head, token) vectors: one fused kernel and one placement workgroup
   int64_t k_blk_x, v_nblk;
   int64_t off_ctr, off_kblk, off_vblk, off_ksup, off_vsup, off_kpos, off_kval, off_vpos, off_vval, off_kdat, total;
 };
@@ -519,8 +521,12 @@ int nuq_plan(int32_t BH, int32_t S, int32_t D, int32_t bits, int32_t start_pos, 
   p.off_vblk = o; o = align256(o + p.v_nblk * 8);
   p.off_ksup = o; o = align256(o + (p.k_blk_x * BH + 63) / 64 * 4);
   p.off_vsup = o; o = align256(o + (p.v_nblk + 63) / 64 * 4);
-  p.off_kpos = o; o = align256(o + p.kb * 4);
-  p.off_kval = o; o = align256(o + p.kb * 2);
+  // a small call's key workgroups stage at the flat index of their first
+  // element (no shared counter to clear)
+  p.small = p.val_cpc == 0 && (int64_t)BH * S <= 256;
+  p.ks = p.small ? (int64_t)BH * S * D : p.kb;
+  p.off_kpos = o; o = align256(o + p.ks * 4);
+  p.off_kval = o; o = align256(o + p.ks * 2);
   // value workgroups stage their outliers at fixed offsets (no shared
   // counter): k_val slots for each token they cover, sinks and padding too
   p.vs = (p.val_cpc == 0 ? (int64_t)BH * S : p.v_nblk * (64 / p.val_cpc)) * floor_frac(frac, D);
@@ -608,6 +614,8 @@ int nuq_call(const uint16_t *keys, const uint16_t *values, int32_t BH, int32_t S
   a.ws_vval = reinterpret_cast<uint16_t *>(ws + p.off_vval);
   a.ws_kdat = ws + p.off_kdat;
   a.k_cap = p.kb;
+  a.k_scap = p.ks;
+  a.small = p.small ? 1 : 0;
   a.v_cap = p.vb;
   a.v_scap = p.vs;
   a.k_blk_x = p.k_blk_x;

@@ -82,6 +82,10 @@ struct NuqArgs {
   int32_t *ws_kpos, *ws_vpos;      // staging
   uint8_t *ws_kdat;                // key fit over more than 8192 tokens: bucketed key bytes [BH][D][round16(n)]
   int64_t k_cap, v_cap;            // list entries (the outlier bounds); key staging is k_cap entries too
+  int64_t k_scap;                  // key staging entries (k_cap, or BH*S*D for a small call)
+  int32_t small;                   // 1: a small call (one fused kernel, then one placement workgroup); key
+                                   // workgroups stage at the flat index of their first element, nothing
+                                   // needs a zeroed counter
   int64_t v_scap;                  // value staging entries: k_val slots for every token of every value workgroup
                                    // (writes past any of these bounds are dropped)
   uint16_t *ws_kval, *ws_vval;

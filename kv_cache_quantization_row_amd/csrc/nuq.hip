@@ -1084,7 +1084,11 @@ __device__ __forceinline__ void key_quant_body(const NuqArgs &a, int bx, int bh,
   uint8_t *kout = a.k_codes + (size_t)bh * a.S * (D * BITS / 8);
   uint32_t omask[KQ_NIT];  // bit e: channel ck*8+e of step it is an outlier
 #pragma unroll
+  for (int it = 0; it < KQ_NIT; ++it) omask[it] = 0;
+  const int wrow0 = (bx * 4 + wv) * (RPW * KQ_NIT);  // the wave's first row
+#pragma unroll
   for (int it = 0; it < KQ_NIT; ++it) {
+    if (wrow0 + it * RPW >= a.S) break;  // this step's rows and all later ones lie past the end
     const int row = row_w + it * RPW;
     const bool valid = row < a.S;
     const bool sink = row < a.n_sink_eff;
@@ -1172,8 +1176,12 @@ __device__ __forceinline__ void key_quant_body(const NuqArgs &a, int bx, int bh,
     btot += wave_cnt[i];
   }
   if (threadIdx.x == 0) {
-    const uint32_t base = btot ? atomicAdd(&a.ws_ctr[0], (uint32_t)btot) : 0u;
-    if (btot) atomicAdd(&a.ws_ksup[blk >> 6], (uint32_t)btot);
+    // a small call stages at the flat index of the workgroup's first element
+    // (its entries never exceed its rows times D); otherwise one atomic
+    // reserves the range and the per-64-workgroup sum feeds the placement
+    const uint32_t base = a.small ? (uint32_t)(((int64_t)bh * a.S + (int64_t)bx * (4 * RPW * KQ_NIT)) * D)
+                                  : (btot ? atomicAdd(&a.ws_ctr[0], (uint32_t)btot) : 0u);
+    if (btot && !a.small) atomicAdd(&a.ws_ksup[blk >> 6], (uint32_t)btot);
     blk_base = base;
     a.ws_kblk[blk * 2] = base;
     a.ws_kblk[blk * 2 + 1] = (uint32_t)btot;
@@ -1192,7 +1200,7 @@ __device__ __forceinline__ void key_quant_body(const NuqArgs &a, int bx, int bh,
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         if (m & (1u << e)) {
-          if (slot < a.k_cap) {  // holds by the outlier bound; never written past otherwise
+          if (slot < a.k_scap) {  // holds by the outlier bound; never written past otherwise
             a.ws_kpos[slot] = fpos + e;
             a.ws_kval[slot] = (uint16_t)(wd[e / 2] >> (16 * (e & 1)));
           }
@@ -1422,21 +1430,29 @@ __device__ __forceinline__ void bsort(uint32_t (&v)[R], int lane) {
   }
 }
 // per-wave LDS of the one-wave-per-token value fit
-struct WaveLds {
-  double pre[257];    // pre[i]: exact sum of the i smallest samples
-  uint16_t key[256];  // the token's order keys, ascending (absent channels 0xffff, last)
-  uint8_t cb[256];    // one code per channel
+struct alignas(16) WaveLds {
+  uint16_t key[256];   // the token's order keys, ascending (absent channels 0xffff, last)
+  uint16_t last8[32];  // last8[r] = key[8r + 7], the last key of each run of 8
+  double pre[257];     // pre[i]: exact sum of the i smallest samples
+  uint8_t cb[256];     // one code per channel
 };
 
-// #{i < N : key[i] <= t} over an ascending LDS array of N (a power of two) keys
+// #{keys <= t} among 8 keys (16 bytes), t repeated in both halves of t2
+__device__ __forceinline__ int count_le8(const uint4 &w, uint32_t t2) {
+  const uint32_t g = pk_gt01(w.x, t2) + pk_gt01(w.y, t2) + pk_gt01(w.z, t2) + pk_gt01(w.w, t2);
+  return 8 - (int)((g & 0xffffu) + (g >> 16));
+}
+// #{i < N : key[i] <= t} over the wave's N ascending keys: a count over the
+// last keys of the runs of 8 gives the number of runs wholly <= t, a count
+// inside the next run finishes (two rounds of 16-byte LDS reads)
 template <int N>
-__device__ __forceinline__ int lds_upper(const uint16_t *key, uint32_t t) {
-  int pos = 0;
+__device__ __forceinline__ int lds_upper(const WaveLds &wl, uint32_t t) {
+  const uint32_t t2 = t * 0x10001u;
+  int r = 0;
 #pragma unroll
-  for (int s_ = N / 2; s_ >= 1; s_ >>= 1)
-    if (key[pos + s_ - 1] <= t) pos += s_;
-  if (pos < N && key[pos] <= t) ++pos;
-  return pos;
+  for (int q = 0; q < N / 64; ++q) r += count_le8(*reinterpret_cast<const uint4 *>(wl.last8 + 8 * q), t2);
+  if (r == N / 8) return N;
+  return 8 * r + count_le8(*reinterpret_cast<const uint4 *>(wl.key + 8 * r), t2);
 }
 
 // lane j < L-1: cut key j between levels j and j+1 of the lane-distributed
@@ -1528,6 +1544,7 @@ __device__ __forceinline__ void value_wave_body(const NuqArgs &a, int64_t tok, b
       if (sl >= E && E < 2) break;  // E = 1: the high halves are padding
       const uint32_t kk = (sl & 1) ? (v[sl >> 1] >> 16) : (v[sl >> 1] & 0xffffu);
       wl.key[sl * 64 + lane] = (uint16_t)kk;
+      if ((lane & 7) == 7) wl.last8[(sl * 64 + lane) >> 3] = (uint16_t)kk;
       const double inc = wscan_d(kk == 0xffffu ? 0.0 : kval(kk)) + carry;
       wl.pre[sl * 64 + lane + 1] = inc;
       carry = rl_d(inc, 63);
@@ -1576,7 +1593,7 @@ __device__ __forceinline__ void value_wave_body(const NuqArgs &a, int64_t tok, b
       int cut = hi;
       double pc = p_hi;
       if (lane < L - 1) {
-        cut = min(max(lds_upper<N>(wl.key, t), lo), hi);
+        cut = min(max(lds_upper<N>(wl, t), lo), hi);
         pc = wl.pre[cut];
       }
       // cell q = (cut q-1, cut q]; lane 0 starts at lo
@@ -1650,7 +1667,7 @@ __device__ __forceinline__ void value_wave_body(const NuqArgs &a, int64_t tok, b
   const int nout = wave_count<E>(out);
   const int64_t base = tok * a.k_val;
   if (active && lane == 0) {
-    if (nout) atomicAdd(&a.ws_vsup[tok >> 6], (uint32_t)nout);
+    if (nout && !a.small) atomicAdd(&a.ws_vsup[tok >> 6], (uint32_t)nout);
     a.ws_vblk[tok * 2] = (uint32_t)base;
     a.ws_vblk[tok * 2 + 1] = (uint32_t)nout;
   }
@@ -1678,57 +1695,51 @@ __global__ __launch_bounds__(64) void nuq_value_wave(NuqArgs a) {
   value_wave_body<E, BITS>(a, blockIdx.x, true, wl);
 }
 
-// Both side-channel lists placed by one workgroup: exclusive scans of the
-// producer counts in producer order, then each thread copies its producer's
-// staged entries.
+// Both side-channel lists placed by one workgroup of 256 threads, the two
+// lists side by side (threads 0..127 the key producers, 128..255 the value
+// producers): exclusive scans of the producer counts in producer order, then
+// each thread copies its producer's staged entries.
 __device__ void place_all(const NuqArgs &a, int64_t kn, int64_t vn) {
   __shared__ uint32_t wsum[4];
-  for (int side = 0; side < 2; ++side) {
-    const int64_t nblk = side ? vn : kn;
-    const uint32_t *info = side ? a.ws_vblk : a.ws_kblk;
-    const int32_t *spos = side ? a.ws_vpos : a.ws_kpos;
-    const uint16_t *sval = side ? a.ws_vval : a.ws_kval;
-    int32_t *opos = side ? a.v_opos : a.k_opos;
-    uint16_t *oval = side ? a.v_oval : a.k_oval;
-    uint32_t running = 0;
-    for (int64_t b0 = 0; b0 < nblk; b0 += 256) {
-      const int64_t b = b0 + threadIdx.x;
-      const uint32_t cnt = b < nblk ? info[2 * b + 1] : 0u;
-      int wtot;
-      const int ex = wave_excl((int)cnt, wtot);
-      if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = (uint32_t)wtot;
-      __syncthreads();
-      uint32_t before = 0, all = 0;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        if (w < (int)(threadIdx.x >> 6)) before += wsum[w];
-        all += wsum[w];
+  const int side = (int)(threadIdx.x >> 7), t = (int)(threadIdx.x & 127);
+  const int64_t nblk = side ? vn : kn;
+  const uint32_t *info = side ? a.ws_vblk : a.ws_kblk;
+  const int32_t *spos = side ? a.ws_vpos : a.ws_kpos;
+  const uint16_t *sval = side ? a.ws_vval : a.ws_kval;
+  int32_t *opos = side ? a.v_opos : a.k_opos;
+  uint16_t *oval = side ? a.v_oval : a.k_oval;
+  const int64_t cap = side ? a.v_cap : a.k_cap, scap = side ? a.v_scap : a.k_scap;
+  const int64_t nmax = kn > vn ? kn : vn;  // the same trip count on both sides (barriers)
+  uint32_t running = 0;
+  for (int64_t b0 = 0; b0 < nmax; b0 += 128) {
+    const int64_t b = b0 + t;
+    const uint32_t cnt = b < nblk ? info[2 * b + 1] : 0u;
+    const uint32_t inc = kb_wscan(cnt);
+    if ((threadIdx.x & 63) == 63) wsum[threadIdx.x >> 6] = inc;
+    __syncthreads();
+    const uint32_t w0 = wsum[2 * side], w1 = wsum[2 * side + 1];
+    if (b < nblk) {
+      const uint32_t off = running + ((threadIdx.x & 64) ? w0 : 0u) + inc - cnt, base = info[2 * b];
+      for (uint32_t i = 0; i < cnt; ++i) {
+        if ((int64_t)off + i >= cap || (int64_t)base + i >= scap) break;
+        opos[off + i] = spos[base + i];
+        oval[off + i] = sval[base + i];
       }
-      if (b < nblk) {
-        const uint32_t off = running + before + (uint32_t)ex, base = info[2 * b];
-        const int64_t cap = side ? a.v_cap : a.k_cap, scap = side ? a.v_scap : a.k_cap;
-        for (uint32_t i = 0; i < cnt; ++i) {
-          if ((int64_t)off + i >= cap || (int64_t)base + i >= scap) break;
-          opos[off + i] = spos[base + i];
-          oval[off + i] = sval[base + i];
-        }
-      }
-      running += all;
-      __syncthreads();
     }
-    if (threadIdx.x == 0) a.out_counts[side] = (int64_t)running;
+    running += w0 + w1;
+    __syncthreads();
   }
+  if (t == 0) a.out_counts[side] = (int64_t)running;
 }
 
-// Small calls: key quantization, the value fits (one token per wave, four
-// per workgroup) and the placement of both side-channel lists in one
-// launch. Workgroups [0, kn) quantize keys, the rest fit values; each
-// workgroup publishes its writes (device-scope fence) and counts itself
-// done, and the one that finishes last places the lists. Nothing waits.
+// Small calls: key quantization and the value fits (one token per wave, four
+// per workgroup) in one launch; workgroups [0, kn) quantize keys, the rest
+// fit values. Every producer stages its outliers at a fixed offset, so no
+// counter needs clearing; one workgroup of nuq_place_small then places both
+// lists.
 template <int E, int BITS>
 __global__ __launch_bounds__(256) void nuq_small(NuqArgs a, int64_t kn, int64_t ntok) {
   __shared__ WaveLds wls[4];
-  __shared__ int last;
   const int64_t b = blockIdx.x;
   if (b < kn) {
     key_quant_body<BITS>(a, (int)(b % a.k_blk_x), (int)(b / a.k_blk_x), b);
@@ -1737,15 +1748,8 @@ __global__ __launch_bounds__(256) void nuq_small(NuqArgs a, int64_t kn, int64_t 
     const int64_t tok = (b - kn) * 4 + wv;
     value_wave_body<E, BITS>(a, tok < ntok ? tok : 0, tok < ntok, wls[wv]);
   }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) last = atomicAdd(&a.ws_ctr[2], 1u) == gridDim.x - 1;
-  __syncthreads();
-  if (last) {
-    __threadfence();
-    place_all(a, kn, ntok);
-  }
 }
+__global__ __launch_bounds__(256) void nuq_place_small(NuqArgs a, int64_t kn, int64_t ntok) { place_all(a, kn, ntok); }
 
 // Place the staged side-channel entries in flat order, keys and values in one
 // launch: workgroups [0, kn) move the key-quant workgroups' entries, the rest
@@ -1774,7 +1778,7 @@ __global__ __launch_bounds__(256) void nuq_place(NuqArgs a, int64_t kn) {
   const uint16_t *sval = isv ? a.ws_vval : a.ws_kval;
   int32_t *opos = isv ? a.v_opos : a.k_opos;
   uint16_t *oval = isv ? a.v_oval : a.k_oval;
-  const int64_t cap = isv ? a.v_cap : a.k_cap, scap = isv ? a.v_scap : a.k_cap;
+  const int64_t cap = isv ? a.v_cap : a.k_cap, scap = isv ? a.v_scap : a.k_scap;
   for (uint32_t i = threadIdx.x; i < cnt; i += 256) {
     if ((int64_t)off + i >= cap || (int64_t)base + i >= scap) break;
     opos[off + i] = spos[base + i];
@@ -1966,10 +1970,8 @@ template <int BITS>
 hipError_t launch_bits(const NuqArgs &a, int key_cpc, int val_cpc, bool fork, hipStream_t st) {
   constexpr int L = 1 << BITS;
   hipError_t e;
-  hipLaunchKernelGGL(nuq_zero, dim3(1), dim3(256), 0, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t ntok = (int64_t)a.BH * a.S;
-  if (val_cpc == 0 && ntok <= 256) {  // decode-sized: one launch for key quant, values and placement
+  if (a.small) {  // decode-sized: key quant and values in one launch, then the placement
     if (a.fit_keys && (e = launch_key_fit<L>(a, key_cpc, st)) != hipSuccess) return e;
     const int64_t kn = a.k_blk_x * (int64_t)a.BH;
     const dim3 grid((unsigned)(kn + (ntok + 3) / 4));
@@ -1979,8 +1981,12 @@ hipError_t launch_bits(const NuqArgs &a, int key_cpc, int val_cpc, bool fork, hi
       hipLaunchKernelGGL((nuq_small<2, BITS>), grid, dim3(256), 0, st, a, kn, ntok);
     else
       hipLaunchKernelGGL((nuq_small<4, BITS>), grid, dim3(256), 0, st, a, kn, ntok);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(nuq_place_small, dim3(1), dim3(256), 0, st, a, kn, ntok);
     return hipGetLastError();
   }
+  hipLaunchKernelGGL(nuq_zero, dim3(1), dim3(256), 0, st, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   if (val_cpc == 0 || !fork) {  // few tokens (a cross-stream join costs more than it hides), or one stream asked for
     if (a.fit_keys && (e = launch_key_fit<L>(a, key_cpc, st)) != hipSuccess) return e;
     hipLaunchKernelGGL((nuq_key_quant<BITS>), dim3((unsigned)a.k_blk_x, a.BH), dim3(256), 0, st, a);

@@ -92,29 +92,42 @@ def _err(rc: int):
 
 
 def _ptr(t):
-    return None if t is None else C.c_void_p(t.data_ptr())
+    # device address as an int: the declared argtypes turn it into void*
+    return None if t is None else t.data_ptr()
+
+
+_raw_stream = None
 
 
 def _stream(stream):
+    """hipStream_t of `stream`, else torch's current stream of the current device."""
+    global _raw_stream
     if stream is not None:
-        return C.c_void_p(stream if isinstance(stream, int) else stream.cuda_stream)
+        return stream if isinstance(stream, int) else stream.cuda_stream
     import torch
-    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if _raw_stream is None:  # torch's accessor of the raw current stream, when it has one
+        _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", False)
+    if _raw_stream:
+        return _raw_stream(torch.cuda.current_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _dev(*ts):
     for t in ts:
-        if t is not None:
-            if not t.is_cuda:
-                raise KvqError(KVQ_ERR_ARG, "tensors must be on the GPU")
-            if not t.is_contiguous():
-                raise KvqError(KVQ_ERR_ARG, "tensors must be contiguous")
+        if t is not None and not (t.is_cuda and t.is_contiguous()):
+            raise KvqError(KVQ_ERR_ARG, "tensors must be contiguous and on the GPU")
+
+
+_DT = None
 
 
 def _dt(kind):
-    import torch
-    return {"f16": (torch.float16, torch.int16), "f32": (torch.float32,), "u8": (torch.uint8,),
-            "i32": (torch.int32,), "i64": (torch.int64,)}[kind]
+    global _DT
+    if _DT is None:
+        import torch
+        _DT = {"f16": (torch.float16, torch.int16), "f32": (torch.float32,), "u8": (torch.uint8,),
+               "i32": (torch.int32,), "i64": (torch.int64,)}
+    return _DT[kind]
 
 
 def _need(t, name, kind, numel=None, ndim=None):
@@ -123,8 +136,9 @@ def _need(t, name, kind, numel=None, ndim=None):
     argument has passed this)."""
     if t is None:
         return
-    if t.dtype not in _dt(kind):
-        raise KvqError(KVQ_ERR_ARG, "%s must be %s (got %s)" % (name, "/".join(str(d) for d in _dt(kind)), t.dtype))
+    dts = _DT[kind] if _DT is not None else _dt(kind)
+    if t.dtype not in dts:
+        raise KvqError(KVQ_ERR_ARG, "%s must be %s (got %s)" % (name, "/".join(str(d) for d in dts), t.dtype))
     if ndim is not None and t.dim() != ndim:
         raise KvqError(KVQ_ERR_SHAPE, "%s must have %d dimensions (got shape %s)" % (name, ndim, tuple(t.shape)))
     if numel is not None and t.numel() < numel:
@@ -132,7 +146,7 @@ def _need(t, name, kind, numel=None, ndim=None):
 
 
 def _same(a, b, what):
-    if a is not None and b is not None and tuple(a.shape) != tuple(b.shape):
+    if a is not None and b is not None and a.shape != b.shape:
         raise KvqError(KVQ_ERR_SHAPE, "%s shapes differ: %s vs %s" % (what, tuple(a.shape), tuple(b.shape)))
 
 
@@ -374,7 +388,7 @@ def _nuq_check(keys, values, bits, key_levels, key_thresh, value_levels, k_codes
     if keys is None or values is None:
         raise KvqError(KVQ_ERR_NULL, "keys and values are required")
     _same(keys, values, "keys and values")
-    BH, S, D = (int(x) for x in keys.shape)
+    BH, S, D = keys.shape
     L = 1 << bits if 1 <= bits <= 4 else 0
     _need(key_levels, "key_levels", "f32", BH * D * L)
     _need(key_thresh, "key_thresh", "f16", BH * D)
@@ -388,8 +402,10 @@ def _nuq_check(keys, values, bits, key_levels, key_thresh, value_levels, k_codes
     _need(out_counts, "out_counts", "i64", 2)
     _need(k_recon, "k_recon", "f16", BH * S * D)
     _need(v_recon, "v_recon", "f16", BH * S * D)
-    out_cap = min(int(t.numel()) for t in (k_opos, k_oval, v_opos, v_oval) if t is not None) \
-        if all(t is not None for t in (k_opos, k_oval, v_opos, v_oval)) else 0
+    if k_opos is None or k_oval is None or v_opos is None or v_oval is None:
+        out_cap = 0
+    else:
+        out_cap = min(k_opos.numel(), k_oval.numel(), v_opos.numel(), v_oval.numel())
     return BH, S, D, out_cap
 
 
