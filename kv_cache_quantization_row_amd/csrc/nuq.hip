@@ -37,11 +37,17 @@
 // Keys at prefill: a counting sort of each channel's samples by the high byte
 // of their order key, then every query of the fit is a table read plus one
 // bucket scan (the "bucketed key fit" section below); sums there are int64.
+// Up to 4,096 vectors the value fit runs one token per wave instead
+// (value_wave_body: keys sorted across the wave, sorted keys and exact
+// prefix sums in the wave's LDS, one level per lane).
 // Codes are #{j : x > T_j}, which equals the first index of the nearest
-// level. The side channel (flat index, fp16 value) is emitted in ascending
-// flat order: each workgroup reserves a staging range with one atomic and
-// adds its count to a per-64-workgroup sum; one placement kernel then puts
-// every workgroup's entries at the sum of the counts before it (no
+// level (a binary search over the sorted cut keys, two samples per packed
+// step). The side channel (flat index, fp16 value) is emitted in ascending
+// flat order: each producer workgroup stages its entries (value workgroups
+// at fixed ranges, k_val slots per token; key workgroups in a range reserved
+// with one atomic, or at the flat index of their first element in a small
+// call) and records its count; the placement kernel puts every workgroup's
+// entries at the sum of the counts before it (per-64-workgroup sums; no
 // inter-workgroup waiting).
 #include <mutex>
 

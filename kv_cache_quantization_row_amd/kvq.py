@@ -186,14 +186,21 @@ def layout(layers, num_pages, page_size, kv_heads, head_dim, bits) -> PagedLayou
     return PagedLayout(layers, num_pages, page_size, kv_heads, head_dim, bits)
 
 
+_PD = {}
+
+
 def _pools(lay, k_codes, k_scales, v_codes, v_scales):
-    pd = kvq_packed_dim(lay.head_dim, lay.bits)
+    key = (lay.head_dim, lay.bits)
+    pd = _PD.get(key)
+    if pd is None:  # a pure function of (head_dim, bits): asked once
+        pd = _PD[key] = kvq_packed_dim(*key)
     if pd <= 0:
         raise KvqError(KVQ_ERR_SHAPE, "head_dim %d is not valid for q%d" % (lay.head_dim, lay.bits))
     rows = lay.layers * lay.num_pages * lay.page_size * lay.kv_heads
-    for c, sc, side in ((k_codes, k_scales, "k"), (v_codes, v_scales, "v")):
-        _need(c, side + "_codes", "u8", rows * pd)
-        _need(sc, side + "_scales", "f16", rows)
+    _need(k_codes, "k_codes", "u8", rows * pd)
+    _need(k_scales, "k_scales", "f16", rows)
+    _need(v_codes, "v_codes", "u8", rows * pd)
+    _need(v_scales, "v_scales", "f16", rows)
 
 
 def kvq_quant_sym(lay: PagedLayout, k, v, slot_mapping, k_codes, k_scales, v_codes, v_scales,
@@ -203,9 +210,9 @@ def kvq_quant_sym(lay: PagedLayout, k, v, slot_mapping, k_codes, k_scales, v_cod
     if x is None:
         raise KvqError(KVQ_ERR_NULL, "neither k nor v given")
     _same(k, v, "k and v")
-    for t, name in ((k, "k"), (v, "v")):
-        _need(t, name, "f16", ndim=4)
-    if tuple(x.shape[2:]) != (lay.kv_heads, lay.head_dim):
+    _need(k, "k", "f16", ndim=4)
+    _need(v, "v", "f16", ndim=4)
+    if x.shape[2:] != (lay.kv_heads, lay.head_dim):
         raise KvqError(KVQ_ERR_SHAPE, "inputs are [n_layers][n_tokens][%d][%d], got %s" %
                        (lay.kv_heads, lay.head_dim, tuple(x.shape)))
     n_layers, n_tokens = int(x.shape[0]), int(x.shape[1])
@@ -231,9 +238,9 @@ def kvq_dequant_sym(lay: PagedLayout, k_codes, k_scales, v_codes, v_scales, bloc
     if o is None:
         raise KvqError(KVQ_ERR_NULL, "neither k_out nor v_out given")
     _same(k_out, v_out, "k_out and v_out")
-    for t, name in ((k_out, "k_out"), (v_out, "v_out")):
-        _need(t, name, "f16", ndim=5)
-    if tuple(o.shape[3:]) != (lay.kv_heads, lay.head_dim):
+    _need(k_out, "k_out", "f16", ndim=5)
+    _need(v_out, "v_out", "f16", ndim=5)
+    if o.shape[3:] != (lay.kv_heads, lay.head_dim):
         raise KvqError(KVQ_ERR_SHAPE, "outputs are [n_layers][n_seqs][max_len][%d][%d], got %s" %
                        (lay.kv_heads, lay.head_dim, tuple(o.shape)))
     n_layers, n_seqs, max_len = int(o.shape[0]), int(o.shape[1]), int(o.shape[2])

@@ -171,14 +171,13 @@ def test_degenerate_data(case, BH):
         compare(g, r, what="%s frac=%g iters=%d" % (case, frac, iters))
 
 
-# key fits whose lanes per channel reach the level count run on one merged,
-# globally sorted sequence per channel: every width at several lane counts,
-# n = 4096 (no padding: the prefix sum at the very end), and the degenerate
-# data of the test above at merged sizes
+# many-token key fits (the bucketed counting sort per channel): every width
+# at several lengths, n = 4096 and 8192 (the whole sample array in LDS),
+# and the degenerate data of the test above at these sizes
 @pytest.mark.parametrize("S,bits", [(400, 2), (600, 1), (600, 2), (1100, 3), (1100, 4), (2500, 4), (4100, 3),
                                     (4100, 2), (8196, 4)])
-def test_merged_key_fit(S, bits):
-    say("nuq merged key fit", S, bits)
+def test_long_key_fits(S, bits):
+    say("nuq long key fit", S, bits)
     BH, D = 2, 32
     k, v = t4((BH, S, D), 80 + S + bits), t4((BH, S, D), 90 + S + bits)
     for frac in (0.01, 0.1):
@@ -189,8 +188,8 @@ def test_merged_key_fit(S, bits):
 
 
 @pytest.mark.parametrize("D,S,BH", [(64, 1500, 3), (128, 1500, 3), (256, 1500, 3), (64, 4100, 2), (256, 8196, 1)])
-def test_merged_key_fit_head_dims(D, S, BH):
-    say("nuq merged key fit D S", D, S)
+def test_long_key_fit_head_dims(D, S, BH):
+    say("nuq long key fit D S", D, S)
     bits = 3
     k, v = t4((BH, S, D), 300 + D + S), t4((BH, S, D), 301 + D + S)
     g = gpu_nuq(k, v, 0, bits, 0.01, 8, 4, 1, want_recon=S < 8000)
@@ -201,8 +200,8 @@ def test_merged_key_fit_head_dims(D, S, BH):
 
 @pytest.mark.parametrize("S,bits", [(1028, 2), (2100, 3)])
 @pytest.mark.parametrize("case", ["ties", "zeros", "signed_zeros", "extremes", "subnormal", "const"])
-def test_merged_key_fit_degenerate(case, S, bits):
-    say("nuq merged degenerate", case, S, bits)
+def test_long_key_fit_degenerate(case, S, bits):
+    say("nuq long key fit degenerate", case, S, bits)
     BH, D = 2, 32
     rng = np.random.default_rng(100 + ["ties", "zeros", "signed_zeros", "extremes", "subnormal", "const"].index(case))
     if case == "ties":
