@@ -150,45 +150,67 @@ __device__ __forceinline__ uint32_t pick_lev16(const uint32_t *LH, uint32_t code
   }
 }
 
+// #{keys <= t} among 8 keys (16 bytes), t repeated in both halves of t2
+__device__ __forceinline__ int count_le8(const uint4 &w, uint32_t t2) {
+  const uint32_t g = pk_gt01(w.x, t2) + pk_gt01(w.y, t2) + pk_gt01(w.z, t2) + pk_gt01(w.w, t2);
+  return 8 - (int)((g & 0xffffu) + (g >> 16));
+}
+// #{i < N : key[i] <= t} over the wave's N ascending keys: a count over the
+// last keys of the runs of 8 gives the number of runs wholly <= t, a count
+// inside the next run finishes (two rounds of 16-byte LDS reads)
+template <int N>
+__device__ __forceinline__ int lds_upper(const uint16_t *key, const uint16_t *last8, uint32_t t) {
+  const uint32_t t2 = t * 0x10001u;
+  int r = 0;
+#pragma unroll
+  for (int q = 0; q < N / 64; ++q) r += count_le8(*reinterpret_cast<const uint4 *>(last8 + 8 * q), t2);
+  if (r == N / 8) return N;
+  return 8 * r + count_le8(*reinterpret_cast<const uint4 *>(key + 8 * r), t2);
+}
+
 // ----------------------------------------------------------------- sorting
 __device__ __forceinline__ void ce(uint32_t &a, uint32_t &b) {
   const u16x2v x = __builtin_bit_cast(u16x2v, a), y = __builtin_bit_cast(u16x2v, b);
   a = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(x, y));
   b = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(x, y));
 }
-// element i of the chunk lives in register i % 64, half i / 64
-template <int K>
-__device__ __forceinline__ void flip(uint32_t *v) {
+// A lane's NR packed registers hold 2*NR keys: element i in register i % NR,
+// half i / NR. Bitonic sort with mirrored ("flip") stages, all ascending.
+template <int NR, int K>
+__device__ __forceinline__ void flip_r(uint32_t *v) {  // i <-> i ^ (K-1) inside one half (K <= NR)
 #pragma unroll
-  for (int r = 0; r < 64; ++r) {
+  for (int r = 0; r < NR; ++r) {
     const int p = r ^ (K - 1);
     if (p > r) ce(v[r], v[p]);
   }
 }
-template <int J>
-__device__ __forceinline__ void disperse(uint32_t *v) {
+template <int NR, int J>
+__device__ __forceinline__ void disp_r(uint32_t *v) {  // i <-> i ^ J inside one half (J < NR)
 #pragma unroll
-  for (int r = 0; r < 64; ++r) {
+  for (int r = 0; r < NR; ++r) {
     const int p = r ^ J;
     if (p > r) ce(v[r], v[p]);
   }
 }
-template <int K>
-__device__ __forceinline__ void merge(uint32_t *v) {
-  flip<K>(v);
-  if constexpr (K / 4 >= 32) disperse<32>(v);
-  if constexpr (K / 4 >= 16) disperse<16>(v);
-  if constexpr (K / 4 >= 8) disperse<8>(v);
-  if constexpr (K / 4 >= 4) disperse<4>(v);
-  if constexpr (K / 4 >= 2) disperse<2>(v);
-  if constexpr (K / 4 >= 1) disperse<1>(v);
+template <int NR, int J>
+__device__ __forceinline__ void disp_down(uint32_t *v) {  // distances J, J/2, ..., 1
+  if constexpr (J >= 1) {
+    disp_r<NR, J>(v);
+    disp_down<NR, J / 2>(v);
+  }
 }
-// the K = 128 flip pairs element r with 127 - r: low half of register r with
-// the high half of register 63 - r, and vice versa
-__device__ __forceinline__ void flip128(uint32_t *v) {
+template <int NR, int K>
+__device__ __forceinline__ void merge_r(uint32_t *v) {
+  flip_r<NR, K>(v);
+  disp_down<NR, K / 4>(v);
+}
+// the flip across the halves: element r of half 0 with element 2NR-1-r,
+// the high half of register NR-1-r (and vice versa)
+template <int NR>
+__device__ __forceinline__ void flip_halves(uint32_t *v) {
 #pragma unroll
-  for (int r = 0; r < 32; ++r) {
-    const int p = 63 - r;
+  for (int r = 0; r < NR / 2; ++r) {
+    const int p = NR - 1 - r;
     const u16x2v a = __builtin_bit_cast(u16x2v, v[r]);
     const u16x2v b = __builtin_bit_cast(u16x2v, v[p]);
     const u16x2v bs = {b.y, b.x};
@@ -197,21 +219,20 @@ __device__ __forceinline__ void flip128(uint32_t *v) {
     v[p] = (uint32_t)mn.y | ((uint32_t)mx.x << 16);
   }
 }
-__device__ __forceinline__ void sort128(uint32_t *v) {
-  merge<2>(v);
-  merge<4>(v);
-  merge<8>(v);
-  merge<16>(v);
-  merge<32>(v);
-  merge<64>(v);
-  flip128(v);
-  disperse<32>(v);
-  disperse<16>(v);
-  disperse<8>(v);
-  disperse<4>(v);
-  disperse<2>(v);
-  disperse<1>(v);
+template <int NR, int K>
+__device__ __forceinline__ void merges_up(uint32_t *v) {  // merge levels K, 2K, ..., NR
+  if constexpr (K <= NR) {
+    merge_r<NR, K>(v);
+    merges_up<NR, 2 * K>(v);
+  }
 }
+template <int NR>
+__device__ __forceinline__ void sort_regs(uint32_t *v) {  // all 2*NR keys ascending
+  merges_up<NR, 2>(v);
+  flip_halves<NR>(v);
+  disp_down<NR, NR / 2>(v);
+}
+__device__ __forceinline__ void sort128(uint32_t *v) { sort_regs<64>(v); }
 
 // ----------------------------------------------------------------- sorted chunk in LDS
 // 64 words per lane; word r holds keys of elements r and 64 + r; the word
@@ -1360,6 +1381,400 @@ __global__ __launch_bounds__(64) void nuq_value(NuqArgs a) {
   }
 }
 
+// ================================================================== one token per quad (D = 128)
+// Many-token value fit at D = 128: four lanes per token (a DPP quad), 32
+// channels per lane, 16 tokens per wave, 64 per workgroup. The quad sorts
+// the token's 128 keys (each lane its 32 in registers, then two cross-lane
+// bitonic merge levels with quad permutes) and keeps, per token in LDS, the
+// sorted keys, the last key of every run of 8 and the exact prefix sums at
+// every 4th position. Every query of the fit is then a fixed-cost LDS
+// lookup, with no per-lane walks: a cut's position is two rounds of 16-byte
+// reads (run ends, then one run), the exact sum below it one table entry
+// plus at most 3 samples. Lane q holds levels LPL*q .. LPL*q + LPL-1 and the
+// cuts above them; neighbours come by quad permutes. The arithmetic is the
+// same as in nuq_value.
+constexpr int QPERM_REV = 0x1b;    // quad_perm [3,2,1,0]
+constexpr int QPERM_NEXT = 0xf9;   // [1,2,3,3]: lane q reads q+1 (lane 3 itself)
+constexpr int QPERM_PREV = 0x90;   // [0,0,1,2]: lane q reads q-1 (lane 0 itself)
+
+struct alignas(16) QuadLds {
+  uint16_t key[128];   // the token's order keys, ascending
+  uint16_t last8[16];  // last8[r] = key[8r + 7]
+  double pre4[33];     // pre4[i]: exact sum of the 4i smallest samples
+};
+
+template <int CTRL>
+__device__ __forceinline__ double dppd_q(double v) {  // a quad permute of a double
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  return __builtin_bit_cast(double, (uint64_t)dppm<CTRL>((uint32_t)b) | ((uint64_t)dppm<CTRL>((uint32_t)(b >> 32)) << 32));
+}
+__device__ __forceinline__ uint32_t qbcast(uint32_t v, int src) {  // value of quad lane src (uniform src)
+  switch (src) {
+    case 0: return dppm<0x00>(v);
+    case 1: return dppm<0x55>(v);
+    case 2: return dppm<0xaa>(v);
+    default: return dppm<0xff>(v);
+  }
+}
+// cross-lane bitonic flip: element p of this lane against element 31-p of
+// the partner (register 15-r, halves swapped); the lower lane keeps minima
+template <int CTRL>
+__device__ __forceinline__ void qflip(uint32_t *v, bool lower) {
+  uint32_t o[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const uint32_t x = dppm<CTRL>(v[15 - r]);
+    o[r] = __builtin_amdgcn_alignbit(x, x, 16);
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const u16x2v a = __builtin_bit_cast(u16x2v, v[r]), b = __builtin_bit_cast(u16x2v, o[r]);
+    v[r] = lower ? __builtin_bit_cast(uint32_t, __builtin_elementwise_min(a, b))
+                 : __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
+  }
+}
+// cross-lane disperse: the same element of the partner lane
+template <int CTRL>
+__device__ __forceinline__ void qdisp(uint32_t *v, bool lower) {
+  uint32_t o[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) o[r] = dppm<CTRL>(v[r]);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const u16x2v a = __builtin_bit_cast(u16x2v, v[r]), b = __builtin_bit_cast(u16x2v, o[r]);
+    v[r] = lower ? __builtin_bit_cast(uint32_t, __builtin_elementwise_min(a, b))
+                 : __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
+  }
+}
+// element p <-> p + 16: the two halves of each register
+__device__ __forceinline__ void half_ce16(uint32_t *v) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const uint32_t lo = v[r] & 0xffffu, hi = v[r] >> 16;
+    v[r] = min(lo, hi) | (max(lo, hi) << 16);
+  }
+}
+// exact sum of the c smallest samples of the token
+__device__ __forceinline__ double quad_pref(const QuadLds &ql, int c) {
+  double s_ = ql.pre4[c >> 2];
+  const int n = c & 3;
+  const uint2 w = *reinterpret_cast<const uint2 *>(ql.key + min(c & ~3, 124));
+  const double a0 = kval(w.x & 0xffffu), a1 = kval(w.x >> 16), a2 = kval(w.y & 0xffffu);
+  s_ = n > 0 ? s_ + a0 : s_;
+  s_ = n > 1 ? s_ + a1 : s_;
+  s_ = n > 2 ? s_ + a2 : s_;
+  return s_;
+}
+
+// lane q's cut keys from its levels (slots s: level LPL*q + s): cut j lies
+// between levels j and j+1; equal neighbours take the cut above (the first
+// copy wins ties); the last cut and slots past it hold 0xffff
+template <int L, int LPL>
+__device__ __forceinline__ void quad_cut_keys(const float *lev, int q, uint32_t *t) {
+  const float inf = __builtin_inff();
+  const float nx0 = __uint_as_float(dppm<QPERM_NEXT>(__float_as_uint(lev[0])));
+#pragma unroll
+  for (int s_ = 0; s_ < LPL; ++s_) {
+    const int j = LPL * q + s_;
+    const float up = s_ + 1 < LPL ? lev[s_ + 1] : (q < 3 ? nx0 : inf);
+    t[s_] = j < L - 1 ? (lev[s_] < up ? key16(thr16(lev[s_], up)) : 0u) : 0xffffu;
+  }
+  // a 0 takes the first nonzero cut above it: inside the lane, then across
+  // lanes (each move runs in every lane before the select)
+#pragma unroll
+  for (int s_ = LPL - 2; s_ >= 0; --s_) t[s_] = t[s_] ? t[s_] : t[s_ + 1];
+#pragma unroll
+  for (int step = 0; step < 3; ++step) {
+    uint32_t nx = dppm<QPERM_NEXT>(t[0]);
+    nx = q < 3 ? nx : 0xffffu;
+    t[LPL - 1] = t[LPL - 1] ? t[LPL - 1] : nx;
+#pragma unroll
+    for (int s_ = LPL - 2; s_ >= 0; --s_) t[s_] = t[s_] ? t[s_] : t[s_ + 1];
+  }
+}
+
+// odd-even transposition over the L levels held LPL per lane (slots past
+// L hold +inf); the same network as sort_levels
+template <int L, int LPL>
+__device__ __forceinline__ void quad_sort_levels(float *lev, int q) {
+  const float inf = __builtin_inff();
+#pragma unroll
+  for (int ph = 0; ph < L; ++ph) {
+    if constexpr (LPL == 1) {
+      if ((ph & 1) == 0) {  // pairs (0,1), (2,3): lane q with q ^ 1
+        const float o = __uint_as_float(dppm<DPP_XOR1>(__float_as_uint(lev[0])));
+        lev[0] = (q & 1) ? fmaxf(lev[0], o) : fminf(lev[0], o);
+      } else {              // pair (1,2): lanes 1 and 2
+        const float up = __uint_as_float(dppm<QPERM_NEXT>(__float_as_uint(lev[0])));
+        const float dn = __uint_as_float(dppm<QPERM_PREV>(__float_as_uint(lev[0])));
+        if (q == 1) lev[0] = fminf(lev[0], up);
+        if (q == 2) lev[0] = fmaxf(lev[0], dn);
+      }
+    } else {
+      if ((ph & 1) == 0) {  // pairs inside the lane: (0,1), (2,3), ...
+#pragma unroll
+        for (int s_ = 0; s_ + 1 < LPL; s_ += 2) {
+          const float x = lev[s_], y = lev[s_ + 1];
+          lev[s_] = fminf(x, y);
+          lev[s_ + 1] = fmaxf(x, y);
+        }
+      } else {              // (1,2), ... inside the lane; (LPL-1, LPL) across lanes
+        const float up = __uint_as_float(dppm<QPERM_NEXT>(__float_as_uint(lev[0])));
+        const float dn = __uint_as_float(dppm<QPERM_PREV>(__float_as_uint(lev[LPL - 1])));
+#pragma unroll
+        for (int s_ = 1; s_ + 1 < LPL; s_ += 2) {
+          const float x = lev[s_], y = lev[s_ + 1];
+          lev[s_] = fminf(x, y);
+          lev[s_ + 1] = fmaxf(x, y);
+        }
+        if (q < 3) lev[LPL - 1] = fminf(lev[LPL - 1], up);
+        if (q > 0) lev[0] = fmaxf(lev[0], dn);
+        (void)inf;
+      }
+    }
+  }
+}
+
+template <int BITS>
+__global__ __launch_bounds__(256) void nuq_value_quad(NuqArgs a) {
+  constexpr int L = 1 << BITS;
+  constexpr int LPL = L >= 4 ? L / 4 : 1;  // levels per lane
+  constexpr int D = 128;
+  __shared__ QuadLds qls[64];
+  __shared__ uint32_t wtot[4];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int q = lane & 3, tq = threadIdx.x >> 2;  // quarter; token within the workgroup
+  QuadLds &ql = qls[tq];
+  const int64_t tok = (int64_t)blockIdx.x * 64 + tq;
+  const int64_t ntok = (int64_t)a.BH * a.S;
+  const bool valid = tok < ntok;
+  const int s_pos = valid ? (int)(tok % a.S) : 0;
+  const bool live = valid && s_pos >= a.n_sink_eff;  // sinks: exact, no fit
+  const uint16_t *row = a.values + (size_t)(valid ? tok : 0) * D + 32 * q;
+  // ---- this lane's 32 channels (element i in word i / 2)
+  uint32_t raw[16];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const uint4 w = valid ? *reinterpret_cast<const uint4 *>(row + 8 * g) : make_uint4(0, 0, 0, 0);
+    raw[4 * g] = w.x; raw[4 * g + 1] = w.y; raw[4 * g + 2] = w.z; raw[4 * g + 3] = w.w;
+  }
+  // ---- sort the token's 128 keys: element p of the lane in register p % 16, half p / 16
+  uint32_t v[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const uint32_t lo = (raw[r / 2] >> (16 * (r & 1))) & 0xffffu;
+    const uint32_t hi = (raw[8 + r / 2] >> (16 * (r & 1))) & 0xffffu;
+    v[r] = key_pair(lo | (hi << 16));
+  }
+  sort_regs<16>(v);
+  qflip<DPP_XOR1>(v, (q & 1) == 0);  // pairs of lanes: 64 keys
+  half_ce16(v);
+  disp_down<16, 8>(v);
+  qflip<QPERM_REV>(v, q < 2);        // the quad: 128 keys
+  qdisp<DPP_XOR1>(v, (q & 1) == 0);
+  half_ce16(v);
+  disp_down<16, 8>(v);
+  // lane q now holds sorted elements 32q .. 32q+31
+  {
+    uint32_t w[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      w[i] = __builtin_amdgcn_perm(v[2 * i + 1], v[2 * i], 0x05040100u);      // positions 2i, 2i+1
+      w[8 + i] = __builtin_amdgcn_perm(v[2 * i + 1], v[2 * i], 0x07060302u);  // positions 16+2i, 17+2i
+    }
+    uint4 *kd = reinterpret_cast<uint4 *>(ql.key + 32 * q);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kd[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+    *reinterpret_cast<uint2 *>(ql.last8 + 4 * q) =
+        make_uint2(__builtin_amdgcn_perm(v[15], v[7], 0x05040100u), __builtin_amdgcn_perm(v[15], v[7], 0x07060302u));
+  }
+  // exact prefix sums every 4th position: group sums of 4, their running
+  // sum in the lane, the lanes below added by quad broadcasts
+  {
+    double g4[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r0 = (4 * j) & 15, h = (4 * j) >> 4;
+      double x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = kval((v[r0 + i] >> (16 * h)) & 0xffffu);
+      g4[j] = (x[0] + x[1]) + (x[2] + x[3]);
+    }
+    double loc[8];
+    loc[0] = 0.0;
+#pragma unroll
+    for (int j = 1; j < 8; ++j) loc[j] = loc[j - 1] + g4[j - 1];
+    const double tot = loc[7] + g4[7];
+    const double t0 = dppd_q<0x00>(tot), t1 = dppd_q<0x55>(tot), t2 = dppd_q<0xaa>(tot);
+    double base = 0.0;
+    base = q > 0 ? base + t0 : base;
+    base = q > 1 ? base + t1 : base;
+    base = q > 2 ? base + t2 : base;
+    double *pd = ql.pre4 + 8 * q;
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) *reinterpret_cast<double2 *>(pd + j) = make_double2(base + loc[j], base + loc[j + 1]);
+    if (q == 3) ql.pre4[32] = base + tot;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  // ---- tau: the (k+1)-th largest |x| (k = floor(frac * D), computed on the host):
+  // the largest min(front_a, back_(k+1-a)) over the splits of the sorted ends
+  uint32_t nneg2 = 0;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) nneg2 += pk_gt01(0x80008000u, v[r]);  // keys below 0x8000: x < 0 or x = -0
+  uint32_t nneg = (nneg2 & 0xffffu) + (nneg2 >> 16);
+  nneg += dppm<DPP_XOR1>(nneg);
+  nneg += dppm<DPP_XOR2>(nneg);
+  const int kp1 = a.k_val + 1;
+  uint32_t best = 0;
+  for (int a0 = 0; a0 <= kp1; a0 += 4) {
+    const int fa = a0 + q, fb = kp1 - fa;
+    if (fa <= kp1 && fa <= (int)nneg && fb <= D - (int)nneg) {
+      const uint32_t af = fa > 0 ? unkey16(ql.key[fa - 1]) & 0x7fffu : 0x8000u;
+      const uint32_t ab = fb > 0 ? unkey16(ql.key[D - fb]) & 0x7fffu : 0x8000u;
+      best = max(best, min(af, ab));
+    }
+  }
+  best = max(best, dppm<DPP_XOR1>(best));
+  best = max(best, dppm<DPP_XOR2>(best));
+  const uint32_t tau = min(best, 0x7bffu);
+  const uint32_t klo = tau == 0 ? key16(0x8000u) : key16(tau | 0x8000u);
+  const int lo = lds_upper<D>(ql.key, ql.last8, klo - 1), hi = lds_upper<D>(ql.key, ql.last8, key16(tau));
+  const int m = hi - lo;
+  // ---- quantile initialisation: level j interpolates between the r-th and
+  // (r+1)-th smallest inliers, r + f = (j + 1/2)(m - 1)/L
+  const float inf = __builtin_inff();
+  float lev[LPL];
+#pragma unroll
+  for (int s_ = 0; s_ < LPL; ++s_) {
+    const int j = LPL * q + s_;
+    lev[s_] = inf;
+    if (j < L) {
+      const long long num = (long long)(2 * j + 1) * (long long)(m - 1);
+      const int r = (int)(num / (2 * L));
+      const int rem = (int)(num % (2 * L));
+      double val = kval(ql.key[lo + r]);
+      if (rem != 0) val = val + ((double)rem / (double)(2 * L)) * (kval(ql.key[lo + r + 1]) - val);
+      lev[s_] = (float)val + 0.0f;
+    }
+  }
+  const double p_lo = quad_pref(ql, lo), p_hi = quad_pref(ql, hi);
+  // ---- Lloyd iterations
+  uint32_t t[LPL];
+  for (int it = 0; it < a.iters; ++it) {
+    quad_cut_keys<L, LPL>(lev, q, t);
+    int cut[LPL];
+    double pc[LPL];
+#pragma unroll
+    for (int s_ = 0; s_ < LPL; ++s_) {
+      const int j = LPL * q + s_;
+      cut[s_] = hi;
+      pc[s_] = p_hi;
+      if (j < L - 1) {
+        cut[s_] = min(max(lds_upper<D>(ql.key, ql.last8, t[s_]), lo), hi);
+        pc[s_] = quad_pref(ql, cut[s_]);
+      }
+    }
+    // the cell of slot 0 starts at the previous lane's last cut (lane 0: lo)
+    int cb = (int)dppm<QPERM_PREV>((uint32_t)cut[LPL - 1]);
+    double pb = dppd_q<QPERM_PREV>(pc[LPL - 1]);
+    cb = q > 0 ? cb : lo;
+    pb = q > 0 ? pb : p_lo;
+#pragma unroll
+    for (int s_ = 0; s_ < LPL; ++s_) {
+      const int j = LPL * q + s_;
+      const int cnt = cut[s_] - cb;
+      if (j < L && cnt > 0) lev[s_] = (float)((pc[s_] - pb) / (double)cnt);
+      cb = cut[s_];
+      pb = pc[s_];
+    }
+    // an empty duplicate keeps its level while its twin moves: keep the table ordered
+    quad_sort_levels<L, LPL>(lev, q);
+  }
+  // ---- codes, reconstruction, level row
+  quad_cut_keys<L, LPL>(lev, q, t);
+  uint32_t T2[L - 1];
+#pragma unroll
+  for (int j = 0; j < L - 1; ++j) T2[j] = live ? qbcast(t[j % LPL], j / LPL) * 0x10001u : 0xffffffffu;
+  uint32_t LH[L / 2];
+#pragma unroll
+  for (int i = 0; i < L / 2; ++i) {
+    const float l0 = __uint_as_float(qbcast(__float_as_uint(lev[(2 * i) % LPL]), (2 * i) / LPL));
+    const float l1 = __uint_as_float(qbcast(__float_as_uint(lev[(2 * i + 1) % LPL]), (2 * i + 1) / LPL));
+    LH[i] = (uint32_t)f2h(l0) | ((uint32_t)f2h(l1) << 16);
+  }
+  if (valid) {
+#pragma unroll
+    for (int s_ = 0; s_ < LPL; ++s_) {
+      const int j = LPL * q + s_;
+      if (j < L) a.value_levels[(size_t)tok * L + j] = live ? lev[s_] : 0.0f;
+    }
+  }
+  const uint32_t tau2 = (live ? tau : 0x7fffu) * 0x10001u;
+  const uint32_t keep_in = live ? 0u : 0xffffffffu;
+  const bool want_rec = valid && a.v_recon != nullptr;
+  uint32_t ob[BITS + 1], om = 0, onum = 0;
+#pragma unroll
+  for (int i = 0; i <= BITS; ++i) ob[i] = 0;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    uint32_t rec[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int e = g * 8 + 2 * w;  // channel (within the lane) of the low half
+      const uint32_t x = raw[4 * g + w];
+      const uint32_t o = pk_gt01(x & 0x7fff7fffu, tau2);
+      onum += o;
+      om |= ((o & 1u) | (o >> 15)) << e;
+      const uint32_t omask = pk_mask01(o);
+      const uint32_t code = code_pair<BITS>(key_pair(x), T2) & ~omask;
+      const uint32_t pcw = (code & 0xffffu) | (code >> (16 - BITS));
+      const int bit = e * BITS;
+      ob[bit / 32] |= pcw << (bit % 32);
+      if (bit % 32 + 2 * BITS > 32) ob[bit / 32 + 1] |= pcw >> (32 - bit % 32);
+      rec[w] = bsel(omask | keep_in, x, pick_lev16<L>(LH, code));
+    }
+    if (want_rec)
+      *reinterpret_cast<uint4 *>(a.v_recon + (size_t)tok * D + 32 * q + 8 * g) = make_uint4(rec[0], rec[1], rec[2], rec[3]);
+  }
+  if (valid) {
+    uint32_t *crow = reinterpret_cast<uint32_t *>(a.v_codes + (size_t)tok * (D * BITS / 8)) + q * BITS;
+#pragma unroll
+    for (int j = 0; j < BITS; ++j) crow[j] = ob[j];
+  }
+  // ---- side channel in flat order (lanes are in flat order): the
+  // workgroup's fixed staging range holds k_val slots per token
+  const int nout = (int)((onum & 0xffffu) + (onum >> 16));
+  const uint32_t incl = kb_wscan((uint32_t)nout);
+  if (lane == 63) wtot[wv] = incl;
+  __syncthreads();
+  uint32_t before = 0, btot = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    before += i < wv ? wtot[i] : 0u;
+    btot += wtot[i];
+  }
+  const int64_t base = (int64_t)blockIdx.x * 64 * a.k_val;
+  if (threadIdx.x == 0) {
+    if (btot) atomicAdd(&a.ws_vsup[blockIdx.x >> 6], btot);
+    a.ws_vblk[blockIdx.x * 2] = (uint32_t)base;
+    a.ws_vblk[blockIdx.x * 2 + 1] = btot;
+  }
+  if (nout) {
+    int64_t slot = base + before + incl - (uint32_t)nout;
+    uint32_t mm = om;
+    while (mm) {
+      const int b = __builtin_ctz(mm);
+      mm &= mm - 1;
+      if (slot < a.v_scap) {
+        a.ws_vpos[slot] = (int32_t)((size_t)tok * D + 32 * q + b);
+        a.ws_vval[slot] = (uint16_t)(raw[b >> 1] >> (16 * (b & 1)));
+      }
+      ++slot;
+    }
+  }
+}
+
 // Value fit + quantize for few tokens (decode steps, short chunks): one wave
 // per token, channel l*E + e in lane l (E = max(1, D/64)). The token's keys
 // are sorted across the wave (bitonic network on packed 16-bit keys, sorted
@@ -1443,23 +1858,6 @@ struct alignas(16) WaveLds {
   uint8_t cb[256];     // one code per channel
 };
 
-// #{keys <= t} among 8 keys (16 bytes), t repeated in both halves of t2
-__device__ __forceinline__ int count_le8(const uint4 &w, uint32_t t2) {
-  const uint32_t g = pk_gt01(w.x, t2) + pk_gt01(w.y, t2) + pk_gt01(w.z, t2) + pk_gt01(w.w, t2);
-  return 8 - (int)((g & 0xffffu) + (g >> 16));
-}
-// #{i < N : key[i] <= t} over the wave's N ascending keys: a count over the
-// last keys of the runs of 8 gives the number of runs wholly <= t, a count
-// inside the next run finishes (two rounds of 16-byte LDS reads)
-template <int N>
-__device__ __forceinline__ int lds_upper(const WaveLds &wl, uint32_t t) {
-  const uint32_t t2 = t * 0x10001u;
-  int r = 0;
-#pragma unroll
-  for (int q = 0; q < N / 64; ++q) r += count_le8(*reinterpret_cast<const uint4 *>(wl.last8 + 8 * q), t2);
-  if (r == N / 8) return N;
-  return 8 * r + count_le8(*reinterpret_cast<const uint4 *>(wl.key + 8 * r), t2);
-}
 
 // lane j < L-1: cut key j between levels j and j+1 of the lane-distributed
 // table (lane j holds level j, lanes >= L hold +inf); equal neighbours take
@@ -1599,7 +1997,7 @@ __device__ __forceinline__ void value_wave_body(const NuqArgs &a, int64_t tok, b
       int cut = hi;
       double pc = p_hi;
       if (lane < L - 1) {
-        cut = min(max(lds_upper<N>(wl, t), lo), hi);
+        cut = min(max(lds_upper<N>(wl.key, wl.last8, t), lo), hi);
         pc = wl.pre[cut];
       }
       // cell q = (cut q-1, cut q]; lane 0 starts at lo
@@ -1964,6 +2362,8 @@ hipError_t launch_values(const NuqArgs &a, int val_cpc, hipStream_t st) {
       hipLaunchKernelGGL((nuq_value_wave<2, BITS>), dim3((unsigned)a.v_nblk), dim3(64), 0, st, a);
     else
       hipLaunchKernelGGL((nuq_value_wave<4, BITS>), dim3((unsigned)a.v_nblk), dim3(64), 0, st, a);
+  } else if (val_cpc == 1 && a.D == 128) {  // one token per quad of lanes
+    hipLaunchKernelGGL((nuq_value_quad<BITS>), dim3((unsigned)a.v_nblk), dim3(256), 0, st, a);
   } else if (val_cpc == 1) {
     hipLaunchKernelGGL((nuq_value<1, BITS>), dim3((unsigned)a.v_nblk), dim3(64), 0, st, a);
   } else {
