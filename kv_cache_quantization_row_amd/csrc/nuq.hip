@@ -340,6 +340,12 @@ __device__ __forceinline__ void cut_keys(const float *lev, uint32_t *T) {
   }
 }
 
+// min / max of two levels by compare and select: level tables hold no NaN
+// and no -0 (a mean is +0 when its sum is 0, sentinels are +-inf), where
+// these equal fminf / fmaxf without the NaN-quieting instructions
+__device__ __forceinline__ float lmin(float x, float y) { return y < x ? y : x; }
+__device__ __forceinline__ float lmax(float x, float y) { return y > x ? y : x; }
+
 // ascending order of the level table after an update (odd-even transposition)
 template <int L>
 __device__ __forceinline__ void sort_levels(float *lev) {
@@ -348,8 +354,8 @@ __device__ __forceinline__ void sort_levels(float *lev) {
 #pragma unroll
     for (int i = p & 1; i + 1 < L; i += 2) {
       const float x = lev[i], y = lev[i + 1];
-      lev[i] = fminf(x, y);
-      lev[i + 1] = fmaxf(x, y);
+      lev[i] = lmin(x, y);
+      lev[i + 1] = lmax(x, y);
     }
   }
 }
@@ -711,14 +717,16 @@ __device__ __forceinline__ uint32_t kb_wscan(uint32_t x) {
   return x;
 }
 
-// wave-uniform sum: DPP inside the rows, then the four row totals
+// wave-uniform sum: DPP inside the rows, the row totals carried by row
+// broadcasts into lane 63, one readlane
 __device__ __forceinline__ uint32_t kb_wsum(uint32_t v) {
   v += dppm<DPP_XOR1>(v);
   v += dppm<DPP_XOR2>(v);
   v += dppm<DPP_HALF_MIRROR>(v);
   v += dppm<DPP_MIRROR>(v);
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, 0) + (uint32_t)__builtin_amdgcn_readlane((int)v, 16) +
-         (uint32_t)__builtin_amdgcn_readlane((int)v, 32) + (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  v += kb_dpp<DPP_ROW_BCAST15, 0xa>(v, 0);
+  v += kb_dpp<DPP_ROW_BCAST31, 0xc>(v, 0);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 __device__ __forceinline__ uint32_t kb_rl(uint32_t v, int lane) { return (uint32_t)__builtin_amdgcn_readlane((int)v, lane); }
@@ -755,33 +763,50 @@ struct KbView {
 
 // count and exact sum of the samples with key <= T[j], for every cut j whose
 // bit is set in `need` (T[j] wave-uniform): one interleaved pass over all the
-// cuts' buckets, then one wave sum per count and per low-byte sum
+// cuts' buckets, four key bytes per read (a byte-wise compare in packed 16-bit
+// arithmetic, a byte mask for the bucket's ends, then v_dot4 for the count
+// and the sum of the selected bytes), then one wave sum per count and per
+// low-byte sum
+__device__ __forceinline__ uint32_t kb_le_bytes(uint32_t w, uint32_t t2) {  // 1 in each byte <= t
+  const uint32_t ge = pk_gt01(w & 0x00ff00ffu, t2), go = pk_gt01((w >> 8) & 0x00ff00ffu, t2);
+  return (ge ^ 0x00010001u) | ((go ^ 0x00010001u) << 8);
+}
+template <typename P>
+__device__ __forceinline__ uint32_t kb_word(P dat, uint32_t pos) {  // 4 key bytes at a multiple of 4
+  return *reinterpret_cast<const uint32_t *>(&dat[pos]);
+}
 template <int NC, typename V>
 __device__ __forceinline__ void kb_le_many(const V &v, const uint32_t *T, uint32_t need, uint32_t *cnt,
                                            int64_t *sum) {
   const int lane = threadIdx.x & 63;
-  uint32_t s0[NC], e0[NC], c[NC], sl[NC];
-  uint32_t maxsz = 0;
+  uint32_t s0[NC], e0[NC], c[NC], sl[NC], t2[NC];
+  uint32_t maxw = 0;
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
     c[j] = sl[j] = 0;
     s0[j] = e0[j] = 0;
+    t2[j] = (T[j] & 0xffu) * 0x10001u;
     if ((need >> j) & 1u) {
       const int b = (int)(T[j] >> 8);
       s0[j] = v.start(b);
       e0[j] = v.end[b];
-      maxsz = max(maxsz, e0[j] - s0[j]);
+      if (e0[j] > s0[j]) maxw = max(maxw, ((e0[j] + 3u) >> 2) - (s0[j] >> 2));
     }
   }
-  for (uint32_t i = lane; i < maxsz; i += 64) {
+  // the bucket's words: from the one holding its first byte to the one
+  // holding its last; bytes outside [s0, e0) are masked off
+  for (uint32_t i = lane; i < maxw; i += 64) {
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
-      const uint32_t idx = s0[j] + i;
-      if (idx < e0[j]) {
-        const uint32_t kl = v.dat[idx];
-        const bool p = kl <= (T[j] & 0xffu);
-        c[j] += p ? 1u : 0u;
-        sl[j] += p ? kl : 0u;
+      const uint32_t p0 = ((s0[j] >> 2) + i) << 2;
+      if (p0 < e0[j]) {
+        const uint32_t w = kb_word(v.dat, p0);
+        const uint32_t nb = min(e0[j] - p0, 4u);                      // bytes before the end
+        const uint32_t sk = s0[j] > p0 ? s0[j] - p0 : 0u;             // bytes before the start
+        const uint32_t m = ((nb == 4u ? 0x01010101u : (0x01010101u & ((1u << (8 * nb)) - 1u))) >> (8 * sk)) << (8 * sk);
+        const uint32_t le = kb_le_bytes(w, t2[j]) & m;
+        c[j] = __builtin_amdgcn_udot4(le, 0x01010101u, c[j], false);
+        sl[j] = __builtin_amdgcn_udot4(w, le, sl[j], false);
       }
     }
   }
@@ -1014,11 +1039,11 @@ __device__ void kb_fit(const V &v, uint32_t n, int kout, int iters, float &lev_m
       const uint32_t x = __float_as_uint(nl);
       if ((p & 1) == 0) {  // pairs (0,1), (2,3), ...
         const float o = __uint_as_float(dppm<DPP_XOR1>(x));
-        nl = (lane & 1) ? fmaxf(nl, o) : fminf(nl, o);
+        nl = (lane & 1) ? lmax(nl, o) : lmin(nl, o);
       } else {             // pairs (1,2), (3,4), ...; lane 0 and lane 15 of the row sit out
         const float up = __uint_as_float(kb_dpp<DPP_ROW_SHL1>(x, __float_as_uint(inf)));
         const float dn = __uint_as_float(kb_dpp<DPP_ROW_SHR1>(x, __float_as_uint(-inf)));
-        nl = (lane & 1) ? fminf(nl, up) : fmaxf(nl, dn);
+        nl = (lane & 1) ? lmin(nl, up) : lmax(nl, dn);
       }
     }
     const bool changed = lane < L && __float_as_uint(nl) != __float_as_uint(lev_me);
@@ -1503,20 +1528,20 @@ __device__ __forceinline__ void quad_sort_levels(float *lev, int q) {
     if constexpr (LPL == 1) {
       if ((ph & 1) == 0) {  // pairs (0,1), (2,3): lane q with q ^ 1
         const float o = __uint_as_float(dppm<DPP_XOR1>(__float_as_uint(lev[0])));
-        lev[0] = (q & 1) ? fmaxf(lev[0], o) : fminf(lev[0], o);
+        lev[0] = (q & 1) ? lmax(lev[0], o) : lmin(lev[0], o);
       } else {              // pair (1,2): lanes 1 and 2
         const float up = __uint_as_float(dppm<QPERM_NEXT>(__float_as_uint(lev[0])));
         const float dn = __uint_as_float(dppm<QPERM_PREV>(__float_as_uint(lev[0])));
-        if (q == 1) lev[0] = fminf(lev[0], up);
-        if (q == 2) lev[0] = fmaxf(lev[0], dn);
+        if (q == 1) lev[0] = lmin(lev[0], up);
+        if (q == 2) lev[0] = lmax(lev[0], dn);
       }
     } else {
       if ((ph & 1) == 0) {  // pairs inside the lane: (0,1), (2,3), ...
 #pragma unroll
         for (int s_ = 0; s_ + 1 < LPL; s_ += 2) {
           const float x = lev[s_], y = lev[s_ + 1];
-          lev[s_] = fminf(x, y);
-          lev[s_ + 1] = fmaxf(x, y);
+          lev[s_] = lmin(x, y);
+          lev[s_ + 1] = lmax(x, y);
         }
       } else {              // (1,2), ... inside the lane; (LPL-1, LPL) across lanes
         const float up = __uint_as_float(dppm<QPERM_NEXT>(__float_as_uint(lev[0])));
@@ -1524,11 +1549,11 @@ __device__ __forceinline__ void quad_sort_levels(float *lev, int q) {
 #pragma unroll
         for (int s_ = 1; s_ + 1 < LPL; s_ += 2) {
           const float x = lev[s_], y = lev[s_ + 1];
-          lev[s_] = fminf(x, y);
-          lev[s_ + 1] = fmaxf(x, y);
+          lev[s_] = lmin(x, y);
+          lev[s_ + 1] = lmax(x, y);
         }
-        if (q < 3) lev[LPL - 1] = fminf(lev[LPL - 1], up);
-        if (q > 0) lev[0] = fmaxf(lev[0], dn);
+        if (q < 3) lev[LPL - 1] = lmin(lev[LPL - 1], up);
+        if (q > 0) lev[0] = lmax(lev[0], dn);
         (void)inf;
       }
     }
@@ -2017,11 +2042,11 @@ __device__ __forceinline__ void value_wave_body(const NuqArgs &a, int64_t tok, b
         const uint32_t xb = __float_as_uint(nl);
         if ((ph & 1) == 0) {  // pairs (0,1), (2,3), ...
           const float o = __uint_as_float(dppm<DPP_XOR1>(xb));
-          nl = (lane & 1) ? fmaxf(nl, o) : fminf(nl, o);
+          nl = (lane & 1) ? lmax(nl, o) : lmin(nl, o);
         } else {              // pairs (1,2), (3,4), ...
           const float up = __uint_as_float(kb_dpp<DPP_ROW_SHL1>(xb, __float_as_uint(inf)));
           const float dn = __uint_as_float(kb_dpp<DPP_ROW_SHR1>(xb, __float_as_uint(-inf)));
-          nl = (lane & 1) ? fminf(nl, up) : fmaxf(nl, dn);
+          nl = (lane & 1) ? lmin(nl, up) : lmax(nl, dn);
         }
       }
       lev_me = lane < L ? nl : inf;
