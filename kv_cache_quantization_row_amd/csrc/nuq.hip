@@ -557,17 +557,20 @@ __device__ void fit_vector(const Chunk &c, int nq, int kout, int iters, float *l
     }
     int prev_cut = lo;
     double prev_p = 0.0;
+    bool empty = false;
 #pragma unroll
     for (int q = 0; q < L; ++q) {
       const int cnt = gsum<CPC>(cut[q] - prev_cut);
       const double sum = gsum<CPC>(P[q] - prev_p);
       if (cnt > 0) lev[q] = (float)(sum / (double)cnt);
+      empty |= cnt <= 0;
       prev_cut = cut[q];
       prev_p = P[q];
     }
-    // an empty duplicate keeps its level while its twin moves: keep the table
-    // ordered so the cells stay contiguous ranges
-    sort_levels<L>(lev);
+    // an empty cell keeps its level while its neighbours move: keep the table
+    // ordered so the cells stay contiguous ranges (without an empty cell the
+    // new means are already ascending; the wave skips the sort then)
+    if (__any(empty)) sort_levels<L>(lev);
   }
 }
 
@@ -1031,11 +1034,13 @@ __device__ void kb_fit(const V &v, uint32_t n, int kout, int iters, float &lev_m
     const int64_t s_top = lane < L - 1 ? s_me : s_hi;
     float nl = lev_me;
     if (lane < L && c_top > c_lo) nl = kb_mean(s_top - s_below, c_top - c_lo);
-    // an empty duplicate keeps its level while its twin moves: keep the table
+    // an empty cell keeps its level while its neighbours move: keep the table
     // ordered so the cells stay contiguous ranges (odd-even transposition
-    // sort over lanes 0..L-1 with DPP moves; lanes above hold +inf)
+    // sort over lanes 0..L-1 with DPP moves; lanes above hold +inf). Without
+    // an empty cell the new means are already ascending: skipped.
+    const bool any_empty = __any(lane < L && c_top <= c_lo);
 #pragma unroll
-    for (int p = 0; p < L; ++p) {
+    for (int p = 0; p < L && any_empty; ++p) {
       const uint32_t x = __float_as_uint(nl);
       if ((p & 1) == 0) {  // pairs (0,1), (2,3), ...
         const float o = __uint_as_float(dppm<DPP_XOR1>(x));
@@ -1505,7 +1510,12 @@ __device__ __forceinline__ void quad_cut_keys(const float *lev, int q, uint32_t 
     t[s_] = j < L - 1 ? (lev[s_] < up ? key16(thr16(lev[s_], up)) : 0u) : 0xffffu;
   }
   // a 0 takes the first nonzero cut above it: inside the lane, then across
-  // lanes (each move runs in every lane before the select)
+  // lanes (each move runs in every lane before the select). Equal neighbours
+  // are rare: the wave skips the fill when none of its tokens has any.
+  bool zero = false;
+#pragma unroll
+  for (int s_ = 0; s_ < LPL; ++s_) zero |= t[s_] == 0;
+  if (!__any(zero)) return;
 #pragma unroll
   for (int s_ = LPL - 2; s_ >= 0; --s_) t[s_] = t[s_] ? t[s_] : t[s_ + 1];
 #pragma unroll
@@ -1705,16 +1715,21 @@ __global__ __launch_bounds__(256) void nuq_value_quad(NuqArgs a) {
     double pb = dppd_q<QPERM_PREV>(pc[LPL - 1]);
     cb = q > 0 ? cb : lo;
     pb = q > 0 ? pb : p_lo;
+    bool empty = false;
 #pragma unroll
     for (int s_ = 0; s_ < LPL; ++s_) {
       const int j = LPL * q + s_;
       const int cnt = cut[s_] - cb;
       if (j < L && cnt > 0) lev[s_] = (float)((pc[s_] - pb) / (double)cnt);
+      empty |= j < L && cnt <= 0;
       cb = cut[s_];
       pb = pc[s_];
     }
-    // an empty duplicate keeps its level while its twin moves: keep the table ordered
-    quad_sort_levels<L, LPL>(lev, q);
+    // an empty cell keeps its level while its neighbours move: keep the table
+    // ordered. Without an empty cell the new table is already ascending (the
+    // cells are ascending ranges of the sorted samples, so are their means),
+    // and the sort would leave it as it is: the wave skips it then.
+    if (__any(empty)) quad_sort_levels<L, LPL>(lev, q);
   }
   // ---- codes, reconstruction, level row
   quad_cut_keys<L, LPL>(lev, q, t);
@@ -2034,11 +2049,13 @@ __device__ __forceinline__ void value_wave_body(const NuqArgs &a, int64_t tok, b
       const int cnt = cut - c_lo;
       float nl = lev_me;
       if (lane < L && cnt > 0) nl = (float)((pc - p_below) / (double)cnt);
-      // an empty duplicate keeps its level while its twin moves: keep the
+      // an empty cell keeps its level while its neighbours move: keep the
       // table ordered (odd-even transposition over lanes 0..L-1 with DPP
-      // moves; lane 0 and lane 15 of the row sit out of the odd phases)
+      // moves; lane 0 and lane 15 of the row sit out of the odd phases).
+      // Without an empty cell the new means are already ascending: skipped.
+      const bool any_empty = __any(lane < L && cnt <= 0);
 #pragma unroll
-      for (int ph = 0; ph < L; ++ph) {
+      for (int ph = 0; ph < L && any_empty; ++ph) {
         const uint32_t xb = __float_as_uint(nl);
         if ((ph & 1) == 0) {  // pairs (0,1), (2,3), ...
           const float o = __uint_as_float(dppm<DPP_XOR1>(xb));
