@@ -391,3 +391,45 @@ def test_frozen_levels_at_adversarial_midpoints(bits):
     g = gpu_nuq(k, v, 300, bits, 0.01, 8, 4, 0, kl, kt)
     r = oracle.nuq_fit_quant(k, v, 300, bits, 0.01, 8, 4, 0, kl, kt)
     compare(g, r, what="adversarial frozen levels")
+
+
+def _degenerate(case, shape, rng):
+    """fp16 samples of the degenerate kinds above: few distinct values (empty
+    cells and equal levels), zeros, signed zeros, the range's ends,
+    subnormals, constants."""
+    if case == "ties":
+        x = rng.integers(-3, 4, size=shape).astype(np.float16)
+    elif case == "zeros":
+        x = np.zeros(shape, np.float16)
+        x[..., ::7] = 1.5
+    elif case == "signed_zeros":
+        x = np.where(rng.random(shape) < 0.5, np.float16(0.0), np.float16(-0.0)).astype(np.float16)
+        x[..., 3] = rng.standard_normal(shape[:-1]).astype(np.float16)
+    elif case == "extremes":
+        x = (rng.standard_t(4, size=shape) * 3000).clip(-65504, 65504).astype(np.float16)
+        x[..., 5] = 65504
+        x[..., 6] = -65504
+    elif case == "subnormal":
+        x = (rng.integers(-40, 40, size=shape) * 2.0 ** -24).astype(np.float16)
+    else:
+        x = np.full(shape, 0.25, np.float16)
+    return x.view(np.uint16)
+
+
+@pytest.mark.parametrize("case", ["ties", "zeros", "signed_zeros", "extremes", "subnormal", "const"])
+@pytest.mark.parametrize("bits,D", [(3, 128), (2, 128), (4, 128), (1, 128), (3, 256), (2, 64)])
+def test_many_tokens_degenerate_values(case, bits, D):
+    """The many-token value fits (a quad of lanes per token at D = 128, lanes
+    per token otherwise) on data with tied samples, so that cells go empty
+    and neighbouring levels become equal: the level sort and the equal-level
+    cut rule run, at several outlier fractions and iteration counts."""
+    say("nuq many tokens degenerate", case, bits, D)
+    BH, S = 33, 130
+    rng = np.random.default_rng(500 + 10 * D + bits)
+    v = _degenerate(case, (BH, S, D), rng)
+    k = t4((BH, S, D), 60 + D + bits)
+    for frac, iters in [(0.05, 8), (0.0, 3), (0.3, 1), (0.01, 0)]:
+        g = gpu_nuq(k, v, 0, bits, frac, iters, 4, 1)
+        r = oracle.nuq_fit_quant(k, v, 0, bits, frac, iters, 4, 1)
+        compare(g, r, keys=["value_levels", "v_codes", "v_recon"],
+                what="%s bits=%d D=%d frac=%g iters=%d" % (case, bits, D, frac, iters))
