@@ -158,6 +158,16 @@ __device__ __forceinline__ int count_le8(const uint4 &w, uint32_t t2) {
 // #{i < N : key[i] <= t} over the wave's N ascending keys: a count over the
 // last keys of the runs of 8 gives the number of runs wholly <= t, a count
 // inside the next run finishes (two rounds of 16-byte LDS reads)
+// the same, with the run ends already in registers (N/16 words, two keys each)
+template <int N>
+__device__ __forceinline__ int lds_upper_r(const uint32_t *l8, const uint16_t *key, uint32_t t) {
+  const uint32_t t2 = t * 0x10001u;
+  int r = 0;
+#pragma unroll
+  for (int q = 0; q < N / 64; ++q) r += count_le8(make_uint4(l8[4 * q], l8[4 * q + 1], l8[4 * q + 2], l8[4 * q + 3]), t2);
+  if (r == N / 8) return N;
+  return 8 * r + count_le8(*reinterpret_cast<const uint4 *>(key + 8 * r), t2);
+}
 template <int N>
 __device__ __forceinline__ int lds_upper(const uint16_t *key, const uint16_t *last8, uint32_t t) {
   const uint32_t t2 = t * 0x10001u;
@@ -1909,6 +1919,7 @@ __device__ __forceinline__ uint32_t lane_cut_key(float lev_me, int lane) {
   const float lnext = __uint_as_float(kb_dpp<DPP_ROW_SHL1>(__float_as_uint(lev_me), __float_as_uint(inf)));
   uint32_t t = 0xffffu;
   if (lane < L - 1) t = lev_me < lnext ? key16(thr16(lev_me, lnext)) : 0u;
+  if (!__any(t == 0u)) return t;  // no equal neighbours in the table (the common case)
   // a 0 takes the first nonzero key above it (lane L-1 holds 0xffff)
   // (row shifts by 1, 2, 4, 8: after the shift by s a lane holds the first
   // nonzero key among its next 2s - 1 neighbours). Each move runs in every
@@ -2031,13 +2042,16 @@ __device__ __forceinline__ void value_wave_body(const NuqArgs &a, int64_t tok, b
       lev_me = (float)val + 0.0f;
     }
     const double p_lo = wl.pre[lo], p_hi = wl.pre[hi];
+    uint32_t l8[N / 16];  // the run ends, kept in registers for the searches
+#pragma unroll
+    for (int i = 0; i < N / 16; ++i) l8[i] = reinterpret_cast<const uint32_t *>(wl.last8)[i];
     // ---- Lloyd iterations
     for (int it = 0; it < a.iters; ++it) {
       const uint32_t t = lane_cut_key<L>(lev_me, lane);
       int cut = hi;
       double pc = p_hi;
       if (lane < L - 1) {
-        cut = min(max(lds_upper<N>(wl.key, wl.last8, t), lo), hi);
+        cut = min(max(lds_upper_r<N>(l8, wl.key, t), lo), hi);
         pc = wl.pre[cut];
       }
       // cell q = (cut q-1, cut q]; lane 0 starts at lo
@@ -2098,13 +2112,26 @@ __device__ __forceinline__ void value_wave_body(const NuqArgs &a, int64_t tok, b
   if (active && lane < L) a.value_levels[(size_t)tok * L + lane] = lev_me;  // 0 for sinks
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  // codes LSB-first along D: lane w builds dword w of the row
+  // codes LSB-first along D: lane w builds dword w of the row from the code
+  // bytes c0 .. c1 that overlap it, read four at a time
   if (active && lane < D * BITS / 32) {
     const int bit0 = 32 * lane;
+    const int c0 = bit0 / BITS, c1 = (bit0 + 31) / BITS;
+    const int w0 = c0 >> 2, nw = (c1 >> 2) - w0 + 1;
+    constexpr int MAXW = (32 / BITS + 1) / 4 + 2;  // dwords any lane needs
+    const uint32_t *cw = reinterpret_cast<const uint32_t *>(wl.cb);
     uint32_t acc = 0;
-    for (int c = bit0 / BITS; c * BITS < bit0 + 32; ++c) {
-      const int sh = c * BITS - bit0;
-      acc |= sh >= 0 ? (uint32_t)wl.cb[c] << sh : (uint32_t)wl.cb[c] >> -sh;
+#pragma unroll
+    for (int i = 0; i < MAXW; ++i) {
+      if (i < nw) {
+        const uint32_t word = cw[w0 + i];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int c = 4 * (w0 + i) + b, sh = c * BITS - bit0;
+          const uint32_t byte = (word >> (8 * b)) & 0xffu;
+          if (c >= c0 && c <= c1) acc |= sh >= 0 ? byte << sh : byte >> -sh;
+        }
+      }
     }
     reinterpret_cast<uint32_t *>(a.v_codes + (size_t)tok * (D * BITS / 8))[lane] = acc;
   }
