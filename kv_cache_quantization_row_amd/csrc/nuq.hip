@@ -980,9 +980,18 @@ __device__ void kb_fit(const V &v, uint32_t n, int kout, int iters, float &lev_m
     }
     if (lane == j) lev_me = (float)x + 0.0f;
   }
-  // Lloyd iterations: cells are key ranges cut at exact fp16 thresholds
-  uint32_t t_me = 0xffffffffu, c_me = hi;  // this lane's cut (none yet) and the count / sum at it
-  int64_t s_me = s_hi;
+  // Lloyd iterations: cells are key ranges cut at exact fp16 thresholds.
+  // The cuts' keys and the count and exact sum at each are wave-uniform
+  // (scalar registers); lane j reads its cell's bounds from lane-indexed
+  // copies built with writelane.
+  uint32_t Tp[L - 1], Cu[L - 1];  // previous cut keys (none yet), counts at the cuts
+  int64_t Su[L - 1];              // exact sums at the cuts
+#pragma unroll
+  for (int j = 0; j < L - 1; ++j) {
+    Tp[j] = 0xffffffffu;
+    Cu[j] = hi;
+    Su[j] = s_hi;
+  }
   const float inf = __builtin_inff();
   if (lane >= L) lev_me = inf;  // lanes above the table sort last
 #pragma unroll 1
@@ -1002,7 +1011,7 @@ __device__ void kb_fit(const V &v, uint32_t n, int kout, int iters, float &lev_m
       if (t) nt = t;
       T[j] = min(max(nt, klo - 1), khi);
       const bool same_up = j < L - 2 && T[j] == T[j + 1];
-      if (T[j] != kb_rl(t_me, j) && !same_up) need |= 1u << j;
+      if (T[j] != Tp[j] && !same_up) need |= 1u << j;
     }
     uint32_t qc[L - 1];
     int64_t qs[L - 1];
@@ -1011,37 +1020,36 @@ __device__ void kb_fit(const V &v, uint32_t n, int kout, int iters, float &lev_m
     int64_t s_up = s_hi;
 #pragma unroll
     for (int j = L - 2; j >= 0; --j) {
-      uint32_t cj;
-      int64_t sj;
       if ((need >> j) & 1u) {
-        cj = qc[j];
-        sj = qs[j];
-      } else if (T[j] == kb_rl(t_me, j)) {
-        cj = kb_rl(c_me, j);
-        sj = (int64_t)(((uint64_t)kb_rl((uint32_t)((uint64_t)s_me >> 32), j) << 32) | kb_rl((uint32_t)s_me, j));
-      } else {
-        cj = c_up;
-        sj = s_up;
+        Cu[j] = qc[j];
+        Su[j] = qs[j];
+      } else if (T[j] != Tp[j]) {  // the same key as the cut above
+        Cu[j] = c_up;
+        Su[j] = s_up;
       }
-      if (lane == j) {
-        t_me = T[j];
-        c_me = cj;
-        s_me = sj;
-      }
-      c_up = cj;
-      s_up = sj;
+      Tp[j] = T[j];
+      c_up = Cu[j];
+      s_up = Su[j];
     }
-    // lane j < L updates level j from its cell (cut j-1, cut j]
-    uint32_t c_lo = kb_dpp<DPP_ROW_SHR1>(c_me, lo);
-    const uint32_t slo_l = kb_dpp<DPP_ROW_SHR1>((uint32_t)s_me, (uint32_t)s_lo);
-    const uint32_t slo_h = kb_dpp<DPP_ROW_SHR1>((uint32_t)((uint64_t)s_me >> 32), (uint32_t)((uint64_t)s_lo >> 32));
+    // lane j < L updates level j from its cell (cut j-1, cut j]: lane j of
+    // c_top / s_top holds cut j (lane L-1: hi), the lane below it cut j-1
+    uint32_t c_top = hi, st_l = (uint32_t)s_hi, st_h = (uint32_t)((uint64_t)s_hi >> 32);
+#pragma unroll
+    for (int j = 0; j < L - 1; ++j) {
+      const bool mine = lane == j;
+      c_top = mine ? Cu[j] : c_top;
+      st_l = mine ? (uint32_t)Su[j] : st_l;
+      st_h = mine ? (uint32_t)((uint64_t)Su[j] >> 32) : st_h;
+    }
+    const int64_t s_top = (int64_t)(((uint64_t)st_h << 32) | st_l);
+    uint32_t c_lo = kb_dpp<DPP_ROW_SHR1>(c_top, lo);
+    const uint32_t slo_l = kb_dpp<DPP_ROW_SHR1>(st_l, (uint32_t)s_lo);
+    const uint32_t slo_h = kb_dpp<DPP_ROW_SHR1>(st_h, (uint32_t)((uint64_t)s_lo >> 32));
     int64_t s_below = (int64_t)(((uint64_t)slo_h << 32) | slo_l);
     if (lane == 0) {
       c_lo = lo;
       s_below = s_lo;
     }
-    const uint32_t c_top = lane < L - 1 ? c_me : hi;
-    const int64_t s_top = lane < L - 1 ? s_me : s_hi;
     float nl = lev_me;
     if (lane < L && c_top > c_lo) nl = kb_mean(s_top - s_below, c_top - c_lo);
     // an empty cell keeps its level while its neighbours move: keep the table
