@@ -39,7 +39,9 @@
 // bucket scan (the "bucketed key fit" section below); sums there are int64.
 // Up to 4,096 vectors the value fit runs one token per wave instead
 // (value_wave_body: keys sorted across the wave, sorted keys and exact
-// prefix sums in the wave's LDS, one level per lane).
+// prefix sums in the wave's LDS, one level per lane); beyond that at D = 128
+// a quad of lanes shares a token (nuq_value_quad: the same LDS tables per
+// token, two levels per lane at 3 bits).
 // Codes are #{j : x > T_j}, which equals the first index of the nearest
 // level (a binary search over the sorted cut keys, two samples per packed
 // step). The side channel (flat index, fp16 value) is emitted in ascending
