@@ -19,6 +19,8 @@
 // spacing is 1, so that single IEEE addition rounds c to the nearest integer
 // with ties to even (the addend is even) and leaves rint(c) + bias in the low
 // mantissa bits.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -31,11 +33,14 @@
 #ifndef KVQ_SYM_DEQ_PPB
 #define KVQ_SYM_DEQ_PPB 16  // most positions per workgroup in the read path (divides page_size)
 #endif
-#ifndef KVQ_SYM_DEQ_UNIT_BYTES
-#define KVQ_SYM_DEQ_UNIT_BYTES 6144  // code bytes staged per read-path workgroup, at most
+#ifndef KVQ_SYM_DEQ_CHUNKS
+#define KVQ_SYM_DEQ_CHUNKS 512  // most 8-element chunks per read-path workgroup (two per thread measured best)
 #endif
 #ifndef KVQ_NT_LOAD
 #define KVQ_NT_LOAD 0  // 1: non-temporal hint on the streaming fp16 loads (write path)
+#endif
+#ifndef KVQ_NT_CODES
+#define KVQ_NT_CODES 1  // non-temporal hint on the packed code stores of the write path (q6 +2%, q8 +0.5% measured)
 #endif
 #ifndef KVQ_NT_STORE
 #define KVQ_NT_STORE 1  // non-temporal hint on the streaming fp16 stores of the read path (+3% measured)
@@ -50,6 +55,14 @@ __device__ __forceinline__ uint4 ld_stream(const uint4 *p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 #else
   return *p;
+#endif
+}
+template <typename T>
+__device__ __forceinline__ void st_codes(T *p, T v) {
+#if KVQ_NT_CODES
+  __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
 #endif
 }
 __device__ __forceinline__ void st_stream(uint4 *p, uint4 v) {
@@ -348,13 +361,16 @@ __global__ __launch_bounds__(256) void sym_quant_v8(SymQuantArgs a) {
     if constexpr (BITS == 8) {
       const uint32_t o0 = __builtin_amdgcn_perm(m[1], m[0], 0x0c0c0400u) | __builtin_amdgcn_perm(m[3], m[2], 0x04000c0cu);
       const uint32_t o1 = __builtin_amdgcn_perm(m[5], m[4], 0x0c0c0400u) | __builtin_amdgcn_perm(m[7], m[6], 0x04000c0cu);
-      if (ok) *reinterpret_cast<uint2 *>(cl + orow * PD + li * 8) = make_uint2(o0, o1);
+      if (ok) {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        st_codes(reinterpret_cast<u32x2 *>(cl + orow * PD + li * 8), u32x2{o0, o1});
+      }
     } else if constexpr (BITS == 4) {
       constexpr uint32_t C = K + (K << 4) + (K << 8) + (K << 12) + (K << 16) + (K << 20) + (K << 24) + (K << 28);
       uint32_t v = m[0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) v += m[i] << (4 * i);
-      if (ok) *reinterpret_cast<uint32_t *>(cl + orow * PD + li * 4) = v - C;
+      if (ok) st_codes(reinterpret_cast<uint32_t *>(cl + orow * PD + li * 4), v - C);
     } else {
       constexpr uint32_t C = K + (K << 6) + (K << 12) + (K << 18);
       const uint32_t g0 = (m[0] + (m[1] << 6) + (m[2] << 12) + (m[3] << 18)) - C;
@@ -365,9 +381,9 @@ __global__ __launch_bounds__(256) void sym_quant_v8(SymQuantArgs a) {
       const uint32_t nlo = dpp<0xf5>(lo), nhi = dpp<0xf5>(hi);
       if (ok && (li & 1) == 0) {
         uint32_t *dst = reinterpret_cast<uint32_t *>(cl + orow * PD + li * 6);
-        dst[0] = lo;
-        dst[1] = hi | (nlo << 16);
-        dst[2] = (nlo >> 16) | (nhi << 16);
+        st_codes(dst, lo);
+        st_codes(dst + 1, hi | (nlo << 16));
+        st_codes(dst + 2, (nlo >> 16) | (nhi << 16));
       }
     }
     if (ok && li == 0) scales[(size_t)(a.layer0 + layer) * a.scale_layer_stride + orow] = s16;
@@ -534,17 +550,26 @@ __global__ __launch_bounds__(256) void sym_dequant_generic(SymDequantArgs a) {
   }
 }
 
-// Page-at-a-time read path (power-of-two head_dim in [16, 1024]). One
-// workgroup dequantizes one block of page_size positions of one sequence:
-// the page's codes are contiguous in the pool ([slot][head][packed_dim]), so
-// they are staged into LDS with 16-byte loads, and the page's output rows are
-// contiguous in the fp16 output, so 8-element chunk c of the page (codes at
-// byte c*bits of the page, output at element 8c) is written by consecutive
-// lanes with 16-byte stores. The block-table entry is read once per page.
+// Page-unit read path (power-of-two head_dim in [16, 1024]). One workgroup
+// dequantizes a unit of positions inside one page of one sequence: the
+// unit's codes are contiguous in the pool ([slot][head][packed_dim]) and its
+// output rows are contiguous in the fp16 output, so 8-element chunk c of the
+// unit (codes at byte c*bits, output at element 8c) is read and written by
+// consecutive lanes: each wave load is one contiguous run of codes, each wave
+// store one contiguous KiB. A thread takes chunks t, t + 256, ...; all its
+// loads are issued before its first store. q6: a chunk's 6 bytes are read as
+// the 8 bytes from the dword boundary at or below c*6 (c even: the chunk and
+// 2 bytes of the next; c odd: 2 bytes of the previous and the chunk); the
+// unit's last chunk has an odd index (D/8 is even), so no window leaves the
+// unit. The block-table entry is read once per unit.
 template <int BITS, int D>
 __global__ __launch_bounds__(256) void sym_dequant_page(SymDequantArgs a) {
   constexpr int PD = D * BITS / 8;
-  extern __shared__ uint4 lds_codes[];
+  // load slots per batch (chunks t + 256k); q8 takes four slots, two of them
+  // idle at 512 chunks per unit, which makes the compiler issue every load
+  // before the first wait (measured at D = 256: +4% at q8 over two slots)
+  constexpr int NC = BITS == 8 ? 4 : KVQ_SYM_DEQ_CHUNKS / 256;
+  typedef std::conditional_t<BITS == 4, uint32_t, uint2> CW;
   const int side = blockIdx.z & 1;
   const uint32_t layer = blockIdx.z >> 1;
   const uint8_t *codes = side ? a.v_codes : a.k_codes;
@@ -554,7 +579,6 @@ __global__ __launch_bounds__(256) void sym_dequant_page(SymDequantArgs a) {
   const uint32_t seq = blockIdx.y;
   const int P = a.page_size, H = a.H;
   const int ppb = a.ppb;                   // positions per workgroup, divides P
-  const int rows = ppb * H;                // rows of this unit
   const int32_t len = a.seq_lens[seq];
   const int32_t p0 = (int32_t)blockIdx.x * ppb;  // first position of the unit
   const int32_t blk = p0 / P;
@@ -565,44 +589,54 @@ __global__ __launch_bounds__(256) void sym_dequant_page(SymDequantArgs a) {
   const int32_t pos_end = min(ppb, a.max_len - p0);  // positions of this unit inside the output
   uint16_t *ob = out + (((size_t)layer * a.n_seqs + seq) * a.max_len + p0) * H * D;
   const int out_chunks = pos_end * H * (D / 8);
-  if (have) {
-    // rows of positions p0.. of the page are contiguous: [slot][head][packed_dim]
-    const size_t first_row = (size_t)page * P * H + (size_t)(p0 - blk * P) * H;
-    const uint4 *src = reinterpret_cast<const uint4 *>(
-        codes + (size_t)(a.layer0 + layer) * a.code_layer_stride + first_row * PD);
-    const int n16 = rows * PD / 16;  // whole unit (a multiple of 16 bytes, checked at launch)
-    for (int i = threadIdx.x; i < n16; i += blockDim.x) lds_codes[i] = src[i];
-  }
-  __syncthreads();
-  const uint16_t *sp = scales + (size_t)(a.layer0 + layer) * a.scale_layer_stride +
-                       (have ? (size_t)page * P * H + (size_t)(p0 - blk * P) * H : 0);
-  const uint8_t *lb = reinterpret_cast<const uint8_t *>(lds_codes);
-  for (int c = threadIdx.x; c < out_chunks; c += blockDim.x) {
-    const int row = c / (D / 8);
-    uint32_t o[4] = {0, 0, 0, 0};
-    if (row < valid_rows) {
-      uint32_t u[8];
-      if constexpr (BITS == 8) {
-        const uint2 w = *reinterpret_cast<const uint2 *>(lb + c * 8);
+  // rows of positions p0.. of the page are contiguous: [slot][head][packed_dim]
+  const size_t first_row = have ? (size_t)page * P * H + (size_t)(p0 - blk * P) * H : 0;
+  const uint8_t *gb = codes + (size_t)(a.layer0 + layer) * a.code_layer_stride + first_row * PD;
+  const uint16_t *sp = scales + (size_t)(a.layer0 + layer) * a.scale_layer_stride + first_row;
+  for (int c0 = threadIdx.x; c0 < out_chunks; c0 += NC * 256) {
+    CW w[NC];
+    uint32_t sc[NC];  // a register each: packing two would wait on the first load
 #pragma unroll
-        for (int i = 0; i < 8; ++i) u[i] = ((i < 4 ? w.x : w.y) >> (8 * (i % 4))) & 0xffu;
-      } else if constexpr (BITS == 4) {
-        const uint32_t w = *reinterpret_cast<const uint32_t *>(lb + c * 4);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) u[i] = (w >> (4 * i)) & 15u;
-      } else {
-        const int off = c * 6;
-        const uint32_t *wp = reinterpret_cast<const uint32_t *>(lb + (off & ~3));
-        const uint64_t w = ((uint64_t)wp[1] << 32 | wp[0]) >> (8 * (off & 3));
-#pragma unroll
-        for (int i = 0; i < 8; ++i) u[i] = (uint32_t)(w >> (6 * i)) & 63u;
+    for (int k = 0; k < NC; ++k) {
+      const int c = c0 + k * 256;
+      const int row = c / (D / 8);
+      w[k] = CW{};
+      sc[k] = 0;
+      if (c < out_chunks && row < valid_rows) {
+        if constexpr (BITS == 6) {  // two dwords at a 4-byte boundary
+          const uint32_t *wp = reinterpret_cast<const uint32_t *>(gb + ((size_t)c * 6 & ~(size_t)3));
+          w[k] = make_uint2(wp[0], wp[1]);
+        } else {
+          w[k] = *reinterpret_cast<const CW *>(gb + (size_t)c * BITS);
+        }
+        sc[k] = sp[row];
       }
-      const _Float16 s = __builtin_bit_cast(_Float16, sp[row]);
-      const h2 ss = {s, s};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = decode_pair<BITS>(u[2 * i], u[2 * i + 1], ss);
     }
-    st_stream(reinterpret_cast<uint4 *>(ob) + c, make_uint4(o[0], o[1], o[2], o[3]));
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      const int c = c0 + k * 256;
+      if (c >= out_chunks) break;
+      uint32_t o[4] = {0, 0, 0, 0};
+      if (c / (D / 8) < valid_rows) {
+        uint32_t u[8];
+        if constexpr (BITS == 8) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) u[i] = ((i < 4 ? w[k].x : w[k].y) >> (8 * (i % 4))) & 0xffu;
+        } else if constexpr (BITS == 4) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) u[i] = (w[k] >> (4 * i)) & 15u;
+        } else {
+          const uint64_t q = ((uint64_t)w[k].y << 32 | w[k].x) >> (16 * (c & 1));
+#pragma unroll
+          for (int i = 0; i < 8; ++i) u[i] = (uint32_t)(q >> (6 * i)) & 63u;
+        }
+        const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)sc[k]);
+        const h2 ss = {sv, sv};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = decode_pair<BITS>(u[2 * i], u[2 * i + 1], ss);
+      }
+      st_stream(reinterpret_cast<uint4 *>(ob) + c, make_uint4(o[0], o[1], o[2], o[3]));
+    }
   }
 }
 
@@ -668,39 +702,29 @@ hipError_t launch_quant_bits(const SymQuantArgs &a, int n_layers, hipStream_t st
     }
   }
 }
-// positions per workgroup: the largest divisor of page_size not above the
-// tuning target whose codes are whole 16-byte units
+// positions per workgroup: the largest divisor of page_size whose unit holds
+// at most KVQ_SYM_DEQ_CHUNKS 8-element chunks (two per thread measured best
+// at D = 256: fewer workgroups with more chunks each, or more with fewer,
+// were slower), else one position
 template <int BITS>
 int pick_ppb(const SymDequantArgs &a) {
-  // the largest unit (positions dividing the page) whose codes stay within
-  // KVQ_SYM_DEQ_UNIT_BYTES: 4-6 KiB of staged codes per workgroup measured
-  // best (q8 at D=256: 4 positions, q6 / q4: 8); else the smallest valid unit
-  int fallback = 0;
-  for (int q = min(KVQ_SYM_DEQ_PPB, a.page_size); q >= 1; --q) {
-    const int64_t bytes = (int64_t)q * a.H * a.D * BITS / 8;
-    if (a.page_size % q != 0 || bytes % 16 != 0) continue;
-    if (bytes <= KVQ_SYM_DEQ_UNIT_BYTES) return q;
-    fallback = q;
-  }
-  return fallback;
+  for (int q = min(KVQ_SYM_DEQ_PPB, a.page_size); q > 1; --q)
+    if (a.page_size % q == 0 && (int64_t)q * a.H * (a.D / 8) <= KVQ_SYM_DEQ_CHUNKS) return q;
+  return 1;
 }
 
 template <int BITS, int D>
 hipError_t launch_page(SymDequantArgs a, int n_layers, hipStream_t st) {
   a.ppb = pick_ppb<BITS>(a);
-  const int rows = a.ppb * a.H;
-  const size_t lds = ((size_t)rows * (D * BITS / 8) + 16 + 15) / 16 * 16;
   dim3 grid((a.max_len + a.ppb - 1) / a.ppb, a.n_seqs, 2 * n_layers);
-  hipLaunchKernelGGL((sym_dequant_page<BITS, D>), grid, dim3(256), lds, st, a);
+  hipLaunchKernelGGL((sym_dequant_page<BITS, D>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
-// page path when a unit's codes fit comfortably in LDS and are whole 16-byte units
+// page path for power-of-two head dims in [16, 1024]
 template <int BITS>
 bool page_path_ok(const SymDequantArgs &a) {
-  const int q = pick_ppb<BITS>(a);
-  const int64_t bytes = (int64_t)q * a.H * a.D * BITS / 8;
-  return q > 0 && bytes <= 32768 && a.D >= 16 && a.D <= 1024 && (a.D & (a.D - 1)) == 0;
+  return a.D >= 16 && a.D <= 1024 && (a.D & (a.D - 1)) == 0;
 }
 
 template <int BITS>
