@@ -16,9 +16,10 @@
 // chosen at launch so that the grid is about one round of resident
 // workgroups (never below 256 positions). Per block a wave computes the score
 // tile S^T = K Q^T (16 positions x 16 query-head slots, G of them used) with
-// 16x16x16 fp16 MFMAs, the online softmax per head in fp32 (base 2; the
-// accumulators are rescaled only when a running maximum grows), and
-// O^T += V^T P^T with the same MFMA: the score tile's accumulator layout
+// 16x16x32 fp16 MFMAs (two k-steps of the lane's K piece each), the online
+// softmax per head in fp32 (base 2; the accumulators are rescaled only when
+// a running maximum grows), and O^T += V^T P^T with 16x16x16 fp16 MFMAs
+// (the block's 16 positions are the contraction): the score tile's accumulator layout
 // (lane l: positions 4*(l/16)+i, head l%16) is the B-operand layout of the
 // second product, so the probabilities feed it from registers. Each chunk
 // leaves (max, sum, unnormalised output) per head in the workspace; a second
@@ -47,11 +48,16 @@
 #include "common.h"
 #include "kernels.h"
 
+#ifndef KVQ_ATTN_X32
+#define KVQ_ATTN_X32 1  // score tile from 16x16x32 fp16 MFMAs (pairs of k-steps)
+#endif
+
 namespace kvq {
 namespace {
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t MAG = 0x64006400u;  // fp16 1024.0 in both halves
@@ -259,13 +265,29 @@ __device__ __forceinline__ void block_step(const uint32_t *kw, uint32_t ksc,
   constexpr int KS = D / 16;
   // ---- scores S^T (positions 4g+i, head n in this lane)
   const h2 kss = __builtin_bit_cast(h2, ksc | (ksc << 16));
-  f4 st0 = {0.f, 0.f, 0.f, 0.f}, st1 = st0;  // two MFMA chains, even and odd k-steps
+  f4 st0 = {0.f, 0.f, 0.f, 0.f}, st1 = st0;  // two MFMA chains
+#if KVQ_ATTN_X32
+  // k-steps 2P and 2P+1 as one 16x16x32 product: both operands put the
+  // first step's four k-values before the second's (the k order inside one
+  // product is free while A and B agree)
+  static_for<0, KS / 2>([&](auto P) {
+    const h4 a0 = k_operand<BITS, 2 * P>(kw, kss, mag), a1 = k_operand<BITS, 2 * P + 1>(kw, kss, mag);
+    const h4 b0 = qb[(2 * P) * QS], b1 = qb[(2 * P + 1) * QS];
+    const h8 av = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    const h8 bv = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+    if constexpr (P % 2 == 0)
+      st0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, st0, 0, 0, 0);
+    else
+      st1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, st1, 0, 0, 0);
+  });
+#else
   static_for<0, KS>([&](auto J) {
     if constexpr (J % 2 == 0)
       st0 = __builtin_amdgcn_mfma_f32_16x16x16f16(k_operand<BITS, J>(kw, kss, mag), qb[J * QS], st0, 0, 0, 0);
     else
       st1 = __builtin_amdgcn_mfma_f32_16x16x16f16(k_operand<BITS, J>(kw, kss, mag), qb[J * QS], st1, 0, 0, 0);
   });
+#endif
   const f4 st = st0 + st1;
   float sv[4], bm = -__builtin_inff();
 #pragma unroll

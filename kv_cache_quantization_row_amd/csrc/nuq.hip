@@ -1115,23 +1115,28 @@ __device__ __forceinline__ void key_quant_body(const NuqArgs &a, int bx, int bh,
   const bool want_rec = a.k_recon != nullptr;
   const int row_w = (bx * 4 + wv) * (RPW * KQ_NIT) + lane / CL;  // first row of this lane
   const uint16_t *kin = a.keys + (size_t)bh * a.S * D + ck * 8;
-  // the first row step's load is issued before the table set-up so that its
-  // latency overlaps it (a decode call has only this step)
-  uint4 first = make_uint4(0, 0, 0, 0);
-  if (row_w < a.S) first = *reinterpret_cast<const uint4 *>(kin + (size_t)row_w * D);
   // ---- cut keys of this (b,h): T[j] = key of thr16(l_j, l_{j+1}) for distinct
   // neighbours; a duplicate level takes the cut above it (empty cell); the
   // last cut is above every finite key
   const float *kl = a.key_levels + (size_t)bh * D * L;
+  uint4 inr[KQ_NIT];
   {
     float lv[(256 * L) / 256];  // all level loads in flight at once
 #pragma unroll
     for (int i = 0; i < L; ++i)
       if (threadIdx.x + 256 * i < D * L) lv[i] = kl[threadIdx.x + 256 * i];
+    const uint32_t tau = threadIdx.x < D ? a.key_thresh[(size_t)bh * D + threadIdx.x] : 0u;
+    // every row step's load is issued after the tables' and before the
+    // set-up, so the wave waits for one load latency, not one per step, and
+    // the set-up waits only for the tables; rows past the end read the last
+    // row (S >= 1) and are not stored
+#pragma unroll
+    for (int it = 0; it < KQ_NIT; ++it)
+      inr[it] = *reinterpret_cast<const uint4 *>(kin + (size_t)min(row_w + it * RPW, a.S - 1) * D);
 #pragma unroll
     for (int i = 0; i < L; ++i)
       if (threadIdx.x + 256 * i < D * L) lev_s[threadIdx.x + 256 * i] = lv[i];
-    if (threadIdx.x < D) tau_s[threadIdx.x] = a.key_thresh[(size_t)bh * D + threadIdx.x];
+    if (threadIdx.x < D) tau_s[threadIdx.x] = (uint16_t)tau;
   }
   __syncthreads();
   for (int t = threadIdx.x; t < D * (L - 1); t += 256) {
@@ -1169,11 +1174,7 @@ __device__ __forceinline__ void key_quant_body(const NuqArgs &a, int bx, int bh,
     const int row = row_w + it * RPW;
     const bool valid = row < a.S;
     const bool sink = row < a.n_sink_eff;
-    uint4 in = first;
-    if (it > 0) {
-      in = make_uint4(0, 0, 0, 0);
-      if (valid) in = *reinterpret_cast<const uint4 *>(kin + (size_t)row * D);
-    }
+    const uint4 in = inr[it];
     const uint32_t wd[4] = {in.x, in.y, in.z, in.w};
     const uint32_t live = sink ? 0u : 0xffffffffu;  // sinks: code 0, no outliers
     uint32_t codes = 0, om = 0;
