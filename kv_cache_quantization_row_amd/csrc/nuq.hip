@@ -984,8 +984,8 @@ __device__ void kb_fit(const V &v, uint32_t n, int kout, int iters, float &lev_m
   }
   // Lloyd iterations: cells are key ranges cut at exact fp16 thresholds.
   // The cuts' keys and the count and exact sum at each are wave-uniform
-  // (scalar registers); lane j reads its cell's bounds from lane-indexed
-  // copies built with writelane.
+  // (scalar registers); lane j picks its cell's upper bound by lane-indexed
+  // selects and the lower one from the lane below (DPP).
   uint32_t Tp[L - 1], Cu[L - 1];  // previous cut keys (none yet), counts at the cuts
   int64_t Su[L - 1];              // exact sums at the cuts
 #pragma unroll
