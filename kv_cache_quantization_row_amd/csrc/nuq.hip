@@ -53,6 +53,7 @@
 // inter-workgroup waiting).
 #include <mutex>
 
+
 #include "common.h"
 #include "kernels.h"
 
@@ -767,13 +768,32 @@ __device__ __forceinline__ double wscan_d(double x) {
   return x;
 }
 
-template <typename DatPtr>
+// H16: the wave's 256-bin histogram as 16-bit counts, two per word (every
+// count is at most n < 65536), so that it takes 512 bytes of LDS instead of
+// 1 KiB; else 32-bit counts
+template <typename DatPtr, bool H16>
 struct KbView {
   const uint64_t *pre;  // [257] exclusive prefix sums (2^-24 units, int64 bits); [256] = total
   const uint32_t *end;  // [256] bucket ends (exclusive prefix of the counts, shifted by one bucket)
   DatPtr dat;           // bucketed key low bytes: bucket b at [start(b), end(b))
-  uint32_t *hist;       // [256] wave scratch
+  uint32_t *hist;       // wave scratch: [128] (H16) or [256] words
   __device__ __forceinline__ uint32_t start(int b) const { return b == 0 ? 0u : end[b - 1]; }
+  __device__ __forceinline__ void hist_zero(int lane) const {
+    if constexpr (H16) *reinterpret_cast<uint2 *>(hist + 2 * lane) = make_uint2(0, 0);
+    else *reinterpret_cast<uint4 *>(hist + 4 * lane) = make_uint4(0, 0, 0, 0);
+  }
+  __device__ __forceinline__ void hist_add(uint32_t bin) const {
+    if constexpr (H16) atomicAdd(&hist[bin >> 1], 1u << (16 * (bin & 1u)));
+    else atomicAdd(&hist[bin], 1u);
+  }
+  __device__ __forceinline__ uint4 hist_read(int lane) const {  // bins 4*lane .. 4*lane+3
+    if constexpr (H16) {
+      const uint2 w = *reinterpret_cast<const uint2 *>(hist + 2 * lane);
+      return make_uint4(w.x & 0xffffu, w.x >> 16, w.y & 0xffffu, w.y >> 16);
+    } else {
+      return *reinterpret_cast<const uint4 *>(hist + 4 * lane);
+    }
+  }
 };
 
 // count and exact sum of the samples with key <= T[j], for every cut j whose
@@ -866,13 +886,13 @@ __device__ __forceinline__ int kb_bucket_hist(const V &v, uint32_t r, uint32_t *
   const uint64_t bal = __ballot(e4.w > r);
   const int b = (int)kb_rl((uint32_t)(4 * lane + i), __ffsll((unsigned long long)bal) - 1);
   const uint32_t s0 = v.start(b), e0 = v.end[b];
-  *reinterpret_cast<uint4 *>(v.hist + 4 * lane) = make_uint4(0, 0, 0, 0);
+  v.hist_zero(lane);
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  for (uint32_t j = s0 + lane; j < e0; j += 64) atomicAdd(&v.hist[v.dat[j]], 1u);
+  for (uint32_t j = s0 + lane; j < e0; j += 64) v.hist_add(v.dat[j]);
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  const uint4 hv = *reinterpret_cast<const uint4 *>(v.hist + 4 * lane);
+  const uint4 hv = v.hist_read(lane);
   h4[0] = hv.x; h4[1] = hv.y; h4[2] = hv.z; h4[3] = hv.w;
   const uint32_t t = h4[0] + h4[1] + h4[2] + h4[3];
   excl = kb_wscan(t) - t;
@@ -922,17 +942,17 @@ __device__ __forceinline__ uint32_t kb_tau(const V &v, uint32_t kp1) {
   const int astar = (int)kb_rl((uint32_t)(f1 ? 2 * lane + 1 : 2 * lane), src);
   const uint32_t q = kp1 - kb_rl(f1 ? above1 : above0, src);  // 1-based, from the top
   // histogram of the |x| low bytes of the bin's two buckets
-  *reinterpret_cast<uint4 *>(v.hist + 4 * lane) = make_uint4(0, 0, 0, 0);
+  v.hist_zero(lane);
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
   {
     const int bp = 0x80 + astar, bn = 0x7f - astar;
-    for (uint32_t j = v.start(bp) + lane; j < v.end[bp]; j += 64) atomicAdd(&v.hist[v.dat[j]], 1u);
-    for (uint32_t j = v.start(bn) + lane; j < v.end[bn]; j += 64) atomicAdd(&v.hist[255u - v.dat[j]], 1u);
+    for (uint32_t j = v.start(bp) + lane; j < v.end[bp]; j += 64) v.hist_add(v.dat[j]);
+    for (uint32_t j = v.start(bn) + lane; j < v.end[bn]; j += 64) v.hist_add(255u - v.dat[j]);
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  const uint4 hv = *reinterpret_cast<const uint4 *>(v.hist + 4 * lane);
+  const uint4 hv = v.hist_read(lane);
   // largest low byte w with #{|x| low >= w} >= q
   const uint32_t t4 = hv.x + hv.y + hv.z + hv.w;
   const uint32_t inc2 = kb_wscan(t4);
@@ -2285,7 +2305,10 @@ __global__ __launch_bounds__(KB_T) void nuq_key_fit_bk(NuqArgs a) {
   extern __shared__ uint64_t kb_lds[];
   uint64_t *tab = kb_lds;                                            // [KB_CH][257]
   uint32_t *cur = reinterpret_cast<uint32_t *>(tab + KB_CH * 257);   // [KB_CH][256]
-  uint32_t *hist = cur + KB_CH * 256;                                // [KB_CH][256]
+  // per-wave histogram words: 16-bit counts with the samples in LDS (n <= KB_LDS_MAX_N)
+  constexpr bool H16 = LDS_DAT;
+  constexpr int KB_HW = H16 ? 128 : 256;
+  uint32_t *hist = cur + KB_CH * 256;                                // [KB_CH][KB_HW]
   // the channel groups of one (b, h) read the same token rows: keep them on
   // one XCD so that its L2 fetches each row once
   const int ngrp = a.D / KB_CH;
@@ -2295,7 +2318,7 @@ __global__ __launch_bounds__(KB_T) void nuq_key_fit_bk(NuqArgs a) {
   const int t0 = a.n_sink_eff;
   const int n = a.S - t0;
   const int npad = (n + 15) & ~15;
-  uint8_t *dat = LDS_DAT ? reinterpret_cast<uint8_t *>(hist + KB_CH * 256)
+  uint8_t *dat = LDS_DAT ? reinterpret_cast<uint8_t *>(hist + KB_CH * KB_HW)
                          : a.ws_kdat + ((size_t)bh * a.D + d0) * (size_t)npad;
   for (int i = tid; i < KB_CH * 257; i += KB_T) tab[i] = 0;
   __syncthreads();
@@ -2383,7 +2406,7 @@ __global__ __launch_bounds__(KB_T) void nuq_key_fit_bk(NuqArgs a) {
   }
   __syncthreads();
   // ---- the fit of channel d0 + w by wave w
-  KbView<const uint8_t *> v{tab + w * 257, cur + w * 256, dat + (size_t)w * npad, hist + w * 256};
+  KbView<const uint8_t *, H16> v{tab + w * 257, cur + w * 256, dat + (size_t)w * npad, hist + w * KB_HW};
   float mine;
   uint16_t tau;
   kb_fit<L>(v, (uint32_t)n, a.k_key, a.iters, mine, tau);
@@ -2398,9 +2421,11 @@ template <int L>
 hipError_t launch_key_fit(const NuqArgs &a, int /*cpc*/, hipStream_t st) {
   const int n = a.S - a.n_sink_eff;
   const dim3 grid((unsigned)(a.D / KB_CH) * (unsigned)a.BH);
-  const size_t tables = (size_t)KB_CH * 257 * 8 + (size_t)KB_CH * 256 * 4 * 2;
-  if (n <= KB_LDS_MAX_N) {  // bucketed samples in LDS
-    hipLaunchKernelGGL((nuq_key_fit_bk<L, true>), grid, dim3(KB_T), tables + (size_t)KB_CH * ((n + 15) & ~15), st, a);
+  const size_t tables = (size_t)KB_CH * 257 * 8 + (size_t)KB_CH * 256 * 4 * 2;  // 32-bit histograms
+  if (n <= KB_LDS_MAX_N) {  // bucketed samples in LDS, 16-bit histograms (n < 65536)
+    static_assert(KB_LDS_MAX_N < 65536, "16-bit histogram counts");
+    hipLaunchKernelGGL((nuq_key_fit_bk<L, true>), grid, dim3(KB_T),
+                       tables - (size_t)KB_CH * 128 * 4 + (size_t)KB_CH * ((n + 15) & ~15), st, a);
   } else {                  // in the workspace
     hipLaunchKernelGGL((nuq_key_fit_bk<L, false>), grid, dim3(KB_T), tables, st, a);
   }
@@ -2409,10 +2434,16 @@ hipError_t launch_key_fit(const NuqArgs &a, int /*cpc*/, hipStream_t st) {
 // The value fit reads nothing the key kernels write, so for many tokens it
 // runs on a second stream of the device, forked from the caller's stream
 // after the counters are cleared and joined before the placement kernel: the
-// two fits then share the machine instead of running back to back. One stream
-// and two events per device, created on first use (default priority); the
-// fork/join section is serialised on the host so that concurrent callers
-// never interleave their event records.
+// two fits then share the machine instead of running back to back. The key
+// fit is submitted before the value fit: it heads the longer chain (key fit,
+// key quantization, placement), and the value workgroups take the LDS the
+// key fit leaves free (two key-fit workgroups with 16-bit histograms leave
+// room for one value workgroup per CU). Submitted the other way round, the
+// value fit filled the CUs first and delayed the key fit (prefill 0.205 ->
+// 0.185 ms in a kernel trace). One stream and two events per device,
+// created on first use (default priority); the fork/join section is
+// serialised on the host so that concurrent callers never interleave their
+// event records.
 struct Fork {
   hipStream_t aux = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
@@ -2483,10 +2514,10 @@ hipError_t launch_bits(const NuqArgs &a, int key_cpc, int val_cpc, bool fork, hi
     Fork *f = nullptr;
     if ((e = fork_for_device(f)) != hipSuccess) return e;
     if ((e = hipEventRecord(f->fork, st)) != hipSuccess) return e;
+    if (a.fit_keys && (e = launch_key_fit<L>(a, key_cpc, st)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(f->aux, f->fork, 0)) != hipSuccess) return e;
     if ((e = launch_values<BITS>(a, val_cpc, f->aux)) != hipSuccess) return e;
     if ((e = hipEventRecord(f->join, f->aux)) != hipSuccess) return e;
-    if (a.fit_keys && (e = launch_key_fit<L>(a, key_cpc, st)) != hipSuccess) return e;
     hipLaunchKernelGGL((nuq_key_quant<BITS>), dim3((unsigned)a.k_blk_x, a.BH), dim3(256), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(st, f->join, 0)) != hipSuccess) return e;
