@@ -112,6 +112,31 @@ def test_paged_ragged_multilayer(bits, H, D):
 
 
 @pytest.mark.parametrize("bits", [8, 6, 4])
+@pytest.mark.parametrize("P,H,D", [(1, 4, 256), (5, 3, 128), (8, 2, 64), (32, 4, 256), (7, 1, 16)])
+def test_paged_page_sizes(bits, P, H, D):
+    """Page sizes other than 16 (the read path's unit is the largest divisor
+    of the page within its chunk budget, down to one position): scattered
+    pages, ragged sequences, a short output window."""
+    say("sym page size", bits, P, H, D)
+    rng = np.random.default_rng(bits * 100 + P * 10 + H + D)
+    lens = np.array([1, P - 1 if P > 1 else 1, P, P + 1, 7 * P + 3], np.int32)
+    blocks = (lens + P - 1) // P
+    num_pages = int(blocks.sum()) + 2
+    perm = rng.permutation(num_pages)
+    bt = np.full((len(lens), int(blocks.max()) + 1), -1, np.int32)
+    o = 0
+    for s, b in enumerate(blocks):
+        bt[s, :b] = perm[o:o + b]
+        o += b
+    slot = np.concatenate([bt[s, np.arange(n) // P] * P + np.arange(n) % P for s, n in enumerate(lens)]).astype(np.int64)
+    T = len(slot)
+    g = torch.Generator().manual_seed(int(rng.integers(1 << 30)))
+    xk = (torch.randn((1, T, H, D), generator=g) * 2).half()
+    xv = torch.randn((1, T, H, D), generator=g).half()
+    _check_roundtrip(xk, xv, bits, H, D, P, num_pages, 1, 0, slot, bt, lens, int(lens.max()) - 2)
+
+
+@pytest.mark.parametrize("bits", [8, 6, 4])
 @pytest.mark.parametrize("H,D", [(4, 256), (8, 128), (2, 64), (3, 256), (1, 16), (2, 512)])
 def test_paged_large_write(bits, H, D):
     """More than 16384 (layer, token, head) rows per call: the write path that
