@@ -43,6 +43,7 @@ def measured_traffic(kernel_class):
     import re
 
     launches, traffic_file = 1, TRAFFIC_FILE
+    grid = {}  # a kernel launched at several grid sizes: the grid this span runs
     if kernel_class.startswith("attn_decode_q"):  # span: one launch pair per layer
         b = kernel_class.split("_q")[1].split("_")[0]
         launches = int(kernel_class.rsplit("_x", 1)[1])
@@ -57,6 +58,18 @@ def measured_traffic(kernel_class):
     elif kernel_class.startswith("kivi_keys_values_b"):
         b = kernel_class[-1]
         names, src = ["kivi_keys_fast<%s, 8, 4, false>" % b, "kivi_values_fast<%s, 8, 4, 1, false>" % b], "kivi.hip"
+    elif kernel_class.startswith("kivi_pack_b"):
+        b = kernel_class[-1]
+        names, src = ["kivi_keys_fast<%s, 8, 4, true>" % b, "kivi_values_fast<%s, 8, 4, 4, true>" % b], "kivi.hip"
+    elif kernel_class.startswith("kivi_unpack_b"):
+        b = kernel_class[-1]
+        names, src = ["kivi_unpack<%s, true>" % b, "kivi_unpack<%s, false>" % b], "kivi.hip"
+    elif kernel_class == "quant_chunks_q6_x64":  # 64 chunk launches of the long-context cache
+        launches, names, src = 64, ["sym_quant_v8<6, 32, 2>"], "sym.hip"
+        grid = {"sym_quant_v8<6, 32, 2>": 8388608}
+    elif kernel_class == "dequant_full_q6":
+        names, src = ["sym_dequant_page<6, 256>"], "sym.hip"
+        grid = {"sym_dequant_page<6, 256>": 538968064}
     else:
         return None
     if not os.path.exists(traffic_file):
@@ -67,6 +80,8 @@ def measured_traffic(kernel_class):
         m = re.match(r"traffic (.+?) grid=(\d+) bytes=(\d+) src_sha1=([0-9a-f]+)", line.strip())
         if m and m.group(1) in names and m.group(4) == sha:
             g = int(m.group(2))
+            if m.group(1) in grid and g != grid[m.group(1)]:
+                continue
             if g > best.get(m.group(1), (0, 0))[0]:
                 best[m.group(1)] = (g, int(m.group(3)))
     if len(best) != len(names):
