@@ -22,12 +22,26 @@ def _records(path):
     return out
 
 
-def test_traffic_classes_sum_their_kernels():
-    rec = _records(bench.TRAFFIC_FILE)
+def test_traffic_classes_sum_their_kernels(tmp_path, monkeypatch):
+    """Each kernel class adds the records of its kernels (the committed
+    records, re-stamped with the current source hashes so that only the
+    mapping is under test)."""
+    import hashlib
+    import re
+
+    sha = {f: hashlib.sha1(open(os.path.join(bench.CSRC, f), "rb").read()).hexdigest() for f in ("sym.hip", "kivi.hip")}
+    text = open(bench.TRAFFIC_FILE).read()
+    text = re.sub(r"(traffic (sym|kivi)\S*.*?src_sha1=)[0-9a-f]+",
+                  lambda m: m.group(1) + sha["sym.hip" if m.group(2) == "sym" else "kivi.hip"], text)
+    f = tmp_path / "traffic.md"
+    f.write_text(text)
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    rec = _records(str(f))
     # the long-context chunk class: 64 launches of the q6 write kernel at the chunk's grid,
     # not the paged prefill's record of the same kernel
     assert bench.measured_traffic("quant_chunks_q6_x64") == 64 * rec[("sym_quant_v8<6, 32, 2>", 8388608)]
     assert bench.measured_traffic("quant_prefill_q6") == rec[("sym_quant_v8<6, 32, 2>", 1073741824)]
+    assert bench.measured_traffic("dequant_full_q6") == rec[("sym_dequant_page<6, 256>", 538968064)]
     assert bench.measured_traffic("kivi_pack_b2") == (rec[("kivi_keys_fast<2, 8, 4, true>", 16515072)] +
                                                       rec[("kivi_values_fast<2, 8, 4, 4, true>", 16515072)])
     assert bench.measured_traffic("no_such_class") is None
