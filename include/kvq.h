@@ -344,7 +344,7 @@ int kvq_nuq_fit_quant(const uint16_t *keys, const uint16_t *values, int32_t BH, 
  * in the array are cleared by the call's first kernel. Arguments, outputs and
  * errors as kvq_nuq_fit_quant, plus KVQ_ERR_CAPACITY when the call needs more
  * workspace than the array holds (kvq_nuq_workspace_bytes gives the need:
- * e.g. 32 (batch, head) vectors x 4096 tokens x D = 128 need about 2 MiB).
+ * e.g. 32 (batch, head) vectors x 4096 tokens x D = 128 need about 3 MiB).
  * All calls on one device share the one array: calls that overlap on a
  * device (other streams, other host threads) race and must be serialised by
  * the caller. */

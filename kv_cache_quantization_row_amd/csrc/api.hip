@@ -479,10 +479,11 @@ struct NuqPlan {
   int n_sink_eff, n_fit, key_cpc, val_cpc;
   int64_t kb, vb;  // outlier bounds
   int64_t vs;      // value staging slots: k_val per token of every value workgroup
-  int64_t ks;      // key staging slots: kb, or BH*S*D for a small call
+  int64_t ks;      // key staging slots: BH*S*D for a small call, else none (the outlier bitmap)
   bool small;      // at most 256 (batch, head, token) vectors: one fused kernel and one placement workgroup
   int64_t k_blk_x, v_nblk;
-  int64_t off_ctr, off_kblk, off_vblk, off_ksup, off_vsup, off_kpos, off_kval, off_vpos, off_vval, off_kdat, total;
+  int64_t off_ctr, off_kblk, off_vblk, off_ksup, off_vsup, off_kpos, off_kval, off_vpos, off_vval, off_kdat, off_kbits,
+      total;
 };
 
 // outliers per vector of n samples: floor(frac * n), one binary64 product
@@ -522,9 +523,10 @@ int nuq_plan(int32_t BH, int32_t S, int32_t D, int32_t bits, int32_t start_pos, 
   p.off_ksup = o; o = align256(o + (p.k_blk_x * BH + 63) / 64 * 4);
   p.off_vsup = o; o = align256(o + (p.v_nblk + 63) / 64 * 4);
   // a small call's key workgroups stage at the flat index of their first
-  // element (no shared counter to clear)
+  // element (no shared counter to clear); other calls mark key outliers in a
+  // bitmap, from which the placement emits them in flat order
   p.small = p.val_cpc == 0 && (int64_t)BH * S <= 256;
-  p.ks = p.small ? (int64_t)BH * S * D : p.kb;
+  p.ks = p.small ? (int64_t)BH * S * D : 0;
   p.off_kpos = o; o = align256(o + p.ks * 4);
   p.off_kval = o; o = align256(o + p.ks * 2);
   // value workgroups stage their outliers at fixed offsets (no shared
@@ -535,6 +537,7 @@ int nuq_plan(int32_t BH, int32_t S, int32_t D, int32_t bits, int32_t start_pos, 
   // a key fit over more tokens than fit in LDS keeps its bucketed samples here
   const int64_t kdat = fit_keys && p.n_fit > kvq::NUQ_KFIT_LDS_N ? (int64_t)BH * D * ((p.n_fit + 15) / 16 * 16) : 0;
   p.off_kdat = o; o = align256(o + kdat);
+  p.off_kbits = o; o = align256(o + (p.small ? 0 : (int64_t)BH * S * (D / 8)));
   p.total = o;
   return KVQ_OK;
 }
@@ -613,6 +616,7 @@ int nuq_call(const uint16_t *keys, const uint16_t *values, int32_t BH, int32_t S
   a.ws_vpos = reinterpret_cast<int32_t *>(ws + p.off_vpos);
   a.ws_vval = reinterpret_cast<uint16_t *>(ws + p.off_vval);
   a.ws_kdat = ws + p.off_kdat;
+  a.ws_kbits = ws + p.off_kbits;
   a.k_cap = p.kb;
   a.k_scap = p.ks;
   a.small = p.small ? 1 : 0;

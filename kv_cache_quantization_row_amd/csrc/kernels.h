@@ -81,8 +81,10 @@ struct NuqArgs {
   uint32_t *ws_ksup, *ws_vsup;     // per 64 workgroups: sum of their counts
   int32_t *ws_kpos, *ws_vpos;      // staging
   uint8_t *ws_kdat;                // key fit over more than 8192 tokens: bucketed key bytes [BH][D][round16(n)]
-  int64_t k_cap, v_cap;            // list entries (the outlier bounds); key staging is k_cap entries too
-  int64_t k_scap;                  // key staging entries (k_cap, or BH*S*D for a small call)
+  uint8_t *ws_kbits;               // calls that are not small: key outlier bitmap [BH][S][D/8], bit e of byte g
+                                   // for channel 8g+e (each key producer writes its bytes; no staging)
+  int64_t k_cap, v_cap;            // list entries (the outlier bounds)
+  int64_t k_scap;                  // key staging entries: BH*S*D for a small call, else 0 (the bitmap)
   int32_t small;                   // 1: a small call (one fused kernel, then one placement workgroup); key
                                    // workgroups stage at the flat index of their first element, nothing
                                    // needs a zeroed counter

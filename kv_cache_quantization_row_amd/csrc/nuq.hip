@@ -37,6 +37,8 @@
 // Keys at prefill: a counting sort of each channel's samples by the high byte
 // of their order key, then every query of the fit is a table read plus one
 // bucket scan (the "bucketed key fit" section below); sums there are int64.
+// The Lloyd iterations of up to 8 levels run four channels per wave, one
+// 16-lane row each ("Lloyd by rows").
 // Up to 4,096 vectors the value fit runs one token per wave instead
 // (value_wave_body: keys sorted across the wave, sorted keys and exact
 // prefix sums in the wave's LDS, one level per lane); beyond that at D = 128
@@ -45,12 +47,15 @@
 // Codes are #{j : x > T_j}, which equals the first index of the nearest
 // level (a binary search over the sorted cut keys, two samples per packed
 // step). The side channel (flat index, fp16 value) is emitted in ascending
-// flat order: each producer workgroup stages its entries (value workgroups
-// at fixed ranges, k_val slots per token; key workgroups in a range reserved
-// with one atomic, or at the flat index of their first element in a small
-// call) and records its count; the placement kernel puts every workgroup's
-// entries at the sum of the counts before it (per-64-workgroup sums; no
-// inter-workgroup waiting).
+// flat order: each producer workgroup records its count of outliers and
+// either stages its entries (value workgroups at fixed ranges, k_val slots
+// per token; key workgroups of a small call at the flat index of their first
+// element) or, for keys otherwise, marks them in a bitmap with one bit per
+// key element; the placement kernel puts every workgroup's entries at the
+// sum of the counts before it (per-64-workgroup sums; no inter-workgroup
+// waiting), a bitmap block's as its set bits in order with the values read
+// back from the keys.
+#include <algorithm>
 #include <mutex>
 
 
@@ -964,13 +969,21 @@ __device__ __forceinline__ uint32_t kb_tau(const V &v, uint32_t kp1) {
   return ((uint32_t)astar << 8) | w;
 }
 
-// the fit of one channel by one wave. Lane j < L holds level j and lane
-// j < L-1 cut j (its key and the count and exact sum at it).
+// a channel's inlier range: keys [klo, khi]; lo samples have keys below klo
+// and hi samples keys at most khi, with exact sums s_lo and s_hi
+struct KbInl {
+  uint32_t klo, khi, lo, hi;
+  int64_t s_lo, s_hi;
+};
+
+// the start of one channel's fit by one wave: tau, the inlier range and the
+// quantile initialisation (lane j < L: level j)
 template <int L, typename V>
-__device__ void kb_fit(const V &v, uint32_t n, int kout, int iters, float &lev_me, uint16_t &tau_out) {
+__device__ void kb_init(const V &v, uint32_t n, int kout, float &lev_me, uint16_t &tau_out, KbInl &r) {
   const int lane = threadIdx.x & 63;
   lev_me = 0.0f;
   tau_out = 0;
+  r = KbInl{0, 0, 0, 0, 0, 0};
   if (n == 0) return;
   const uint32_t tau = kb_tau(v, (uint32_t)kout + 1u);
   tau_out = (uint16_t)tau;
@@ -1002,6 +1015,16 @@ __device__ void kb_fit(const V &v, uint32_t n, int kout, int iters, float &lev_m
     }
     if (lane == j) lev_me = (float)x + 0.0f;
   }
+  r = KbInl{klo, khi, lo, hi, s_lo, s_hi};
+}
+
+// Lloyd iterations of one channel by one wave. Lane j < L holds level j and
+// lane j < L-1 cut j (its key and the count and exact sum at it).
+template <int L, typename V>
+__device__ void kb_lloyd_wave(const V &v, const KbInl &r, int iters, float &lev_me) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t klo = r.klo, khi = r.khi, lo = r.lo, hi = r.hi;
+  const int64_t s_lo = r.s_lo, s_hi = r.s_hi;
   // Lloyd iterations: cells are key ranges cut at exact fp16 thresholds.
   // The cuts' keys and the count and exact sum at each are wave-uniform
   // (scalar registers); lane j picks its cell's upper bound by lane-indexed
@@ -1098,15 +1121,180 @@ __device__ void kb_fit(const V &v, uint32_t n, int kout, int iters, float &lev_m
   if (lane >= L) lev_me = 0.0f;
 }
 
+// ------------------------------------------------------------------ Lloyd by rows
+// The Lloyd iterations of four channels per wave, one 16-lane row each (up
+// to KB_ROW_MAX_L levels). Every lane of a row holds the channel's whole
+// level table and every cut; the bucket scans stride over the row's 16
+// lanes, and a row sum takes four DPP adds (no readlane). Each lane j < L
+// of the row computes the mean of cell j, and the row reads the new table
+// back from its LDS slot. The arithmetic is that of kb_lloyd_wave: the same
+// cut keys, exact int64 cell sums, binary32 means and ordering rule.
+constexpr int KB_ROW_MAX_L = 8;
+
+// sum over the lane's 16-lane row, in every lane of the row
+__device__ __forceinline__ uint32_t row_sum(uint32_t v) {
+  v += dppm<DPP_XOR1>(v);
+  v += dppm<DPP_XOR2>(v);
+  v += dppm<DPP_HALF_MIRROR>(v);
+  v += dppm<DPP_MIRROR>(v);
+  return v;
+}
+
+// kb_le_many for the row's channel (tables pre / end, bucketed low bytes
+// dat): count and exact sum at every cut whose bit is set in need
+template <int NC>
+__device__ __forceinline__ void kb_le_rows(const uint64_t *pre, const uint32_t *end, const uint8_t *dat,
+                                           const uint32_t *T, uint32_t need, uint32_t *cnt, int64_t *sum) {
+  const uint32_t gl = threadIdx.x & 15;
+  uint32_t s0[NC], e0[NC], c[NC], sl[NC], t2[NC];
+  uint32_t maxw = 0;
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    c[j] = sl[j] = 0;
+    t2[j] = (T[j] & 0xffu) * 0x10001u;
+    const int b = (int)(T[j] >> 8);
+    const bool nd = (need >> j) & 1u;
+    s0[j] = nd && b > 0 ? end[b - 1] : 0u;
+    e0[j] = nd ? end[b] : 0u;
+    if (e0[j] > s0[j]) maxw = max(maxw, ((e0[j] + 3u) >> 2) - (s0[j] >> 2));
+  }
+  for (uint32_t i = gl; i < maxw; i += 16) {
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const uint32_t p0 = ((s0[j] >> 2) + i) << 2;
+      if (p0 < e0[j]) {
+        const uint32_t w = kb_word(dat, p0);
+        const uint32_t nb = min(e0[j] - p0, 4u);
+        const uint32_t sk = s0[j] > p0 ? s0[j] - p0 : 0u;
+        const uint32_t m = ((nb == 4u ? 0x01010101u : (0x01010101u & ((1u << (8 * nb)) - 1u))) >> (8 * sk)) << (8 * sk);
+        const uint32_t le = kb_le_bytes(w, t2[j]) & m;
+        c[j] = __builtin_amdgcn_udot4(le, 0x01010101u, c[j], false);
+        sl[j] = __builtin_amdgcn_udot4(w, le, sl[j], false);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    cnt[j] = 0;
+    sum[j] = 0;
+    if (!__any((need >> j) & 1u)) continue;
+    const uint32_t cc = row_sum(c[j]), ss = row_sum(sl[j]);
+    const int b = (int)(T[j] >> 8);
+    bool neg;
+    int sh;
+    uint32_t mbase;
+    kb_bucket(b, neg, sh, mbase);
+    const uint64_t hl = neg ? (uint64_t)cc * 255u - ss : (uint64_t)ss;
+    const int64_t u = (int64_t)(((uint64_t)cc * mbase + hl) << sh);
+    cnt[j] = s0[j] + cc;
+    sum[j] = (int64_t)pre[b] + (neg ? -u : u);
+  }
+}
+
+// lev: the row's level table (ascending, in every lane); xch: the row's LDS
+// slot of L floats
+template <int L>
+__device__ void kb_lloyd_rows(const uint64_t *pre, const uint32_t *end, const uint8_t *dat, float *xch,
+                              const KbInl &r, int iters, float (&lev)[L]) {
+  const uint32_t gl = threadIdx.x & 15;
+  uint32_t Tp[L - 1], Cu[L - 1];  // previous cut keys (none yet), counts at the cuts
+  int64_t Su[L - 1];              // exact sums at the cuts
+#pragma unroll
+  for (int j = 0; j < L - 1; ++j) {
+    Tp[j] = 0xffffffffu;
+    Cu[j] = r.hi;
+    Su[j] = r.s_hi;
+  }
+#pragma unroll 1
+  for (int it = 0; it < iters; ++it) {
+    // cut keys from the top (equal levels take the cut above), clamped to
+    // the inliers; a cut where it was last iteration, or where the cut
+    // above it is, keeps that result
+    uint32_t T[L - 1];
+    uint32_t need = 0, nt = 0xffffu;
+#pragma unroll
+    for (int j = L - 2; j >= 0; --j) {
+      if (lev[j] < lev[j + 1]) nt = key16(thr16(lev[j], lev[j + 1]));
+      T[j] = min(max(nt, r.klo - 1), r.khi);
+      const bool same_up = j < L - 2 && T[j] == T[j + 1];
+      if (T[j] != Tp[j] && !same_up) need |= 1u << j;
+    }
+    uint32_t qc[L - 1];
+    int64_t qs[L - 1];
+    kb_le_rows<L - 1>(pre, end, dat, T, need, qc, qs);
+    uint32_t c_up = r.hi;
+    int64_t s_up = r.s_hi;
+#pragma unroll
+    for (int j = L - 2; j >= 0; --j) {
+      if ((need >> j) & 1u) {
+        Cu[j] = qc[j];
+        Su[j] = qs[j];
+      } else if (T[j] != Tp[j]) {  // the same key as the cut above
+        Cu[j] = c_up;
+        Su[j] = s_up;
+      }
+      Tp[j] = T[j];
+      c_up = Cu[j];
+      s_up = Su[j];
+    }
+    // lane gl < L: level gl from its cell (cut gl-1, cut gl] (cut -1: lo,
+    // cut L-1: hi); an empty cell keeps its level
+    uint32_t c_top = r.hi, c_bot = r.lo;
+    int64_t s_top = r.s_hi, s_bot = r.s_lo;
+    float nl = 0.0f;
+#pragma unroll
+    for (int j = 0; j < L; ++j) nl = gl == (uint32_t)j ? lev[j] : nl;
+#pragma unroll
+    for (int j = 0; j < L - 1; ++j) {
+      c_top = gl == (uint32_t)j ? Cu[j] : c_top;
+      s_top = gl == (uint32_t)j ? Su[j] : s_top;
+      c_bot = gl == (uint32_t)j + 1 ? Cu[j] : c_bot;
+      s_bot = gl == (uint32_t)j + 1 ? Su[j] : s_bot;
+    }
+    const bool mine = gl < (uint32_t)L;
+    if (mine && c_top > c_bot) nl = kb_mean(s_top - s_bot, c_top - c_bot);
+    const bool any_empty = __any(mine && c_top <= c_bot);
+    if (mine) xch[gl] = nl;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    float nw[L];
+#pragma unroll
+    for (int j = 0; j < L; ++j) nw[j] = xch[j];
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    // with an empty cell, keep the table ordered (the odd-even transposition
+    // network of kb_lloyd_wave); without one the means are already ascending
+    if (any_empty) {
+#pragma unroll
+      for (int p = 0; p < L; ++p) {
+#pragma unroll
+        for (int j = p & 1; j + 1 < L; j += 2) {
+          const float x = nw[j], y = nw[j + 1];
+          nw[j] = lmin(x, y);
+          nw[j + 1] = lmax(x, y);
+        }
+      }
+    }
+    bool changed = false;
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+      changed |= __float_as_uint(nw[j]) != __float_as_uint(lev[j]);
+      lev[j] = nw[j];
+    }
+    if (__ballot(changed) == 0) break;  // every row at a fixed point
+  }
+}
+
 }  // namespace
 
 // ================================================================== kernels
 // staging counters and the per-64-workgroup count sums start at zero
 __global__ __launch_bounds__(256) void nuq_zero(NuqArgs a) {
-  if (threadIdx.x < 4) a.ws_ctr[threadIdx.x] = 0;
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x, nthr = (int64_t)gridDim.x * 256;
+  if (g < 4) a.ws_ctr[g] = 0;
   const int64_t ks = (a.k_blk_x * a.BH + 63) >> 6, vs = (a.v_nblk + 63) >> 6;
-  for (int64_t i = threadIdx.x; i < ks; i += 256) a.ws_ksup[i] = 0;
-  for (int64_t i = threadIdx.x; i < vs; i += 256) a.ws_vsup[i] = 0;
+  for (int64_t i = g; i < ks; i += nthr) a.ws_ksup[i] = 0;
+  for (int64_t i = g; i < vs; i += nthr) a.ws_vsup[i] = 0;
 }
 
 // Key quantize against the (frozen or just fitted) per-channel tables. A
@@ -1239,9 +1427,31 @@ __device__ __forceinline__ void key_quant_body(const NuqArgs &a, int bx, int bh,
       *reinterpret_cast<uint4 *>(a.k_recon + ((size_t)bh * a.S + row) * D + ck * 8) =
           make_uint4(rec[0], rec[1], rec[2], rec[3]);
   }
-  // ---- ordered compaction: flat order is (wave, step, lane, channel). Step
-  // counts (<= 8 per lane, <= 512 per wave) are scanned three at a time in
-  // 10-bit fields of one word.
+  if (!a.small) {
+    // ---- the outlier bitmap (byte ck of each row: this lane's 8 channels)
+    // and the block's count; the placement emits the entries in flat order
+    uint8_t *kbits = a.ws_kbits + (size_t)bh * a.S * (D / 8) + ck;
+    int n = 0;
+#pragma unroll
+    for (int it = 0; it < KQ_NIT; ++it) {
+      const int row = row_w + it * RPW;
+      if (row < a.S) kbits[(size_t)row * (D / 8)] = (uint8_t)omask[it];
+      n += __builtin_popcount(omask[it]);
+    }
+    int tot;
+    (void)wave_excl(n, tot);
+    if (lane == 0) wave_cnt[wv] = tot;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const uint32_t btot = (uint32_t)(wave_cnt[0] + wave_cnt[1] + wave_cnt[2] + wave_cnt[3]);
+      a.ws_kblk[blk * 2 + 1] = btot;  // the block's only producer
+      if (btot) atomicAdd(&a.ws_ksup[blk >> 6], btot);
+    }
+    return;
+  }
+  // ---- ordered compaction (a small call): flat order is (wave, step, lane,
+  // channel). Step counts (<= 8 per lane, <= 512 per wave) are scanned three
+  // at a time in 10-bit fields of one word.
   int pre[KQ_NIT], stot[KQ_NIT];
 #pragma unroll
   for (int g = 0; g < KQ_NIT; g += 3) {
@@ -1275,11 +1485,8 @@ __device__ __forceinline__ void key_quant_body(const NuqArgs &a, int bx, int bh,
   }
   if (threadIdx.x == 0) {
     // a small call stages at the flat index of the workgroup's first element
-    // (its entries never exceed its rows times D); otherwise one atomic
-    // reserves the range and the per-64-workgroup sum feeds the placement
-    const uint32_t base = a.small ? (uint32_t)(((int64_t)bh * a.S + (int64_t)bx * (4 * RPW * KQ_NIT)) * D)
-                                  : (btot ? atomicAdd(&a.ws_ctr[0], (uint32_t)btot) : 0u);
-    if (btot && !a.small) atomicAdd(&a.ws_ksup[blk >> 6], (uint32_t)btot);
+    // (its entries never exceed its rows times D)
+    const uint32_t base = (uint32_t)(((int64_t)bh * a.S + (int64_t)bx * (4 * RPW * KQ_NIT)) * D);
     blk_base = base;
     a.ws_kblk[blk * 2] = base;
     a.ws_kblk[blk * 2 + 1] = (uint32_t)btot;
@@ -2277,6 +2484,47 @@ __global__ __launch_bounds__(256) void nuq_place(NuqArgs a, int64_t kn) {
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = part;
   __syncthreads();
   const uint32_t off = red[0] + red[1] + red[2] + red[3];
+  if (!isv) {
+    // key block b: 16384/D rows of one (b, h), 2048 bitmap bytes in flat
+    // order; thread t holds bytes [8t, 8t + 8) (elements 64t .. 64t + 63),
+    // an exclusive prefix of the threads' counts orders the entries, and
+    // each value is read back from the keys
+    const int64_t bh = b / a.k_blk_x, RB = 16384 / a.D;
+    const int64_t r0 = (b - bh * a.k_blk_x) * RB;
+    const int64_t nbytes = (min(RB, (int64_t)a.S - r0)) * (a.D / 8);
+    const int64_t e0 = ((int64_t)bh * a.S + r0) * a.D;  // flat index of the block's first element
+    const uint32_t *bw = reinterpret_cast<const uint32_t *>(a.ws_kbits + e0 / 8);
+    uint32_t m0 = 0, m1 = 0;
+    if (8 * (int64_t)threadIdx.x < nbytes) {  // the rows' bytes come in whole 4-byte words (D/8 >= 4)
+      m0 = bw[2 * threadIdx.x];
+      if (8 * (int64_t)threadIdx.x + 4 < nbytes) m1 = bw[2 * threadIdx.x + 1];
+    }
+    const uint32_t c = (uint32_t)(__builtin_popcount(m0) + __builtin_popcount(m1));
+    const uint32_t incl = kb_wscan(c);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 63) red[threadIdx.x >> 6] = incl;
+    __syncthreads();
+    uint32_t pre = incl - c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pre += i < (int)(threadIdx.x >> 6) ? red[i] : 0u;
+    int64_t slot = (int64_t)off + pre;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t m = h ? m1 : m0;
+      while (m) {
+        const int k = __builtin_ctz(m);
+        m &= m - 1;
+        const int64_t e = e0 + 64 * (int64_t)threadIdx.x + 32 * h + k;
+        if (slot < a.k_cap) {  // holds by the outlier bound; never written past otherwise
+          a.k_opos[slot] = (int32_t)e;
+          a.k_oval[slot] = a.keys[e];
+        }
+        ++slot;
+      }
+    }
+    if (b == nblk - 1 && threadIdx.x == 255) a.out_counts[0] = (int64_t)off + pre + c;  // the last thread's end
+    return;
+  }
   const uint32_t base = info[2 * b], cnt = info[2 * b + 1];
   const int32_t *spos = isv ? a.ws_vpos : a.ws_kpos;
   const uint16_t *sval = isv ? a.ws_vval : a.ws_kval;
@@ -2405,14 +2653,39 @@ __global__ __launch_bounds__(KB_T) void nuq_key_fit_bk(NuqArgs a) {
     }
   }
   __syncthreads();
-  // ---- the fit of channel d0 + w by wave w
+  // ---- the fit of channel d0 + w by wave w: tau, inliers, initial levels
   KbView<const uint8_t *, H16> v{tab + w * 257, cur + w * 256, dat + (size_t)w * npad, hist + w * KB_HW};
   float mine;
   uint16_t tau;
-  kb_fit<L>(v, (uint32_t)n, a.k_key, a.iters, mine, tau);
+  KbInl inl;
+  kb_init<L>(v, (uint32_t)n, a.k_key, mine, tau, inl);
   const size_t ch = (size_t)bh * a.D + d0 + w;
-  if (lane < L) a.key_levels[ch * L + lane] = mine;
   if (lane == 0) a.key_thresh[ch] = tau;
+  if constexpr (L > KB_ROW_MAX_L) {
+    if (n > 0) kb_lloyd_wave<L>(v, inl, a.iters, mine);
+    if (lane < L) a.key_levels[ch * L + lane] = mine;
+  } else {
+    // ---- Lloyd iterations by rows: wave w hands its channel over in its
+    // histogram words (free now: the level table, then the inlier range), and
+    // waves 0 .. KB_CH/4 - 1 take four channels each
+    static_assert(KB_CH % 4 == 0 && 16 * 4 + sizeof(KbInl) <= 128 * 4, "row slots");
+    float *slot = reinterpret_cast<float *>(hist + w * KB_HW);
+    if (lane < L) slot[lane] = mine;
+    if (lane == 0) *reinterpret_cast<KbInl *>(slot + 16) = inl;
+    __syncthreads();
+    if (w >= KB_CH / 4) return;
+    const int c = 4 * w + (lane >> 4), gl = lane & 15;
+    float *cs = reinterpret_cast<float *>(hist + c * KB_HW);
+    const KbInl r = *reinterpret_cast<const KbInl *>(cs + 16);
+    float lev[L];
+#pragma unroll
+    for (int j = 0; j < L; ++j) lev[j] = cs[j];
+    if (n > 0) kb_lloyd_rows<L>(tab + c * 257, cur + c * 256, dat + (size_t)c * npad, cs, r, a.iters, lev);
+    float out = 0.0f;
+#pragma unroll
+    for (int j = 0; j < L; ++j) out = gl == j ? lev[j] : out;
+    if (gl < L) a.key_levels[((size_t)bh * a.D + d0 + c) * L + gl] = out;
+  }
 }
 
 // ================================================================== launch
@@ -2432,21 +2705,23 @@ hipError_t launch_key_fit(const NuqArgs &a, int /*cpc*/, hipStream_t st) {
   return hipGetLastError();
 }
 // The value fit reads nothing the key kernels write, so for many tokens it
-// runs on a second stream of the device, forked from the caller's stream
-// after the counters are cleared and joined before the placement kernel: the
-// two fits then share the machine instead of running back to back. The key
-// fit is submitted before the value fit: it heads the longer chain (key fit,
-// key quantization, placement), and the value workgroups take the LDS the
-// key fit leaves free (two key-fit workgroups with 16-bit histograms leave
-// room for one value workgroup per CU). Submitted the other way round, the
-// value fit filled the CUs first and delayed the key fit (prefill 0.205 ->
-// 0.185 ms in a kernel trace). One stream and two events per device,
-// created on first use (default priority); the fork/join section is
-// serialised on the host so that concurrent callers never interleave their
-// event records.
+// runs on a second stream of the device, forked from the caller's stream at
+// the start of the call and joined before the placement kernel: the two fits
+// then share the machine instead of running back to back. The key fit is
+// submitted first, right after the fork point: it heads the longer chain (key
+// fit, key quantization, placement), and the value workgroups take the LDS
+// the key fit leaves free (two key-fit workgroups with 16-bit histograms
+// leave room for one value workgroup per CU). Submitted the other way round,
+// the value fit filled the CUs first and delayed the key fit (prefill 0.205
+// -> 0.185 ms in a kernel trace). The counters are cleared on the second
+// stream ahead of the value fit, and the key quantization waits for that
+// clear (a third event), so that no launch stands between the fork point and
+// the key fit. One stream and three events per device, created on first use
+// (default priority); the fork/join section is serialised on the host so
+// that concurrent callers never interleave their event records.
 struct Fork {
   hipStream_t aux = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr, zero = nullptr;
 };
 std::mutex g_fork_mu;
 Fork g_fork[64];
@@ -2459,6 +2734,7 @@ hipError_t fork_for_device(Fork *&f) {  // g_fork_mu held
   if (f->aux == nullptr) {
     if ((e = hipEventCreateWithFlags(&f->fork, hipEventDisableTiming)) != hipSuccess) return e;
     if ((e = hipEventCreateWithFlags(&f->join, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&f->zero, hipEventDisableTiming)) != hipSuccess) return e;
     if ((e = hipStreamCreateWithFlags(&f->aux, hipStreamNonBlocking)) != hipSuccess) return e;
   }
   return hipSuccess;
@@ -2502,22 +2778,31 @@ hipError_t launch_bits(const NuqArgs &a, int key_cpc, int val_cpc, bool fork, hi
     hipLaunchKernelGGL(nuq_place_small, dim3(1), dim3(256), 0, st, a, kn, ntok);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(nuq_zero, dim3(1), dim3(256), 0, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const dim3 zgrid((unsigned)std::min<int64_t>(
+      (std::max<int64_t>(a.k_blk_x * a.BH, a.v_nblk) / 64 + 4095) / 4096 + 1, 256));
   if (val_cpc == 0 || !fork) {  // few tokens (a cross-stream join costs more than it hides), or one stream asked for
+    hipLaunchKernelGGL(nuq_zero, zgrid, dim3(256), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     if (a.fit_keys && (e = launch_key_fit<L>(a, key_cpc, st)) != hipSuccess) return e;
     hipLaunchKernelGGL((nuq_key_quant<BITS>), dim3((unsigned)a.k_blk_x, a.BH), dim3(256), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = launch_values<BITS>(a, val_cpc, st)) != hipSuccess) return e;
   } else {
+    // the key fit starts first, right after the fork point; the counters
+    // are cleared on the second stream ahead of the value fit, and the key
+    // quantization (their other user) waits for that
     std::lock_guard<std::mutex> lock(g_fork_mu);
     Fork *f = nullptr;
     if ((e = fork_for_device(f)) != hipSuccess) return e;
     if ((e = hipEventRecord(f->fork, st)) != hipSuccess) return e;
     if (a.fit_keys && (e = launch_key_fit<L>(a, key_cpc, st)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(f->aux, f->fork, 0)) != hipSuccess) return e;
+    hipLaunchKernelGGL(nuq_zero, zgrid, dim3(256), 0, f->aux, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = hipEventRecord(f->zero, f->aux)) != hipSuccess) return e;
     if ((e = launch_values<BITS>(a, val_cpc, f->aux)) != hipSuccess) return e;
     if ((e = hipEventRecord(f->join, f->aux)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(st, f->zero, 0)) != hipSuccess) return e;
     hipLaunchKernelGGL((nuq_key_quant<BITS>), dim3((unsigned)a.k_blk_x, a.BH), dim3(256), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(st, f->join, 0)) != hipSuccess) return e;

@@ -143,7 +143,7 @@ int main() {
   EXPECT(kvq_nuq_fit_quant(F16, F16, 32, 64, 128, big, 3, 0.01, big, big, 0, Ff, F16, Ff, F, F, Fi, F16, Fi, F16,
                            INT64_MAX, Fl, nullptr, nullptr, F, INT64_MAX, nullptr),
          KVQ_ERR_ARG);
-  EXPECT(kvq_nuq_fit_quant_noalloc(F16, F16, 64, 1000, 128, 5, 3, 0.01, 8, 4, 0, Ff, F16, Ff, F, F, Fi, F16, Fi,
+  EXPECT(kvq_nuq_fit_quant_noalloc(F16, F16, 64, 2000, 128, 5, 3, 0.5, 8, 4, 0, Ff, F16, Ff, F, F, Fi, F16, Fi,
                                    F16, INT64_MAX, Fl, nullptr, nullptr, nullptr),
          KVQ_ERR_CAPACITY);
   EXPECT(kvq_nuq_fit_quant_noalloc(F16, F16, 2, 64, 96, 0, 3, 0.01, 8, 4, 1, Ff, F16, Ff, F, F, Fi, F16, Fi, F16,

@@ -433,3 +433,26 @@ def test_many_tokens_degenerate_values(case, bits, D):
         r = oracle.nuq_fit_quant(k, v, 0, bits, frac, iters, 4, 1)
         compare(g, r, keys=["value_levels", "v_codes", "v_recon"],
                 what="%s bits=%d D=%d frac=%g iters=%d" % (case, bits, D, frac, iters))
+
+
+@pytest.mark.parametrize("D,bits", [(128, 3), (32, 2), (256, 4)])
+def test_frozen_levels_dense_outliers(D, bits):
+    """A prefill-sized call against given key levels and thresholds (not a
+    small call): key outliers come from the per-row bitmap, so channels with a
+    low threshold put many outliers in every row and in every key block
+    (16384/D rows), the last block is ragged, and the first rows are sinks.
+    Codes, reconstructions and both outlier lists match the oracle."""
+    say("nuq frozen dense outliers", D, bits)
+    L = 1 << bits
+    rb = 16384 // D
+    BH, S = 3, 2 * rb + 37
+    k, v = t4((BH, S, D), 900 + D), t4((BH, S, D), 950 + D)
+    fit = oracle.nuq_fit_quant(k[:, :64], v[:, :64], 0, bits, 0.05, 4, 0, 1)  # levels from a short fit
+    kl = fit["key_levels"]
+    kt = fit["key_thresh"].copy()
+    kt[:, ::3] = np.float16(0.5).view(np.uint16)   # about half of these channels' samples are outliers
+    kt[:, 1::5] = np.float16(0.0).view(np.uint16)  # every nonzero sample of these is one
+    g = gpu_nuq(k, v, 0, bits, 0.03, 8, 4, 0, kl, kt)
+    r = oracle.nuq_fit_quant(k, v, 0, bits, 0.03, 8, 4, 0, kl, kt)
+    assert len(r["k_out"][0]) > BH * S * D // 8, "the case must be dense in key outliers"
+    compare(g, r, what="frozen dense outliers")

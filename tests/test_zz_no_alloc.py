@@ -89,12 +89,12 @@ def test_noalloc_matches_the_workspace_entry_on_consecutive_calls():
 
 def test_noalloc_refuses_a_call_above_its_workspace():
     d = dev()
-    BH, S, D = 64, 1000, 128  # decode-style call: every key may be an outlier, > 32 MiB of staging
-    assert kvq.kvq_nuq_workspace_bytes(BH, S, D, 3, 5, 4, 0.01, 0) > kvq.NUQ_NOALLOC_WORKSPACE_BYTES
+    BH, S, D = 64, 2000, 128  # half of every token's values may be outliers: > 32 MiB of value staging
+    assert kvq.kvq_nuq_workspace_bytes(BH, S, D, 3, 5, 4, 0.5, 0) > kvq.NUQ_NOALLOC_WORKSPACE_BYTES
     k = torch.zeros((BH, S, D), dtype=torch.float16, device=d)
-    o = _outputs(BH, S, D, 3, 5, 4, 0.01, 0, d)
+    o = _outputs(BH, S, D, 3, 5, 4, 0.5, 0, d)
     with pytest.raises(kvq.KvqError) as e:
-        kvq.kvq_nuq_fit_quant_noalloc(k, k, 5, 3, 0.01, 8, 4, 0, o["key_levels"], o["key_thresh"],
+        kvq.kvq_nuq_fit_quant_noalloc(k, k, 5, 3, 0.5, 8, 4, 0, o["key_levels"], o["key_thresh"],
                                       o["value_levels"], o["k_codes"], o["v_codes"], o["k_opos"], o["k_oval"],
                                       o["v_opos"], o["v_oval"], o["out_counts"])
     assert e.value.code == kvq.KVQ_ERR_CAPACITY
