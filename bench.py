@@ -965,7 +965,31 @@ class Caches:
                             "8192-token prefill) 32 one-token steps returning the whole fp16 K/V"}
 
     def cpu_baseline(self, budget_tokens):
-        return None
+        """Oracle cache model (KiviPackedCacheModel) on one of the 128 batch
+        rows of the packed KIVI cache: its 8192-token prefill untimed, then
+        one-token decode steps, each handing back the whole fp16 K/V (the same
+        elements per row as the GPU figure). The NUQ cache steps are not in
+        the sample."""
+        import numpy as np
+        import torch as _t
+        from oracle.caches import KiviPackedCacheModel
+        from kv_cache_quantization_row_amd import inputs
+
+        H, D, n0, steps = 8, 64, 8192, 64  # two group flushes among the steps, as on the GPU
+        kk, vv = inputs.kivi_kv(1, H, n0 + steps, D, seed=1003)
+        k, v = (x.contiguous().view(_t.int16).numpy().view(np.uint16) for x in (kk, vv))
+        m = KiviPackedCacheModel(2, 32, 128)
+        m.update(k[:, :, :n0], v[:, :, :n0])
+        t0 = time.perf_counter()
+        elems = 0
+        for t in range(steps):
+            ko, vo = m.update(k[:, :, n0 + t:n0 + t + 1], v[:, :, n0 + t:n0 + t + 1])
+            elems += ko.size + vo.size
+        dt = time.perf_counter() - t0
+        return {"value": round(2 * elems / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": "packed KIVI cache model, one batch row (8 KV heads x D=64, b=2, group 32, residual "
+                          "128): %d one-token decode steps after an untimed 8192-token prefill (%.1f s); the "
+                          "NUQ cache steps are not in the sample" % (steps, dt)}
 
 
 class Copy:
