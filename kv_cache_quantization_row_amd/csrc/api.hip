@@ -482,7 +482,7 @@ struct NuqPlan {
   int64_t ks;      // key staging slots: BH*S*D for a small call, else none (the outlier bitmap)
   bool small;      // at most 256 (batch, head, token) vectors: one fused kernel and one placement workgroup
   int64_t k_blk_x, v_nblk;
-  int64_t off_ctr, off_kblk, off_vblk, off_ksup, off_vsup, off_kpos, off_kval, off_vpos, off_vval, off_kdat, off_kbits,
+  int64_t off_kblk, off_vblk, off_ksup, off_vsup, off_kpos, off_kval, off_vpos, off_vval, off_kdat, off_kbits,
       total;
 };
 
@@ -517,7 +517,6 @@ int nuq_plan(int32_t BH, int32_t S, int32_t D, int32_t bits, int32_t start_pos, 
   p.k_blk_x = (S + rpb - 1) / rpb;
   p.v_nblk = p.val_cpc == 0 ? (int64_t)BH * S : ((int64_t)BH * S + (64 / p.val_cpc) - 1) / (64 / p.val_cpc);
   int64_t o = 0;
-  p.off_ctr = o; o = align256(o + 16);
   p.off_kblk = o; o = align256(o + p.k_blk_x * BH * 8);
   p.off_vblk = o; o = align256(o + p.v_nblk * 8);
   p.off_ksup = o; o = align256(o + (p.k_blk_x * BH + 63) / 64 * 4);
@@ -606,7 +605,6 @@ int nuq_call(const uint16_t *keys, const uint16_t *values, int32_t BH, int32_t S
   a.out_counts = out_counts;
   a.k_recon = k_recon;
   a.v_recon = v_recon;
-  a.ws_ctr = reinterpret_cast<uint32_t *>(ws + p.off_ctr);
   a.ws_kblk = reinterpret_cast<uint32_t *>(ws + p.off_kblk);
   a.ws_vblk = reinterpret_cast<uint32_t *>(ws + p.off_vblk);
   a.ws_ksup = reinterpret_cast<uint32_t *>(ws + p.off_ksup);

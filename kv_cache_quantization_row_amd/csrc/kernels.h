@@ -76,7 +76,6 @@ struct NuqArgs {
   int64_t *out_counts;             // [2]
   uint16_t *k_recon, *v_recon;     // optional
   // workspace
-  uint32_t *ws_ctr;                // 4 counters
   uint32_t *ws_kblk, *ws_vblk;     // per workgroup (staging base, count)
   uint32_t *ws_ksup, *ws_vsup;     // per 64 workgroups: sum of their counts
   int32_t *ws_kpos, *ws_vpos;      // staging

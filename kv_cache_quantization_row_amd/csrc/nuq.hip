@@ -1288,10 +1288,9 @@ __device__ void kb_lloyd_rows(const uint64_t *pre, const uint32_t *end, const ui
 }  // namespace
 
 // ================================================================== kernels
-// staging counters and the per-64-workgroup count sums start at zero
+// the per-64-workgroup count sums start at zero
 __global__ __launch_bounds__(256) void nuq_zero(NuqArgs a) {
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x, nthr = (int64_t)gridDim.x * 256;
-  if (g < 4) a.ws_ctr[g] = 0;
   const int64_t ks = (a.k_blk_x * a.BH + 63) >> 6, vs = (a.v_nblk + 63) >> 6;
   for (int64_t i = g; i < ks; i += nthr) a.ws_ksup[i] = 0;
   for (int64_t i = g; i < vs; i += nthr) a.ws_vsup[i] = 0;
@@ -2788,8 +2787,8 @@ hipError_t launch_bits(const NuqArgs &a, int key_cpc, int val_cpc, bool fork, hi
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = launch_values<BITS>(a, val_cpc, st)) != hipSuccess) return e;
   } else {
-    // the key fit starts first, right after the fork point; the counters
-    // are cleared on the second stream ahead of the value fit, and the key
+    // the key fit starts first, right after the fork point; the sums are
+    // cleared on the second stream ahead of the value fit, and the key
     // quantization (their other user) waits for that
     std::lock_guard<std::mutex> lock(g_fork_mu);
     Fork *f = nullptr;
