@@ -37,8 +37,8 @@
 // Keys at prefill: a counting sort of each channel's samples by the high byte
 // of their order key, then every query of the fit is a table read plus one
 // bucket scan (the "bucketed key fit" section below); sums there are int64.
-// The Lloyd iterations of up to 8 levels run four channels per wave, one
-// 16-lane row each ("Lloyd by rows").
+// The Lloyd iterations of up to 8 levels run two channels per wave, 32 lanes
+// each ("Lloyd by rows").
 // Up to 4,096 vectors the value fit runs one token per wave instead
 // (value_wave_body: keys sorted across the wave, sorted keys and exact
 // prefix sums in the wave's LDS, one level per lane); beyond that at D = 128
@@ -1122,30 +1122,39 @@ __device__ void kb_lloyd_wave(const V &v, const KbInl &r, int iters, float &lev_
 }
 
 // ------------------------------------------------------------------ Lloyd by rows
-// The Lloyd iterations of four channels per wave, one 16-lane row each (up
-// to KB_ROW_MAX_L levels). Every lane of a row holds the channel's whole
-// level table and every cut; the bucket scans stride over the row's 16
-// lanes, and a row sum takes four DPP adds (no readlane). Each lane j < L
-// of the row computes the mean of cell j, and the row reads the new table
-// back from its LDS slot. The arithmetic is that of kb_lloyd_wave: the same
-// cut keys, exact int64 cell sums, binary32 means and ordering rule.
+// The Lloyd iterations of 64/G channels per wave, G lanes each (up to
+// KB_ROW_MAX_L levels). Every lane of a group holds the channel's whole level
+// table and every cut; the bucket scans stride over the group's G lanes, and
+// a group sum takes four DPP adds inside each 16-lane row (plus one
+// cross-row shuffle at G = 32; no readlane). Each lane j < L of the group
+// computes the mean of cell j, and the group reads the new table back from
+// its LDS slot. The arithmetic is that of kb_lloyd_wave: the same cut keys,
+// exact int64 cell sums, binary32 means and ordering rule. G = 32 (two
+// channels per wave, four waves of a workgroup) against G = 16 (four
+// channels per wave, two waves): 75 against 81 us for the key fit alone,
+// the second wave per SIMD hiding the iteration's latency.
 constexpr int KB_ROW_MAX_L = 8;
 
-// sum over the lane's 16-lane row, in every lane of the row
+constexpr int KB_G = 32;  // lanes per channel in the Lloyd loop (16 or 32)
+
+// sum over the lane's group of G lanes (one or two 16-lane rows), in every
+// lane of the group
+template <int G>
 __device__ __forceinline__ uint32_t row_sum(uint32_t v) {
   v += dppm<DPP_XOR1>(v);
   v += dppm<DPP_XOR2>(v);
   v += dppm<DPP_HALF_MIRROR>(v);
   v += dppm<DPP_MIRROR>(v);
+  if constexpr (G == 32) v += (uint32_t)__shfl_xor((int)v, 16);
   return v;
 }
 
-// kb_le_many for the row's channel (tables pre / end, bucketed low bytes
+// kb_le_many for the group's channel (tables pre / end, bucketed low bytes
 // dat): count and exact sum at every cut whose bit is set in need
-template <int NC>
+template <int NC, int G>
 __device__ __forceinline__ void kb_le_rows(const uint64_t *pre, const uint32_t *end, const uint8_t *dat,
                                            const uint32_t *T, uint32_t need, uint32_t *cnt, int64_t *sum) {
-  const uint32_t gl = threadIdx.x & 15;
+  const uint32_t gl = threadIdx.x & (G - 1);
   uint32_t s0[NC], e0[NC], c[NC], sl[NC], t2[NC];
   uint32_t maxw = 0;
 #pragma unroll
@@ -1158,7 +1167,7 @@ __device__ __forceinline__ void kb_le_rows(const uint64_t *pre, const uint32_t *
     e0[j] = nd ? end[b] : 0u;
     if (e0[j] > s0[j]) maxw = max(maxw, ((e0[j] + 3u) >> 2) - (s0[j] >> 2));
   }
-  for (uint32_t i = gl; i < maxw; i += 16) {
+  for (uint32_t i = gl; i < maxw; i += G) {
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
       const uint32_t p0 = ((s0[j] >> 2) + i) << 2;
@@ -1178,7 +1187,7 @@ __device__ __forceinline__ void kb_le_rows(const uint64_t *pre, const uint32_t *
     cnt[j] = 0;
     sum[j] = 0;
     if (!__any((need >> j) & 1u)) continue;
-    const uint32_t cc = row_sum(c[j]), ss = row_sum(sl[j]);
+    const uint32_t cc = row_sum<G>(c[j]), ss = row_sum<G>(sl[j]);
     const int b = (int)(T[j] >> 8);
     bool neg;
     int sh;
@@ -1191,12 +1200,12 @@ __device__ __forceinline__ void kb_le_rows(const uint64_t *pre, const uint32_t *
   }
 }
 
-// lev: the row's level table (ascending, in every lane); xch: the row's LDS
-// slot of L floats
-template <int L>
+// lev: the group's level table (ascending, in every lane); xch: the group's
+// LDS slot of L floats
+template <int L, int G>
 __device__ void kb_lloyd_rows(const uint64_t *pre, const uint32_t *end, const uint8_t *dat, float *xch,
                               const KbInl &r, int iters, float (&lev)[L]) {
-  const uint32_t gl = threadIdx.x & 15;
+  const uint32_t gl = threadIdx.x & (G - 1);
   uint32_t Tp[L - 1], Cu[L - 1];  // previous cut keys (none yet), counts at the cuts
   int64_t Su[L - 1];              // exact sums at the cuts
 #pragma unroll
@@ -1221,7 +1230,7 @@ __device__ void kb_lloyd_rows(const uint64_t *pre, const uint32_t *end, const ui
     }
     uint32_t qc[L - 1];
     int64_t qs[L - 1];
-    kb_le_rows<L - 1>(pre, end, dat, T, need, qc, qs);
+    kb_le_rows<L - 1, G>(pre, end, dat, T, need, qc, qs);
     uint32_t c_up = r.hi;
     int64_t s_up = r.s_hi;
 #pragma unroll
@@ -2666,20 +2675,21 @@ __global__ __launch_bounds__(KB_T) void nuq_key_fit_bk(NuqArgs a) {
   } else {
     // ---- Lloyd iterations by rows: wave w hands its channel over in its
     // histogram words (free now: the level table, then the inlier range), and
-    // waves 0 .. KB_CH/4 - 1 take four channels each
+    // waves 0 .. KB_CH/CPW - 1 take CPW channels each
     static_assert(KB_CH % 4 == 0 && 16 * 4 + sizeof(KbInl) <= 128 * 4, "row slots");
     float *slot = reinterpret_cast<float *>(hist + w * KB_HW);
     if (lane < L) slot[lane] = mine;
     if (lane == 0) *reinterpret_cast<KbInl *>(slot + 16) = inl;
     __syncthreads();
-    if (w >= KB_CH / 4) return;
-    const int c = 4 * w + (lane >> 4), gl = lane & 15;
+    constexpr int CPW = 64 / KB_G;  // channels per wave
+    if (w >= KB_CH / CPW) return;
+    const int c = CPW * w + lane / KB_G, gl = lane & (KB_G - 1);
     float *cs = reinterpret_cast<float *>(hist + c * KB_HW);
     const KbInl r = *reinterpret_cast<const KbInl *>(cs + 16);
     float lev[L];
 #pragma unroll
     for (int j = 0; j < L; ++j) lev[j] = cs[j];
-    if (n > 0) kb_lloyd_rows<L>(tab + c * 257, cur + c * 256, dat + (size_t)c * npad, cs, r, a.iters, lev);
+    if (n > 0) kb_lloyd_rows<L, KB_G>(tab + c * 257, cur + c * 256, dat + (size_t)c * npad, cs, r, a.iters, lev);
     float out = 0.0f;
 #pragma unroll
     for (int j = 0; j < L; ++j) out = gl == j ? lev[j] : out;
