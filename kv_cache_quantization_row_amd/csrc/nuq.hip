@@ -1312,8 +1312,10 @@ __global__ __launch_bounds__(256) void nuq_zero(NuqArgs a) {
 // (one 16-byte load). The workgroup first turns the D level tables into cut
 // keys in LDS; each lane then keeps the cut keys and |x| thresholds of its 8
 // channels in registers, packed in channel pairs, and classifies two samples
-// per packed 16-bit operation. Outliers are recorded as per-step bit masks
-// and written in flat order once the workgroup has reserved its staging range.
+// per packed 16-bit operation. Outliers are recorded as per-step bit masks:
+// in a small call written in flat order at the flat index of the workgroup's
+// first element, otherwise stored as the bitmap bytes of its rows (one byte
+// per row and lane) with the workgroup's count.
 constexpr int KQ_NIT = 8;
 template <int BITS>
 __device__ __forceinline__ void key_quant_body(const NuqArgs &a, int bx, int bh, int64_t blk) {
@@ -2470,13 +2472,13 @@ __global__ __launch_bounds__(256) void nuq_small(NuqArgs a, int64_t kn, int64_t 
 }
 __global__ __launch_bounds__(256) void nuq_place_small(NuqArgs a, int64_t kn, int64_t ntok) { place_all(a, kn, ntok); }
 
-// Place the staged side-channel entries in flat order, keys and values in one
-// launch: workgroups [0, kn) move the key-quant workgroups' entries, the rest
-// the value workgroups'. A producer workgroup b left (staging base, count) in
-// info[2b], info[2b+1] and added its count to sup[b/64]; the output offset of
-// b is the sum of the counts before it, read as whole groups of 64 from sup
-// plus single counts inside its own group. The last workgroup of each list
-// writes the list length.
+// Place the side-channel entries in flat order, keys and values in one
+// launch: workgroups [0, kn) expand the key blocks' bitmaps, the rest move the
+// value workgroups' staged entries. A producer workgroup b left its count in
+// info[2b + 1] (a value workgroup also its staging base in info[2b]) and
+// added it to sup[b/64]; the output offset of b is the sum of the counts
+// before it, read as whole groups of 64 from sup plus single counts inside
+// its own group. The last workgroup of each list writes the list length.
 __global__ __launch_bounds__(256) void nuq_place(NuqArgs a, int64_t kn) {
   __shared__ uint32_t red[4];
   const bool isv = (int64_t)blockIdx.x >= kn;
