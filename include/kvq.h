@@ -296,7 +296,10 @@ int64_t kvq_nuq_outlier_bound(int32_t BH, int32_t S, int32_t D, int32_t start_po
                               double frac, int32_t fit_keys, int32_t which);
 
 /* [host] Bytes of device workspace kvq_nuq_fit_quant needs for these sizes
- * (scratch: per-channel thresholds, per-block counters, outlier staging).
+ * (scratch: per-block outlier counts and their per-64-block sums, value
+ * outlier staging, the key outliers (a bitmap of one bit per key element, or
+ * staging slots in a call of at most 256 vectors), and for a key fit over
+ * more than 8,192 tokens one byte per key sample).
  * -1 on invalid arguments. */
 int64_t kvq_nuq_workspace_bytes(int32_t BH, int32_t S, int32_t D, int32_t bits, int32_t start_pos,
                                 int32_t n_sink, double frac, int32_t fit_keys);
