@@ -336,10 +336,12 @@ class NuqCache:
     dequantized K/V. With refit_interval = N > 0 the key tables are fit again
     on every N-th call after the one that last fit them, from that call's
     tokens (level lifecycle, read for decode calls of one token).
-    Nothing in a call waits for the device: outlier counts stay in device
-    memory and are read only when outlier_count or the byte properties are
-    asked for, and the per-call buffers for a given call length are
-    allocated once and reused.
+    Nothing in a call waits for the device: each call writes its outlier
+    counts to its own slot of a device log (summed on the device every
+    _CLOG calls) that is read only when outlier_count or the byte
+    properties are asked for; the per-call buffers for a given call length
+    are allocated once and reused; keys and values share one fp16 buffer,
+    so one copy appends a call's reconstructions.
     Byte accounting (a reading of the page's byte-accounting description):
     codes at `bits` per element, fp32 level tables and fp16 key thresholds
     (one key table held at a time), 6 bytes per outlier (fp16 value + int32
@@ -353,14 +355,19 @@ class NuqCache:
         self._bufs = {}  # (S, fit, start == 0) -> per-call buffers
         self._reset()
 
+    _CLOG = 1024  # count-log slots
+
     def _reset(self):
         self.keys = self.values = None
+        self._kv = None         # fp16 [2][B][H][cap][D]: keys, values
         self.offset = 0
         self.key_levels = self.key_thresh = None
         self.value_levels = None  # of the latest call
         self.sink_kept = 0
         self._kc = self._vc = self._kf = self._vf = 0  # host-known byte parts
-        self._counts = None     # device int64 [2]: outliers emitted since the last fold
+        self._counts = None     # device int64 [2]: outliers of folded-in count-log rounds
+        self._clog = None       # device int64 [_CLOG][2]: one slot per call
+        self._ci = 0            # next count-log slot
         self._folded = [0, 0]   # outliers already folded into the host totals
         self._shape = None
         self._since_fit = 0     # calls since the key tables were fit
@@ -381,8 +388,7 @@ class NuqCache:
             b = dict(kc=e(BH, S, cb, dt=torch.uint8), vc=e(BH, S, cb, dt=torch.uint8),
                      lists=[e(cap, dt=torch.int32), e(cap, dt=torch.int16), e(cap, dt=torch.int32),
                             e(cap, dt=torch.int16)],
-                     cnt=e(2, dt=torch.int64), ws=e(wsb, dt=torch.uint8),
-                     kr=e(BH, S, D, dt=torch.float16), vr=e(BH, S, D, dt=torch.float16))
+                     ws=e(wsb, dt=torch.uint8), kvr=e(2, BH, S, D, dt=torch.float16))
             self._bufs[key] = b
         return b
 
@@ -402,18 +408,24 @@ class NuqCache:
             self.key_levels = torch.empty((BH, D, L), dtype=torch.float32, device=d)
             self.key_thresh = torch.empty((BH, D), dtype=torch.int16, device=d)
             self._counts = torch.zeros(2, dtype=torch.int64, device=d)
+            self._clog = torch.zeros((self._CLOG, 2), dtype=torch.int64, device=d)
+            self._ci = 0
+        if self._ci == self._CLOG:  # a full log: fold it on the device
+            self._counts += self._clog.sum(0)
+            self._ci = 0
         k = keys.reshape(BH, S, D).contiguous()
         v = values.reshape(BH, S, D).contiguous()
         b = self._call_buffers(BH, S, D, fit, d)
         vl = torch.empty((BH, S, L), dtype=torch.float32, device=d)  # kept as value_levels
+        cnt = self._clog[self._ci]
         kvq.kvq_nuq_fit_quant(k, v, self.offset, self.bits, self.outlier_fraction, self.lloyd_iters, self.n_sink,
-                              fit, self.key_levels, self.key_thresh, vl, b["kc"], b["vc"], *b["lists"], b["cnt"],
-                              b["ws"], b["kr"], b["vr"])
-        self._counts += b["cnt"]
+                              fit, self.key_levels, self.key_thresh, vl, b["kc"], b["vc"], *b["lists"], cnt,
+                              b["ws"], b["kvr"][0], b["kvr"][1])
+        self._ci += 1
         sinks = min(self.n_sink, S) if self.offset == 0 else 0
         self.sink_kept += sinks
         self.value_levels = vl
-        self._last = b
+        self._last = dict(b, cnt=cnt)
         codes = BH * S * D * self.bits // 8
         sink_bytes = BH * sinks * D * 2
         self._kc += codes + sink_bytes + (BH * D * (L * 4 + 2) if first else 0)
@@ -422,10 +434,14 @@ class NuqCache:
         self._kf += BH * S * D * 2
         self._vf += BH * S * D * 2
         end = self.offset + S
-        self.keys = _fp16_buffer(self.keys, B, H, end, D, self.step, d)
-        self.values = _fp16_buffer(self.values, B, H, end, D, self.step, d)
-        self.keys[:, :, self.offset:end].copy_(b["kr"].view(B, H, S, D))
-        self.values[:, :, self.offset:end].copy_(b["vr"].view(B, H, S, D))
+        if self._kv is None or self._kv.shape[3] < end:
+            cap = -(-end // self.step) * self.step
+            kv = torch.empty((2, B, H, cap, D), dtype=torch.float16, device=d)
+            if self._kv is not None:
+                kv[:, :, :, : self._kv.shape[3]].copy_(self._kv)
+            self._kv = kv
+            self.keys, self.values = kv[0], kv[1]
+        self._kv[:, :, :, self.offset:end].copy_(b["kvr"].view(2, B, H, S, D))
         self.offset = end
         return self.keys[:, :, : self.offset], self.values[:, :, : self.offset]
 
@@ -434,8 +450,9 @@ class NuqCache:
         """Move the device outlier counts into the host totals (one sync)."""
         if self._counts is None:
             return
-        c = [int(x) for x in self._counts.cpu()]
+        c = [int(x) for x in (self._counts + self._clog[: self._ci].sum(0)).cpu()]
         self._counts.zero_()
+        self._ci = 0
         self._kc += 6 * c[0]
         self._vc += 6 * c[1]
         self._folded[0] += c[0]

@@ -195,6 +195,28 @@ def test_nuq_cache_lifecycle():
     push(1, "second sequence decode")
 
 
+def test_nuq_cache_count_log_rounds():
+    """Outlier counts go to a count log of 3 slots over more calls than it
+    holds, read only at the end: the device-side sums of full logs plus the
+    final read give the model's total, and the returned K/V match after every
+    call."""
+    say("nuq cache count log")
+    d = dev()
+    B, H, D, bits = 1, 4, 128, 3
+    n = 64 + 10
+    kt = inputs.student_t((B * H, n, D), 4, seed=41).view(B, H, n, D)
+    vt = inputs.student_t((B * H, n, D), 4, seed=42).view(B, H, n, D)
+    kn, vn = u16(kt), u16(vt)
+    c, m = caches.NuqCache(bits, 0.05, 8, 4), NuqCacheModel(bits, 0.05, 8, 4)
+    c._CLOG = 3
+    for t0, t1 in [(0, 64)] + [(t, t + 1) for t in range(64, n)]:
+        ko, vo = c.update_and_fetch(kt[:, :, t0:t1].to(d).contiguous(), vt[:, :, t0:t1].to(d).contiguous())
+        m.update(kn[:, :, t0:t1], vn[:, :, t0:t1])
+        assert first_diff(u16(ko), m.k) is None and first_diff(u16(vo), m.v) is None, t1
+    assert m.outlier_count > 0
+    assert c.outlier_count == m.outlier_count
+
+
 @pytest.mark.parametrize("bits", [6, 8, 4])
 def test_paged_sym_cache_lifecycle(bits):
     """Three sequences share a small page pool: batched appends, decode steps,
